@@ -1,0 +1,188 @@
+"""Python binding of the CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU
+baseline may import this package.  The HIP library and its binding never do.
+
+Every function takes and returns float64 numpy arrays in the layouts the
+pages' convolution uses: x NCHW, W OIHW, y/g NCHW, col (C*kH*kW) x (B*OH*OW)
+row-major; GEMM operands packed as the two transpose-flag index formulas
+("Transpose via Flags", directcompute-nn page) describe.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP) into oracle/liboracle.so."""
+    if not force and os.path.exists(LIB_PATH) and \
+            os.path.getmtime(LIB_PATH) >= os.path.getmtime(SRC_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-Wextra", "-o", tmp, SRC_PATH]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run oracle.build() or __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(ctypes.c_double)
+        L = ctypes.c_longlong
+        conv_args = [L] * 9
+        lib.oracle_conv_forward.argtypes = [P, P, P, P] + conv_args
+        lib.oracle_conv_backward_filter.argtypes = [P, P, P] + conv_args
+        lib.oracle_conv_backward_data.argtypes = [P, P, P] + conv_args
+        lib.oracle_conv_backward_bias.argtypes = [P, P, L, L, L]
+        lib.oracle_gemm.argtypes = [P, P, P, L, L, L, ctypes.c_int]
+        lib.oracle_im2col_spec.argtypes = [P, P] + [L] * 8
+        lib.oracle_col2im_spec.argtypes = [P, P] + [L] * 8
+        lib.oracle_out_dims.argtypes = [L] * 6 + [ctypes.POINTER(L)] * 2
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def out_dims(H: int, W: int, kH: int, kW: int, s: int, p: int) -> Tuple[int, int]:
+    oh, ow = ctypes.c_longlong(), ctypes.c_longlong()
+    rc = _load().oracle_out_dims(H, W, kH, kW, s, p, ctypes.byref(oh), ctypes.byref(ow))
+    if rc != 0:
+        raise ValueError("invalid convolution geometry")
+    return int(oh.value), int(ow.value)
+
+
+def _geom(x_shape, w_shape, stride, padding):
+    B, C, H, W = x_shape
+    O, C2, kH, kW = w_shape
+    if C != C2:
+        raise ValueError("channel mismatch between x and W")
+    OH, OW = out_dims(H, W, kH, kW, stride, padding)
+    if OH < 1 or OW < 1:
+        raise ValueError("kernel larger than the padded input")
+    return B, C, H, W, O, kH, kW, OH, OW
+
+
+def conv_forward(x, w, bias=None, stride=1, padding=0) -> np.ndarray:
+    """y = conv(x; W) + bias, direct summation over the kernel window."""
+    x, w = _f64(x), _f64(w)
+    B, C, H, W, O, kH, kW, OH, OW = _geom(x.shape, w.shape, stride, padding)
+    b = None if bias is None else _f64(bias)
+    y = np.empty((B, O, OH, OW), dtype=np.float64)
+    rc = _load().oracle_conv_forward(_ptr(x), _ptr(w), _ptr(b), _ptr(y),
+                                     B, C, H, W, O, kH, kW, stride, padding)
+    if rc != 0:
+        raise ValueError("oracle_conv_forward rejected the shape")
+    return y
+
+
+def conv_backward_filter(x, g, w_shape, stride=1, padding=0) -> np.ndarray:
+    x, g = _f64(x), _f64(g)
+    B, C, H, W, O, kH, kW, OH, OW = _geom(x.shape, w_shape, stride, padding)
+    if g.shape != (B, O, OH, OW):
+        raise ValueError("g shape mismatch")
+    dw = np.empty((O, C, kH, kW), dtype=np.float64)
+    rc = _load().oracle_conv_backward_filter(_ptr(x), _ptr(g), _ptr(dw),
+                                             B, C, H, W, O, kH, kW, stride, padding)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward_filter rejected the shape")
+    return dw
+
+
+def conv_backward_bias(g) -> np.ndarray:
+    g = _f64(g)
+    B, O = g.shape[0], g.shape[1]
+    P = int(np.prod(g.shape[2:]))
+    db = np.empty((O,), dtype=np.float64)
+    rc = _load().oracle_conv_backward_bias(_ptr(g), _ptr(db), B, O, P)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward_bias rejected the shape")
+    return db
+
+
+def conv_backward_data(g, w, x_shape, stride=1, padding=0) -> np.ndarray:
+    g, w = _f64(g), _f64(w)
+    B, C, H, W, O, kH, kW, OH, OW = _geom(x_shape, w.shape, stride, padding)
+    if g.shape != (B, O, OH, OW):
+        raise ValueError("g shape mismatch")
+    dx = np.empty((B, C, H, W), dtype=np.float64)
+    rc = _load().oracle_conv_backward_data(_ptr(g), _ptr(w), _ptr(dx),
+                                           B, C, H, W, O, kH, kW, stride, padding)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward_data rejected the shape")
+    return dx
+
+
+def gemm(A, Bm, M: int, K: int, N: int, flags: int) -> np.ndarray:
+    """C[M,N] = op(A) op(B) from packed storage, per the flag index formulas."""
+    A, Bm = _f64(A).reshape(-1), _f64(Bm).reshape(-1)
+    if A.size != M * K or Bm.size != K * N:
+        raise ValueError("operand size mismatch")
+    C = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm(_ptr(A), _ptr(Bm), _ptr(C), M, K, N, int(flags))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected the arguments")
+    return C
+
+
+def im2col_spec(x, kH: int, kW: int, stride: int, padding: int) -> np.ndarray:
+    x = _f64(x)
+    B, C, H, W = x.shape
+    OH, OW = out_dims(H, W, kH, kW, stride, padding)
+    col = np.empty((C * kH * kW, B * OH * OW), dtype=np.float64)
+    rc = _load().oracle_im2col_spec(_ptr(x), _ptr(col), B, C, H, W, kH, kW,
+                                    stride, padding)
+    if rc != 0:
+        raise ValueError("oracle_im2col_spec rejected the shape")
+    return col
+
+
+def col2im_spec(col, x_shape, kH: int, kW: int, stride: int, padding: int) -> np.ndarray:
+    col = _f64(col)
+    B, C, H, W = x_shape
+    OH, OW = out_dims(H, W, kH, kW, stride, padding)
+    if col.shape != (C * kH * kW, B * OH * OW):
+        raise ValueError("col shape mismatch")
+    dx = np.empty((B, C, H, W), dtype=np.float64)
+    rc = _load().oracle_col2im_spec(_ptr(col), _ptr(dx), B, C, H, W, kH, kW,
+                                    stride, padding)
+    if rc != 0:
+        raise ValueError("oracle_col2im_spec rejected the shape")
+    return dx
+

@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: large CPU oracle runs")
+
+
+def _ensure_oracle():
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+
+
+_ensure_oracle()
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    return oracle
