@@ -1,0 +1,494 @@
+// C ABI of libd4r_conv (declared in include/d4r_conv.h): argument
+// validation, output extents, workspace layout, GEMM tile / split-K choice
+// and the launch sequence of each pass.  Everything is validated before the
+// first HIP call, so an invalid call enqueues nothing.
+//
+// Pass sequences (directcompute-nn page, "Convolution: The im2col
+// Approach"):
+//   forward          im2col(x) -> col;  GEMM NN  Wmat[O x Kc] * col[Kc x N]
+//                    with the conv_reshape + bias store fused in its epilogue
+//   backward_data    dy -> Gt[N x O] (reshape, transposed), W -> Wt[Kc x O];
+//                    GEMM dcol[Kc x N] = Wmat^T * G, both operands read with
+//                    k contiguous; col2im(dcol) -> dx
+//   backward_filter  [im2col(x) -> col]; dy -> G[O x N];
+//                    GEMM NT  dW[O x Kc] = G * col^T, split over k with
+//                    partial sums reduced in a fixed order; db by reduction
+#include <new>
+#include <stdio.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include "../../include/d4r_conv.h"
+#include "internal.hpp"
+
+using namespace d4r;
+
+namespace {
+
+thread_local char g_err[512];
+
+d4r_status fail(d4r_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+d4r_status ok()
+{
+    g_err[0] = 0;
+    return D4R_OK;
+}
+
+constexpr long long kMaxElems = 0x7fffffffLL;  // every tensor < 2^31 elements
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct GemmPlan {
+    int cfg;
+    int splits;
+    int k_per_split;
+};
+
+// Tile and split-K choice from the problem shape and the chip's 256 compute
+// units: whole-chip coverage needs several hundred workgroups, and each
+// split keeps at least four K stages.
+GemmPlan plan_gemm(int M, int N, int K, int dt)
+{
+    GemmPlan pl;
+    if (M <= 32)
+        pl.cfg = TILE_32x128;
+    else if (M <= 64 || N <= 64)
+        pl.cfg = TILE_64x64;
+    else if (M % 128 != 0 && M % 96 == 0 && M <= 192)
+        pl.cfg = TILE_96x128;
+    else
+        pl.cfg = TILE_128x128;
+    TileShape ts = tile_shape(pl.cfg);
+    const int bk = gemm_bk(dt);
+    const long long tiles = (long long)((M + ts.bm - 1) / ts.bm) * ((N + ts.bn - 1) / ts.bn);
+    const int ktiles = (K + bk - 1) / bk;
+    int splits = 1;
+    if (tiles < 256) {
+        long long want = (512 + tiles - 1) / tiles;
+        long long cap = ktiles / 4;
+        if (want > cap)
+            want = cap;
+        if (want > 256)
+            want = 256;
+        if (want > 1)
+            splits = (int)want;
+    }
+    int kts_per = (ktiles + splits - 1) / splits;
+    pl.k_per_split = kts_per * bk;
+    pl.splits = (K + pl.k_per_split - 1) / pl.k_per_split;
+    if (pl.splits < 1)
+        pl.splits = 1;
+    return pl;
+}
+
+size_t plan_partial_bytes(const GemmPlan &pl, int M, int N)
+{
+    return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void *A, int lda,
+                    const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
+                    const float *bias, int P, float *partial, hipStream_t s)
+{
+    const int vw = dt == DT_F32 ? 4 : 8;
+    GemmParams p;
+    p.A = A;
+    p.B = B;
+    p.bias = bias;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.P = P;
+    p.k_per_split = pl.k_per_split;
+    p.splits = pl.splits;
+    p.a_vec = (lda % vw) == 0;
+    p.b_vec = (ldb % vw) == 0;
+    if (pl.splits > 1) {
+        p.C = partial;
+        p.ldc = N;
+        p.epi = EPI_ROWMAJOR;
+        p.c_split_stride = (long long)M * N;
+    } else {
+        p.C = C;
+        p.ldc = ldc;
+        p.epi = epi;
+        p.c_split_stride = 0;
+    }
+    hipError_t e = launch_gemm(dt, pl.cfg, a_kc, b_kc, p, s);
+    if (e != hipSuccess || pl.splits == 1)
+        return e;
+    return launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, s);
+}
+
+bool valid_dtype(int dt) { return dt == D4R_F32 || dt == D4R_F16 || dt == D4R_BF16; }
+
+}  // namespace
+
+struct d4r_conv {
+    ConvGeom g;
+    int dt;
+    int es;
+    GemmPlan fwd, bwd_data, bwd_filter;
+    int bias_splits;
+    size_t off_g, off_wt, off_bias, off_big, ws_bytes;
+    size_t col_bytes;
+};
+
+namespace d4r {
+
+int gemm_bk(int dt) { return dt == DT_F32 ? 32 : 64; }
+
+hipError_t launch_gemm_f32(int, bool, bool, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_f16(int, bool, bool, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_bf16(int, bool, bool, const GemmParams &, hipStream_t);
+
+hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
+{
+    switch (dt) {
+    case DT_F32: return launch_gemm_f32(cfg, a_kc, b_kc, p, s);
+    case DT_F16: return launch_gemm_f16(cfg, a_kc, b_kc, p, s);
+    default: return launch_gemm_bf16(cfg, a_kc, b_kc, p, s);
+    }
+}
+
+}  // namespace d4r
+
+extern "C" {
+
+const char *d4r_status_string(d4r_status s)
+{
+    switch (s) {
+    case D4R_OK: return "D4R_OK";
+    case D4R_ERR_INVALID_ARG: return "D4R_ERR_INVALID_ARG";
+    case D4R_ERR_UNSUPPORTED: return "D4R_ERR_UNSUPPORTED";
+    case D4R_ERR_WORKSPACE: return "D4R_ERR_WORKSPACE";
+    case D4R_ERR_LAUNCH: return "D4R_ERR_LAUNCH";
+    case D4R_ERR_INTERNAL: return "D4R_ERR_INTERNAL";
+    }
+    return "unknown d4r_status";
+}
+
+const char *d4r_last_error(void) { return g_err; }
+
+d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW, int kH, int kW,
+                           int stride, int padding, int outC, d4r_dtype dtype)
+{
+    if (!out)
+        return fail(D4R_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (batch < 1 || inC < 1 || inH < 1 || inW < 1 || kH < 1 || kW < 1 || outC < 1)
+        return fail(D4R_ERR_INVALID_ARG, "every size must be >= 1");
+    if (stride < 1)
+        return fail(D4R_ERR_INVALID_ARG, "stride must be >= 1");
+    if (padding < 0)
+        return fail(D4R_ERR_INVALID_ARG, "padding must be >= 0");
+    if (!valid_dtype(dtype))
+        return fail(D4R_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    long long span_h = (long long)inH + 2LL * padding - kH;
+    long long span_w = (long long)inW + 2LL * padding - kW;
+    if (span_h < 0 || span_w < 0)
+        return fail(D4R_ERR_INVALID_ARG, "kernel larger than the padded input");
+    long long OH = span_h / stride + 1, OW = span_w / stride + 1;
+    long long P = OH * OW, Kc = (long long)inC * kH * kW, N = (long long)batch * P;
+    long long x_el = (long long)batch * inC * inH * inW;
+    long long y_el = (long long)outC * N;
+    long long w_el = (long long)outC * Kc;
+    long long col_el = Kc * N;
+    if (x_el > kMaxElems || y_el > kMaxElems || w_el > kMaxElems || col_el > kMaxElems)
+        return fail(D4R_ERR_UNSUPPORTED, "a tensor or the col matrix reaches 2^31 elements");
+
+    d4r_conv *h = new (std::nothrow) d4r_conv;
+    if (!h)
+        return fail(D4R_ERR_INTERNAL, "host allocation failed");
+    ConvGeom &g = h->g;
+    g.B = batch; g.C = inC; g.H = inH; g.W = inW; g.O = outC; g.kH = kH; g.kW = kW;
+    g.s = stride; g.p = padding; g.OH = (int)OH; g.OW = (int)OW;
+    g.P = (int)P; g.Kc = (int)Kc; g.N = (int)N;
+    h->dt = dtype;
+    h->es = dt_size(dtype);
+    h->fwd = plan_gemm(g.O, g.N, g.Kc, dtype);
+    h->bwd_data = plan_gemm(g.Kc, g.N, g.O, dtype);
+    h->bwd_filter = plan_gemm(g.O, g.Kc, g.N, dtype);
+    h->bias_splits = bias_grad_splits(g);
+
+    h->col_bytes = (size_t)col_el * h->es;
+    size_t off = align_up(h->col_bytes);
+    h->off_g = off;
+    off += align_up((size_t)y_el * h->es);
+    h->off_wt = off;
+    off += align_up((size_t)w_el * h->es);
+    h->off_bias = off;
+    off += align_up((size_t)outC * h->bias_splits * sizeof(float));
+    h->off_big = off;
+    size_t big = plan_partial_bytes(h->fwd, g.O, g.N);
+    size_t dd = align_up((size_t)col_el * sizeof(float)) + plan_partial_bytes(h->bwd_data, g.Kc, g.N);
+    if (dd > big)
+        big = dd;
+    size_t wf = plan_partial_bytes(h->bwd_filter, g.O, g.Kc);
+    if (wf > big)
+        big = wf;
+    h->ws_bytes = off + align_up(big);
+    *out = h;
+    return ok();
+}
+
+d4r_status d4r_conv_destroy(d4r_conv_t h)
+{
+    delete h;
+    return ok();
+}
+
+d4r_status d4r_conv_output_dims(d4r_conv_t h, int *outH, int *outW)
+{
+    if (!h || !outH || !outW)
+        return fail(D4R_ERR_INVALID_ARG, "NULL argument");
+    *outH = h->g.OH;
+    *outW = h->g.OW;
+    return ok();
+}
+
+d4r_status d4r_conv_workspace_size(d4r_conv_t h, size_t *bytes)
+{
+    if (!h || !bytes)
+        return fail(D4R_ERR_INVALID_ARG, "NULL argument");
+    *bytes = h->ws_bytes;
+    return ok();
+}
+
+namespace {
+
+d4r_status check_tensor(const void *p, const char *name)
+{
+    if (!p)
+        return fail(D4R_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, 16))
+        return fail(D4R_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return D4R_OK;
+}
+
+d4r_status check_vec(const void *p, const char *name)
+{
+    if (p && !aligned(p, 4))
+        return fail(D4R_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+    return D4R_OK;
+}
+
+d4r_status check_ws(const d4r_conv *h, const void *ws, size_t ws_bytes)
+{
+    if (!ws)
+        return fail(D4R_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", h->ws_bytes);
+    if (!aligned(ws, kAlign))
+        return fail(D4R_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < h->ws_bytes)
+        return fail(D4R_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, h->ws_bytes);
+    return D4R_OK;
+}
+
+d4r_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(D4R_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define D4R_TRY(x)                   \
+    do {                             \
+        d4r_status st_ = (x);        \
+        if (st_ != D4R_OK)           \
+            return st_;              \
+    } while (0)
+
+#define D4R_LAUNCH(call, what)                       \
+    do {                                             \
+        hipError_t e_ = (call);                      \
+        if (e_ != hipSuccess)                        \
+            return launched(e_, what);               \
+    } while (0)
+
+}  // namespace
+
+d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const float *bias, float *y,
+                            void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(y, "y"));
+    D4R_TRY(check_vec(bias, "bias"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const ConvGeom &g = h->g;
+    char *wsb = (char *)ws;
+    void *col = wsb;
+    float *partial = (float *)(wsb + h->off_big);
+    D4R_LAUNCH(launch_im2col(h->dt, g, x, col, s), "im2col");
+    D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
+                        bias, g.P, partial, s),
+               "forward GEMM");
+    return ok();
+}
+
+d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws,
+                                  size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const ConvGeom &g = h->g;
+    char *wsb = (char *)ws;
+    void *gt = wsb + h->off_g;
+    void *wt = wsb + h->off_wt;
+    float *dcol = (float *)(wsb + h->off_big);
+    float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
+    // Gt[b*P + pix][o] = dy[b][o][pix]: a batch of O x P transposes
+    D4R_LAUNCH(launch_transpose(h->dt, g.B, g.O, g.P, dy, gt, s), "grad reshape");
+    D4R_LAUNCH(launch_transpose(h->dt, 1, g.O, g.Kc, w, wt, s), "filter transpose");
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, true, true, wt, g.O, gt, g.O, g.Kc, g.N, g.O, EPI_ROWMAJOR,
+                        dcol, g.N, nullptr, 0, partial, s),
+               "data-gradient GEMM");
+    D4R_LAUNCH(launch_col2im(g, dcol, dx, s), "col2im");
+    return ok();
+}
+
+d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy, float *dw, float *db,
+                                    int reuse_col, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    if (reuse_col != 0 && reuse_col != 1)
+        return fail(D4R_ERR_INVALID_ARG, "reuse_col must be 0 or 1");
+    if (reuse_col && x)
+        return fail(D4R_ERR_INVALID_ARG, "x must be NULL when reuse_col = 1");
+    if (!reuse_col)
+        D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dw, "dw"));
+    D4R_TRY(check_vec(db, "db"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const ConvGeom &g = h->g;
+    char *wsb = (char *)ws;
+    void *col = wsb;
+    void *G = wsb + h->off_g;
+    float *partial = (float *)(wsb + h->off_big);
+    if (!reuse_col)
+        D4R_LAUNCH(launch_im2col(h->dt, g, x, col, s), "im2col");
+    D4R_LAUNCH(launch_grad_reshape(h->dt, g, dy, G, s), "grad reshape");
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, true, true, G, g.N, col, g.N, g.O, g.Kc, g.N,
+                        EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s),
+               "filter-gradient GEMM");
+    if (db)
+        D4R_LAUNCH(launch_bias_grad(h->dt, g, dy, db, (float *)(wsb + h->off_bias), h->bias_splits, s),
+                   "bias gradient");
+    return ok();
+}
+
+d4r_status d4r_conv_im2col(d4r_conv_t h, const void *x, void *col, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(col, "col"));
+    D4R_LAUNCH(launch_im2col(h->dt, h->g, x, col, (hipStream_t)hip_stream), "im2col");
+    return ok();
+}
+
+d4r_status d4r_conv_col2im(d4r_conv_t h, const float *dcol, float *dx, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(dcol, "dcol"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_LAUNCH(launch_col2im(h->g, dcol, dx, (hipStream_t)hip_stream), "col2im");
+    return ok();
+}
+
+d4r_status d4r_conv_bias_grad(d4r_conv_t h, const void *dy, float *db, void *ws, size_t ws_bytes,
+                              void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(dy, "dy"));
+    if (!db)
+        return fail(D4R_ERR_INVALID_ARG, "db is NULL");
+    D4R_TRY(check_vec(db, "db"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    D4R_LAUNCH(launch_bias_grad(h->dt, h->g, dy, db, (float *)((char *)ws + h->off_bias), h->bias_splits,
+                                (hipStream_t)hip_stream),
+               "bias gradient");
+    return ok();
+}
+
+namespace {
+
+d4r_status check_gemm_args(int M, int K, int N, int flags, int dtype)
+{
+    if (M < 1 || K < 1 || N < 1)
+        return fail(D4R_ERR_INVALID_ARG, "M, K and N must be >= 1");
+    if (flags < 0 || flags > 3)
+        return fail(D4R_ERR_INVALID_ARG, "flags must be 0..3");
+    if (!valid_dtype(dtype))
+        return fail(D4R_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if ((long long)M * K > kMaxElems || (long long)K * N > kMaxElems || (long long)M * N > kMaxElems)
+        return fail(D4R_ERR_UNSUPPORTED, "an operand reaches 2^31 elements");
+    return D4R_OK;
+}
+
+}  // namespace
+
+d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dtype, size_t *bytes)
+{
+    D4R_TRY(check_gemm_args(M, K, N, flags, dtype));
+    if (!bytes)
+        return fail(D4R_ERR_INVALID_ARG, "bytes is NULL");
+    GemmPlan pl = plan_gemm(M, N, K, dtype);
+    *bytes = plan_partial_bytes(pl, M, N);
+    return ok();
+}
+
+d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
+                    float *C, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    D4R_TRY(check_gemm_args(M, K, N, flags, dtype));
+    D4R_TRY(check_tensor(A, "A"));
+    D4R_TRY(check_tensor(B, "B"));
+    D4R_TRY(check_tensor(C, "C"));
+    GemmPlan pl = plan_gemm(M, N, K, dtype);
+    size_t need = plan_partial_bytes(pl, M, N);
+    if (need) {
+        if (!ws)
+            return fail(D4R_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+        if (!aligned(ws, kAlign))
+            return fail(D4R_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(D4R_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+    }
+    const bool a_kc = !(flags & 1);
+    const bool b_kc = (flags & 2) != 0;
+    const int lda = a_kc ? K : M;
+    const int ldb = b_kc ? K : N;
+    D4R_LAUNCH(run_gemm(dtype, pl, a_kc, b_kc, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
+                        (float *)ws, (hipStream_t)hip_stream),
+               "GEMM");
+    return ok();
+}
+
+}  // extern "C"

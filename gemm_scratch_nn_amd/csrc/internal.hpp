@@ -1,0 +1,87 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels of
+// libd4r_conv.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace d4r {
+
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+inline int dt_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// GEMM tile shapes: a workgroup is NWM x NWN wavefronts (64 lanes each); a
+// wavefront owns TM x TN blocks of 32x32 outputs.
+enum TileCfg : int {
+    TILE_128x128 = 0,  // 2x2 waves, 2x2 blocks
+    TILE_64x64 = 1,    // 2x2 waves, 1x1 block
+    TILE_32x128 = 2,   // 1x4 waves, 1x1 block (M <= 32)
+    TILE_96x128 = 3,   // 1x4 waves, 3x1 blocks (M = 96)
+    TILE_COUNT = 4
+};
+
+struct TileShape { int bm, bn; };
+inline TileShape tile_shape(int cfg)
+{
+    switch (cfg) {
+    case TILE_128x128: return {128, 128};
+    case TILE_64x64: return {64, 64};
+    case TILE_32x128: return {32, 128};
+    default: return {96, 128};
+    }
+}
+
+enum Epilogue : int {
+    EPI_ROWMAJOR = 0,  // C[m*ldc + n] (+ blockIdx.z * c_split_stride)
+    EPI_NCHW = 1       // y[((n/P)*M + m)*P + n%P] = acc + bias[m]
+};
+
+// C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
+// Operand "rows" are m for A and n for B.  a_kc / b_kc: the operand is
+// stored with k contiguous (A[m*lda + k], B[n*ldb + k]); otherwise the row
+// index is contiguous (A[k*lda + m], B[k*ldb + n]).
+struct GemmParams {
+    const void *A;
+    const void *B;
+    float *C;
+    const float *bias;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int P;              // EPI_NCHW: pixels per image
+    int epi;
+    int k_per_split;    // multiple of the tile's K depth
+    int splits;
+    long long c_split_stride;
+    int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned)
+};
+
+hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p,
+                       hipStream_t s);
+int gemm_bk(int dt);  // K depth of one LDS stage, in elements
+
+struct ConvGeom {
+    int B, C, H, W, O, kH, kW, s, p, OH, OW;
+    int P;    // OH*OW
+    int Kc;   // C*kH*kW
+    int N;    // B*P
+};
+
+hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s);
+hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s);
+// G[o][n] = dy[b][o][pix], n = b*P + pix  (O x N row-major)
+hipError_t launch_grad_reshape(int dt, const ConvGeom &g, const void *dy, void *G, hipStream_t s);
+// out[b][c][r] = in[b][r][c] for a batch of R x Cc matrices of dt elements
+hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, void *out,
+                            hipStream_t s);
+// db[o] = sum_{b,pix} dy[b][o][pix]; partial holds O*splits floats
+hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db,
+                            float *partial, int splits, hipStream_t s);
+int bias_grad_splits(const ConvGeom &g);
+// out = sum over s of part[s] (fixed order) with the GEMM epilogue
+hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
+                                long long split_stride, int epi, float *C, int ldc,
+                                const float *bias, int P, hipStream_t s);
+
+}  // namespace d4r

@@ -1,0 +1,200 @@
+/*
+ * d4r_conv.h -- C ABI of libd4r_conv.so: convolution lowered to matrix
+ * multiplication on AMD Instinct MI355X (gfx950).
+ *
+ * The method (directcompute-nn 0.1.0 page, "Convolution: The im2col
+ * Approach"):
+ *   forward   x --im2col--> col (C*kH*kW x B*OH*OW)
+ *             Cmat = Wmat (O x C*kH*kW) * col
+ *             y = conv_reshape(Cmat) + bias       -> (B, O, OH, OW)
+ *   backward  G = conv_grad_reshape(dy)           (O x B*OH*OW)
+ *             dW = G * col^T                      (matmul flags = 2)
+ *             dcol = Wmat^T * G                   (matmul flags = 1)
+ *             dx = col2im(dcol)
+ *             db[o] = sum of row o of G
+ * Transposes are expressed by the matmul flags ("Transpose via Flags"):
+ * flags & 1 reads A as stored transposed, flags & 2 reads B as stored
+ * transposed; no transpose kernels are run.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Geometry.  Square stride and symmetric zero padding (one value each, as
+ * the page's im2col parameter list has); kH and kW may differ.  Output
+ * extent OH = floor((inH + 2*padding - kH) / stride) + 1, likewise OW.  No
+ * dilation, no groups.
+ *
+ * Layouts (all packed, row-major, no leading dimensions):
+ *   x, dx       (batch, inC, inH, inW)        NCHW
+ *   w, dw       (outC, inC, kH, kW)           OIHW, i.e. Wmat O x Kc
+ *   y, dy       (batch, outC, OH, OW)         NCHW
+ *   bias, db    (outC)
+ *   col         Kc x N row-major, Kc = inC*kH*kW rows ordered (c, u, v) with
+ *               v fastest, N = batch*OH*OW columns ordered (b, i, j) with j
+ *               fastest; col[(c*kH+u)*kW+v][(b*OH+i)*OW+j] =
+ *               x[b][c][i*stride-padding+u][j*stride-padding+v], or 0 when
+ *               that position falls in the padding.
+ *
+ * Types.  x, w, dy and GEMM operands A, B are in the handle's / call's
+ * d4r_dtype (float32, IEEE binary16 or bfloat16).  bias, y, dx, dw, db and
+ * GEMM C are always float32.  Half-precision products accumulate in float32.
+ *
+ * Memory ownership.  Every pointer argument is a caller-owned device
+ * pointer (e.g. a torch tensor's data_ptr()).  The library never allocates,
+ * frees or keeps device memory.  Pointers to tensors must be 16-byte
+ * aligned, bias and db 4-byte aligned, ws 256-byte aligned.
+ *
+ * Workspace.  Scratch memory (the col matrix, the reshaped gradient, the
+ * float32 dcol, split-K partial sums) lives in a caller buffer ws of at least
+ * d4r_conv_workspace_size() bytes.  d4r_conv_forward leaves the col matrix
+ * of x at the start of ws; d4r_conv_backward_data does not touch that
+ * region, so a following d4r_conv_backward_filter with reuse_col = 1 and the
+ * same ws reuses it (the page saves the im2col buffer in forward for the
+ * filter gradient, "Memory Management").
+ *
+ * Streams.  hip_stream is a hipStream_t (NULL = the null stream).  Calls
+ * only enqueue kernels on it: no host synchronisation, no allocation.
+ * Results are deterministic: no atomics, fixed summation orders.
+ *
+ * Errors.  Every call returns a d4r_status.  All argument validation runs
+ * before any HIP call, so an invalid call enqueues nothing.  A kernel launch
+ * error is returned as D4R_ERR_LAUNCH; faults inside kernels surface at the
+ * caller's next synchronisation.  d4r_last_error() gives a thread-local
+ * message for the last failing call on the calling thread.
+ *
+ * Sizes.  Every tensor, col and dcol must hold fewer than 2^31 elements.
+ */
+#ifndef D4R_CONV_H
+#define D4R_CONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    D4R_F32 = 0,  /* IEEE binary32 */
+    D4R_F16 = 1,  /* IEEE binary16, float32 accumulation */
+    D4R_BF16 = 2  /* bfloat16, float32 accumulation */
+} d4r_dtype;
+
+typedef enum {
+    D4R_OK = 0,
+    D4R_ERR_INVALID_ARG = 1, /* bad size, NULL/misaligned pointer, bad flag or dtype */
+    D4R_ERR_UNSUPPORTED = 2, /* valid request this build cannot run (e.g. > 2^31 elements) */
+    D4R_ERR_WORKSPACE = 3,   /* ws NULL or smaller than the size query returned */
+    D4R_ERR_LAUNCH = 4,      /* a HIP launch failed */
+    D4R_ERR_INTERNAL = 5
+} d4r_status;
+
+typedef struct d4r_conv *d4r_conv_t;
+
+/*
+ * Create a host-side handle for one convolution shape.  Argument order is
+ * the problem statement's (batch, inC, inH, inW, kH, kW, stride, padding,
+ * outC); the page's im2col parameter block ("Constant Buffer Convention")
+ * carries the same fields.  Validates the geometry, computes OH/OW and
+ * chooses the GEMM tilings and split-K factors of the three passes.  The
+ * handle is immutable and may be shared between threads; free it with
+ * d4r_conv_destroy.  Errors: D4R_ERR_INVALID_ARG (out NULL, a size < 1,
+ * stride < 1, padding < 0, OH or OW < 1, unknown dtype),
+ * D4R_ERR_UNSUPPORTED (a tensor reaches 2^31 elements).
+ */
+d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW,
+                           int kH, int kW, int stride, int padding, int outC,
+                           d4r_dtype dtype);
+
+/* Free a handle.  NULL is accepted and ignored. */
+d4r_status d4r_conv_destroy(d4r_conv_t h);
+
+/* Output extent of the handle's convolution. */
+d4r_status d4r_conv_output_dims(d4r_conv_t h, int *outH, int *outW);
+
+/*
+ * Bytes of workspace every pass of this handle needs (the maximum over
+ * forward, backward_data and backward_filter); at least the size of col.
+ */
+d4r_status d4r_conv_workspace_size(d4r_conv_t h, size_t *bytes);
+
+/*
+ * Forward (page: im2col -> matmul flags 0 -> conv_reshape with bias):
+ * y = conv(x; w) + bias.  x, w in the handle's dtype; bias float32 or NULL
+ * (no bias); y float32.  Leaves col at the start of ws.
+ */
+d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w,
+                            const float *bias, float *y, void *ws,
+                            size_t ws_bytes, void *hip_stream);
+
+/*
+ * Data gradient (page: Input gradients = filters^T x grad_reshaped, then
+ * col2im): dx = col2im(Wmat^T * G).  w, dy in the handle's dtype; dx
+ * float32, fully overwritten.  dcol is float32 in ws, after the col region.
+ */
+d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy,
+                                  float *dx, void *ws, size_t ws_bytes,
+                                  void *hip_stream);
+
+/*
+ * Filter and bias gradients (page: Filter gradients = grad_reshaped x
+ * im2col_matrix^T, reusing the saved im2col; Bias gradients = per-channel
+ * sum of grad_reshaped): dw = G * col^T (float32, OIHW), db[o] = sum over
+ * batch and both spatial axes of dy[:, o] (float32; db NULL skips it).
+ * reuse_col = 0: x must be given and col is rebuilt in ws.  reuse_col = 1:
+ * x must be NULL and ws must still hold the col of the same x written by
+ * d4r_conv_forward (or d4r_conv_im2col) with this handle.
+ */
+d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
+                                    float *dw, float *db, int reuse_col,
+                                    void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Single steps of the path, for measurement and for checking the index
+ * maps bit for bit.
+ *
+ * d4r_conv_im2col: col (Kc x N, handle dtype) = im2col(x), the layout given
+ * above; a raw bit copy (no arithmetic).  col needs Kc*N elements.
+ *
+ * d4r_conv_col2im: dx (float32 NCHW) = col2im(dcol) for a float32 Kc x N
+ * dcol: a gather (no atomics); each dx element sums its in-image dcol
+ * entries in the order u ascending, then v ascending.
+ *
+ * d4r_conv_bias_grad: db[o] = sum_{b,i,j} dy[b][o][i][j] (float32).  Needs
+ * d4r_conv_workspace_size() bytes of ws for per-block partial sums.
+ */
+d4r_status d4r_conv_im2col(d4r_conv_t h, const void *x, void *col, void *hip_stream);
+d4r_status d4r_conv_col2im(d4r_conv_t h, const float *dcol, float *dx, void *hip_stream);
+d4r_status d4r_conv_bias_grad(d4r_conv_t h, const void *dy, float *db, void *ws,
+                              size_t ws_bytes, void *hip_stream);
+
+/*
+ * Workspace bytes d4r_gemm needs for these arguments (0 when it runs
+ * without split-K).  Same validation as d4r_gemm.
+ */
+d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dtype,
+                                   size_t *bytes);
+
+/*
+ * C = op(A) * op(B), C float32 M x N row-major, overwritten (no alpha/beta).
+ * The parameter block {M, K, N, flags} and the operand index formulas are
+ * the page's ("Matmul Shaders", "Transpose via Flags"):
+ *   op(A)[m][k] = A[m*K + k], or A[k*M + m] when flags & 1;
+ *   op(B)[k][n] = B[k*N + n], or B[n*K + k] when flags & 2.
+ * flags 0 = NN, 1 = TN, 2 = NT, 3 = TT.  A, B in dtype.
+ * Errors: D4R_ERR_INVALID_ARG for M, K or N < 1, flags outside 0..3, NULL or
+ * misaligned pointers; D4R_ERR_WORKSPACE when ws is short.
+ */
+d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A,
+                    const void *B, float *C, void *ws, size_t ws_bytes,
+                    void *hip_stream);
+
+/* Static string naming a status code. */
+const char *d4r_status_string(d4r_status s);
+
+/* Thread-local message describing the last failing call ("" if none). */
+const char *d4r_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* D4R_CONV_H */

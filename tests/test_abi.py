@@ -1,0 +1,184 @@
+"""C-ABI library: loads, exports every declared symbol, and rejects invalid
+calls on the host before any HIP call (so these run without a GPU)."""
+import pytest
+
+import gemm_scratch_nn_amd as d4r
+from gemm_scratch_nn_amd import D4RError, D4R_F32, D4R_F16, D4R_BF16
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 1 << 20            # a 16-byte aligned fake device address
+MISALIGNED = (1 << 20) + 4
+
+
+def test_every_declared_symbol_is_exported():
+    names = d4r.declared_functions()
+    expected = {"d4r_conv_create", "d4r_conv_destroy", "d4r_conv_output_dims",
+                "d4r_conv_workspace_size", "d4r_conv_forward", "d4r_conv_backward_data",
+                "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
+                "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
+                "d4r_status_string", "d4r_last_error"}
+    assert expected <= set(names)
+    for n in names:
+        assert d4r.exported(n), n
+        assert hasattr(d4r, n), f"python binding lacks {n}"
+
+
+def test_status_strings():
+    assert d4r.d4r_status_string(0) == "D4R_OK"
+    assert d4r.d4r_status_string(3) == "D4R_ERR_WORKSPACE"
+    assert "unknown" in d4r.d4r_status_string(99)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 5, 5, 3, 3, 1, 0, 1),      # batch 0
+    (1, 0, 5, 5, 3, 3, 1, 0, 1),      # inC 0
+    (1, 1, 5, 5, 3, 3, 0, 0, 1),      # stride 0
+    (1, 1, 5, 5, 3, 3, 1, -1, 1),     # negative padding
+    (1, 1, 2, 2, 5, 5, 1, 1, 1),      # kernel larger than padded input
+    (1, 1, 5, 5, 3, 3, 1, 0, 0),      # outC 0
+])
+def test_create_rejects_bad_geometry(args):
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_create(*args, D4R_F32)
+    assert e.value.status == INVALID
+
+
+def test_create_rejects_bad_dtype():
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_create(1, 1, 5, 5, 3, 3, 1, 0, 1, 7)
+    assert e.value.status == INVALID
+
+
+def test_create_rejects_2_pow_31():
+    # col = 2304 x (64*13*13*100) > 2^31 elements
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_create(6400, 256, 13, 13, 3, 3, 1, 1, 384, D4R_F32)
+    assert e.value.status == UNSUPPORTED
+
+
+@pytest.mark.parametrize("geom,dims", [
+    ((32, 3, 224, 224, 11, 11, 4, 2, 96), (55, 55)),
+    ((4, 256, 46, 80, 3, 3, 2, 1, 128), (23, 40)),
+    ((8, 1, 28, 28, 5, 5, 1, 0, 6), (24, 24)),
+    ((1, 1, 7, 5, 3, 2, 3, 1, 1), (3, 2)),
+])
+def test_output_dims_and_workspace(geom, dims):
+    for dt, es in ((D4R_F32, 4), (D4R_BF16, 2)):
+        h = d4r.d4r_conv_create(*geom, dt)
+        try:
+            assert d4r.d4r_conv_output_dims(h) == dims
+            B, C, H, W, kH, kW, s, p, O = geom
+            col = C * kH * kW * B * dims[0] * dims[1]
+            ws = d4r.d4r_conv_workspace_size(h)
+            # col (dtype) plus an f32 dcol at least
+            assert ws >= col * es + col * 4
+            assert ws % 256 == 0
+        finally:
+            d4r.d4r_conv_destroy(h)
+
+
+def test_destroy_null_is_ok():
+    d4r.d4r_conv_destroy(None)
+
+
+@pytest.fixture
+def handle():
+    h = d4r.d4r_conv_create(2, 3, 9, 9, 3, 3, 1, 1, 4, D4R_F32)
+    yield h
+    d4r.d4r_conv_destroy(h)
+
+
+def _ws(h):
+    return d4r.d4r_conv_workspace_size(h)
+
+
+def test_forward_argument_errors(handle):
+    ws = _ws(handle)
+    cases = [
+        ((None, FAKE, None, FAKE, FAKE, ws), INVALID),        # x NULL
+        ((FAKE, None, None, FAKE, FAKE, ws), INVALID),        # w NULL
+        ((FAKE, FAKE, None, None, FAKE, ws), INVALID),        # y NULL
+        ((MISALIGNED, FAKE, None, FAKE, FAKE, ws), INVALID),  # x misaligned
+        ((FAKE, FAKE, FAKE + 2, FAKE, FAKE, ws), INVALID),    # bias misaligned
+        ((FAKE, FAKE, None, FAKE, None, ws), WORKSPACE),      # ws NULL
+        ((FAKE, FAKE, None, FAKE, FAKE, ws - 1), WORKSPACE),  # ws short
+        ((FAKE, FAKE, None, FAKE, FAKE + 16, ws), INVALID),   # ws not 256-aligned
+    ]
+    for (x, w, b, y, wsp, nb), code in cases:
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_forward(handle, x, w, b, y, wsp, nb, stream=0)
+        assert e.value.status == code, (x, w, b, y, wsp, nb)
+        assert d4r.d4r_last_error()
+
+
+def test_backward_argument_errors(handle):
+    ws = _ws(handle)
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_backward_data(handle, FAKE, None, FAKE, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_backward_data(handle, FAKE, FAKE, FAKE, FAKE, 10, stream=0)
+    assert e.value.status == WORKSPACE
+    # reuse_col = 1 requires x == NULL
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_backward_filter(handle, FAKE, FAKE, FAKE, None, 1, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    # reuse_col = 0 requires x
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_backward_filter(handle, None, FAKE, FAKE, None, 0, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_backward_filter(handle, None, FAKE, FAKE, None, 2, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_bias_grad(handle, FAKE, None, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_im2col(handle, FAKE, MISALIGNED, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_col2im(handle, None, FAKE, stream=0)
+    assert e.value.status == INVALID
+
+
+def test_null_handle():
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_forward(None, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError):
+        d4r.d4r_conv_output_dims(None)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 4, 4, 0, D4R_F32), INVALID),
+    ((4, 4, 4, 4, D4R_F32), INVALID),
+    ((4, 4, 4, -1, D4R_F32), INVALID),
+    ((4, 4, 4, 0, 9), INVALID),
+    ((1 << 16, 1 << 16, 4, 0, D4R_F16), UNSUPPORTED),
+])
+def test_gemm_argument_errors(args, code):
+    M, K, N, flags, dt = args
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm_workspace_size(M, K, N, flags, dt)
+    assert e.value.status == code
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm(M, K, N, flags, dt, FAKE, FAKE, FAKE, None, 0, stream=0)
+    assert e.value.status == code
+
+
+def test_gemm_pointer_and_workspace_errors():
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm(64, 256, 120, 0, D4R_F32, None, FAKE, FAKE, None, 0, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm(64, 256, 120, 0, D4R_F32, FAKE, FAKE, MISALIGNED, None, 0, stream=0)
+    assert e.value.status == INVALID
+    # a long-K GEMM plans split-K and needs workspace
+    need = d4r.d4r_gemm_workspace_size(96, 96800, 363, 2, D4R_F32)
+    assert need > 0
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm(96, 96800, 363, 2, D4R_F32, FAKE, FAKE, FAKE, None, 0, stream=0)
+    assert e.value.status == WORKSPACE
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm(96, 96800, 363, 2, D4R_F32, FAKE, FAKE, FAKE, FAKE, need - 4, stream=0)
+    assert e.value.status == WORKSPACE

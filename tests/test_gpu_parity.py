@@ -1,0 +1,324 @@
+"""GPU parity: libd4r_conv (through its C ABI) against the CPU oracle.
+
+* im2col and col2im index maps: bit-exact against the oracle's index-map
+  specifications (iota codes, raw 16-bit patterns, small-integer dcol).
+* GEMM with flags 0..3 in f32 / f16 / bf16 on odd shapes.
+* Whole-tensor parity of forward, data, filter and bias gradients on every
+  workload at a batch the oracle finishes in seconds (several tiles, ragged
+  tails).
+* Full-size parity (the bench's launch configuration) on sampled channel /
+  image blocks, which the oracle computes exactly because y[b, o] depends
+  only on x[b] and W[o], dx[b, c] only on dy[b] and W[:, c], and dW[o, c]
+  only on x[:, c] and dy[:, o].
+Tolerances: relative Frobenius error 1e-5 (f32), 2e-3 (f16 / bf16 inputs
+with f32 accumulation).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_scratch_nn_amd as d4r
+import oracle
+import workloads as wl
+from gpu_util import DT_CODE, TOL, bits16, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+TINY = [
+    # (B, C, H, W, O, kH, kW, s, p)
+    (1, 1, 5, 5, 1, 3, 3, 1, 0),
+    (2, 3, 7, 6, 5, 3, 2, 1, 1),
+    (2, 2, 7, 7, 3, 5, 5, 2, 2),
+    (1, 3, 6, 7, 2, 2, 3, 3, 1),
+    (3, 1, 7, 5, 2, 1, 1, 4, 0),
+    (1, 2, 4, 4, 2, 2, 2, 1, 3),
+    (2, 2, 3, 3, 1, 3, 3, 1, 0),
+    (2, 5, 17, 19, 33, 3, 3, 1, 1),
+    (3, 7, 23, 29, 65, 5, 3, 2, 2),
+    (2, 17, 12, 12, 130, 3, 3, 1, 1),
+]
+
+
+def _shape(t):
+    B, C, H, W, O, kH, kW, s, p = t
+    return wl.ConvShape(B, C, H, W, kH, kW, s, p, O)
+
+
+def _plan(sh: wl.ConvShape, dt: str) -> d4r.ConvPlan:
+    return d4r.ConvPlan(sh.batch, sh.inC, sh.inH, sh.inW, sh.kH, sh.kW, sh.stride, sh.padding,
+                        sh.outC, DT_CODE[dt])
+
+
+# ---------------------------------------------------------------------------
+# index maps
+# ---------------------------------------------------------------------------
+
+def _im2col_cases():
+    cases = [(_shape(t), dt) for t in TINY for dt in ("f32", "bf16")]
+    for key, w in wl.WORKLOADS.items():
+        for layer in w.layers:
+            sh = layer.shape
+            cases.append((sh.with_batch(min(sh.batch, 2)), w.dtypes[-1]))
+    return cases
+
+
+@pytest.mark.parametrize("sh,dt", _im2col_cases(), ids=lambda v: str(v))
+def test_im2col_bit_exact(sh, dt):
+    _say("im2col", sh, dt)
+    n = int(np.prod(sh.x_shape()))
+    codes = np.arange(1, n + 1, dtype=np.int64)
+    if dt == "f32":
+        assert n < 2 ** 24
+        x = torch.from_numpy(codes.astype(np.float32).reshape(sh.x_shape())).cuda()
+        ref = oracle.im2col_spec(codes.reshape(sh.x_shape()).astype(np.float64), sh.kH, sh.kW,
+                                 sh.stride, sh.padding)
+    else:
+        pat = (codes * 2654435761) % 65521 + 1          # nonzero 16-bit patterns
+        x = torch.from_numpy(pat.astype(np.uint16).view(np.int16).reshape(sh.x_shape())).cuda()
+        x = x.view(torch.bfloat16 if dt == "bf16" else torch.float16)
+        ref = oracle.im2col_spec(pat.reshape(sh.x_shape()).astype(np.float64), sh.kH, sh.kW,
+                                 sh.stride, sh.padding)
+    pl = _plan(sh, dt)
+    col = torch.empty((sh.Kc, sh.N), dtype=x.dtype, device="cuda")
+    d4r.d4r_conv_im2col(pl.h, x, col)
+    torch.cuda.synchronize()
+    if dt == "f32":
+        got = col.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref)
+    else:
+        assert np.array_equal(bits16(col).astype(np.int64), ref.astype(np.int64))
+
+
+@pytest.mark.parametrize("sh", [_shape(t) for t in TINY] +
+                         [l.shape.with_batch(min(l.shape.batch, 2)) for w in wl.WORKLOADS.values()
+                          for l in w.layers], ids=str)
+def test_col2im_bit_exact(sh):
+    _say("col2im", sh)
+    rng = np.random.default_rng(31)
+    dcol = rng.integers(-8, 9, size=(sh.Kc, sh.N)).astype(np.float32)
+    ref = oracle.col2im_spec(dcol.astype(np.float64), sh.x_shape(), sh.kH, sh.kW, sh.stride, sh.padding)
+    pl = _plan(sh, "f32")
+    dx = torch.empty(sh.x_shape(), dtype=torch.float32, device="cuda")
+    d4r.d4r_conv_col2im(pl.h, torch.from_numpy(dcol).cuda(), dx)
+    torch.cuda.synchronize()
+    assert np.array_equal(dx.cpu().numpy().astype(np.float64), ref)
+
+
+def test_col2im_coverage_closed_form():
+    sh = wl.ConvShape(2, 3, 224, 224, 11, 11, 4, 2, 4)
+    pl = _plan(sh, "f32")
+    dx = torch.empty(sh.x_shape(), dtype=torch.float32, device="cuda")
+    d4r.d4r_conv_col2im(pl.h, torch.ones((sh.Kc, sh.N), device="cuda"), dx)
+    torch.cuda.synchronize()
+
+    def cov(n, k, s, p):
+        out = (n + 2 * p - k) // s + 1
+        return np.array([max(0, min(out - 1, (h + p) // s) - max(0, -((-(h + p - k + 1)) // s)) + 1)
+                         for h in range(n)])
+    expect = np.outer(cov(224, 11, 4, 2), cov(224, 11, 4, 2))
+    assert np.array_equal(dx.cpu().numpy()[1, 2], expect.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# GEMM with transpose flags
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 1, 1), (7, 17, 5), (16, 63, 65), (6, 25, 4608), (33, 129, 127),
+               (64, 256, 120), (64, 120, 84), (130, 300, 257), (96, 1000, 363),
+               (384, 72, 200), (257, 64, 129)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_parity(dt, flags, M, K, N):
+    rng = np.random.default_rng(M * 1000003 + K * 101 + N + flags)
+    a = wl.quantize(rng.normal(size=(K, M) if flags & 1 else (M, K)), dt)
+    b = wl.quantize(rng.normal(size=(N, K) if flags & 2 else (K, N)), dt)
+    ref = oracle.gemm(a.exact, b.exact, M, K, N, flags)
+    C = d4r.gemm(dev(a), dev(b), M, K, N, flags)
+    torch.cuda.synchronize()
+    err = rel_err(host(C), ref)
+    assert err < TOL[dt], err
+
+
+def test_gemm_long_k_split_f32():
+    """AlexNet conv1 filter-gradient shape: K = 96800 (split-K path)."""
+    M, K, N = 96, 96800, 363
+    rng = np.random.default_rng(5)
+    a = wl.quantize(rng.normal(size=(M, K)), "f32")
+    b = wl.quantize(rng.uniform(size=(N, K)), "f32")
+    ref = oracle.gemm(a.exact, b.exact, M, K, N, 2)
+    C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
+    torch.cuda.synchronize()
+    err = rel_err(host(C), ref)
+    _say("long-K f32 rel err", err)
+    assert err < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# whole-tensor conv parity
+# ---------------------------------------------------------------------------
+
+def _run_conv(sh, dt, ops):
+    pl = _plan(sh, dt)
+    x, w, g = dev(ops["x"]), dev(ops["w"]), dev(ops["g"])
+    bias = dev(ops["bias"])
+    y = pl.forward(x, w, bias)
+    dx = pl.backward_data(w, g)
+    dw, db = pl.backward_filter(None, g, reuse_col=True)
+    torch.cuda.synchronize()
+    return pl, y, dx, dw, db
+
+
+def _check_whole(sh, dt, ops, tag):
+    _say("conv", tag, sh, dt)
+    pl, y, dx, dw, db = _run_conv(sh, dt, ops)
+    s, p = sh.stride, sh.padding
+    ry = oracle.conv_forward(ops["x"].exact, ops["w"].exact, ops["bias"].exact, s, p)
+    rdx = oracle.conv_backward_data(ops["g"].exact, ops["w"].exact, sh.x_shape(), s, p)
+    rdw = oracle.conv_backward_filter(ops["x"].exact, ops["g"].exact, sh.w_shape(), s, p)
+    rdb = oracle.conv_backward_bias(ops["g"].exact)
+    errs = {"y": rel_err(host(y), ry), "dx": rel_err(host(dx), rdx),
+            "dw": rel_err(host(dw), rdw), "db": rel_err(host(db), rdb)}
+    _say("  rel errors", errs)
+    for k, e in errs.items():
+        assert e < TOL[dt], (tag, k, e)
+    return y, dx, dw, db
+
+
+@pytest.mark.parametrize("t", TINY, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_conv_tiny_shapes(t, dt):
+    sh = _shape(t)
+    ops = wl.random_conv(sh, dt, seed=sum(t))
+    _check_whole(sh, dt, ops, "tiny")
+
+
+def _config_cases(max_batch):
+    out = []
+    for key, w in wl.WORKLOADS.items():
+        for li, layer in enumerate(w.layers):
+            for dt in w.dtypes:
+                out.append((key, li, dt, min(layer.shape.batch, max_batch[key])))
+    return out
+
+
+REDUCED = {"c1": 8, "c2": 64, "c3": 2, "c4": 3, "c5": 1}
+
+
+@pytest.mark.parametrize("key,li,dt,batch", _config_cases(REDUCED), ids=str)
+def test_conv_config_whole_tensor(key, li, dt, batch):
+    w = wl.WORKLOADS[key]
+    sh = w.layers[li].shape.with_batch(batch)
+    ops = wl.conv_inputs(w, li, dt, batch=batch)
+    _check_whole(sh, dt, ops, f"{key}/{w.layers[li].name}/b{batch}")
+
+
+def test_c2_fc_gemms():
+    w = wl.WORKLOADS["c2"]
+    for i, c in enumerate(w.gemms):
+        ops = wl.gemm_inputs(w, i, "f32")
+        ref = oracle.gemm(ops["A"].exact, ops["B"].exact, c.M, c.K, c.N, c.flags)
+        C = d4r.gemm(dev(ops["A"]), dev(ops["B"]), c.M, c.K, c.N, c.flags)
+        torch.cuda.synchronize()
+        err = rel_err(host(C), ref)
+        _say("fc", c.name, err)
+        assert err < TOL["f32"], (c.name, err)
+
+
+# ---------------------------------------------------------------------------
+# full-size parity on sampled blocks (the bench's launch configuration)
+# ---------------------------------------------------------------------------
+
+def _sample_idx(n, k):
+    return np.unique(np.linspace(0, n - 1, num=min(n, k)).round().astype(int))
+
+
+@pytest.mark.parametrize("key,li,dt", [(k, li, dt) for k, w in wl.WORKLOADS.items()
+                                       for li in range(len(w.layers)) for dt in w.dtypes], ids=str)
+def test_conv_full_size_sampled(key, li, dt):
+    w = wl.WORKLOADS[key]
+    sh = w.layers[li].shape
+    ops = wl.conv_inputs(w, li, dt)
+    _say("full-size", key, w.layers[li].name, dt, sh)
+    pl, y, dx, dw, db = _run_conv(sh, dt, ops)
+    s, p = sh.stride, sh.padding
+    X, Wt, G, bias = ops["x"].exact, ops["w"].exact, ops["g"].exact, ops["bias"].exact
+    bs = _sample_idx(sh.batch, 2)
+    os_ = _sample_idx(sh.outC, 6)
+    cs = _sample_idx(sh.inC, 6)
+    ry = oracle.conv_forward(X[bs], Wt[os_], bias[os_], s, p)
+    gy = host(y)[np.ix_(bs, os_)]
+    rdx = oracle.conv_backward_data(G[bs], Wt[:, cs], (len(bs), len(cs), sh.inH, sh.inW), s, p)
+    gdx = host(dx)[np.ix_(bs, cs)]
+    rdw = oracle.conv_backward_filter(X[:, cs], G[:, os_], (len(os_), len(cs), sh.kH, sh.kW), s, p)
+    gdw = host(dw)[np.ix_(os_, cs)]
+    rdb = oracle.conv_backward_bias(G)
+    errs = {"y": rel_err(gy, ry), "dx": rel_err(gdx, rdx), "dw": rel_err(gdw, rdw),
+            "db": rel_err(host(db), rdb)}
+    _say("  sampled rel errors", errs)
+    for k, e in errs.items():
+        assert e < TOL[dt], (k, e)
+    # independent of the oracle: <y - bias, g> = <x, dx> = <W, dW>
+    ysb = host(y) - bias[None, :, None, None]
+    lhs = float(np.vdot(ysb, G))
+    scale = float(np.abs(ysb).ravel() @ np.abs(G).ravel()) + 1.0
+    assert abs(lhs - float(np.vdot(X, host(dx)))) / scale < 1e-5
+    assert abs(lhs - float(np.vdot(Wt, host(dw)))) / scale < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# determinism and the saved-col contract
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bitwise_deterministic(dt):
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[1].shape.with_batch(8)
+    ops = wl.conv_inputs(w, 1, dt, batch=8)
+    a = _run_conv(sh, dt, ops)[1:]
+    b = _run_conv(sh, dt, ops)[1:]
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_reuse_col_matches_fresh_im2col():
+    w = wl.WORKLOADS["c3"]
+    sh = w.layers[0].shape.with_batch(2)
+    ops = wl.conv_inputs(w, 0, "f32", batch=2)
+    pl = _plan(sh, "f32")
+    x, wt, g = dev(ops["x"]), dev(ops["w"]), dev(ops["g"])
+    pl.forward(x, wt, dev(ops["bias"]))
+    pl.backward_data(wt, g)          # must not disturb the saved col
+    dw1, db1 = pl.backward_filter(None, g, reuse_col=True)
+    dw2, db2 = pl.backward_filter(x, g, reuse_col=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2) and torch.equal(db1, db2)
+
+
+def test_forward_without_bias():
+    sh = _shape((2, 3, 9, 9, 4, 3, 3, 1, 1))
+    ops = wl.random_conv(sh, "f32", seed=3)
+    pl = _plan(sh, "f32")
+    y = pl.forward(dev(ops["x"]), dev(ops["w"]), None)
+    torch.cuda.synchronize()
+    ref = oracle.conv_forward(ops["x"].exact, ops["w"].exact, None, 1, 1)
+    assert rel_err(host(y), ref) < 1e-5
