@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of convolution lowered to GEMM on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic input, for
+every conv layer of the workload: forward (im2col -> GEMM NN with the
+conv_reshape + bias epilogue), data gradient (reshape dy, GEMM, col2im) and
+filter + bias gradients (reshape dy, split-K GEMM NT on the saved col,
+reduction, bias row sum).  Inputs are resident in HBM before timing starts.
+
+Default workload: the AlexNet conv3-5 stack (batch 64, 256x13x13 -> 384 ->
+384 -> 256 filters 3x3 pad 1) in fp32, the largest GEMM-dominated
+configuration; ``--workload`` / ``--dtype`` select the others.
+
+Printed: one JSON line.  ``value`` = algorithmic TFLOP/s of the step
+(3 GEMMs x 2*O*Kc*N per layer, padding zeros included, divided by the step
+time).  ``roofline`` describes the kernel with the largest share of the
+step, timed with HIP events the library records on its own launch stream.
+``cpu_baseline`` times the CPU oracle (direct convolution, float64) on a
+bounded batch sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# AMD's published MI355X dense peaks (TFLOP/s) and HBM3E bandwidth (GB/s).
+MFMA_PEAK = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+HBM_PEAK_GBPS = 8000.0
+METRIC = "conv fwd+bwd TFLOP/s and % of MFMA peak; im2col/col2im GB/s vs HBM peak"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", help="c1..c5")
+    ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: workload's first)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", default=None, help="write per-kernel detail JSON here")
+    return ap.parse_args()
+
+
+def layer_flops(sh) -> float:
+    return 3.0 * sh.gemm_flops()
+
+
+def cpu_baseline(wl, dtype: str, target_s: float) -> dict:
+    """The oracle as it stands, on a prefix of the batch, timed on this host."""
+    import oracle
+    import workloads as W
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+
+    def run(bs: int) -> float:
+        total = 0.0
+        for li, layer in enumerate(wl.layers):
+            sh = layer.shape
+            b = min(bs, sh.batch)
+            ops = W.conv_inputs(wl, li, dtype, batch=b)
+            x, w, g, bias = ops["x"].exact, ops["w"].exact, ops["g"].exact, ops["bias"].exact
+            t0 = time.perf_counter()
+            oracle.conv_forward(x, w, bias, sh.stride, sh.padding)
+            oracle.conv_backward_data(g, w, x.shape, sh.stride, sh.padding)
+            oracle.conv_backward_filter(x, g, w.shape, sh.stride, sh.padding)
+            oracle.conv_backward_bias(g)
+            total += time.perf_counter() - t0
+        return total
+
+    t1 = run(1)
+    full = max(l.shape.batch for l in wl.layers)
+    bs = int(max(1, min(full, target_s / max(t1, 1e-6))))
+    t = t1 if bs == 1 else run(bs)
+    flops = sum(layer_flops(l.shape.with_batch(min(bs, l.shape.batch))) for l in wl.layers)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{wl.key} {dtype}: all layers, forward + data/filter/bias gradients, "
+                      f"first {bs} of {full} images (float64 direct loops); {t:.2f} s",
+            "seconds": t}
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
+              "multi-GPU batch sharding is a design note only", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gemm_scratch_nn_amd as d4r
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dtype = args.dtype or wl.dtypes[0]
+    code = {"f32": d4r.D4R_F32, "f16": d4r.D4R_F16, "bf16": d4r.D4R_BF16}[dtype]
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+    def to_dev(op):
+        import numpy as np
+        if op.dtype == "f32":
+            return torch.from_numpy(op.stored).to(dev)
+        return torch.from_numpy(op.stored.view(np.int16)).to(dev).view(tdt)
+
+    layers = []
+    for li, layer in enumerate(wl.layers):
+        sh = layer.shape
+        ops = W.conv_inputs(wl, li, dtype)
+        pl = d4r.ConvPlan(sh.batch, sh.inC, sh.inH, sh.inW, sh.kH, sh.kW, sh.stride, sh.padding,
+                          sh.outC, code, device=dev)
+        t = {k: to_dev(ops[k]) for k in ("x", "w", "g")}
+        t["bias"] = torch.from_numpy(ops["bias"].stored).to(dev)
+        t["y"] = torch.empty(sh.y_shape(), dtype=torch.float32, device=dev)
+        t["dx"] = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
+        t["dw"] = torch.empty(sh.w_shape(), dtype=torch.float32, device=dev)
+        t["db"] = torch.empty((sh.outC,), dtype=torch.float32, device=dev)
+        layers.append((layer, pl, t))
+
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        for layer, pl, t in layers:
+            d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
+            d4r.d4r_conv_backward_data(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
+            d4r.d4r_conv_backward_filter(pl.h, None, t["g"], t["dw"], t["db"], 1, pl.ws, pl.ws_bytes,
+                                         stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    d4r.d4r_profile_reset()
+    d4r.d4r_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    d4r.d4r_profile_enable(False)
+    stats = d4r.d4r_profile_read()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_flops = sum(layer_flops(l.shape) for l, _, _ in layers)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # per kernel symbol (the part before ':' is one template instantiation)
+    by_kernel = {}
+    for s in stats:
+        k = s["name"].split(":")[0]
+        a = by_kernel.setdefault(k, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        for f in ("launches", "ms", "flops", "bytes"):
+            a[f] += s[f]
+    kernels = {}
+    for k, a in by_kernel.items():
+        e = {"launches": a["launches"], "avg_us": 1e3 * a["ms"] / a["launches"],
+             "share": a["ms"] / max(1e-12, sum(v["ms"] for v in by_kernel.values()))}
+        if a["flops"] > 0:
+            e["TFLOPs"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
+            e["frac_mfma"] = e["TFLOPs"] / MFMA_PEAK[dtype]
+        else:
+            e["GBps"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+            e["frac_hbm"] = e["GBps"] / HBM_PEAK_GBPS
+        kernels[k] = e
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
+    d = by_kernel[dom]
+    if d["flops"] > 0:
+        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK[dtype],
+                "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK[dtype], "traffic": None,
+                "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
+    else:
+        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
+
+    def stage(prefix):
+        sel = [v for k, v in by_kernel.items() if k.startswith(prefix)]
+        if not sel:
+            return None
+        ms = sum(v["ms"] for v in sel)
+        gbps = sum(v["bytes"] for v in sel) / (ms * 1e-3) / 1e9
+        return {"GBps": gbps, "frac_hbm": gbps / HBM_PEAK_GBPS}
+
+    gemm_ms = sum(v["ms"] for k, v in by_kernel.items() if k.startswith("gemm"))
+    gemm_tf = sum(v["flops"] for k, v in by_kernel.items() if k.startswith("gemm")) / (gemm_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, dtype, args.cpu_seconds)
+        cpu.pop("seconds", None)
+
+    desc = "; ".join(f"{l.name} {l.shape.inC}x{l.shape.inH}x{l.shape.inW}->{l.shape.outC} "
+                     f"{l.shape.kH}x{l.shape.kW} s{l.shape.stride} p{l.shape.padding}"
+                     for l in wl.layers)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
+                   "dtype": dtype, "step_gflop": step_flops / 1e9},
+        "pct_mfma_peak": value / MFMA_PEAK[dtype],
+        "gemm_TFLOPs": gemm_tf,
+        "gemm_frac_mfma": gemm_tf / MFMA_PEAK[dtype],
+        "im2col": stage("im2col"),
+        "col2im": stage("col2im"),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"line": line, "stats": stats}, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -79,9 +79,20 @@ _c = {
     "d4r_conv_bias_grad": _sig("d4r_conv_bias_grad", [_vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_gemm_workspace_size": _sig("d4r_gemm_workspace_size", [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "d4r_gemm": _sig("d4r_gemm", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_profile_enable": _sig("d4r_profile_enable", [_i]),
+    "d4r_profile_reset": _sig("d4r_profile_reset", []),
     "d4r_status_string": _sig("d4r_status_string", [_i], ctypes.c_char_p),
     "d4r_last_error": _sig("d4r_last_error", [], ctypes.c_char_p),
 }
+
+
+class d4r_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int), ("ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+_c["d4r_profile_read"] = _sig("d4r_profile_read",
+                              [ctypes.POINTER(d4r_kernel_stat), _i, ctypes.POINTER(_i)])
 
 
 class D4RError(RuntimeError):
@@ -214,6 +225,24 @@ def d4r_gemm(M, K, N, flags, dtype, A, B, C, ws=None, ws_bytes=None, stream=None
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_gemm", _c["d4r_gemm"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(C), _ptr(ws), nb,
                                       _stream(stream)))
+
+
+def d4r_profile_enable(on: bool) -> None:
+    _check("d4r_profile_enable", _c["d4r_profile_enable"](1 if on else 0))
+
+
+def d4r_profile_reset() -> None:
+    _check("d4r_profile_reset", _c["d4r_profile_reset"]())
+
+
+def d4r_profile_read() -> list:
+    """Per kernel class: dict(name, launches, ms, flops, bytes).  Synchronises."""
+    n = _i()
+    _check("d4r_profile_read", _c["d4r_profile_read"](None, 0, ctypes.byref(n)))
+    buf = (d4r_kernel_stat * max(1, n.value))()
+    _check("d4r_profile_read", _c["d4r_profile_read"](buf, n.value, ctypes.byref(n)))
+    return [{"name": buf[i].name.decode(), "launches": buf[i].launches, "ms": buf[i].ms,
+             "flops": buf[i].flops, "bytes": buf[i].bytes} for i in range(n.value)]
 
 
 # ---------------------------------------------------------------------------

@@ -13,7 +13,11 @@
 //   backward_filter  [im2col(x) -> col]; dy -> G[O x N];
 //                    GEMM NT  dW[O x Kc] = G * col^T, split over k with
 //                    partial sums reduced in a fixed order; db by reduction
+#include <mutex>
 #include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
 #include <stdio.h>
 #include <stdarg.h>
 #include <string.h>
@@ -97,9 +101,81 @@ size_t plan_partial_bytes(const GemmPlan &pl, int M, int N)
     return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 
+const char *dt_name(int dt) { return dt == DT_F32 ? "f32" : (dt == DT_F16 ? "f16" : "bf16"); }
+
+// ---------------------------------------------------------------------------
+// Kernel timing: HIP event pairs around each launch, on the launch stream.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+    hipEvent_t a, b;
+    int key;
+    double flops, bytes;
+};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    std::vector<ProfRec> recs;       // pool; the first `used` are live
+    size_t used = 0;
+    std::vector<std::string> names;  // key -> name (never shrinks)
+    std::unordered_map<std::string, int> ids;
+};
+
+Profiler &prof()
+{
+    static Profiler *p = new Profiler;  // never destroyed: names stay valid
+    return *p;
+}
+
+// Brackets one launch.  Constructed before the launch, finished after it.
+struct ProfScope {
+    ProfRec *rec = nullptr;
+    hipStream_t s;
+    ProfScope(hipStream_t st, const std::string &name, double flops, double bytes) : s(st)
+    {
+        Profiler &P = prof();
+        std::lock_guard<std::mutex> lk(P.mu);
+        if (!P.on)
+            return;
+        auto it = P.ids.find(name);
+        int key;
+        if (it == P.ids.end()) {
+            key = (int)P.names.size();
+            P.names.push_back(name);
+            P.ids[name] = key;
+        } else {
+            key = it->second;
+        }
+        if (P.used == P.recs.size()) {
+            ProfRec r{};
+            if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess)
+                return;
+            P.recs.push_back(r);
+        }
+        rec = &P.recs[P.used++];
+        rec->key = key;
+        rec->flops = flops;
+        rec->bytes = bytes;
+        (void)hipEventRecord(rec->a, s);
+    }
+    void done()
+    {
+        if (rec)
+            (void)hipEventRecord(rec->b, s);
+    }
+};
+
+std::string gemm_kernel_name(int dt, int cfg, bool a_kc, bool b_kc)
+{
+    TileShape ts = tile_shape(cfg);
+    return std::string("gemm_") + dt_name(dt) + "_" + std::to_string(ts.bm) + "x" + std::to_string(ts.bn) +
+           "_" + (a_kc ? "k" : "m") + (b_kc ? "k" : "n");
+}
+
+
 hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
-                    const float *bias, int P, float *partial, hipStream_t s)
+                    const float *bias, int P, float *partial, hipStream_t s, const char *pass)
 {
     const int vw = dt == DT_F32 ? 4 : 8;
     GemmParams p;
@@ -127,10 +203,18 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
         p.epi = epi;
         p.c_split_stride = 0;
     }
+    const int es = dt_size(dt);
+    ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, a_kc, b_kc) + ":" + pass, 2.0 * M * N * K,
+                 (double)es * ((double)M * K + (double)K * N) + 4.0 * M * N);
     hipError_t e = launch_gemm(dt, pl.cfg, a_kc, b_kc, p, s);
+    ps.done();
     if (e != hipSuccess || pl.splits == 1)
         return e;
-    return launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, s);
+    ProfScope pr(s, std::string("splitk_reduce:") + pass, 0.0,
+                 4.0 * (double)M * N * (pl.splits + 1));
+    e = launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, s);
+    pr.done();
+    return e;
 }
 
 bool valid_dtype(int dt) { return dt == D4R_F32 || dt == D4R_F16 || dt == D4R_BF16; }
@@ -145,6 +229,7 @@ struct d4r_conv {
     int bias_splits;
     size_t off_g, off_wt, off_bias, off_big, ws_bytes;
     size_t col_bytes;
+    double in_image_col;  // col entries copied from inside the image
 };
 
 namespace d4r {
@@ -165,6 +250,61 @@ hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &
 }
 
 }  // namespace d4r
+
+namespace {
+
+// Launch wrappers that tag each step with its algorithmic bytes.
+hipError_t step_im2col(const d4r_conv *h, const void *x, void *col, hipStream_t s, const char *pass)
+{
+    const ConvGeom &g = h->g;
+    double bytes = (double)h->es * ((double)g.B * g.C * g.H * g.W + (double)g.Kc * g.N);
+    ProfScope ps(s, std::string("im2col_") + dt_name(h->dt) + ":" + pass, 0.0, bytes);
+    hipError_t e = launch_im2col(h->dt, g, x, col, s);
+    ps.done();
+    return e;
+}
+
+hipError_t step_col2im(const d4r_conv *h, const float *dcol, float *dx, hipStream_t s, const char *pass)
+{
+    const ConvGeom &g = h->g;
+    double bytes = 4.0 * h->in_image_col + 4.0 * ((double)g.B * g.C * g.H * g.W);
+    ProfScope ps(s, std::string("col2im_f32:") + pass, 0.0, bytes);
+    hipError_t e = launch_col2im(g, dcol, dx, s);
+    ps.done();
+    return e;
+}
+
+hipError_t step_transpose(const d4r_conv *h, int batch, int R, int C, const void *in, void *out,
+                          hipStream_t s, const char *what)
+{
+    double bytes = 2.0 * h->es * (double)batch * R * C;
+    ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":" + what, 0.0, bytes);
+    hipError_t e = launch_transpose(h->dt, batch, R, C, in, out, s);
+    ps.done();
+    return e;
+}
+
+hipError_t step_grad_reshape(const d4r_conv *h, const void *dy, void *G, hipStream_t s)
+{
+    const ConvGeom &g = h->g;
+    ProfScope ps(s, std::string("grad_reshape_") + dt_name(h->dt) + ":wgrad", 0.0,
+                 2.0 * h->es * (double)g.O * g.N);
+    hipError_t e = launch_grad_reshape(h->dt, g, dy, G, s);
+    ps.done();
+    return e;
+}
+
+hipError_t step_bias(const d4r_conv *h, const void *dy, float *db, float *partial, hipStream_t s)
+{
+    const ConvGeom &g = h->g;
+    ProfScope ps(s, std::string("bias_grad_") + dt_name(h->dt) + ":wgrad", 0.0,
+                 (double)h->es * g.O * g.N + 4.0 * g.O);
+    hipError_t e = launch_bias_grad(h->dt, g, dy, db, partial, h->bias_splits, s);
+    ps.done();
+    return e;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -223,6 +363,21 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->bwd_data = plan_gemm(g.Kc, g.N, g.O, dtype);
     h->bwd_filter = plan_gemm(g.O, g.Kc, g.N, dtype);
     h->bias_splits = bias_grad_splits(g);
+    {
+        // sum over output rows i of the taps u that land inside the image
+        long long rows = 0, cols = 0;
+        for (int i = 0; i < g.OH; ++i)
+            for (int u = 0; u < kH; ++u) {
+                int hh = i * stride - padding + u;
+                rows += (hh >= 0 && hh < inH);
+            }
+        for (int j = 0; j < g.OW; ++j)
+            for (int v = 0; v < kW; ++v) {
+                int ww = j * stride - padding + v;
+                cols += (ww >= 0 && ww < inW);
+            }
+        h->in_image_col = (double)batch * inC * (double)rows * (double)cols;
+    }
 
     h->col_bytes = (size_t)col_el * h->es;
     size_t off = align_up(h->col_bytes);
@@ -335,9 +490,9 @@ d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const fl
     char *wsb = (char *)ws;
     void *col = wsb;
     float *partial = (float *)(wsb + h->off_big);
-    D4R_LAUNCH(launch_im2col(h->dt, g, x, col, s), "im2col");
+    D4R_LAUNCH(step_im2col(h, x, col, s, "fwd"), "im2col");
     D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
-                        bias, g.P, partial, s),
+                        bias, g.P, partial, s, "fwd"),
                "forward GEMM");
     return ok();
 }
@@ -359,12 +514,12 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, f
     float *dcol = (float *)(wsb + h->off_big);
     float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
     // Gt[b*P + pix][o] = dy[b][o][pix]: a batch of O x P transposes
-    D4R_LAUNCH(launch_transpose(h->dt, g.B, g.O, g.P, dy, gt, s), "grad reshape");
-    D4R_LAUNCH(launch_transpose(h->dt, 1, g.O, g.Kc, w, wt, s), "filter transpose");
+    D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad reshape");
+    D4R_LAUNCH(step_transpose(h, 1, g.O, g.Kc, w, wt, s, "dgrad_w"), "filter transpose");
     D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, true, true, wt, g.O, gt, g.O, g.Kc, g.N, g.O, EPI_ROWMAJOR,
-                        dcol, g.N, nullptr, 0, partial, s),
+                        dcol, g.N, nullptr, 0, partial, s, "dgrad"),
                "data-gradient GEMM");
-    D4R_LAUNCH(launch_col2im(g, dcol, dx, s), "col2im");
+    D4R_LAUNCH(step_col2im(h, dcol, dx, s, "dgrad"), "col2im");
     return ok();
 }
 
@@ -390,13 +545,13 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     void *G = wsb + h->off_g;
     float *partial = (float *)(wsb + h->off_big);
     if (!reuse_col)
-        D4R_LAUNCH(launch_im2col(h->dt, g, x, col, s), "im2col");
-    D4R_LAUNCH(launch_grad_reshape(h->dt, g, dy, G, s), "grad reshape");
+        D4R_LAUNCH(step_im2col(h, x, col, s, "wgrad"), "im2col");
+    D4R_LAUNCH(step_grad_reshape(h, dy, G, s), "grad reshape");
     D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, true, true, G, g.N, col, g.N, g.O, g.Kc, g.N,
-                        EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s),
+                        EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad"),
                "filter-gradient GEMM");
     if (db)
-        D4R_LAUNCH(launch_bias_grad(h->dt, g, dy, db, (float *)(wsb + h->off_bias), h->bias_splits, s),
+        D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s),
                    "bias gradient");
     return ok();
 }
@@ -407,7 +562,7 @@ d4r_status d4r_conv_im2col(d4r_conv_t h, const void *x, void *col, void *hip_str
         return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
     D4R_TRY(check_tensor(x, "x"));
     D4R_TRY(check_tensor(col, "col"));
-    D4R_LAUNCH(launch_im2col(h->dt, h->g, x, col, (hipStream_t)hip_stream), "im2col");
+    D4R_LAUNCH(step_im2col(h, x, col, (hipStream_t)hip_stream, "step"), "im2col");
     return ok();
 }
 
@@ -417,7 +572,7 @@ d4r_status d4r_conv_col2im(d4r_conv_t h, const float *dcol, float *dx, void *hip
         return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
     D4R_TRY(check_tensor(dcol, "dcol"));
     D4R_TRY(check_tensor(dx, "dx"));
-    D4R_LAUNCH(launch_col2im(h->g, dcol, dx, (hipStream_t)hip_stream), "col2im");
+    D4R_LAUNCH(step_col2im(h, dcol, dx, (hipStream_t)hip_stream, "step"), "col2im");
     return ok();
 }
 
@@ -431,8 +586,7 @@ d4r_status d4r_conv_bias_grad(d4r_conv_t h, const void *dy, float *db, void *ws,
         return fail(D4R_ERR_INVALID_ARG, "db is NULL");
     D4R_TRY(check_vec(db, "db"));
     D4R_TRY(check_ws(h, ws, ws_bytes));
-    D4R_LAUNCH(launch_bias_grad(h->dt, h->g, dy, db, (float *)((char *)ws + h->off_bias), h->bias_splits,
-                                (hipStream_t)hip_stream),
+    D4R_LAUNCH(step_bias(h, dy, db, (float *)((char *)ws + h->off_bias), (hipStream_t)hip_stream),
                "bias gradient");
     return ok();
 }
@@ -486,8 +640,59 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
     const int lda = a_kc ? K : M;
     const int ldb = b_kc ? K : N;
     D4R_LAUNCH(run_gemm(dtype, pl, a_kc, b_kc, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
-                        (float *)ws, (hipStream_t)hip_stream),
+                        (float *)ws, (hipStream_t)hip_stream, "gemm"),
                "GEMM");
+    return ok();
+}
+
+d4r_status d4r_profile_enable(int on)
+{
+    Profiler &P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.on = on != 0;
+    return ok();
+}
+
+d4r_status d4r_profile_reset(void)
+{
+    Profiler &P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.used = 0;
+    return ok();
+}
+
+d4r_status d4r_profile_read(d4r_kernel_stat *out, int max, int *count)
+{
+    if (!count || (max > 0 && !out))
+        return fail(D4R_ERR_INVALID_ARG, "NULL argument");
+    Profiler &P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    std::vector<d4r_kernel_stat> agg(P.names.size());
+    for (size_t k = 0; k < P.names.size(); ++k)
+        agg[k] = d4r_kernel_stat{P.names[k].c_str(), 0, 0.0, 0.0, 0.0};
+    for (size_t i = 0; i < P.used; ++i) {
+        ProfRec &r = P.recs[i];
+        hipError_t e = hipEventSynchronize(r.b);
+        float ms = 0.0f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess)
+            return fail(D4R_ERR_LAUNCH, "event timing: %s", hipGetErrorString(e));
+        d4r_kernel_stat &a = agg[r.key];
+        a.launches += 1;
+        a.ms += ms;
+        a.flops += r.flops;
+        a.bytes += r.bytes;
+    }
+    int n = 0;
+    for (auto &a : agg) {
+        if (a.launches == 0)
+            continue;
+        if (n < max)
+            out[n] = a;
+        ++n;
+    }
+    *count = n;
     return ok();
 }
 

@@ -14,7 +14,9 @@
  *             db[o] = sum of row o of G
  * Transposes are expressed by the matmul flags ("Transpose via Flags"):
  * flags & 1 reads A as stored transposed, flags & 2 reads B as stored
- * transposed; no transpose kernels are run.
+ * transposed.  (For the data gradient this library reshapes dy straight
+ * into G^T and keeps a transposed copy of the small filter matrix, so both
+ * MFMA operands stream with k contiguous; the product is the same.)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -186,6 +188,33 @@ d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dty
 d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A,
                     const void *B, float *C, void *ws, size_t ws_bytes,
                     void *hip_stream);
+
+/*
+ * Kernel timing (measurement aid).  While enabled, every kernel launch made
+ * by the calls above is bracketed by a pair of HIP events recorded on the
+ * call's stream, and tagged with the launch's algorithmic work: flops for
+ * the GEMMs (2*M*N*K, padding zeros included), bytes for the data-movement
+ * kernels (bytes the step must read plus bytes it must write).  Disabled by
+ * default; when disabled it costs one branch per launch.
+ *
+ * d4r_profile_read synchronises on the recorded events and returns one
+ * entry per kernel class, named "<kernel>:<pass>", e.g.
+ * "gemm_f32_128x128_kk:wgrad" or "im2col_f32:fwd".  Names stay valid for the
+ * life of the process.  *count receives the number of classes (entries
+ * beyond max are dropped).  d4r_profile_reset forgets all records.  The
+ * recorder is process-wide and guarded by a mutex.
+ */
+typedef struct {
+    const char *name;
+    int launches;
+    double ms;     /* summed event-to-event time of all launches */
+    double flops;  /* summed algorithmic flops (0 for data movement) */
+    double bytes;  /* summed algorithmic bytes */
+} d4r_kernel_stat;
+
+d4r_status d4r_profile_enable(int on);
+d4r_status d4r_profile_reset(void);
+d4r_status d4r_profile_read(d4r_kernel_stat *out, int max, int *count);
 
 /* Static string naming a status code. */
 const char *d4r_status_string(d4r_status s);

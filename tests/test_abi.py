@@ -16,7 +16,8 @@ def test_every_declared_symbol_is_exported():
                 "d4r_conv_workspace_size", "d4r_conv_forward", "d4r_conv_backward_data",
                 "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
                 "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
-                "d4r_status_string", "d4r_last_error"}
+                "d4r_status_string", "d4r_last_error", "d4r_profile_enable",
+                "d4r_profile_reset", "d4r_profile_read"}
     assert expected <= set(names)
     for n in names:
         assert d4r.exported(n), n
@@ -182,3 +183,10 @@ def test_gemm_pointer_and_workspace_errors():
     with pytest.raises(D4RError) as e:
         d4r.d4r_gemm(96, 96800, 363, 2, D4R_F32, FAKE, FAKE, FAKE, FAKE, need - 4, stream=0)
     assert e.value.status == WORKSPACE
+
+
+def test_profile_recorder_host_side():
+    d4r.d4r_profile_reset()
+    d4r.d4r_profile_enable(True)
+    d4r.d4r_profile_enable(False)
+    assert d4r.d4r_profile_read() == []
