@@ -47,6 +47,9 @@ def parse_args():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", default=None, help="write per-kernel detail JSON here")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before warmup (counter "
+                         "calibration for rocprofv3 --pmc runs; untimed)")
     return ap.parse_args()
 
 
@@ -128,6 +131,15 @@ def main() -> int:
         layers.append((layer, pl, t))
 
     stream = torch.cuda.current_stream().cuda_stream
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         for layer, pl, t in layers:

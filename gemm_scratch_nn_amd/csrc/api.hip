@@ -59,9 +59,24 @@ struct GemmPlan {
     int k_per_split;
 };
 
-// Tile and split-K choice from the problem shape and the chip's 256 compute
-// units: whole-chip coverage needs several hundred workgroups, and each
-// split keeps at least four K stages.
+// Tile and split-K choice.  The chip has 256 compute units; a tile config
+// keeps wg_per_cu workgroups resident per CU (from its LDS and register
+// use), so a launch runs in ceil(workgroups / slots) waves.  Splitting K
+// into s slices multiplies the workgroups by s and divides each one's work
+// by s, at the price of writing and re-reading s partial M x N slabs.  The
+// split count minimises a small cost model of those two terms.
+constexpr int kComputeUnits = 256;
+
+int wg_per_cu(int cfg)
+{
+    switch (cfg) {
+    case TILE_128x128: return 2;
+    case TILE_64x64: return 4;
+    case TILE_32x128: return 3;
+    default: return 2;
+    }
+}
+
 GemmPlan plan_gemm(int M, int N, int K, int dt)
 {
     GemmPlan pl;
@@ -76,23 +91,34 @@ GemmPlan plan_gemm(int M, int N, int K, int dt)
     TileShape ts = tile_shape(pl.cfg);
     const int bk = gemm_bk(dt);
     const long long tiles = (long long)((M + ts.bm - 1) / ts.bm) * ((N + ts.bn - 1) / ts.bn);
-    const int ktiles = (K + bk - 1) / bk;
-    int splits = 1;
-    if (tiles < 256) {
-        long long want = (512 + tiles - 1) / tiles;
-        long long cap = ktiles / 4;
-        if (want > cap)
-            want = cap;
-        if (want > 256)
-            want = 256;
-        if (want > 1)
-            splits = (int)want;
+    const long long ktiles = (K + bk - 1) / bk;
+    const long long slots = (long long)kComputeUnits * wg_per_cu(pl.cfg);
+    // seconds per K stage of one workgroup when every slot is busy, at a
+    // sustained fraction of the dtype's MFMA peak
+    const double peak = dt == DT_F32 ? 157.3e12 * 0.6 : 2516.6e12 * 0.25;
+    const double t_stage = 2.0 * ts.bm * ts.bn * bk / (peak / (double)slots);
+    const double bw = 3.0e12;       // bytes/s for the partial-sum round trip
+    const double t_launch = 3e-6;   // one extra kernel
+    double best = 1e30;
+    long long best_s = 1, best_per = ktiles;
+    const long long smax = ktiles < 256 ? ktiles : 256;
+    for (long long sp = 1; sp <= smax; ++sp) {
+        long long per = (ktiles + sp - 1) / sp;
+        long long se = (ktiles + per - 1) / per;
+        if (se != sp)
+            continue;
+        long long waves = (tiles * se + slots - 1) / slots;
+        double t = (double)waves * per * t_stage;
+        if (se > 1)
+            t += (double)(se + 1) * M * N * 4.0 / bw + t_launch;
+        if (t < best * 0.999) {
+            best = t;
+            best_s = se;
+            best_per = per;
+        }
     }
-    int kts_per = (ktiles + splits - 1) / splits;
-    pl.k_per_split = kts_per * bk;
-    pl.splits = (K + pl.k_per_split - 1) / pl.k_per_split;
-    if (pl.splits < 1)
-        pl.splits = 1;
+    pl.splits = (int)best_s;
+    pl.k_per_split = (int)(best_per * bk);
     return pl;
 }
 

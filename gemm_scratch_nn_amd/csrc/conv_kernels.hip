@@ -36,9 +36,11 @@ __device__ __forceinline__ float to_f32(uint16_t v, int dt)
 
 // ---------------------------------------------------------------------------
 // im2col: col[r][n] = xt(b, c, i*s - p + u, j*s - p + v) with r = (c*kH+u)*kW+v
-// and n = (b*OH + i)*OW + j.  One thread writes VW consecutive n of one row
-// as a single 16-byte store (scalar stores when N is not a multiple of VW).
-// Raw bit copy: T is the storage word of the dtype.
+// and n = (b*OH + i)*OW + j.  A thread owns VW consecutive n (one 16-byte
+// store per row) and one (c, u) pair, and walks the kW rows v = 0..kW-1 of
+// that pair: the x row segment it gathers from is the same for every v up
+// to a shift, so after the first v it is served from L1 / L2 instead of
+// HBM.  Raw bit copy: T is the storage word of the dtype.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *__restrict__ col,
@@ -48,25 +50,18 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
     const int n0 = (blockIdx.x * NT + threadIdx.x) * VW;
     if (n0 >= g.N)
         return;
-    const int khw = g.kH * g.kW;
-    for (int r = blockIdx.y; r < g.Kc; r += gridDim.y) {
-        const int c = r / khw;
-        const int uv = r - c * khw;
-        const int u = uv / g.kW;
-        const int v = uv - u * g.kW;
+    // per element: image plane offset (b*C*H*W) and the window origin
+    int base[VW], h0[VW], w0[VW];
+    {
         int b = n0 / g.P;
         int rem = n0 - b * g.P;
         int i = rem / g.OW;
         int j = rem - i * g.OW;
-        typename Vec16<T>::type out;
 #pragma unroll
         for (int e = 0; e < VW; ++e) {
-            const int hh = i * g.s - g.p + u;
-            const int ww = j * g.s - g.p + v;
-            T val = 0;
-            if (b < g.B && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W)
-                val = x[((b * g.C + c) * g.H + hh) * g.W + ww];
-            out[e] = val;
+            base[e] = b < g.B ? b * g.C * g.H * g.W : -1;
+            h0[e] = i * g.s - g.p;
+            w0[e] = j * g.s - g.p;
             if (++j == g.OW) {
                 j = 0;
                 if (++i == g.OH) {
@@ -75,14 +70,32 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
                 }
             }
         }
-        T *dst = col + (long long)r * g.N + n0;
-        if (vec_store) {
-            *(typename Vec16<T>::type *)dst = out;
-        } else {
+    }
+    const int CU = g.C * g.kH;
+    for (int cu = blockIdx.y; cu < CU; cu += gridDim.y) {
+        const int c = cu / g.kH;
+        const int u = cu - c * g.kH;
+        const int plane = c * g.H * g.W;
+        for (int v = 0; v < g.kW; ++v) {
+            typename Vec16<T>::type out;
 #pragma unroll
-            for (int e = 0; e < VW; ++e)
-                if (n0 + e < g.N)
-                    dst[e] = out[e];
+            for (int e = 0; e < VW; ++e) {
+                const int hh = h0[e] + u;
+                const int ww = w0[e] + v;
+                T val = 0;
+                if (base[e] >= 0 && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W)
+                    val = x[base[e] + plane + hh * g.W + ww];
+                out[e] = val;
+            }
+            T *dst = col + (long long)(cu * g.kW + v) * g.N + n0;
+            if (vec_store) {
+                *(typename Vec16<T>::type *)dst = out;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    if (n0 + e < g.N)
+                        dst[e] = out[e];
+            }
         }
     }
 }
@@ -92,8 +105,11 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
 // entries that im2col copied from (b, c, h, w).  Tap u contributes when
 // h + p - u >= 0, divisible by s and (h + p - u)/s < OH, i.e. u runs over one
 // residue class mod s between u_lo and u_hi; same for v.  Order: u
-// ascending, then v ascending.
+// ascending, then v ascending.  TU / TV > 0 fix the number of candidate taps
+// per axis (ceil(k / s)) at compile time so every load of a thread is issued
+// before the adds; TU = TV = 0 is the general loop.
 // ---------------------------------------------------------------------------
+template <int TU, int TV>
 __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dcol,
                                                     float *__restrict__ dx, ConvGeom g, int total)
 {
@@ -120,15 +136,37 @@ __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dc
     v_lo += ((wp - v_lo) % g.s);
     const int v_hi = min(g.kW - 1, wp);
 
-    float acc = 0.0f;
     const long long Nl = g.N;
     const int nb = b * g.P;
-    for (int u = u_lo; u <= u_hi; u += g.s) {
-        const int i = (hp - u) / g.s;
-        const int rbase = (c * g.kH + u) * g.kW;
-        for (int v = v_lo; v <= v_hi; v += g.s) {
-            const int j = (wp - v) / g.s;
-            acc += dcol[(long long)(rbase + v) * Nl + nb + i * g.OW + j];
+    float acc = 0.0f;
+    if constexpr (TU > 0) {
+        float vals[TU][TV];
+#pragma unroll
+        for (int a = 0; a < TU; ++a) {
+            const int u = u_lo + a * g.s;
+            const int i = (hp - u) / g.s;
+#pragma unroll
+            for (int q = 0; q < TV; ++q) {
+                const int v = v_lo + q * g.s;
+                const int j = (wp - v) / g.s;
+                const bool ok = (u <= u_hi) && (v <= v_hi);
+                vals[a][q] = ok ? dcol[(long long)((c * g.kH + u) * g.kW + v) * Nl + nb + i * g.OW + j]
+                                : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < TU; ++a)
+#pragma unroll
+            for (int q = 0; q < TV; ++q)
+                acc += vals[a][q];
+    } else {
+        for (int u = u_lo; u <= u_hi; u += g.s) {
+            const int i = (hp - u) / g.s;
+            const int rbase = (c * g.kH + u) * g.kW;
+            for (int v = v_lo; v <= v_hi; v += g.s) {
+                const int j = (wp - v) / g.s;
+                acc += dcol[(long long)(rbase + v) * Nl + nb + i * g.OW + j];
+            }
         }
     }
     dx[idx] = acc;
@@ -286,7 +324,7 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
 {
     const int VW = dt == DT_F32 ? 4 : 8;
     const long long threads = (g.N + VW - 1) / VW;
-    dim3 grid = grid2((threads + NT - 1) / NT, g.Kc);
+    dim3 grid = grid2((threads + NT - 1) / NT, (long long)g.C * g.kH);
     const int vec = (g.N % VW) == 0;
     if (dt == DT_F32)
         hipLaunchKernelGGL(im2col_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)x,
@@ -300,7 +338,18 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s)
 {
     const int total = g.B * g.C * g.H * g.W;
-    hipLaunchKernelGGL(col2im_kernel, dim3((total + NT - 1) / NT), dim3(NT), 0, s, dcol, dx, g, total);
+    const dim3 grid((total + NT - 1) / NT), block(NT);
+    const int tu = (g.kH + g.s - 1) / g.s, tv = (g.kW + g.s - 1) / g.s;
+    if (tu == 1 && tv == 1)
+        hipLaunchKernelGGL((col2im_kernel<1, 1>), grid, block, 0, s, dcol, dx, g, total);
+    else if (tu == 2 && tv == 2)
+        hipLaunchKernelGGL((col2im_kernel<2, 2>), grid, block, 0, s, dcol, dx, g, total);
+    else if (tu == 3 && tv == 3)
+        hipLaunchKernelGGL((col2im_kernel<3, 3>), grid, block, 0, s, dcol, dx, g, total);
+    else if (tu == 5 && tv == 5)
+        hipLaunchKernelGGL((col2im_kernel<5, 5>), grid, block, 0, s, dcol, dx, g, total);
+    else
+        hipLaunchKernelGGL((col2im_kernel<0, 0>), grid, block, 0, s, dcol, dx, g, total);
     return hipGetLastError();
 }
 
