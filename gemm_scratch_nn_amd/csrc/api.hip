@@ -19,6 +19,7 @@
 #include <unordered_map>
 #include <vector>
 #include <stdio.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <string.h>
 
@@ -67,58 +68,99 @@ struct GemmPlan {
 // split count minimises a small cost model of those two terms.
 constexpr int kComputeUnits = 256;
 
-int wg_per_cu(int cfg)
+// Workgroups resident per CU for each tile config (LDS and register use of
+// the compiled kernels), f32 and 16-bit builds respectively.
+int wg_per_cu(int cfg, int dt)
 {
+    const bool h = dt != DT_F32;
     switch (cfg) {
     case TILE_128x128: return 2;
-    case TILE_64x64: return 4;
+    case TILE_64x64: return h ? 3 : 4;
     case TILE_32x128: return 3;
-    default: return 2;
+    case TILE_96x128: return 2;
+    default: return 1;  // 128x256, 256x128 (16-bit only)
     }
+}
+
+struct TileCand {
+    int cfg;
+    double eff;  // relative sustained MFMA rate per CU (L2 traffic per flop)
+};
+
+int tile_from_env(int dt)
+{
+    // experiment override, e.g. D4R_GEMM_TILE=128x256
+    const char *e = getenv("D4R_GEMM_TILE");
+    if (!e)
+        return -1;
+    for (int c = 0; c < TILE_COUNT; ++c) {
+        if (dt == DT_F32 && (c == TILE_128x256 || c == TILE_256x128))
+            continue;
+        TileShape ts = tile_shape(c);
+        char buf[32];
+        snprintf(buf, sizeof buf, "%dx%d", ts.bm, ts.bn);
+        if (strcmp(buf, e) == 0)
+            return c;
+    }
+    return -1;
 }
 
 GemmPlan plan_gemm(int M, int N, int K, int dt)
 {
-    GemmPlan pl;
-    if (M <= 32)
-        pl.cfg = TILE_32x128;
-    else if (M <= 64 || N <= 64)
-        pl.cfg = TILE_64x64;
-    else if (M % 128 != 0 && M % 96 == 0 && M <= 192)
-        pl.cfg = TILE_96x128;
-    else
-        pl.cfg = TILE_128x128;
-    TileShape ts = tile_shape(pl.cfg);
+    TileCand cands[4];
+    int nc = 0;
+    if (M <= 32) {
+        cands[nc++] = {TILE_32x128, 1.0};
+    } else if (M <= 64 || N <= 64) {
+        cands[nc++] = {TILE_64x64, 1.0};
+    } else if (dt == DT_F32) {
+        if (M % 128 != 0 && M % 96 == 0 && M <= 192)
+            cands[nc++] = {TILE_96x128, 1.0};
+        else
+            cands[nc++] = {TILE_128x128, 1.0};
+    } else {
+        cands[nc++] = {TILE_128x128, 0.85};
+        cands[nc++] = {TILE_128x256, 1.0};
+        cands[nc++] = {TILE_256x128, 1.0};
+        if (M % 128 != 0 && M % 96 == 0 && M <= 192)
+            cands[nc++] = {TILE_96x128, 0.8};
+    }
+    const int forced = tile_from_env(dt);
+    if (forced >= 0) {
+        nc = 1;
+        cands[0] = {forced, 1.0};
+    }
     const int bk = gemm_bk(dt);
-    const long long tiles = (long long)((M + ts.bm - 1) / ts.bm) * ((N + ts.bn - 1) / ts.bn);
     const long long ktiles = (K + bk - 1) / bk;
-    const long long slots = (long long)kComputeUnits * wg_per_cu(pl.cfg);
-    // seconds per K stage of one workgroup when every slot is busy, at a
-    // sustained fraction of the dtype's MFMA peak
-    const double peak = dt == DT_F32 ? 157.3e12 * 0.6 : 2516.6e12 * 0.25;
-    const double t_stage = 2.0 * ts.bm * ts.bn * bk / (peak / (double)slots);
+    const double peak = dt == DT_F32 ? 157.3e12 * 0.6 : 2516.6e12 * 0.3;
     const double bw = 3.0e12;       // bytes/s for the partial-sum round trip
     const double t_launch = 3e-6;   // one extra kernel
     double best = 1e30;
-    long long best_s = 1, best_per = ktiles;
-    const long long smax = ktiles < 256 ? ktiles : 256;
-    for (long long sp = 1; sp <= smax; ++sp) {
-        long long per = (ktiles + sp - 1) / sp;
-        long long se = (ktiles + per - 1) / per;
-        if (se != sp)
-            continue;
-        long long waves = (tiles * se + slots - 1) / slots;
-        double t = (double)waves * per * t_stage;
-        if (se > 1)
-            t += (double)(se + 1) * M * N * 4.0 / bw + t_launch;
-        if (t < best * 0.999) {
-            best = t;
-            best_s = se;
-            best_per = per;
+    GemmPlan pl{cands[0].cfg, 1, (int)(ktiles * bk)};
+    for (int ci = 0; ci < nc; ++ci) {
+        const TileShape ts = tile_shape(cands[ci].cfg);
+        const long long tiles = (long long)((M + ts.bm - 1) / ts.bm) * ((N + ts.bn - 1) / ts.bn);
+        const long long slots = (long long)kComputeUnits * wg_per_cu(cands[ci].cfg, dt);
+        // seconds per K stage of one workgroup when every slot is busy
+        const double t_stage = 2.0 * ts.bm * ts.bn * bk / (peak * cands[ci].eff / (double)slots);
+        const long long smax = ktiles < 256 ? ktiles : 256;
+        for (long long sp = 1; sp <= smax; ++sp) {
+            const long long per = (ktiles + sp - 1) / sp;
+            const long long se = (ktiles + per - 1) / per;
+            if (se != sp)
+                continue;
+            const long long waves = (tiles * se + slots - 1) / slots;
+            double t = (double)waves * per * t_stage;
+            if (se > 1)
+                t += (double)(se + 1) * M * N * 4.0 / bw + t_launch;
+            if (t < best * 0.999) {
+                best = t;
+                pl.cfg = cands[ci].cfg;
+                pl.splits = (int)se;
+                pl.k_per_split = (int)(per * bk);
+            }
         }
     }
-    pl.splits = (int)best_s;
-    pl.k_per_split = (int)(best_per * bk);
     return pl;
 }
 
@@ -216,8 +258,10 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
     p.P = P;
     p.k_per_split = pl.k_per_split;
     p.splits = pl.splits;
-    p.a_vec = (lda % vw) == 0;
-    p.b_vec = (ldb % vw) == 0;
+    // vector loads need every 16-byte vector wholly inside or outside the
+    // operand: leading dimension and the contiguous extent multiples of vw
+    p.a_vec = (lda % vw) == 0 && ((a_kc ? K : M) % vw) == 0;
+    p.b_vec = (ldb % vw) == 0 && ((b_kc ? K : N) % vw) == 0;
     if (pl.splits > 1) {
         p.C = partial;
         p.ldc = N;

@@ -1,0 +1,379 @@
+// MFMA GEMM for 16-bit operands (f16 / bf16, f32 accumulation) on gfx950.
+//
+// Same contract as the f32 kernel (C = op(A) op(B) with the page's transpose
+// flags), specialised for the short K stages of the 16-bit MFMAs:
+//  * v_mfma_f32_32x32x16_{f16,bf16}: one 32x32 block per 16 k; a 64-deep K
+//    stage is only ~512 MFMA cycles per wave, so global loads are issued two
+//    stages ahead: two register sets alternate (loop unrolled by two so each
+//    set stays in fixed registers) while two LDS buffers alternate behind
+//    them; one barrier per stage.
+//  * LDS holds every operand as [row][k] with 128-byte rows (64 halves =
+//    eight 16-byte chunks).  Chunk c of row r is stored at chunk
+//    c ^ ((r ^ (r >> 3)) & 7): the 16-byte fragment reads of 8 consecutive
+//    rows then touch 8 different chunk positions (all banks, no conflict),
+//    and so do the transposed 8-byte stores described next.
+//  * Operands stored row-contiguous in memory (A[k*lda + m] / B[k*ldb + n])
+//    are loaded as 4 k-rows x 8 rows per thread (four 16-byte loads), turned
+//    into 8 rows x 4 k in registers (16 half-word permutes) and stored as
+//    8-byte LDS writes, so fragment reads are 16-byte reads for every layout.
+//  * Workgroups are renumbered so that consecutive tiles land on the same
+//    XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each
+//    with its own L2): the M tiles that share a B panel then share one L2.
+#pragma once
+
+#include "internal.hpp"
+
+namespace d4r {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <int DTID>
+__device__ __forceinline__ f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c)
+{
+    if constexpr (DTID == DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// One operand tile of BR rows x 64 k, 16-bit elements.
+template <int BR, bool KC>
+struct Tile16 {
+    static constexpr int NT = 256;
+    static constexpr int BK = 64;
+    static constexpr int LDS_BYTES = BR * 128;
+    // k-contiguous: one 16-byte chunk per slot, 8 slots per row
+    static constexpr int KC_SLOTS = BR * 8;
+    // row-contiguous: one (8-row group, 4-k quad) block per slot; row groups
+    // are padded to a multiple of 8 (slots with rg >= BR/8 do nothing)
+    static constexpr int RGH = (BR / 8 + 7) / 8;
+    static constexpr int MN_SLOTS = RGH * 8 * 16;
+    static constexpr int SLOTS = KC ? KC_SLOTS : MN_SLOTS;
+    static constexpr int PER = (SLOTS + NT - 1) / NT;
+    static constexpr int NVEC = KC ? PER : 4 * PER;  // 16-byte vectors held per thread
+
+    u32x4_t r[NVEC];
+    uint32_t okmask;  // bit i: vector r[i] lies inside the matrix (VEC loads)
+
+    // row-contiguous slot decoding: lanes 0..7 take 8 consecutive row groups,
+    // lane bit 3 the low bit of the k quad, so 16 consecutive lanes store to
+    // 16 distinct (chunk, half) positions.
+    __device__ __forceinline__ static void mn_slot(int id, int &rg, int &kq)
+    {
+        const int lo = id & 7, b3 = (id >> 3) & 1, rest = id >> 4;
+        // rest in [0, RGH*8) enumerates (row-group high part, k-quad high part)
+        const int rgh = rest % RGH, kqh = rest / RGH;
+        rg = rgh * 8 + lo;
+        kq = kqh * 2 + b3;
+    }
+
+    // VEC: the operand's leading dimension and K are multiples of 8, so every
+    // 16-byte vector is either wholly inside or wholly outside the matrix.
+    // Then each load is issued unconditionally (from offset 0 when outside)
+    // and zeroed by a select: no branches, so the compiler can count the
+    // loads in flight and wait only for the register set it stores next.
+    template <bool VEC>
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ X, int ld, int R, int K, int r0,
+                                         int k0, int tid)
+    {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int id = s * NT + tid;
+            if (KC) {
+                const int row = (id < SLOTS ? id : 0) >> 3, ch = id & 7;
+                const int rr = r0 + row, kk = k0 + ch * 8;
+                const bool ok = id < SLOTS && rr < R && kk < K;
+                if constexpr (VEC) {
+                    const long long off = ok ? (long long)rr * ld + kk : 0;
+                    r[s] = *(const u32x4_t *)(X + off);
+                    okmask = (s == 0 ? 0u : okmask) | ((ok ? 1u : 0u) << s);
+                } else {
+                    u32x4_t v = {0u, 0u, 0u, 0u};
+                    const long long off = (long long)rr * ld + kk;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        uint32_t hv = (ok && kk + e < K) ? (uint32_t)X[off + e] : 0u;
+                        v[e >> 1] |= hv << (16 * (e & 1));
+                    }
+                    r[s] = v;
+                }
+            } else {
+                int rg = 0, kq = 0;
+                if (id < SLOTS)
+                    mn_slot(id, rg, kq);
+                const bool live = id < SLOTS && rg < BR / 8;
+                const int rr = r0 + rg * 8;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kk = k0 + kq * 4 + i;
+                    const bool ok = live && kk < K && rr < R;
+                    if constexpr (VEC) {
+                        const long long off = ok ? (long long)kk * ld + rr : 0;
+                        r[4 * s + i] = *(const u32x4_t *)(X + off);
+                        okmask = (s == 0 && i == 0 ? 0u : okmask) | ((ok ? 1u : 0u) << (4 * s + i));
+                    } else {
+                        u32x4_t v = {0u, 0u, 0u, 0u};
+                        const long long off = (long long)kk * ld + rr;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            uint32_t hv = (ok && rr + e < R) ? (uint32_t)X[off + e] : 0u;
+                            v[e >> 1] |= hv << (16 * (e & 1));
+                        }
+                        r[4 * s + i] = v;
+                    }
+                }
+            }
+        }
+    }
+
+    // Writes the held vectors to LDS.  With VEC loads, vectors outside the
+    // matrix were loaded from offset 0 and are replaced by zeros here, so the
+    // wait for their data happens at the store, not at the load.
+    template <bool VEC>
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int id = s * NT + tid;
+            if constexpr (SLOTS % NT != 0) {
+                if (id >= SLOTS)
+                    break;
+            }
+            if (KC) {
+                const int row = id >> 3, ch = id & 7;
+                const u32x4_t v = (!VEC || ((okmask >> s) & 1u)) ? r[s] : z;
+                *(u32x4_t *)(lds + row * 128 + ((ch ^ swz(row)) << 4)) = v;
+            } else {
+                int rg, kq;
+                mn_slot(id, rg, kq);
+                if constexpr ((BR / 8) % 8 != 0) {
+                    if (rg >= BR / 8)
+                        continue;
+                }
+                const u32x4_t a = (!VEC || ((okmask >> (4 * s + 0)) & 1u)) ? r[4 * s + 0] : z;
+                const u32x4_t b = (!VEC || ((okmask >> (4 * s + 1)) & 1u)) ? r[4 * s + 1] : z;
+                const u32x4_t c = (!VEC || ((okmask >> (4 * s + 2)) & 1u)) ? r[4 * s + 2] : z;
+                const u32x4_t d = (!VEC || ((okmask >> (4 * s + 3)) & 1u)) ? r[4 * s + 3] : z;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // row rg*8+e: halves k = 4kq..4kq+3 taken from element e of a, b, c, d
+                    const int w = e >> 1;
+                    uint32_t lo, hi;
+                    if (e & 1) {
+                        lo = (a[w] >> 16) | (b[w] & 0xffff0000u);
+                        hi = (c[w] >> 16) | (d[w] & 0xffff0000u);
+                    } else {
+                        lo = (a[w] & 0xffffu) | (b[w] << 16);
+                        hi = (c[w] & 0xffffu) | (d[w] << 16);
+                    }
+                    const int row = rg * 8 + e;
+                    const int ch = kq >> 1;
+                    u32x2_t v = {lo, hi};
+                    *(u32x2_t *)(lds + row * 128 + ((ch ^ swz(row)) << 4) + ((kq & 1) << 3)) = v;
+                }
+            }
+        }
+    }
+};
+
+// 16-byte fragment: row `row`, 8 consecutive k = 16q + 8h .. +7.
+__device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h)
+{
+    const int ch = 2 * q + h;
+    return *(const u32x4_t *)(lds + row * 128 + ((ch ^ swz(row)) << 4));
+}
+
+template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC>
+__global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
+{
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = 64;
+    static_assert(NWM * NWN == 4, "four wavefronts per workgroup");
+    using TA = Tile16<BM, A_KC>;
+    using TB = Tile16<BN, B_KC>;
+    constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % NWM, wn = wave / NWM;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const int mt = (p.M + BM - 1) / BM;
+    const int ntiles = mt * ((p.N + BN - 1) / BN);
+    const int tile = xcd_tile(blockIdx.x, ntiles);
+    const int m_blk = (tile % mt) * BM;
+    const int n_blk = (tile / mt) * BN;
+
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    TA ta0, ta1;
+    TB tb0, tb1;
+
+    auto compute = [&](const char *la, const char *lb) {
+#pragma unroll
+        for (int q = 0; q < BK / 16; ++q) {
+            u32x4_t af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = frag16(la, (wm * TM + i) * 32 + l32, q, h);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bf[j] = frag16(lb, (wn * TN + j) * 32 + l32, q, h);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = mfma16<DTID>(af[i], bf[j], acc[i][j]);
+        }
+    };
+
+    if (nk > 0) {
+        // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
+        ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg, tid);
+        tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg, tid);
+        if (nk > 1) {
+            ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + BK, tid);
+            tb1.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + BK, tid);
+        }
+        ta0.template store<VEC>(smem, tid);
+        tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
+        __syncthreads();
+        if (nk > 2) {
+            ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + 2 * BK, tid);
+            tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + 2 * BK, tid);
+        }
+        // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
+        // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
+        // it is then refilled with stage t+3.  Two stages per iteration keep
+        // each register set in fixed registers; an odd last stage is peeled.
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            compute(smem, smem + TA::LDS_BYTES);
+            ta1.template store<VEC>(smem + STAGE, tid);
+            tb1.template store<VEC>(smem + STAGE + TA::LDS_BYTES, tid);
+            __syncthreads();
+            if (t + 3 < nk) {
+                ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 3) * BK, tid);
+                tb1.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + (t + 3) * BK, tid);
+            }
+            compute(smem + STAGE, smem + STAGE + TA::LDS_BYTES);
+            if (t + 2 < nk) {
+                ta0.template store<VEC>(smem, tid);
+                tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
+            }
+            __syncthreads();
+            if (t + 4 < nk) {
+                ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 4) * BK, tid);
+                tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + (t + 4) * BK, tid);
+            }
+        }
+        if (t < nk)
+            compute(smem, smem + TA::LDS_BYTES);
+    }
+
+    // Epilogue: accumulator element e of a 32x32 block is row
+    // 8*(e/4) + 4*h + (e%4), column l32.
+    float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n_blk + (wn * TN + j) * 32 + l32;
+        if (n >= p.N)
+            continue;
+        long long col_off;
+        if (p.epi == EPI_NCHW) {
+            const int b = n / p.P;
+            col_off = (long long)b * p.M * p.P + (n - b * p.P);
+        } else {
+            col_off = n;
+        }
+        const long long row_stride = (p.epi == EPI_NCHW) ? p.P : p.ldc;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m_blk + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < p.M) {
+                    float v = acc[i][j][e];
+                    if (p.epi == EPI_NCHW && p.bias)
+                        v += p.bias[m];
+                    C[col_off + (long long)m * row_stride] = v;
+                }
+            }
+        }
+    }
+}
+
+template <int DTID, bool A_KC, bool B_KC, bool VEC>
+hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
+{
+    TileShape ts = tile_shape(cfg);
+    const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
+    const dim3 grid(tiles, 1, p.splits), block(256);
+    switch (cfg) {
+    case TILE_128x128:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    case TILE_64x64:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    case TILE_32x128:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    case TILE_96x128:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    case TILE_128x256:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 4, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    case TILE_256x128:
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 4, 2, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int DTID, bool A_KC, bool B_KC>
+hipError_t launch_gemm16_layout(int cfg, const GemmParams &p, hipStream_t s)
+{
+    if (p.a_vec && p.b_vec)
+        return launch_gemm16_vec<DTID, A_KC, B_KC, true>(cfg, p, s);
+    return launch_gemm16_vec<DTID, A_KC, B_KC, false>(cfg, p, s);
+}
+
+template <int DTID>
+hipError_t launch_gemm16(int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
+{
+    if (a_kc && b_kc)
+        return launch_gemm16_layout<DTID, true, true>(cfg, p, s);
+    if (a_kc && !b_kc)
+        return launch_gemm16_layout<DTID, true, false>(cfg, p, s);
+    if (!a_kc && b_kc)
+        return launch_gemm16_layout<DTID, false, true>(cfg, p, s);
+    return launch_gemm16_layout<DTID, false, false>(cfg, p, s);
+}
+
+}  // namespace d4r

@@ -20,6 +20,8 @@
 //    for A and B.
 //  * Out-of-range rows and k are zero-filled in LDS; the MFMAs run on whole
 //    blocks and the epilogue masks the stores.
+//  * Workgroups are renumbered so that consecutive tiles share an XCD (and
+//    its L2).
 #pragma once
 
 #include "internal.hpp"
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     const int h = lane >> 5, l32 = lane & 31;
 
     const int mt = (p.M + BM - 1) / BM;
-    const int tile = blockIdx.x;
+    const int tile = xcd_tile(blockIdx.x, mt * ((p.N + BN - 1) / BN));
     const int m_blk = (tile % mt) * BM;
     const int n_blk = (tile / mt) * BN;
 
@@ -325,9 +327,11 @@ hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
     case TILE_32x128:
         hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 1, 1, A_KC, B_KC>), grid, dim3(256), 0, s, p);
         break;
-    default:
+    case TILE_96x128:
         hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 3, 1, A_KC, B_KC>), grid, dim3(256), 0, s, p);
         break;
+    default:
+        return hipErrorInvalidValue;  // tile shape not built for this dtype
     }
     return hipGetLastError();
 }

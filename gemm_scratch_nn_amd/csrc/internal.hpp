@@ -19,7 +19,9 @@ enum TileCfg : int {
     TILE_64x64 = 1,    // 2x2 waves, 1x1 block
     TILE_32x128 = 2,   // 1x4 waves, 1x1 block (M <= 32)
     TILE_96x128 = 3,   // 1x4 waves, 3x1 blocks (M = 96)
-    TILE_COUNT = 4
+    TILE_128x256 = 4,  // 2x2 waves, 2x4 blocks (16-bit operands only)
+    TILE_256x128 = 5,  // 2x2 waves, 4x2 blocks (16-bit operands only)
+    TILE_COUNT = 6
 };
 
 struct TileShape { int bm, bn; };
@@ -29,8 +31,26 @@ inline TileShape tile_shape(int cfg)
     case TILE_128x128: return {128, 128};
     case TILE_64x64: return {64, 64};
     case TILE_32x128: return {32, 128};
-    default: return {96, 128};
+    case TILE_96x128: return {96, 128};
+    case TILE_128x256: return {128, 256};
+    default: return {256, 128};
     }
+}
+
+// Bijective renumbering of workgroup ids so that the ids the dispatcher
+// deals to one XCD (round-robin over the 8 XCDs of MI355X, each with its own
+// L2) form one contiguous range of tiles.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int pid, int n)
+{
+    const int per = (n + kXcds - 1) / kXcds;
+    int tall = n % kXcds;
+    if (tall == 0)
+        tall = kXcds;
+    const int xcd = pid % kXcds, local = pid / kXcds;
+    if (xcd < tall)
+        return xcd * per + local;
+    return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
 enum Epilogue : int {

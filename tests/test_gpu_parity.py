@@ -322,3 +322,36 @@ def test_forward_without_bias():
     torch.cuda.synchronize()
     ref = oracle.conv_forward(ops["x"].exact, ops["w"].exact, None, 1, 1)
     assert rel_err(host(y), ref) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# every GEMM tile configuration on ragged shapes (planner override)
+# ---------------------------------------------------------------------------
+
+TILES = {"f32": ["128x128", "64x64", "32x128", "96x128"],
+         "f16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"],
+         "bf16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"]}
+
+
+@pytest.mark.parametrize("dt,tile", [(d, t) for d in TILES for t in TILES[d]])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_gemm_every_tile_config(dt, tile, flags, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    for (M, K, N) in [(300, 200, 333), (97, 1000, 65), (257, 136, 520)]:
+        rng = np.random.default_rng(M + K + N + flags)
+        a = wl.quantize(rng.normal(size=(K, M) if flags & 1 else (M, K)), dt)
+        b = wl.quantize(rng.normal(size=(N, K) if flags & 2 else (K, N)), dt)
+        ref = oracle.gemm(a.exact, b.exact, M, K, N, flags)
+        C = d4r.gemm(dev(a), dev(b), M, K, N, flags)
+        torch.cuda.synchronize()
+        err = rel_err(host(C), ref)
+        assert err < TOL[dt], (tile, M, K, N, err)
+
+
+@pytest.mark.parametrize("tile", ["128x128", "128x256", "256x128"])
+def test_conv_bf16_every_big_tile(tile, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[2].shape.with_batch(3)
+    ops = wl.conv_inputs(w, 2, "bf16", batch=3)
+    _check_whole(sh, "bf16", ops, f"c4/conv5/b3/{tile}")
