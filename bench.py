@@ -47,6 +47,9 @@ def parse_args():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", default=None, help="write per-kernel detail JSON here")
+    ap.add_argument("--forward", choices=("explicit", "implicit"), default="explicit",
+                    help="explicit: im2col + GEMM (col saved for the filter gradient); "
+                         "implicit: implicit-GEMM forward, im2col redone in the filter gradient")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (counter "
                          "calibration for rocprofv3 --pmc runs; untimed)")
@@ -141,12 +144,18 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    implicit = args.forward == "implicit"
+
     def step():
         for layer, pl, t in layers:
-            d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
+            if implicit:
+                d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes,
+                                              stream)
+            else:
+                d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
             d4r.d4r_conv_backward_data(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
-            d4r.d4r_conv_backward_filter(pl.h, None, t["g"], t["dw"], t["db"], 1, pl.ws, pl.ws_bytes,
-                                         stream)
+            d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
+                                         0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
 
     for _ in range(args.warmup):
         step()
@@ -231,7 +240,7 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "step_gflop": step_flops / 1e9},
+                   "dtype": dtype, "forward": args.forward, "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],
         "gemm_TFLOPs": gemm_tf,
         "gemm_frac_mfma": gemm_tf / MFMA_PEAK[dtype],

@@ -71,6 +71,8 @@ _c = {
     "d4r_conv_output_dims": _sig("d4r_conv_output_dims", [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "d4r_conv_workspace_size": _sig("d4r_conv_workspace_size", [_vp, ctypes.POINTER(_sz)]),
     "d4r_conv_forward": _sig("d4r_conv_forward", [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_conv_forward_implicit": _sig("d4r_conv_forward_implicit",
+                                      [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_data": _sig("d4r_conv_backward_data", [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_filter": _sig("d4r_conv_backward_filter",
                                      [_vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -186,6 +188,13 @@ def d4r_conv_forward(h, x, w, bias, y, ws, ws_bytes=None, stream=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_conv_forward", _c["d4r_conv_forward"](h, _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
                                                       _ptr(ws), nb, _stream(stream)))
+
+
+def d4r_conv_forward_implicit(h, x, w, bias, y, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_conv_forward_implicit",
+           _c["d4r_conv_forward_implicit"](h, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(ws), nb,
+                                           _stream(stream)))
 
 
 def d4r_conv_backward_data(h, w, dy, dx, ws, ws_bytes=None, stream=None) -> None:
@@ -319,6 +328,17 @@ class ConvPlan:
         if y is None:
             y = torch.empty(self.y_shape, dtype=torch.float32, device=x.device)
         d4r_conv_forward(self.h, x, w, bias, y, self.ws, self.ws_bytes)
+        return y
+
+    def forward_implicit(self, x, w, bias=None, y=None):
+        import torch
+        _require(x, "x", self.dtype, self.x_shape)
+        _require(w, "w", self.dtype, self.w_shape)
+        if bias is not None:
+            _require(bias, "bias", D4R_F32, (self.shape[8],))
+        if y is None:
+            y = torch.empty(self.y_shape, dtype=torch.float32, device=x.device)
+        d4r_conv_forward_implicit(self.h, x, w, bias, y, self.ws, self.ws_bytes)
         return y
 
     def backward_data(self, w, dy, dx=None):

@@ -241,9 +241,13 @@ std::string gemm_kernel_name(int dt, int cfg, bool a_kc, bool b_kc)
 }
 
 
+// Runs one planned GEMM (split-K partials + reduction when the plan splits).
+// With `implicit` set, B is the conv input x and op(B) = im2col(x) is
+// gathered inside the GEMM (A must be k-contiguous, B row-contiguous).
 hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
-                    const float *bias, int P, float *partial, hipStream_t s, const char *pass)
+                    const float *bias, int P, float *partial, hipStream_t s, const char *pass,
+                    const ConvGeom *implicit = nullptr)
 {
     const int vw = dt == DT_F32 ? 4 : 8;
     GemmParams p;
@@ -261,7 +265,11 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
     // vector loads need every 16-byte vector wholly inside or outside the
     // operand: leading dimension and the contiguous extent multiples of vw
     p.a_vec = (lda % vw) == 0 && ((a_kc ? K : M) % vw) == 0;
-    p.b_vec = (ldb % vw) == 0 && ((b_kc ? K : N) % vw) == 0;
+    p.b_vec = implicit ? 1 : ((ldb % vw) == 0 && ((b_kc ? K : N) % vw) == 0);
+    if (implicit)
+        p.g = *implicit;
+    else
+        memset(&p.g, 0, sizeof p.g);
     if (pl.splits > 1) {
         p.C = partial;
         p.ldc = N;
@@ -274,9 +282,11 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
         p.c_split_stride = 0;
     }
     const int es = dt_size(dt);
-    ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, a_kc, b_kc) + ":" + pass, 2.0 * M * N * K,
-                 (double)es * ((double)M * K + (double)K * N) + 4.0 * M * N);
-    hipError_t e = launch_gemm(dt, pl.cfg, a_kc, b_kc, p, s);
+    const double b_bytes = implicit ? (double)implicit->B * implicit->C * implicit->H * implicit->W
+                                    : (double)K * N;
+    ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, a_kc, b_kc) + (implicit ? "_implicit:" : ":") + pass,
+                 2.0 * M * N * K, (double)es * ((double)M * K + b_bytes) + 4.0 * M * N);
+    hipError_t e = implicit ? launch_gemm_implicit(dt, pl.cfg, p, s) : launch_gemm(dt, pl.cfg, a_kc, b_kc, p, s);
     ps.done();
     if (e != hipSuccess || pl.splits == 1)
         return e;
@@ -309,6 +319,19 @@ int gemm_bk(int dt) { return dt == DT_F32 ? 32 : 64; }
 hipError_t launch_gemm_f32(int, bool, bool, const GemmParams &, hipStream_t);
 hipError_t launch_gemm_f16(int, bool, bool, const GemmParams &, hipStream_t);
 hipError_t launch_gemm_bf16(int, bool, bool, const GemmParams &, hipStream_t);
+
+hipError_t launch_gemm_implicit_f32(int, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_implicit_f16(int, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_implicit_bf16(int, const GemmParams &, hipStream_t);
+
+hipError_t launch_gemm_implicit(int dt, int cfg, const GemmParams &p, hipStream_t s)
+{
+    switch (dt) {
+    case DT_F32: return launch_gemm_implicit_f32(cfg, p, s);
+    case DT_F16: return launch_gemm_implicit_f16(cfg, p, s);
+    default: return launch_gemm_implicit_bf16(cfg, p, s);
+    }
+}
 
 hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
 {
@@ -564,6 +587,25 @@ d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const fl
     D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
                         bias, g.P, partial, s, "fwd"),
                "forward GEMM");
+    return ok();
+}
+
+d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w, const float *bias,
+                                     float *y, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(y, "y"));
+    D4R_TRY(check_vec(bias, "bias"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const ConvGeom &g = h->g;
+    float *partial = (float *)((char *)ws + h->off_big);
+    D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0, bias,
+                        g.P, partial, s, "fwd", &g),
+               "implicit forward GEMM");
     return ok();
 }
 

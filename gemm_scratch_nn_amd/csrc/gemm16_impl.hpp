@@ -21,6 +21,8 @@
 //    with its own L2): the M tiles that share a B panel then share one L2.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace d4r {
@@ -185,6 +187,92 @@ struct Tile16 {
     }
 };
 
+// Forward-GEMM B operand gathered straight from x (the implicit GEMM), in the
+// row-contiguous path of Tile16: a thread gathers 4 kc rows x 8 consecutive
+// columns n per slot and stores them through the same in-register transpose.
+// The thread's 8 columns are fixed for the whole K loop, so their image
+// offsets and window origins are decoded once.
+// Image offsets and window origins of a thread's 8 columns (fixed for the
+// whole K loop, shared by both register sets).
+template <int BR>
+struct ImplicitCols16 {
+    int nb[8], nh[8], nw[8];  // image offset (-1 past N or unused), window origin
+
+    __device__ __forceinline__ void setup(const ConvGeom &g, int n_blk, int tid)
+    {
+        constexpr int RGH = Tile16<BR, false>::RGH;
+        const int rg = ((tid >> 4) % RGH) * 8 + (tid & 7);
+        const int n0 = n_blk + rg * 8;
+        int b = n0 / g.P;
+        int rem = n0 - b * g.P;
+        int i = rem / g.OW;
+        int j = rem - i * g.OW;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            nb[e] = (rg < BR / 8 && n0 + e < g.N) ? b * g.C * g.H * g.W : -1;
+            nh[e] = i * g.s - g.p;
+            nw[e] = j * g.s - g.p;
+            if (++j == g.OW) {
+                j = 0;
+                if (++i == g.OH) {
+                    i = 0;
+                    ++b;
+                }
+            }
+        }
+    }
+};
+
+template <int BR>
+struct ImplicitTile16 : Tile16<BR, false> {
+    using Base = Tile16<BR, false>;
+    using Base::NT;
+    using Base::PER;
+    using Base::SLOTS;
+    using Base::r;
+
+    __device__ __forceinline__ void gather(const uint16_t *__restrict__ x, const ConvGeom &g,
+                                           const ImplicitCols16<BR> &cols, int K, int k0, int tid)
+    {
+        const int *nb = cols.nb, *nh = cols.nh, *nw = cols.nw;
+        const int khw = g.kH * g.kW;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int id = s * NT + tid;
+            int rg = 0, kq = 0;
+            if (id < SLOTS)
+                Base::mn_slot(id, rg, kq);
+            const bool live = id < SLOTS && rg < BR / 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = k0 + kq * 4 + i;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (live && k < K) {
+                    const int c = k / khw;
+                    const int rr = k - c * khw;
+                    const int u = rr / g.kW;
+                    const int vv = rr - u * g.kW;
+                    const int plane = c * g.H * g.W;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int hh = nh[e] + u, ww = nw[e] + vv;
+                        const bool ok = nb[e] >= 0 && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W;
+                        const uint32_t hv = ok ? (uint32_t)x[nb[e] + plane + hh * g.W + ww] : 0u;
+                        v[e >> 1] |= hv << (16 * (e & 1));
+                    }
+                }
+                r[4 * s + i] = v;
+            }
+        }
+    }
+
+    template <bool VEC>
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+        Base::template store<false>(lds, tid);
+    }
+};
+
 // 16-byte fragment: row `row`, 8 consecutive k = 16q + 8h .. +7.
 __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h)
 {
@@ -192,13 +280,14 @@ __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h
     return *(const u32x4_t *)(lds + row * 128 + ((ch ^ swz(row)) << 4));
 }
 
-template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC>
+template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
 __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
 {
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = 64;
     static_assert(NWM * NWN == 4, "four wavefronts per workgroup");
+    static_assert(!IMPL || !B_KC, "implicit B uses the row-contiguous path");
     using TA = Tile16<BM, A_KC>;
-    using TB = Tile16<BN, B_KC>;
+    using TB = std::conditional_t<IMPL, ImplicitTile16<BN>, Tile16<BN, B_KC>>;
     constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -231,6 +320,16 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
     TA ta0, ta1;
     TB tb0, tb1;
 
+    ImplicitCols16<BN> cols;
+    if constexpr (IMPL)
+        cols.setup(p.g, n_blk, tid);
+    auto load_b = [&](TB &t, int k0) {
+        if constexpr (IMPL)
+            t.gather(B, p.g, cols, kend, k0, tid);
+        else
+            t.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
+    };
+
     auto compute = [&](const char *la, const char *lb) {
 #pragma unroll
         for (int q = 0; q < BK / 16; ++q) {
@@ -252,17 +351,17 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
     if (nk > 0) {
         // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
         ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg, tid);
-        tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg, tid);
+        load_b(tb0, kbeg);
         if (nk > 1) {
             ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + BK, tid);
-            tb1.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + BK, tid);
+            load_b(tb1, kbeg + BK);
         }
         ta0.template store<VEC>(smem, tid);
         tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
         __syncthreads();
         if (nk > 2) {
             ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + 2 * BK, tid);
-            tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + 2 * BK, tid);
+            load_b(tb0, kbeg + 2 * BK);
         }
         // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
         // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
@@ -276,7 +375,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
             __syncthreads();
             if (t + 3 < nk) {
                 ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 3) * BK, tid);
-                tb1.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + (t + 3) * BK, tid);
+                load_b(tb1, kbeg + (t + 3) * BK);
             }
             compute(smem + STAGE, smem + STAGE + TA::LDS_BYTES);
             if (t + 2 < nk) {
@@ -286,7 +385,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
             __syncthreads();
             if (t + 4 < nk) {
                 ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 4) * BK, tid);
-                tb0.template load<VEC>(B, p.ldb, p.N, kend, n_blk, kbeg + (t + 4) * BK, tid);
+                load_b(tb0, kbeg + (t + 4) * BK);
             }
         }
         if (t < nk)
@@ -325,7 +424,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
     }
 }
 
-template <int DTID, bool A_KC, bool B_KC, bool VEC>
+template <int DTID, bool A_KC, bool B_KC, bool VEC, bool IMPL = false>
 hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -333,22 +432,22 @@ hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
     const dim3 grid(tiles, 1, p.splits), block(256);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 4, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 4, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 4, 2, A_KC, B_KC, VEC>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 4, 2, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -362,6 +461,14 @@ hipError_t launch_gemm16_layout(int cfg, const GemmParams &p, hipStream_t s)
     if (p.a_vec && p.b_vec)
         return launch_gemm16_vec<DTID, A_KC, B_KC, true>(cfg, p, s);
     return launch_gemm16_vec<DTID, A_KC, B_KC, false>(cfg, p, s);
+}
+
+template <int DTID>
+hipError_t launch_gemm16_implicit(int cfg, const GemmParams &p, hipStream_t s)
+{
+    if (p.a_vec)
+        return launch_gemm16_vec<DTID, true, false, true, true>(cfg, p, s);
+    return launch_gemm16_vec<DTID, true, false, false, true>(cfg, p, s);
 }
 
 template <int DTID>

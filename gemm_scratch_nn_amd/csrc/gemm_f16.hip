@@ -8,4 +8,9 @@ hipError_t launch_gemm_f16(int cfg, bool a_kc, bool b_kc, const GemmParams &p, h
     return launch_gemm16<DT_F16>(cfg, a_kc, b_kc, p, s);
 }
 
+hipError_t launch_gemm_implicit_f16(int cfg, const GemmParams &p, hipStream_t s)
+{
+    return launch_gemm16_implicit<DT_F16>(cfg, p, s);
+}
+
 }  // namespace d4r

@@ -8,4 +8,9 @@ hipError_t launch_gemm_f32(int cfg, bool a_kc, bool b_kc, const GemmParams &p, h
     return launch_gemm_dt<DtF32>(cfg, a_kc, b_kc, p, s);
 }
 
+hipError_t launch_gemm_implicit_f32(int cfg, const GemmParams &p, hipStream_t s)
+{
+    return launch_gemm_layout<DtF32, true, false, true>(cfg, p, s);
+}
+
 }  // namespace d4r

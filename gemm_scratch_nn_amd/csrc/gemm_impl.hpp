@@ -24,6 +24,8 @@
 //    its L2).
 #pragma once
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace d4r {
@@ -132,6 +134,86 @@ struct OperandTile {
     }
 };
 
+// Forward-GEMM B operand gathered straight from x (the implicit GEMM):
+// op(B)[kc][n] = xt(b, c, i*s - p + u, j*s - p + v), kc = (c*kH + u)*kW + v,
+// n = (b*OH + i)*OW + j, stored in the same [k][n] LDS layout as a
+// row-contiguous operand.  A thread's four columns n are the same in every
+// K stage, so their image offsets and window origins are decoded once; each
+// stage decodes only the thread's kc rows.
+template <int BR, int NT>
+struct ImplicitTileF32 {
+    using Base = OperandTile<DtF32, BR, false, NT>;
+    static constexpr int VW = 4, BK = 32;
+    static constexpr int PITCH = Base::PITCH, LDS_BYTES = Base::LDS_BYTES;
+    static constexpr int NV = Base::NV, PER = Base::PER;
+    static_assert(NT % (BR / VW) == 0, "a thread's columns must not change between slots");
+
+    u32x4 reg[PER];
+    int nb[VW], nh[VW], nw[VW];  // image offset (-1 past N), window origin row / column
+
+    __device__ __forceinline__ void setup(const ConvGeom &g, int n_blk, int tid)
+    {
+        const int n0 = n_blk + (tid % (BR / VW)) * VW;
+        int b = n0 / g.P;
+        int rem = n0 - b * g.P;
+        int i = rem / g.OW;
+        int j = rem - i * g.OW;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+            nb[e] = (n0 + e < g.N) ? b * g.C * g.H * g.W : -1;
+            nh[e] = i * g.s - g.p;
+            nw[e] = j * g.s - g.p;
+            if (++j == g.OW) {
+                j = 0;
+                if (++i == g.OH) {
+                    i = 0;
+                    ++b;
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ x, const ConvGeom &g, int K, int k0,
+                                         int tid)
+    {
+        const int khw = g.kH * g.kW;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int id = s * NT + tid;
+            if (NV % NT != 0 && id >= NV)
+                break;
+            const int k = k0 + id / (BR / VW);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k < K) {
+                const int c = k / khw;
+                const int r = k - c * khw;
+                const int u = r / g.kW;
+                const int vv = r - u * g.kW;
+                const int plane = c * g.H * g.W;
+#pragma unroll
+                for (int e = 0; e < VW; ++e) {
+                    const int hh = nh[e] + u, ww = nw[e] + vv;
+                    const bool ok = nb[e] >= 0 && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W;
+                    v[e] = ok ? x[nb[e] + plane + hh * g.W + ww] : 0u;
+                }
+            }
+            reg[s] = v;
+        }
+    }
+
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int id = s * NT + tid;
+            if (NV % NT != 0 && id >= NV)
+                break;
+            const int kk = id / (BR / VW), row = (id % (BR / VW)) * VW;
+            *(u32x4 *)(lds + (kk * PITCH + row) * 4) = reg[s];
+        }
+    }
+};
+
 // Fragment reads.  f32: 8 consecutive k (one k group of 16, lane half h)
 // for one 32-row block; the 8 MFMAs of the group use element t.
 template <bool KC, int PITCH>
@@ -182,15 +264,16 @@ __device__ __forceinline__ f32x16 mfma_h(u32x4 a, u32x4 b, f32x16 c)
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <class DT, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC>
+template <class DT, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool IMPL>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = NWM * NWN * 64;
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
     using TR = GemmTraits<DT>;
     constexpr int BK = TR::BK;
+    static_assert(!IMPL || (!B_KC && DT::ID == DT_F32), "implicit B: f32, [k][n] layout");
     using TA = OperandTile<DT, BM, A_KC, NT>;
-    using TB = OperandTile<DT, BN, B_KC, NT>;
+    using TB = std::conditional_t<IMPL, ImplicitTileF32<BN, NT>, OperandTile<DT, BN, B_KC, NT>>;
     __shared__ __attribute__((aligned(16))) char smem[2 * (TA::LDS_BYTES + TB::LDS_BYTES)];
 
     const int tid = threadIdx.x;
@@ -221,9 +304,17 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     const char *Ab = (const char *)p.A;
     const char *Bb = (const char *)p.B;
     // K bound for this split: the loaders zero-fill k >= kend.
+    auto load_b = [&](int k0) {
+        if constexpr (IMPL)
+            tb.load((const uint32_t *)p.B, p.g, kend, k0, tid);
+        else
+            tb.load(Bb, p.ldb, p.N, kend, n_blk, k0, p.b_vec, tid);
+    };
+    if constexpr (IMPL)
+        tb.setup(p.g, n_blk, tid);
     if (nk > 0) {
         ta.load(Ab, p.lda, p.M, kend, m_blk, kbeg, p.a_vec, tid);
-        tb.load(Bb, p.ldb, p.N, kend, n_blk, kbeg, p.b_vec, tid);
+        load_b(kbeg);
     }
     for (int kt = 0; kt < nk; ++kt) {
         char *la = smem + (kt & 1) * (TA::LDS_BYTES + TB::LDS_BYTES);
@@ -234,7 +325,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
         if (kt + 1 < nk) {
             int k0 = kbeg + (kt + 1) * BK;
             ta.load(Ab, p.lda, p.M, kend, m_blk, k0, p.a_vec, tid);
-            tb.load(Bb, p.ldb, p.N, kend, n_blk, k0, p.b_vec, tid);
+            load_b(k0);
         }
         if constexpr (DT::ID == DT_F32) {
             const float *fa = (const float *)la;
@@ -311,7 +402,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     }
 }
 
-template <class DT, bool A_KC, bool B_KC>
+template <class DT, bool A_KC, bool B_KC, bool IMPL = false>
 hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -319,16 +410,16 @@ hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
     dim3 grid(tiles, 1, p.splits);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 2, 2, A_KC, B_KC>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 2, 2, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 1, 1, A_KC, B_KC>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 1, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 1, 1, A_KC, B_KC>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 1, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 3, 1, A_KC, B_KC>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 3, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;  // tile shape not built for this dtype

@@ -58,6 +58,13 @@ enum Epilogue : int {
     EPI_NCHW = 1       // y[((n/P)*M + m)*P + n%P] = acc + bias[m]
 };
 
+struct ConvGeom {
+    int B, C, H, W, O, kH, kW, s, p, OH, OW;
+    int P;    // OH*OW
+    int Kc;   // C*kH*kW
+    int N;    // B*P
+};
+
 // C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
 // Operand "rows" are m for A and n for B.  a_kc / b_kc: the operand is
 // stored with k contiguous (A[m*lda + k], B[n*ldb + k]); otherwise the row
@@ -75,18 +82,17 @@ struct GemmParams {
     int splits;
     long long c_split_stride;
     int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned)
+    ConvGeom g;         // implicit B operand: B = x and op(B)[kc][n] = im2col(x)
 };
 
 hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p,
                        hipStream_t s);
+// Forward GEMM whose B operand is the im2col of x (p.B = x, geometry p.g),
+// gathered into LDS by the loader: A = Wmat (k contiguous), NCHW epilogue.
+hipError_t launch_gemm_implicit(int dt, int cfg, const GemmParams &p, hipStream_t s);
 int gemm_bk(int dt);  // K depth of one LDS stage, in elements
 
-struct ConvGeom {
-    int B, C, H, W, O, kH, kW, s, p, OH, OW;
-    int P;    // OH*OW
-    int Kc;   // C*kH*kW
-    int N;    // B*P
-};
+
 
 hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s);
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s);

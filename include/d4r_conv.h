@@ -128,6 +128,18 @@ d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w,
                             size_t ws_bytes, void *hip_stream);
 
 /*
+ * Forward as an implicit GEMM (same result as d4r_conv_forward up to
+ * summation order; the mlvc.cpp design page runs dense spatial convolution
+ * as an implicit GEMM, "Driver-only AOT cubin direction").  The GEMM gathers
+ * each col tile from x into on-chip memory, so the col matrix is never
+ * written: ws is used only for split-K partial sums and does NOT hold col
+ * afterwards (a following d4r_conv_backward_filter must pass reuse_col = 0).
+ */
+d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
+                                     const float *bias, float *y, void *ws,
+                                     size_t ws_bytes, void *hip_stream);
+
+/*
  * Data gradient (page: Input gradients = filters^T x grad_reshaped, then
  * col2im): dx = col2im(Wmat^T * G).  w, dy in the handle's dtype; dx
  * float32, fully overwritten.  dcol is float32 in ws, after the col region.

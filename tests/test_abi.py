@@ -13,7 +13,8 @@ MISALIGNED = (1 << 20) + 4
 def test_every_declared_symbol_is_exported():
     names = d4r.declared_functions()
     expected = {"d4r_conv_create", "d4r_conv_destroy", "d4r_conv_output_dims",
-                "d4r_conv_workspace_size", "d4r_conv_forward", "d4r_conv_backward_data",
+                "d4r_conv_workspace_size", "d4r_conv_forward", "d4r_conv_forward_implicit",
+                "d4r_conv_backward_data",
                 "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
                 "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
                 "d4r_status_string", "d4r_last_error", "d4r_profile_enable",
@@ -110,6 +111,16 @@ def test_forward_argument_errors(handle):
             d4r.d4r_conv_forward(handle, x, w, b, y, wsp, nb, stream=0)
         assert e.value.status == code, (x, w, b, y, wsp, nb)
         assert d4r.d4r_last_error()
+
+
+def test_forward_implicit_argument_errors(handle):
+    ws = _ws(handle)
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_forward_implicit(handle, None, FAKE, None, FAKE, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_forward_implicit(handle, FAKE, FAKE, None, FAKE, FAKE, ws - 1, stream=0)
+    assert e.value.status == WORKSPACE
 
 
 def test_backward_argument_errors(handle):

@@ -355,3 +355,58 @@ def test_conv_bf16_every_big_tile(tile, monkeypatch):
     sh = w.layers[2].shape.with_batch(3)
     ops = wl.conv_inputs(w, 2, "bf16", batch=3)
     _check_whole(sh, "bf16", ops, f"c4/conv5/b3/{tile}")
+
+
+# ---------------------------------------------------------------------------
+# implicit-GEMM forward (no col matrix in HBM)
+# ---------------------------------------------------------------------------
+
+def _check_implicit(sh, dt, ops, tag, sample=False):
+    _say("implicit fwd", tag, sh, dt)
+    pl = _plan(sh, dt)
+    x, w, bias = dev(ops["x"]), dev(ops["w"]), dev(ops["bias"])
+    y = pl.forward_implicit(x, w, bias)
+    y2 = pl.forward(x, w, bias)
+    torch.cuda.synchronize()
+    s, p = sh.stride, sh.padding
+    if sample:
+        bs = _sample_idx(sh.batch, 2)
+        os_ = _sample_idx(sh.outC, 6)
+        ref = oracle.conv_forward(ops["x"].exact[bs], ops["w"].exact[os_], ops["bias"].exact[os_], s, p)
+        got = host(y)[np.ix_(bs, os_)]
+    else:
+        ref = oracle.conv_forward(ops["x"].exact, ops["w"].exact, ops["bias"].exact, s, p)
+        got = host(y)
+    err = rel_err(got, ref)
+    _say("  rel err", err, "vs explicit", rel_err(host(y), host(y2)))
+    assert err < TOL[dt], (tag, err)
+
+
+@pytest.mark.parametrize("t", TINY, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_implicit_forward_tiny(t, dt):
+    sh = _shape(t)
+    _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=sum(t) + 7), "tiny")
+
+
+@pytest.mark.parametrize("key,li,dt,batch", _config_cases(REDUCED), ids=str)
+def test_implicit_forward_configs(key, li, dt, batch):
+    w = wl.WORKLOADS[key]
+    sh = w.layers[li].shape.with_batch(batch)
+    _check_implicit(sh, dt, wl.conv_inputs(w, li, dt, batch=batch), f"{key}/{w.layers[li].name}/b{batch}")
+
+
+@pytest.mark.parametrize("key,li,dt", [(k, li, dt) for k, w in wl.WORKLOADS.items()
+                                       for li in range(len(w.layers)) for dt in w.dtypes], ids=str)
+def test_implicit_forward_full_size_sampled(key, li, dt):
+    w = wl.WORKLOADS[key]
+    _check_implicit(w.layers[li].shape, dt, wl.conv_inputs(w, li, dt), f"{key}/full", sample=True)
+
+
+@pytest.mark.parametrize("dt,tile", [(d, t) for d in TILES for t in TILES[d]])
+def test_implicit_forward_every_tile(dt, tile, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    sh = _shape((3, 7, 23, 29, 65, 5, 3, 2, 2))
+    _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=11), f"tile {tile}")
+    sh = _shape((2, 17, 12, 12, 130, 3, 3, 1, 1))
+    _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=12), f"tile {tile}")
