@@ -101,6 +101,128 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
 }
 
 // ---------------------------------------------------------------------------
+// im2col through LDS.  A block owns one channel c, images [b0, b0+BB) and
+// output rows [i0, i1) (a row range only when BB = 1).  It copies the
+// zero-padded input window those outputs read into LDS with coalesced loads,
+// then writes, for every tap (u, v), the col segment of its outputs, which
+// is one contiguous run n = (b0*OH + i0)*OW .. of BB*(i1-i0)*OW elements, with
+// 16-byte stores (element stores at the two unaligned ends).  x is read from
+// HBM once, col written once in long runs.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x, T *__restrict__ col,
+                                                        ConvGeom g, int RB, int BB, int Rl, int Wl,
+                                                        int vec_store)
+{
+    constexpr int VW = Vec16<T>::N;
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    T *lds = (T *)lds_raw;
+    const int c = blockIdx.y;
+    const int b0 = blockIdx.z * BB;
+    const int nbb = min(BB, g.B - b0);
+    const int i0 = blockIdx.x * RB;
+    const int i1 = min(g.OH, i0 + RB);
+    const int rows = i1 - i0;
+    const int plane = Rl * Wl;
+    const int h_org = i0 * g.s - g.p, w_org = -g.p;
+
+    // Fill: a thread keeps one window column q and walks the window rows
+    // (rows_per_pass of them are filled per pass), so no per-element division.
+    {
+        const int rpp = Wl <= NT ? NT / Wl : 1;
+        const int r_off = Wl <= NT ? threadIdx.x / Wl : 0;
+        const int q0 = Wl <= NT ? threadIdx.x - r_off * Wl : threadIdx.x;
+        const int total_rows = nbb * Rl;
+        if (r_off < rpp) {
+            int bb = 0, r = r_off;
+            while (r >= Rl) {
+                r -= Rl;
+                ++bb;
+            }
+            for (int rr = r_off; rr < total_rows; rr += rpp) {
+                const int hh = h_org + r;
+                const bool row_ok = hh >= 0 && hh < g.H;
+                const long long xrow = (((long long)(b0 + bb) * g.C + c) * g.H + hh) * g.W;
+                T *drow = lds + (bb * Rl + r) * Wl;
+                for (int q = q0; q < Wl; q += (Wl <= NT ? Wl : NT)) {
+                    const int ww = w_org + q;
+                    T val = 0;
+                    if (row_ok && ww >= 0 && ww < g.W)
+                        val = x[xrow + ww];
+                    drow[q] = val;
+                }
+                r += rpp;
+                while (r >= Rl) {
+                    r -= Rl;
+                    ++bb;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // Output phase: a thread owns one 16-byte vector of columns, resolves its
+    // VW LDS offsets once, then walks every tap (u, v): one LDS read per
+    // element and one store per tap (the window in LDS already holds the
+    // padding zeros).
+    const int khw = g.kH * g.kW;
+    const int n_start = (b0 * g.OH + i0) * g.OW;
+    const int per_img = rows * g.OW;
+    const int L = nbb * per_img;
+    const int n_al = n_start - (n_start % VW);
+    const int nvec = (n_start + L - n_al + VW - 1) / VW;
+    const long long row_stride = g.N;
+    for (int q = threadIdx.x; q < nvec; q += NT) {
+        const int n0 = n_al + q * VW;
+        const int lo = n0 - n_start;
+        int off[VW];
+        bool in[VW];
+        {
+            const int e0 = lo < 0 ? -lo : 0;
+            const int loc = lo + e0;
+            int bb = loc / per_img;
+            const int rem = loc - bb * per_img;
+            int il = rem / g.OW;
+            int j = rem - il * g.OW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                in[e] = e >= e0 && lo + e < L;
+                off[e] = in[e] ? bb * plane + il * g.s * Wl + j * g.s : 0;
+                if (in[e]) {
+                    if (++j == g.OW) {
+                        j = 0;
+                        if (++il == rows) {
+                            il = 0;
+                            ++bb;
+                        }
+                    }
+                }
+            }
+        }
+        const bool full = vec_store && lo >= 0 && lo + VW <= L;
+        T *dst = col + (long long)c * khw * row_stride + n0;
+        for (int u = 0; u < g.kH; ++u) {
+            for (int v = 0; v < g.kW; ++v) {
+                const int tap = u * Wl + v;
+                typename Vec16<T>::type out;
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    out[e] = lds[off[e] + tap];
+                if (full) {
+                    *(typename Vec16<T>::type *)dst = out;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VW; ++e)
+                        if (in[e])
+                            dst[e] = out[e];
+                }
+                dst += row_stride;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // col2im as a gather: one thread per dx element (b, c, h, w) sums the dcol
 // entries that im2col copied from (b, c, h, w).  Tap u contributes when
 // h + p - u >= 0, divisible by s and (h + p - u)/s < OH, i.e. u runs over one
@@ -110,12 +232,8 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
 // before the adds; TU = TV = 0 is the general loop.
 // ---------------------------------------------------------------------------
 template <int TU, int TV>
-__global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dcol,
-                                                    float *__restrict__ dx, ConvGeom g, int total)
+__device__ __forceinline__ float col2im_one(const float *__restrict__ dcol, const ConvGeom &g, int idx)
 {
-    const int idx = blockIdx.x * NT + threadIdx.x;
-    if (idx >= total)
-        return;
     const int w = idx % g.W;
     int t = idx / g.W;
     const int h = t % g.H;
@@ -169,7 +287,134 @@ __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dc
             }
         }
     }
-    dx[idx] = acc;
+    return acc;
+}
+
+// A thread computes COLS_PER_THREAD dx elements NT apart (so the lanes of a
+// wavefront stay on consecutive elements for every tap); with the tap counts
+// fixed at compile time all their loads are in flight before the first add.
+constexpr int COLS_PER_THREAD = 4;
+
+template <int TU, int TV>
+__global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dcol,
+                                                    float *__restrict__ dx, ConvGeom g, int total)
+{
+    const int base = blockIdx.x * NT * COLS_PER_THREAD + threadIdx.x;
+    float r[COLS_PER_THREAD];
+#pragma unroll
+    for (int e = 0; e < COLS_PER_THREAD; ++e) {
+        const int idx = base + e * NT;
+        r[e] = (idx < total) ? col2im_one<TU, TV>(dcol, g, idx) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < COLS_PER_THREAD; ++e) {
+        const int idx = base + e * NT;
+        if (idx < total)
+            dx[idx] = r[e];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// col2im as the adjoint of the LDS im2col.  A block owns channel c and whole
+// images [b0, b0+BB); LDS holds their zero-initialised padded windows (the
+// same window im2col reads).  A thread owns up to QMAX 16-byte vectors of
+// dcol columns n and resolves their window offsets once; then, tap by tap in
+// the order u ascending, v ascending, it loads its dcol vectors (coalesced)
+// and adds each value into the window position the column read in im2col.
+// Within one tap every column hits a distinct position, and a barrier
+// separates taps, so each dx element is summed in the fixed tap order with
+// no atomics.  Finally the window interior is written to dx.
+// ---------------------------------------------------------------------------
+constexpr int C2I_QMAX = 4;
+
+__global__ __launch_bounds__(NT) void col2im_lds_kernel(const float *__restrict__ dcol,
+                                                        float *__restrict__ dx, ConvGeom g, int BB,
+                                                        int Rl, int Wl, int vec_load)
+{
+    constexpr int VW = 4;
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    float *lds = (float *)lds_raw;
+    const int c = blockIdx.y;
+    const int b0 = blockIdx.z * BB;
+    const int nbb = min(BB, g.B - b0);
+    const int plane = Rl * Wl;
+    for (int t = threadIdx.x; t < nbb * plane; t += NT)
+        lds[t] = 0.0f;
+
+    const int n_start = b0 * g.P;
+    const int L = nbb * g.P;
+    const int n_al = n_start - (n_start % VW);
+    const int nvec = (n_start + L - n_al + VW - 1) / VW;
+    int off[C2I_QMAX][VW];
+    bool in[C2I_QMAX][VW];
+#pragma unroll
+    for (int qi = 0; qi < C2I_QMAX; ++qi) {
+        const int q = threadIdx.x + qi * NT;
+        const int n0 = n_al + q * VW;
+        const int lo = n0 - n_start;
+        const int e0 = lo < 0 ? -lo : 0;
+        const int loc = lo + e0;
+        int bb = loc / g.P;
+        const int rem = loc - bb * g.P;
+        int i = rem / g.OW;
+        int j = rem - i * g.OW;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+            in[qi][e] = q < nvec && e >= e0 && lo + e < L;
+            off[qi][e] = in[qi][e] ? bb * plane + i * g.s * Wl + j * g.s : 0;
+            if (in[qi][e] && ++j == g.OW) {
+                j = 0;
+                if (++i == g.OH) {
+                    i = 0;
+                    ++bb;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int khw = g.kH * g.kW;
+    const float *src = dcol + (long long)c * khw * g.N + n_al;
+    for (int u = 0; u < g.kH; ++u) {
+        for (int v = 0; v < g.kW; ++v) {
+            const int tap = u * Wl + v;
+#pragma unroll
+            for (int qi = 0; qi < C2I_QMAX; ++qi) {
+                const int q = threadIdx.x + qi * NT;
+                if (q < nvec) {
+                    float val[VW];
+                    if (vec_load && in[qi][0] && in[qi][VW - 1]) {
+                        const float4 f = *(const float4 *)(src + q * VW);
+                        val[0] = f.x;
+                        val[1] = f.y;
+                        val[2] = f.z;
+                        val[3] = f.w;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VW; ++e)
+                            val[e] = in[qi][e] ? src[q * VW + e] : 0.0f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < VW; ++e)
+                        if (in[qi][e])
+                            lds[off[qi][e] + tap] += val[e];
+                }
+            }
+            src += g.N;
+            __syncthreads();
+        }
+    }
+
+    const int hw = g.H * g.W;
+    for (int t = threadIdx.x; t < nbb * hw; t += NT) {
+        const int bb = t / hw;
+        const int r = t - bb * hw;
+        const int h = r / g.W;
+        const int w = r - h * g.W;
+        const int wr = h + g.p, wc = w + g.p;
+        const float val = (wr < Rl && wc < Wl) ? lds[bb * plane + wr * Wl + wc] : 0.0f;
+        dx[(((long long)(b0 + bb) * g.C + c) * g.H + h) * g.W + w] = val;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -323,6 +568,43 @@ inline dim3 grid2(long long x, long long y)
 hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s)
 {
     const int VW = dt == DT_F32 ? 4 : 8;
+    const int es = dt == DT_F32 ? 4 : 2;
+    // LDS-staged path: a block covers ~16K col elements (whole images of one
+    // channel when an image is small, else a range of output rows) and its
+    // input window must fit in 48 KB; otherwise the direct gather below.
+    {
+        const int khw = g.kH * g.kW;
+        const int Wl = (g.OW - 1) * g.s + g.kW;
+        const long long per_img = (long long)khw * g.OH * g.OW;
+        const long long target = 16384;
+        int RB = g.OH, BB = 1;
+        if (per_img >= target) {
+            RB = (int)(target / ((long long)khw * g.OW));
+            RB = RB < 1 ? 1 : (RB > g.OH ? g.OH : RB);
+        } else {
+            BB = (int)(target / per_img);
+            BB = BB < 1 ? 1 : (BB > g.B ? g.B : BB);
+        }
+        int Rl = (RB - 1) * g.s + g.kH;
+        while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
+            BB = (BB + 1) / 2;
+        while (RB > 1 && (long long)Rl * Wl * es > 48 * 1024) {
+            RB = (RB + 1) / 2;
+            Rl = (RB - 1) * g.s + g.kH;
+        }
+        const size_t shm = (size_t)BB * Rl * Wl * es;
+        if (shm <= 48 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535) {
+            dim3 grid((g.OH + RB - 1) / RB, g.C, (g.B + BB - 1) / BB);
+            const int vec = (g.N % VW) == 0;
+            if (dt == DT_F32)
+                hipLaunchKernelGGL(im2col_lds_kernel<uint32_t>, grid, dim3(NT), shm, s, (const uint32_t *)x,
+                                   (uint32_t *)col, g, RB, BB, Rl, Wl, vec);
+            else
+                hipLaunchKernelGGL(im2col_lds_kernel<uint16_t>, grid, dim3(NT), shm, s, (const uint16_t *)x,
+                                   (uint16_t *)col, g, RB, BB, Rl, Wl, vec);
+            return hipGetLastError();
+        }
+    }
     const long long threads = (g.N + VW - 1) / VW;
     dim3 grid = grid2((threads + NT - 1) / NT, (long long)g.C * g.kH);
     const int vec = (g.N % VW) == 0;
@@ -337,8 +619,34 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
 
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s)
 {
+    // LDS path: whole padded image windows of one channel fit in 48 KB and a
+    // block's columns fit in QMAX vectors per thread.
+    {
+        const int Rl = (g.OH - 1) * g.s + g.kH;
+        const int Wl = (g.OW - 1) * g.s + g.kW;
+        const long long win = (long long)Rl * Wl * 4;
+        const long long max_cols = (long long)C2I_QMAX * NT * 4 - 4;
+        if (win <= 48 * 1024 && g.P <= max_cols && g.C <= 65535) {
+            long long BB = (48 * 1024) / win;
+            const long long by_cols = max_cols / g.P;
+            if (BB > by_cols)
+                BB = by_cols;
+            if (BB > g.B)
+                BB = g.B;
+            if (BB < 1)
+                BB = 1;
+            if ((g.B + BB - 1) / BB <= 65535) {
+                dim3 grid(1, g.C, (unsigned)((g.B + BB - 1) / BB));
+                const int vec = (g.N % 4) == 0;
+                hipLaunchKernelGGL(col2im_lds_kernel, grid, dim3(NT), (size_t)(BB * win), s, dcol, dx, g,
+                                   (int)BB, Rl, Wl, vec);
+                return hipGetLastError();
+            }
+        }
+    }
     const int total = g.B * g.C * g.H * g.W;
-    const dim3 grid((total + NT - 1) / NT), block(NT);
+    const int threads = (total + COLS_PER_THREAD - 1) / COLS_PER_THREAD;
+    const dim3 grid((threads + NT - 1) / NT), block(NT);
     const int tu = (g.kH + g.s - 1) / g.s, tv = (g.kW + g.s - 1) / g.s;
     if (tu == 1 && tv == 1)
         hipLaunchKernelGGL((col2im_kernel<1, 1>), grid, block, 0, s, dcol, dx, g, total);
