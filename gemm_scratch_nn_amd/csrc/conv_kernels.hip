@@ -100,6 +100,24 @@ __global__ __launch_bounds__(NT) void im2col_kernel(const T *__restrict__ x, T *
     }
 }
 
+// LDS window padding: one 4-byte word after every 32 words.  Threads that own
+// 16-byte column vectors read window positions 4 words apart, which without
+// padding fall on only 8 of the 32 banks.
+template <typename T>
+__device__ __forceinline__ int lds_pad(int a)
+{
+    if constexpr (sizeof(T) == 4)
+        return a + (a >> 5);
+    else
+        return a + ((a >> 6) << 1);
+}
+
+template <typename T>
+constexpr long long lds_padded_elems(long long n)
+{
+    return sizeof(T) == 4 ? n + n / 32 + 1 : n + 2 * (n / 64) + 2;
+}
+
 // ---------------------------------------------------------------------------
 // im2col through LDS.  A block owns one channel c, images [b0, b0+BB) and
 // output rows [i0, i1) (a row range only when BB = 1).  It copies the
@@ -143,13 +161,13 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
                 const int hh = h_org + r;
                 const bool row_ok = hh >= 0 && hh < g.H;
                 const long long xrow = (((long long)(b0 + bb) * g.C + c) * g.H + hh) * g.W;
-                T *drow = lds + (bb * Rl + r) * Wl;
+                const int drow = (bb * Rl + r) * Wl;
                 for (int q = q0; q < Wl; q += (Wl <= NT ? Wl : NT)) {
                     const int ww = w_org + q;
                     T val = 0;
                     if (row_ok && ww >= 0 && ww < g.W)
                         val = x[xrow + ww];
-                    drow[q] = val;
+                    lds[lds_pad<T>(drow + q)] = val;
                 }
                 r += rpp;
                 while (r >= Rl) {
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
                 typename Vec16<T>::type out;
 #pragma unroll
                 for (int e = 0; e < VW; ++e)
-                    out[e] = lds[off[e] + tap];
+                    out[e] = lds[lds_pad<T>(off[e] + tap)];
                 if (full) {
                     *(typename Vec16<T>::type *)dst = out;
                 } else {
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(NT) void col2im_lds_kernel(const float *__restrict_
     const int b0 = blockIdx.z * BB;
     const int nbb = min(BB, g.B - b0);
     const int plane = Rl * Wl;
-    for (int t = threadIdx.x; t < nbb * plane; t += NT)
+    for (int t = threadIdx.x; t < lds_padded_elems<float>((long long)nbb * plane); t += NT)
         lds[t] = 0.0f;
 
     const int n_start = b0 * g.P;
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(NT) void col2im_lds_kernel(const float *__restrict_
 #pragma unroll
                     for (int e = 0; e < VW; ++e)
                         if (in[qi][e])
-                            lds[off[qi][e] + tap] += val[e];
+                            lds[lds_pad<float>(off[qi][e] + tap)] += val[e];
                 }
             }
             src += g.N;
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(NT) void col2im_lds_kernel(const float *__restrict_
         const int h = r / g.W;
         const int w = r - h * g.W;
         const int wr = h + g.p, wc = w + g.p;
-        const float val = (wr < Rl && wc < Wl) ? lds[bb * plane + wr * Wl + wc] : 0.0f;
+        const float val = (wr < Rl && wc < Wl) ? lds[lds_pad<float>(bb * plane + wr * Wl + wc)] : 0.0f;
         dx[(((long long)(b0 + bb) * g.C + c) * g.H + h) * g.W + w] = val;
     }
 }
@@ -592,8 +610,10 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
             RB = (RB + 1) / 2;
             Rl = (RB - 1) * g.s + g.kH;
         }
-        const size_t shm = (size_t)BB * Rl * Wl * es;
-        if (shm <= 48 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535) {
+        const long long win_elems = (long long)BB * Rl * Wl;
+        const size_t shm = (size_t)(es == 4 ? lds_padded_elems<uint32_t>(win_elems)
+                                            : lds_padded_elems<uint16_t>(win_elems)) * es;
+        if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535) {
             dim3 grid((g.OH + RB - 1) / RB, g.C, (g.B + BB - 1) / BB);
             const int vec = (g.N % VW) == 0;
             if (dt == DT_F32)
@@ -638,8 +658,9 @@ hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStr
             if ((g.B + BB - 1) / BB <= 65535) {
                 dim3 grid(1, g.C, (unsigned)((g.B + BB - 1) / BB));
                 const int vec = (g.N % 4) == 0;
-                hipLaunchKernelGGL(col2im_lds_kernel, grid, dim3(NT), (size_t)(BB * win), s, dcol, dx, g,
-                                   (int)BB, Rl, Wl, vec);
+                const size_t shm = (size_t)lds_padded_elems<float>(BB * (long long)Rl * Wl) * 4;
+                hipLaunchKernelGGL(col2im_lds_kernel, grid, dim3(NT), shm, s, dcol, dx, g, (int)BB, Rl, Wl,
+                                   vec);
                 return hipGetLastError();
             }
         }
