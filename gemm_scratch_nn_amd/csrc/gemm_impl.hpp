@@ -1,15 +1,21 @@
-// MFMA GEMM for gfx950: C(f32) = op(A) * op(B) with the transpose flags of
-// the directcompute-nn page ("Matmul Shaders", "Transpose via Flags").
+// MFMA GEMM for f32 operands on gfx950: C(f32) = op(A) * op(B) with the
+// transpose flags of the directcompute-nn page ("Matmul Shaders", "Transpose
+// via Flags").  (f16 / bf16 operands have their own kernel, gemm16_impl.hpp.)
 //
 // Design (CDNA4, 64-lane wavefronts):
 //  * A workgroup of NWM x NWN wavefronts computes a BM x BN tile; each
 //    wavefront owns TM x TN blocks of 32x32 outputs held in MFMA
-//    accumulators (16 floats per lane per block).
-//  * f32 operands use v_mfma_f32_32x32x2_f32; f16 / bf16 operands use the
-//    gfx950 v_mfma_f32_32x32x16_{f16,bf16}.  Accumulation is f32 throughout.
-//  * Each K stage (BK = 128 bytes of k per operand row) is loaded from global
-//    memory with 16-byte vector loads into registers one stage ahead, then
-//    written to one of two LDS buffers, so each stage costs one barrier.
+//    accumulators (16 floats per lane per block), fed by
+//    v_mfma_f32_32x32x2_f32.
+//  * A K stage is 32 floats (128 bytes) of k per operand row.  Two register
+//    sets alternate (loop unrolled by two so each set stays in fixed
+//    registers): while stage t is computed from one LDS buffer, the global
+//    loads of stages t+1 and t+2 are in flight; one barrier per stage.
+//  * With VEC (leading dimension and contiguous extent multiples of 4, so
+//    every 16-byte vector is wholly inside or outside the matrix) the loads
+//    are issued unconditionally and the zero mask is applied when the
+//    registers are written to LDS: no branches around the loads, so the
+//    compiler waits only for the register set being stored.
 //  * LDS layout follows the global layout: an operand stored with k
 //    contiguous is kept as [row][k] (row pitch padded by 16 bytes so the
 //    16-byte fragment reads of 8 consecutive rows hit distinct banks); an
@@ -31,35 +37,26 @@
 namespace d4r {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct DtF32 { static constexpr int ES = 4; static constexpr int ID = DT_F32; };
-struct DtF16 { static constexpr int ES = 2; static constexpr int ID = DT_F16; };
-struct DtBF16 { static constexpr int ES = 2; static constexpr int ID = DT_BF16; };
 
-template <class DT>
-struct GemmTraits {
-    static constexpr int ES = DT::ES;
-    static constexpr int VW = 16 / ES;      // elements per 16-byte vector
-    static constexpr int BK = 128 / ES;     // k depth of one stage
-    static constexpr int PAD = 16 / ES;     // 16 bytes of row padding
-};
+constexpr int kBK32 = 32;   // k depth of one stage (floats)
+constexpr int kPad32 = 4;   // 16 bytes of row padding
 
-// One operand's global -> register -> LDS path.
+// One operand's global -> register -> LDS path (f32 elements).
 //   KC = true : global X[r*ld + k], LDS [r][k] with pitch BK + PAD
 //   KC = false: global X[k*ld + r], LDS [k][r] with pitch BR + PAD
-template <class DT, int BR, bool KC, int NT>
+template <int BR, bool KC, int NT>
 struct OperandTile {
-    using TR = GemmTraits<DT>;
-    static constexpr int ES = TR::ES, VW = TR::VW, BK = TR::BK, PAD = TR::PAD;
+    static constexpr int VW = 4, BK = kBK32, PAD = kPad32;
     static constexpr int PITCH = KC ? (BK + PAD) : (BR + PAD);
-    static constexpr int LDS_BYTES = (KC ? BR : BK) * PITCH * ES;
+    static constexpr int LDS_BYTES = (KC ? BR : BK) * PITCH * 4;
     static constexpr int NV = BR * BK / VW;
     static constexpr int PER = (NV + NT - 1) / NT;
 
     u32x4 reg[PER];
+    uint32_t okmask;  // bit s: reg[s] lies inside the matrix (VEC loads)
 
     __device__ __forceinline__ static void slot(int id, int &row, int &kk)
     {
@@ -72,64 +69,49 @@ struct OperandTile {
         }
     }
 
-    __device__ __forceinline__ void load(const char *__restrict__ base, int ld, int R, int K,
-                                         int r0, int k0, bool vec_ok, int tid)
+    template <bool VEC>
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, int ld, int R, int K, int r0,
+                                         int k0, int tid)
     {
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
-            int id = s * NT + tid;
-            if (NV % NT != 0 && id >= NV)
-                break;
+            const int id = s * NT + tid;
+            const bool live = NV % NT == 0 || id < NV;
             int row, kk;
-            slot(id, row, kk);
-            int r = r0 + row, k = k0 + kk;
-            bool full;
-            long long off;
-            if (KC) {
-                full = vec_ok && r < R && k + VW <= K;
-                off = (long long)r * ld + k;
-            } else {
-                full = vec_ok && k < K && r + VW <= R;
-                off = (long long)k * ld + r;
-            }
-            if (full) {
-                reg[s] = *(const u32x4 *)(base + off * ES);
+            slot(live ? id : 0, row, kk);
+            const int r = r0 + row, k = k0 + kk;
+            const long long off = KC ? (long long)r * ld + k : (long long)k * ld + r;
+            if constexpr (VEC) {
+                const bool ok = live && r < R && k < K;
+                reg[s] = *(const u32x4 *)(X + (ok ? off : 0));
+                okmask = (s == 0 ? 0u : okmask) | ((ok ? 1u : 0u) << s);
             } else {
                 u32x4 v = {0u, 0u, 0u, 0u};
-                if (ES == 4) {
-                    const uint32_t *p = (const uint32_t *)base;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bool ok = KC ? (r < R && k + e < K) : (k < K && r + e < R);
-                        long long o = KC ? ((long long)r * ld + k + e) : ((long long)k * ld + r + e);
-                        v[e] = ok ? p[o] : 0u;
-                    }
-                } else {
-                    const uint16_t *p = (const uint16_t *)base;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        bool ok = KC ? (r < R && k + e < K) : (k < K && r + e < R);
-                        long long o = KC ? ((long long)r * ld + k + e) : ((long long)k * ld + r + e);
-                        uint32_t h = ok ? (uint32_t)p[o] : 0u;
-                        v[e >> 1] |= h << (16 * (e & 1));
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = live && (KC ? (r < R && k + e < K) : (k < K && r + e < R));
+                    v[e] = ok ? X[off + e] : 0u;
                 }
                 reg[s] = v;
             }
         }
     }
 
+    template <bool VEC>
     __device__ __forceinline__ void store(char *lds, int tid) const
     {
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
-            int id = s * NT + tid;
-            if (NV % NT != 0 && id >= NV)
-                break;
+            const int id = s * NT + tid;
+            if constexpr (NV % NT != 0) {
+                if (id >= NV)
+                    break;
+            }
             int row, kk;
             slot(id, row, kk);
-            int e = KC ? (row * PITCH + kk) : (kk * PITCH + row);
-            *(u32x4 *)(lds + e * ES) = reg[s];
+            const int e = KC ? (row * PITCH + kk) : (kk * PITCH + row);
+            *(u32x4 *)(lds + e * 4) = (!VEC || ((okmask >> s) & 1u)) ? reg[s] : z;
         }
     }
 };
@@ -138,17 +120,12 @@ struct OperandTile {
 // op(B)[kc][n] = xt(b, c, i*s - p + u, j*s - p + v), kc = (c*kH + u)*kW + v,
 // n = (b*OH + i)*OW + j, stored in the same [k][n] LDS layout as a
 // row-contiguous operand.  A thread's four columns n are the same in every
-// K stage, so their image offsets and window origins are decoded once; each
-// stage decodes only the thread's kc rows.
+// K stage, so their image offsets and window origins are decoded once (in
+// ImplicitColsF32, shared by both register sets); each stage decodes only
+// the thread's kc rows.
 template <int BR, int NT>
-struct ImplicitTileF32 {
-    using Base = OperandTile<DtF32, BR, false, NT>;
-    static constexpr int VW = 4, BK = 32;
-    static constexpr int PITCH = Base::PITCH, LDS_BYTES = Base::LDS_BYTES;
-    static constexpr int NV = Base::NV, PER = Base::PER;
-    static_assert(NT % (BR / VW) == 0, "a thread's columns must not change between slots");
-
-    u32x4 reg[PER];
+struct ImplicitColsF32 {
+    static constexpr int VW = 4;
     int nb[VW], nh[VW], nw[VW];  // image offset (-1 past N), window origin row / column
 
     __device__ __forceinline__ void setup(const ConvGeom &g, int n_blk, int tid)
@@ -172,9 +149,20 @@ struct ImplicitTileF32 {
             }
         }
     }
+};
 
-    __device__ __forceinline__ void load(const uint32_t *__restrict__ x, const ConvGeom &g, int K, int k0,
-                                         int tid)
+template <int BR, int NT>
+struct ImplicitTileF32 {
+    using Base = OperandTile<BR, false, NT>;
+    static constexpr int VW = 4, BK = kBK32;
+    static constexpr int PITCH = Base::PITCH, LDS_BYTES = Base::LDS_BYTES;
+    static constexpr int NV = Base::NV, PER = Base::PER;
+    static_assert(NT % (BR / VW) == 0, "a thread's columns must not change between slots");
+
+    u32x4 reg[PER];
+
+    __device__ __forceinline__ void gather(const uint32_t *__restrict__ x, const ConvGeom &g,
+                                           const ImplicitColsF32<BR, NT> &cols, int K, int k0, int tid)
     {
         const int khw = g.kH * g.kW;
 #pragma unroll
@@ -192,15 +180,16 @@ struct ImplicitTileF32 {
                 const int plane = c * g.H * g.W;
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
-                    const int hh = nh[e] + u, ww = nw[e] + vv;
-                    const bool ok = nb[e] >= 0 && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W;
-                    v[e] = ok ? x[nb[e] + plane + hh * g.W + ww] : 0u;
+                    const int hh = cols.nh[e] + u, ww = cols.nw[e] + vv;
+                    const bool ok = cols.nb[e] >= 0 && hh >= 0 && hh < g.H && ww >= 0 && ww < g.W;
+                    v[e] = ok ? x[cols.nb[e] + plane + hh * g.W + ww] : 0u;
                 }
             }
             reg[s] = v;
         }
     }
 
+    template <bool VEC>
     __device__ __forceinline__ void store(char *lds, int tid) const
     {
 #pragma unroll
@@ -214,8 +203,8 @@ struct ImplicitTileF32 {
     }
 };
 
-// Fragment reads.  f32: 8 consecutive k (one k group of 16, lane half h)
-// for one 32-row block; the 8 MFMAs of the group use element t.
+// Fragment reads: 8 consecutive k (one k group of 16, lane half h) for one
+// 32-row block; the 8 MFMAs of the group use element t.
 template <bool KC, int PITCH>
 __device__ __forceinline__ void frag_f32(const float *lds, int row, int kg, int h, float (&f)[8])
 {
@@ -235,46 +224,17 @@ __device__ __forceinline__ void frag_f32(const float *lds, int row, int kg, int 
     }
 }
 
-// 16-bit: 8 consecutive k of k group q for lane half h, packed in 4 dwords.
-template <bool KC, int PITCH>
-__device__ __forceinline__ u32x4 frag_h(const uint16_t *lds, int row, int q, int h)
-{
-    if (KC) {
-        return *(const u32x4 *)(lds + row * PITCH + q * 16 + h * 8);
-    } else {
-        u32x4 v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t lo = lds[(q * 16 + h * 8 + 2 * j) * PITCH + row];
-            uint32_t hi = lds[(q * 16 + h * 8 + 2 * j + 1) * PITCH + row];
-            v[j] = lo | (hi << 16);
-        }
-        return v;
-    }
-}
-
-template <class DT>
-__device__ __forceinline__ f32x16 mfma_h(u32x4 a, u32x4 b, f32x16 c)
-{
-    if constexpr (DT::ID == DT_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <class DT, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool IMPL>
+template <int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = NWM * NWN * 64;
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
-    using TR = GemmTraits<DT>;
-    constexpr int BK = TR::BK;
-    static_assert(!IMPL || (!B_KC && DT::ID == DT_F32), "implicit B: f32, [k][n] layout");
-    using TA = OperandTile<DT, BM, A_KC, NT>;
-    using TB = std::conditional_t<IMPL, ImplicitTileF32<BN, NT>, OperandTile<DT, BN, B_KC, NT>>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * (TA::LDS_BYTES + TB::LDS_BYTES)];
+    constexpr int BK = kBK32;
+    static_assert(!IMPL || !B_KC, "implicit B uses the [k][n] layout");
+    using TA = OperandTile<BM, A_KC, NT>;
+    using TB = std::conditional_t<IMPL, ImplicitTileF32<BN, NT>, OperandTile<BN, B_KC, NT>>;
+    constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -299,74 +259,76 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.0f;
 
-    TA ta;
-    TB tb;
-    const char *Ab = (const char *)p.A;
-    const char *Bb = (const char *)p.B;
-    // K bound for this split: the loaders zero-fill k >= kend.
-    auto load_b = [&](int k0) {
-        if constexpr (IMPL)
-            tb.load((const uint32_t *)p.B, p.g, kend, k0, tid);
-        else
-            tb.load(Bb, p.ldb, p.N, kend, n_blk, k0, p.b_vec, tid);
-    };
+    const uint32_t *A = (const uint32_t *)p.A;
+    const uint32_t *B = (const uint32_t *)p.B;
+    TA ta0, ta1;
+    TB tb0, tb1;
+    ImplicitColsF32<BN, NT> cols;
     if constexpr (IMPL)
-        tb.setup(p.g, n_blk, tid);
-    if (nk > 0) {
-        ta.load(Ab, p.lda, p.M, kend, m_blk, kbeg, p.a_vec, tid);
-        load_b(kbeg);
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        char *la = smem + (kt & 1) * (TA::LDS_BYTES + TB::LDS_BYTES);
-        char *lb = la + TA::LDS_BYTES;
-        ta.store(la, tid);
-        tb.store(lb, tid);
-        __syncthreads();
-        if (kt + 1 < nk) {
-            int k0 = kbeg + (kt + 1) * BK;
-            ta.load(Ab, p.lda, p.M, kend, m_blk, k0, p.a_vec, tid);
-            load_b(k0);
-        }
-        if constexpr (DT::ID == DT_F32) {
-            const float *fa = (const float *)la;
-            const float *fb = (const float *)lb;
+        cols.setup(p.g, n_blk, tid);
+    // K bound for this split: the loaders zero-fill k >= kend.
+    auto load = [&](TA &a, TB &b, int k0) {
+        a.template load<VEC>(A, p.lda, p.M, kend, m_blk, k0, tid);
+        if constexpr (IMPL)
+            b.gather(B, p.g, cols, kend, k0, tid);
+        else
+            b.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
+    };
+    auto store = [&](const TA &a, const TB &b, char *buf) {
+        a.template store<VEC>(buf, tid);
+        b.template store<VEC>(buf + TA::LDS_BYTES, tid);
+    };
+    auto compute = [&](const char *buf) {
+        const float *fa = (const float *)buf;
+        const float *fb = (const float *)(buf + TA::LDS_BYTES);
 #pragma unroll
-            for (int kg = 0; kg < BK / 16; ++kg) {
-                float af[TM][8], bf[TN][8];
+        for (int kg = 0; kg < BK / 16; ++kg) {
+            float af[TM][8], bf[TN][8];
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    frag_f32<A_KC, TA::PITCH>(fa, (wm * TM + i) * 32 + l32, kg, h, af[i]);
+            for (int i = 0; i < TM; ++i)
+                frag_f32<A_KC, TA::PITCH>(fa, (wm * TM + i) * 32 + l32, kg, h, af[i]);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    frag_f32<B_KC, TB::PITCH>(fb, (wn * TN + j) * 32 + l32, kg, h, bf[j]);
+            for (int j = 0; j < TN; ++j)
+                frag_f32<B_KC, TB::PITCH>(fb, (wn * TN + j) * 32 + l32, kg, h, bf[j]);
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][t], bf[j][t],
-                                                                             acc[i][j], 0, 0, 0);
-            }
-        } else {
-            const uint16_t *ha = (const uint16_t *)la;
-            const uint16_t *hb = (const uint16_t *)lb;
-#pragma unroll
-            for (int q = 0; q < BK / 16; ++q) {
-                u32x4 af[TM], bf[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    af[i] = frag_h<A_KC, TA::PITCH>(ha, (wm * TM + i) * 32 + l32, q, h);
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    bf[j] = frag_h<B_KC, TB::PITCH>(hb, (wn * TN + j) * 32 + l32, q, h);
+            for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = mfma_h<DT>(af[i], bf[j], acc[i][j]);
-            }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][t], bf[j][t], acc[i][j], 0,
+                                                                         0, 0);
         }
+    };
+
+    if (nk > 0) {
+        // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
+        load(ta0, tb0, kbeg);
+        if (nk > 1)
+            load(ta1, tb1, kbeg + BK);
+        store(ta0, tb0, smem);
+        __syncthreads();
+        if (nk > 2)
+            load(ta0, tb0, kbeg + 2 * BK);
+        // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
+        // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
+        // it is then refilled with stage t+3.  An odd last stage is peeled.
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            compute(smem);
+            store(ta1, tb1, smem + STAGE);
+            __syncthreads();
+            if (t + 3 < nk)
+                load(ta1, tb1, kbeg + (t + 3) * BK);
+            compute(smem + STAGE);
+            if (t + 2 < nk)
+                store(ta0, tb0, smem);
+            __syncthreads();
+            if (t + 4 < nk)
+                load(ta0, tb0, kbeg + (t + 4) * BK);
+        }
+        if (t < nk)
+            compute(smem);
     }
 
     // Epilogue.  Accumulator element e of a 32x32 block sits at
@@ -402,29 +364,39 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     }
 }
 
-template <class DT, bool A_KC, bool B_KC, bool IMPL = false>
-hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
+template <bool A_KC, bool B_KC, bool VEC, bool IMPL>
+hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
     dim3 grid(tiles, 1, p.splits);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 2, 2, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm_kernel<DT, 2, 2, 1, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 1, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm_kernel<DT, 1, 4, 3, 1, A_KC, B_KC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
         break;
     default:
-        return hipErrorInvalidValue;  // tile shape not built for this dtype
+        return hipErrorInvalidValue;  // tile shape not built for f32
     }
     return hipGetLastError();
+}
+
+template <class DT, bool A_KC, bool B_KC, bool IMPL = false>
+hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
+{
+    static_assert(DT::ID == DT_F32, "f32 kernel");
+    const bool vec = IMPL ? (p.a_vec != 0) : (p.a_vec && p.b_vec);
+    if (vec)
+        return launch_gemm32_vec<A_KC, B_KC, true, IMPL>(cfg, p, s);
+    return launch_gemm32_vec<A_KC, B_KC, false, IMPL>(cfg, p, s);
 }
 
 template <class DT>
