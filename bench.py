@@ -50,10 +50,38 @@ def parse_args():
     ap.add_argument("--forward", choices=("explicit", "implicit"), default="explicit",
                     help="explicit: im2col + GEMM (col saved for the filter gradient); "
                          "implicit: implicit-GEMM forward, im2col redone in the filter gradient")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step as a HIP graph (stream capture) and time its replays; "
+                         "per-kernel event timing is then unavailable")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (counter "
                          "calibration for rocprofv3 --pmc runs; untimed)")
     return ap.parse_args()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summaries
+    (profiles/traffic_*.txt), or None when none matches or the kernel's source
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt"))):
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic_") and ":" in line:
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("traffic_kernel") != kernel:
+            continue
+        src = os.path.join(ROOT, fields.get("traffic_source", ""))
+        if not os.path.isfile(src):
+            continue
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != fields.get("traffic_source_sha256"):
+                continue
+        return float(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None
 
 
 def layer_flops(sh) -> float:
@@ -146,7 +174,7 @@ def main() -> int:
 
     implicit = args.forward == "implicit"
 
-    def step():
+    def step(stream=stream):
         for layer, pl, t in layers:
             if implicit:
                 d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes,
@@ -161,14 +189,34 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    d4r.d4r_profile_reset()
-    d4r.d4r_profile_enable(True)
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream().cuda_stream)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # Timed region: K steps with no event recording (a recorded event pair per
+    # launch adds GPU-side gaps between kernels).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is None:
+            step()
+        else:
+            graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # Kernel timing: the same K steps again, eager, with the library's HIP
+    # event pair around every launch on its stream.
+    d4r.d4r_profile_reset()
+    d4r.d4r_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     d4r.d4r_profile_enable(False)
     stats = d4r.d4r_profile_read()
 
@@ -207,6 +255,12 @@ def main() -> int:
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                 "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
 
+    tr = recorded_traffic(dom)
+    if tr is not None:
+        roof["traffic"] = tr[0]
+        roof["traffic_source"] = tr[1]
+        roof["algorithmic_bytes_per_launch"] = d["bytes"] / d["launches"]
+
     def stage(prefix):
         sel = [v for k, v in by_kernel.items() if k.startswith(prefix)]
         if not sel:
@@ -240,13 +294,16 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "forward": args.forward, "step_gflop": step_flops / 1e9},
+                   "dtype": dtype, "forward": args.forward, "hip_graph": bool(args.graph),
+                   "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],
         "gemm_TFLOPs": gemm_tf,
         "gemm_frac_mfma": gemm_tf / MFMA_PEAK[dtype],
         "im2col": stage("im2col"),
         "col2im": stage("col2im"),
         "roofline": roof,
+        "kernel_timing": "HIP event pair per launch, recorded by the library on its launch stream "
+                         "during a second pass of the same steps (step time from an event-free pass)",
         "cpu_baseline": cpu,
         "kernels": kernels,
     }

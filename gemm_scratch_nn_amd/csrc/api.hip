@@ -216,7 +216,11 @@ struct ProfScope {
         }
         if (P.used == P.recs.size()) {
             ProfRec r{};
-            if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess)
+            // no system-scope fence on record: the events only time kernels
+            // on this device, and a fenced record stalls the queue between
+            // launches
+            if (hipEventCreateWithFlags(&r.a, hipEventDisableSystemFence) != hipSuccess ||
+                hipEventCreateWithFlags(&r.b, hipEventDisableSystemFence) != hipSuccess)
                 return;
             P.recs.push_back(r);
         }

@@ -603,6 +603,14 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
             BB = (int)(target / per_img);
             BB = BB < 1 ? 1 : (BB > g.B ? g.B : BB);
         }
+        // enough blocks to fill the chip: split images, then output rows
+        auto blocks = [&](int rb, int bb) {
+            return (long long)((g.OH + rb - 1) / rb) * g.C * ((g.B + bb - 1) / bb);
+        };
+        while (BB > 1 && blocks(RB, BB) < 1024)
+            BB = (BB + 1) / 2;
+        while (RB > 1 && blocks(RB, BB) < 1024)
+            RB = (RB + 1) / 2;
         int Rl = (RB - 1) * g.s + g.kH;
         while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
             BB = (BB + 1) / 2;
@@ -655,7 +663,10 @@ hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStr
                 BB = g.B;
             if (BB < 1)
                 BB = 1;
-            if ((g.B + BB - 1) / BB <= 65535) {
+            // enough blocks to fill the chip, else the element-parallel gather
+            while (BB > 1 && (long long)g.C * ((g.B + BB - 1) / BB) < 1024)
+                BB = (BB + 1) / 2;
+            if ((long long)g.C * ((g.B + BB - 1) / BB) >= 256 && (g.B + BB - 1) / BB <= 65535) {
                 dim3 grid(1, g.C, (unsigned)((g.B + BB - 1) / BB));
                 const int vec = (g.N % 4) == 0;
                 const size_t shm = (size_t)lds_padded_elems<float>(BB * (long long)Rl * Wl) * 4;
