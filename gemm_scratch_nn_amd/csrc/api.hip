@@ -237,22 +237,28 @@ struct ProfScope {
     }
 };
 
-std::string gemm_kernel_name(int dt, int cfg, bool a_kc, bool b_kc)
+// Kernel names: gemm_<dtype>_<tile>_<A><B>, one letter per operand form:
+// k = k-contiguous, m / n = row-contiguous A / B, g = NCHW gradient read in
+// place; the implicit forward adds "_implicit".
+std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
 {
     TileShape ts = tile_shape(cfg);
+    const char a = amode == OP_KC ? 'k' : (amode == OP_NCHW ? 'g' : 'm');
+    const char b = (bmode == OP_KC) ? 'k' : (bmode == OP_NCHW ? 'g' : 'n');
     return std::string("gemm_") + dt_name(dt) + "_" + std::to_string(ts.bm) + "x" + std::to_string(ts.bn) +
-           "_" + (a_kc ? "k" : "m") + (b_kc ? "k" : "n");
+           "_" + a + b + (bmode == OP_IMPL ? "_implicit" : "");
 }
 
 
 // Runs one planned GEMM (split-K partials + reduction when the plan splits).
-// With `implicit` set, B is the conv input x and op(B) = im2col(x) is
-// gathered inside the GEMM (A must be k-contiguous, B row-contiguous).
-hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void *A, int lda,
+// Operand forms follow OperandMode; OP_IMPL (B = x, op(B) = im2col(x)) and
+// OP_NCHW (the gradient dy read in place) take their geometry from `geom`.
+hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
                     const float *bias, int P, float *partial, hipStream_t s, const char *pass,
-                    const ConvGeom *implicit = nullptr)
+                    const ConvGeom *geom = nullptr)
 {
+    const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
     GemmParams p;
     p.A = A;
@@ -268,10 +274,10 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
     p.splits = pl.splits;
     // vector loads need every 16-byte vector wholly inside or outside the
     // operand: leading dimension and the contiguous extent multiples of vw
-    p.a_vec = (lda % vw) == 0 && ((a_kc ? K : M) % vw) == 0;
-    p.b_vec = implicit ? 1 : ((ldb % vw) == 0 && ((b_kc ? K : N) % vw) == 0);
-    if (implicit)
-        p.g = *implicit;
+    p.a_vec = (lda % vw) == 0 && ((amode == OP_KC ? K : M) % vw) == 0;
+    p.b_vec = (ldb % vw) == 0 && ((bmode == OP_KC ? K : N) % vw) == 0;
+    if (geom)
+        p.g = *geom;
     else
         memset(&p.g, 0, sizeof p.g);
     if (pl.splits > 1) {
@@ -286,11 +292,10 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, bool a_kc, bool b_kc, const void
         p.c_split_stride = 0;
     }
     const int es = dt_size(dt);
-    const double b_bytes = implicit ? (double)implicit->B * implicit->C * implicit->H * implicit->W
-                                    : (double)K * N;
-    ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, a_kc, b_kc) + (implicit ? "_implicit:" : ":") + pass,
-                 2.0 * M * N * K, (double)es * ((double)M * K + b_bytes) + 4.0 * M * N);
-    hipError_t e = implicit ? launch_gemm_implicit(dt, pl.cfg, p, s) : launch_gemm(dt, pl.cfg, a_kc, b_kc, p, s);
+    const double b_bytes = implicit ? (double)geom->B * geom->C * geom->H * geom->W : (double)K * N;
+    ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, amode, bmode) + ":" + pass, 2.0 * M * N * K,
+                 (double)es * ((double)M * K + b_bytes) + 4.0 * M * N);
+    hipError_t e = launch_gemm(dt, pl.cfg, amode, bmode, p, s);
     ps.done();
     if (e != hipSuccess || pl.splits == 1)
         return e;
@@ -305,13 +310,21 @@ bool valid_dtype(int dt) { return dt == D4R_F32 || dt == D4R_F16 || dt == D4R_BF
 
 }  // namespace
 
+// How the gradient GEMMs take dy.  GP_INPLACE reads it where it lies (NCHW
+// operand loaders, f32 only): no copy, but single-element loads inside the
+// GEMM.  GP_COPY first copies it into the workspace with 16-byte-friendly
+// rows: transposed (N x O) for the data gradient, reshaped (O x N) for the
+// filter gradient.
+enum GradPath : int { GP_INPLACE = 0, GP_COPY = 1 };
+
 struct d4r_conv {
     ConvGeom g;
     int dt;
     int es;
     GemmPlan fwd, bwd_data, bwd_filter;
     int bias_splits;
-    size_t off_g, off_wt, off_bias, off_big, ws_bytes;
+    size_t off_g, off_bias, off_big, ws_bytes;
+    GradPath dgrad, wgrad;  // how the gradient GEMMs take dy and W
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -320,29 +333,16 @@ namespace d4r {
 
 int gemm_bk(int dt) { return dt == DT_F32 ? 32 : 64; }
 
-hipError_t launch_gemm_f32(int, bool, bool, const GemmParams &, hipStream_t);
-hipError_t launch_gemm_f16(int, bool, bool, const GemmParams &, hipStream_t);
-hipError_t launch_gemm_bf16(int, bool, bool, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_f32(int, int, int, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_f16(int, int, int, const GemmParams &, hipStream_t);
+hipError_t launch_gemm_bf16(int, int, int, const GemmParams &, hipStream_t);
 
-hipError_t launch_gemm_implicit_f32(int, const GemmParams &, hipStream_t);
-hipError_t launch_gemm_implicit_f16(int, const GemmParams &, hipStream_t);
-hipError_t launch_gemm_implicit_bf16(int, const GemmParams &, hipStream_t);
-
-hipError_t launch_gemm_implicit(int dt, int cfg, const GemmParams &p, hipStream_t s)
+hipError_t launch_gemm(int dt, int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
     switch (dt) {
-    case DT_F32: return launch_gemm_implicit_f32(cfg, p, s);
-    case DT_F16: return launch_gemm_implicit_f16(cfg, p, s);
-    default: return launch_gemm_implicit_bf16(cfg, p, s);
-    }
-}
-
-hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
-{
-    switch (dt) {
-    case DT_F32: return launch_gemm_f32(cfg, a_kc, b_kc, p, s);
-    case DT_F16: return launch_gemm_f16(cfg, a_kc, b_kc, p, s);
-    default: return launch_gemm_bf16(cfg, a_kc, b_kc, p, s);
+    case DT_F32: return launch_gemm_f32(cfg, amode, bmode, p, s);
+    case DT_F16: return launch_gemm_f16(cfg, amode, bmode, p, s);
+    default: return launch_gemm_bf16(cfg, amode, bmode, p, s);
     }
 }
 
@@ -420,6 +420,42 @@ const char *d4r_status_string(d4r_status s)
 
 const char *d4r_last_error(void) { return g_err; }
 
+namespace {
+
+// Experiment / test override: D4R_GRAD_PATH=inplace|copy (f32 only).
+GradPath grad_path_env(GradPath dflt)
+{
+    const char *e = getenv("D4R_GRAD_PATH");
+    if (!e)
+        return dflt;
+    if (!strcmp(e, "inplace"))
+        return GP_INPLACE;
+    if (!strcmp(e, "copy"))
+        return GP_COPY;
+    return dflt;
+}
+
+// The in-place loaders issue single-element loads where a copied operand
+// takes 16-byte vectors, which costs a roughly fixed fraction of every GEMM
+// stage; the copy costs one pass over dy.  The GEMM work per dy element is
+// Kc multiply-adds, so the copy pays off for large Kc.  Measured on the
+// full step: in place is 4% faster at Kc = 363 (AlexNet conv1), the copy 5%
+// faster at Kc = 2304-3456 (conv3-5); the switch sits at Kc = 1024.
+constexpr int kInplaceMaxKc = 1024;
+
+void choose_grad_paths(d4r_conv *h)
+{
+    GradPath gp = GP_COPY;
+    if (h->dt == D4R_F32) {
+        gp = h->g.Kc < kInplaceMaxKc ? GP_INPLACE : GP_COPY;
+        gp = grad_path_env(gp);
+    }
+    h->dgrad = gp;
+    h->wgrad = gp;
+}
+
+}  // namespace
+
 d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW, int kH, int kW,
                            int stride, int padding, int outC, d4r_dtype dtype)
 {
@@ -476,12 +512,12 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->in_image_col = (double)batch * inC * (double)rows * (double)cols;
     }
 
+    choose_grad_paths(h);
     h->col_bytes = (size_t)col_el * h->es;
     size_t off = align_up(h->col_bytes);
     h->off_g = off;
-    off += align_up((size_t)y_el * h->es);
-    h->off_wt = off;
-    off += align_up((size_t)w_el * h->es);
+    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
+        off += align_up((size_t)y_el * h->es);
     h->off_bias = off;
     off += align_up((size_t)outC * h->bias_splits * sizeof(float));
     h->off_big = off;
@@ -588,7 +624,7 @@ d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const fl
     void *col = wsb;
     float *partial = (float *)(wsb + h->off_big);
     D4R_LAUNCH(step_im2col(h, x, col, s, "fwd"), "im2col");
-    D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
+    D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_ROWS, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
                         bias, g.P, partial, s, "fwd"),
                "forward GEMM");
     return ok();
@@ -607,7 +643,7 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
     hipStream_t s = (hipStream_t)hip_stream;
     const ConvGeom &g = h->g;
     float *partial = (float *)((char *)ws + h->off_big);
-    D4R_LAUNCH(run_gemm(h->dt, h->fwd, true, false, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0, bias,
+    D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_IMPL, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0, bias,
                         g.P, partial, s, "fwd", &g),
                "implicit forward GEMM");
     return ok();
@@ -625,16 +661,22 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, f
     hipStream_t s = (hipStream_t)hip_stream;
     const ConvGeom &g = h->g;
     char *wsb = (char *)ws;
-    void *gt = wsb + h->off_g;
-    void *wt = wsb + h->off_wt;
     float *dcol = (float *)(wsb + h->off_big);
     float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
-    // Gt[b*P + pix][o] = dy[b][o][pix]: a batch of O x P transposes
-    D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad reshape");
-    D4R_LAUNCH(step_transpose(h, 1, g.O, g.Kc, w, wt, s, "dgrad_w"), "filter transpose");
-    D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, true, true, wt, g.O, gt, g.O, g.Kc, g.N, g.O, EPI_ROWMAJOR,
-                        dcol, g.N, nullptr, 0, partial, s, "dgrad"),
-               "data-gradient GEMM");
+    // dcol = Wmat^T * G with A = Wmat (O x Kc) read row-contiguous as
+    // op(A) = Wmat^T and B = G (O x N) read from dy in place or from its
+    // transpose Gt[b*P + pix][o] = dy[b][o][pix]
+    if (h->dgrad == GP_INPLACE) {
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_NCHW, w, g.Kc, dy, 0, g.Kc, g.N, g.O,
+                            EPI_ROWMAJOR, dcol, g.N, nullptr, 0, partial, s, "dgrad", &g),
+                   "data-gradient GEMM");
+    } else {
+        void *gt = wsb + h->off_g;
+        D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad transpose");
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_KC, w, g.Kc, gt, g.O, g.Kc, g.N, g.O,
+                            EPI_ROWMAJOR, dcol, g.N, nullptr, 0, partial, s, "dgrad"),
+                   "data-gradient GEMM");
+    }
     D4R_LAUNCH(step_col2im(h, dcol, dx, s, "dgrad"), "col2im");
     return ok();
 }
@@ -658,14 +700,22 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     const ConvGeom &g = h->g;
     char *wsb = (char *)ws;
     void *col = wsb;
-    void *G = wsb + h->off_g;
     float *partial = (float *)(wsb + h->off_big);
     if (!reuse_col)
         D4R_LAUNCH(step_im2col(h, x, col, s, "wgrad"), "im2col");
-    D4R_LAUNCH(step_grad_reshape(h, dy, G, s), "grad reshape");
-    D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, true, true, G, g.N, col, g.N, g.O, g.Kc, g.N,
-                        EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad"),
-               "filter-gradient GEMM");
+    // dW = G * col^T: A = G (O x N), read from dy in place or reshaped;
+    // B = col (Kc x N) read k-contiguous as op(B) = col^T
+    if (h->wgrad == GP_INPLACE) {
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_NCHW, OP_KC, dy, 0, col, g.N, g.O, g.Kc, g.N,
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g),
+                   "filter-gradient GEMM");
+    } else {
+        void *G = wsb + h->off_g;
+        D4R_LAUNCH(step_grad_reshape(h, dy, G, s), "grad reshape");
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N,
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad"),
+                   "filter-gradient GEMM");
+    }
     if (db)
         D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s),
                    "bias gradient");
@@ -751,11 +801,13 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
         if (ws_bytes < need)
             return fail(D4R_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
     }
-    const bool a_kc = !(flags & 1);
-    const bool b_kc = (flags & 2) != 0;
-    const int lda = a_kc ? K : M;
-    const int ldb = b_kc ? K : N;
-    D4R_LAUNCH(run_gemm(dtype, pl, a_kc, b_kc, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
+    // flags bit 0: A stored K x M (op(A) = A^T, read row-contiguous);
+    // bit 1: B stored N x K (op(B) = B^T, read k-contiguous)
+    const int amode = (flags & 1) ? OP_ROWS : OP_KC;
+    const int bmode = (flags & 2) ? OP_KC : OP_ROWS;
+    const int lda = amode == OP_KC ? K : M;
+    const int ldb = bmode == OP_KC ? K : N;
+    D4R_LAUNCH(run_gemm(dtype, pl, amode, bmode, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
                         (float *)ws, (hipStream_t)hip_stream, "gemm"),
                "GEMM");
     return ok();

@@ -352,41 +352,37 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
         // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
         ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg, tid);
         load_b(tb0, kbeg);
-        if (nk > 1) {
-            ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + BK, tid);
-            load_b(tb1, kbeg + BK);
-        }
+        ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + BK, tid);
+        load_b(tb1, kbeg + BK);
         ta0.template store<VEC>(smem, tid);
         tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
         __syncthreads();
-        if (nk > 2) {
-            ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + 2 * BK, tid);
-            load_b(tb0, kbeg + 2 * BK);
-        }
+        ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + 2 * BK, tid);
+        load_b(tb0, kbeg + 2 * BK);
         // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
         // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
         // it is then refilled with stage t+3.  Two stages per iteration keep
         // each register set in fixed registers; an odd last stage is peeled.
+        // Loads and stores are unconditional (a stage past the end has every
+        // k >= kend: it reads nothing and stores zeros), and a scheduling
+        // barrier keeps each stage's loads right after the workgroup barrier,
+        // so two stages of loads stay in flight during each compute.
         int t = 0;
         for (; t + 1 < nk; t += 2) {
             compute(smem, smem + TA::LDS_BYTES);
             ta1.template store<VEC>(smem + STAGE, tid);
             tb1.template store<VEC>(smem + STAGE + TA::LDS_BYTES, tid);
             __syncthreads();
-            if (t + 3 < nk) {
-                ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 3) * BK, tid);
-                load_b(tb1, kbeg + (t + 3) * BK);
-            }
+            ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 3) * BK, tid);
+            load_b(tb1, kbeg + (t + 3) * BK);
+            __builtin_amdgcn_sched_barrier(0);
             compute(smem + STAGE, smem + STAGE + TA::LDS_BYTES);
-            if (t + 2 < nk) {
-                ta0.template store<VEC>(smem, tid);
-                tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
-            }
+            ta0.template store<VEC>(smem, tid);
+            tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
             __syncthreads();
-            if (t + 4 < nk) {
-                ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 4) * BK, tid);
-                load_b(tb0, kbeg + (t + 4) * BK);
-            }
+            ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 4) * BK, tid);
+            load_b(tb0, kbeg + (t + 4) * BK);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (t < nk)
             compute(smem, smem + TA::LDS_BYTES);
@@ -463,17 +459,21 @@ hipError_t launch_gemm16_layout(int cfg, const GemmParams &p, hipStream_t s)
     return launch_gemm16_vec<DTID, A_KC, B_KC, false>(cfg, p, s);
 }
 
+// Supported (A, B) modes: every pair of OP_ROWS / OP_KC, and (OP_KC,
+// OP_IMPL) for the implicit forward (VEC then covers A only).
 template <int DTID>
-hipError_t launch_gemm16_implicit(int cfg, const GemmParams &p, hipStream_t s)
+hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
-    if (p.a_vec)
-        return launch_gemm16_vec<DTID, true, false, true, true>(cfg, p, s);
-    return launch_gemm16_vec<DTID, true, false, false, true>(cfg, p, s);
-}
-
-template <int DTID>
-hipError_t launch_gemm16(int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
-{
+    if (amode == OP_KC && bmode == OP_IMPL) {
+        if (p.a_vec)
+            return launch_gemm16_vec<DTID, true, false, true, true>(cfg, p, s);
+        return launch_gemm16_vec<DTID, true, false, false, true>(cfg, p, s);
+    }
+    const bool a_ok = amode == OP_ROWS || amode == OP_KC;
+    const bool b_ok = bmode == OP_ROWS || bmode == OP_KC;
+    if (!a_ok || !b_ok)
+        return hipErrorInvalidValue;
+    const bool a_kc = amode == OP_KC, b_kc = bmode == OP_KC;
     if (a_kc && b_kc)
         return launch_gemm16_layout<DTID, true, true>(cfg, p, s);
     if (a_kc && !b_kc)

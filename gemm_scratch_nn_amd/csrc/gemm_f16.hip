@@ -3,14 +3,9 @@
 
 namespace d4r {
 
-hipError_t launch_gemm_f16(int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
+hipError_t launch_gemm_f16(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
-    return launch_gemm16<DT_F16>(cfg, a_kc, b_kc, p, s);
-}
-
-hipError_t launch_gemm_implicit_f16(int cfg, const GemmParams &p, hipStream_t s)
-{
-    return launch_gemm16_implicit<DT_F16>(cfg, p, s);
+    return launch_gemm16<DT_F16>(cfg, amode, bmode, p, s);
 }
 
 }  // namespace d4r

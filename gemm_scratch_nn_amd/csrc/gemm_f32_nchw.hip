@@ -1,0 +1,18 @@
+// Instantiation of the gfx950 MFMA GEMM for f32 operands whose A or B is an
+// NCHW gradient read in place: the data-gradient product (A = Wmat read
+// row-contiguous, B = dy) and the filter-gradient product (A = dy, B = col
+// read k-contiguous).
+#include "gemm_impl.hpp"
+
+namespace d4r {
+
+hipError_t launch_gemm_f32_nchw(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
+{
+    if (amode == OP_ROWS && bmode == OP_NCHW)
+        return launch_gemm32_modes<OP_ROWS, OP_NCHW>(cfg, p, s);
+    if (amode == OP_NCHW && bmode == OP_KC)
+        return launch_gemm32_modes<OP_NCHW, OP_KC>(cfg, p, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace d4r

@@ -16,6 +16,11 @@
 //    are issued unconditionally and the zero mask is applied when the
 //    registers are written to LDS: no branches around the loads, so the
 //    compiler waits only for the register set being stored.
+//  * Operands come in four forms (OperandMode): row- or k-contiguous
+//    matrices, the im2col of x gathered on the fly (implicit forward), and
+//    an NCHW gradient dy read in place as the O x (B*P) matrix of the
+//    filter- and data-gradient products, so dy is never reshaped or
+//    transposed in HBM.
 //  * LDS layout follows the global layout: an operand stored with k
 //    contiguous is kept as [row][k] (row pitch padded by 16 bytes so the
 //    16-byte fragment reads of 8 consecutive rows hit distinct banks); an
@@ -38,8 +43,6 @@ namespace d4r {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-struct DtF32 { static constexpr int ES = 4; static constexpr int ID = DT_F32; };
 
 constexpr int kBK32 = 32;   // k depth of one stage (floats)
 constexpr int kPad32 = 4;   // 16 bytes of row padding
@@ -203,6 +206,102 @@ struct ImplicitTileF32 {
     }
 };
 
+// A operand read straight from an NCHW gradient dy[b][o][pix]: row m = o,
+// k = b*P + pix, so op(A)[m][k] = dy[(k / P)*O*P + m*P + k % P].  Kept in LDS
+// as [m][k] like a k-contiguous operand.  The 32 lanes of a half-wave take
+// 32 consecutive k of one row (pixel runs, split at most once per image
+// boundary), so each load instruction reads whole 128-byte runs; a thread
+// decodes its k once per stage.  Loads are unconditional (offset 0 when
+// outside) and zeroed at the LDS store.
+template <int BR, int NT>
+struct NchwKTile {
+    static constexpr int BK = kBK32, PAD = kPad32, PITCH = BK + PAD;
+    static constexpr int LDS_BYTES = BR * PITCH * 4;
+    static constexpr int RSTEP = NT / BK;  // rows per pass
+    static constexpr int PER = BR / RSTEP;
+    static_assert(NT % BK == 0 && BR % RSTEP == 0, "whole passes");
+
+    uint32_t reg[PER];
+    uint32_t okmask;
+
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g, int R, int K,
+                                         int r0, int k0, int tid)
+    {
+        const int k = k0 + tid % BK;
+        const int b = k / g.P;
+        const long long base = (long long)b * g.O * g.P + (k - b * g.P);
+        const bool kok = k < K;
+        okmask = 0u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int r = r0 + tid / BK + j * RSTEP;
+            const bool ok = kok && r < R;
+            reg[j] = X[ok ? base + (long long)r * g.P : 0];
+            okmask |= (ok ? 1u : 0u) << j;
+        }
+    }
+
+    template <bool VEC>
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+        uint32_t *l = (uint32_t *)lds;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            l[(tid / BK + j * RSTEP) * PITCH + tid % BK] = ((okmask >> j) & 1u) ? reg[j] : 0u;
+    }
+};
+
+// B operand read straight from an NCHW gradient dy[b][o][pix]: k = o,
+// column n = b*P + pix, so op(B)[k][n] = dy[(n / P)*O*P + k*P + n % P].  Kept
+// in LDS as [k][n] like a row-contiguous operand.  Each thread owns one
+// column for the whole K loop (decoded once, in NchwCol); consecutive lanes
+// take consecutive columns, so a load instruction reads pixel runs.
+struct NchwCol {
+    long long off;  // element offset of (b, o = 0, pix)
+    bool ok;        // n < N
+
+    __device__ __forceinline__ void setup(const ConvGeom &g, int n)
+    {
+        ok = n < g.N;
+        const int b = n / g.P;
+        off = (long long)b * g.O * g.P + (n - b * g.P);
+    }
+};
+
+template <int BR, int NT>
+struct NchwNTile {
+    static constexpr int BK = kBK32, PAD = kPad32, PITCH = BR + PAD;
+    static constexpr int LDS_BYTES = BK * PITCH * 4;
+    static constexpr int KSTEP = NT / BR;  // k rows per pass
+    static constexpr int PER = BK / KSTEP;
+    static_assert(NT % BR == 0 && BK % KSTEP == 0, "whole passes");
+
+    uint32_t reg[PER];
+    uint32_t okmask;
+
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g,
+                                         const NchwCol &c, int K, int k0, int tid)
+    {
+        okmask = 0u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int k = k0 + tid / BR + j * KSTEP;
+            const bool ok = c.ok && k < K;
+            reg[j] = X[ok ? c.off + (long long)k * g.P : 0];
+            okmask |= (ok ? 1u : 0u) << j;
+        }
+    }
+
+    template <bool VEC>
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+        uint32_t *l = (uint32_t *)lds;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            l[(tid / BR + j * KSTEP) * PITCH + tid % BR] = ((okmask >> j) & 1u) ? reg[j] : 0u;
+    }
+};
+
 // Fragment reads: 8 consecutive k (one k group of 16, lane half h) for one
 // 32-row block; the 8 MFMAs of the group use element t.
 template <bool KC, int PITCH>
@@ -224,15 +323,21 @@ __device__ __forceinline__ void frag_f32(const float *lds, int row, int kg, int 
     }
 }
 
-template <int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
+template <int NWM, int NWN, int TM, int TN, int AMODE, int BMODE, bool VEC>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = NWM * NWN * 64;
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
     constexpr int BK = kBK32;
-    static_assert(!IMPL || !B_KC, "implicit B uses the [k][n] layout");
-    using TA = OperandTile<BM, A_KC, NT>;
-    using TB = std::conditional_t<IMPL, ImplicitTileF32<BN, NT>, OperandTile<BN, B_KC, NT>>;
+    static_assert(AMODE == OP_ROWS || AMODE == OP_KC || AMODE == OP_NCHW, "A mode");
+    // LDS layouts: [m][k] unless A is row-contiguous; [n][k] only for a
+    // k-contiguous B
+    constexpr bool A_KC = AMODE != OP_ROWS;
+    constexpr bool B_KC = BMODE == OP_KC;
+    using TA = std::conditional_t<AMODE == OP_NCHW, NchwKTile<BM, NT>, OperandTile<BM, A_KC, NT>>;
+    using TB = std::conditional_t<
+        BMODE == OP_IMPL, ImplicitTileF32<BN, NT>,
+        std::conditional_t<BMODE == OP_NCHW, NchwNTile<BN, NT>, OperandTile<BN, B_KC, NT>>>;
     constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -264,13 +369,21 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     TA ta0, ta1;
     TB tb0, tb1;
     ImplicitColsF32<BN, NT> cols;
-    if constexpr (IMPL)
+    if constexpr (BMODE == OP_IMPL)
         cols.setup(p.g, n_blk, tid);
+    NchwCol ncol;
+    if constexpr (BMODE == OP_NCHW)
+        ncol.setup(p.g, n_blk + tid % BN);
     // K bound for this split: the loaders zero-fill k >= kend.
     auto load = [&](TA &a, TB &b, int k0) {
-        a.template load<VEC>(A, p.lda, p.M, kend, m_blk, k0, tid);
-        if constexpr (IMPL)
+        if constexpr (AMODE == OP_NCHW)
+            a.load(A, p.g, p.M, kend, m_blk, k0, tid);
+        else
+            a.template load<VEC>(A, p.lda, p.M, kend, m_blk, k0, tid);
+        if constexpr (BMODE == OP_IMPL)
             b.gather(B, p.g, cols, kend, k0, tid);
+        else if constexpr (BMODE == OP_NCHW)
+            b.load(B, p.g, ncol, kend, k0, tid);
         else
             b.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
     };
@@ -304,28 +417,29 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     if (nk > 0) {
         // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
         load(ta0, tb0, kbeg);
-        if (nk > 1)
-            load(ta1, tb1, kbeg + BK);
+        load(ta1, tb1, kbeg + BK);
         store(ta0, tb0, smem);
         __syncthreads();
-        if (nk > 2)
-            load(ta0, tb0, kbeg + 2 * BK);
+        load(ta0, tb0, kbeg + 2 * BK);
         // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
         // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
         // it is then refilled with stage t+3.  An odd last stage is peeled.
+        // Loads and stores are unconditional (a stage past the end has every
+        // k >= kend: it reads nothing and stores zeros), and a scheduling
+        // barrier keeps each stage's loads right after the workgroup barrier,
+        // so two stages of loads stay in flight during each compute.
         int t = 0;
         for (; t + 1 < nk; t += 2) {
             compute(smem);
             store(ta1, tb1, smem + STAGE);
             __syncthreads();
-            if (t + 3 < nk)
-                load(ta1, tb1, kbeg + (t + 3) * BK);
+            load(ta1, tb1, kbeg + (t + 3) * BK);
+            __builtin_amdgcn_sched_barrier(0);
             compute(smem + STAGE);
-            if (t + 2 < nk)
-                store(ta0, tb0, smem);
+            store(ta0, tb0, smem);
             __syncthreads();
-            if (t + 4 < nk)
-                load(ta0, tb0, kbeg + (t + 4) * BK);
+            load(ta0, tb0, kbeg + (t + 4) * BK);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (t < nk)
             compute(smem);
@@ -364,7 +478,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     }
 }
 
-template <bool A_KC, bool B_KC, bool VEC, bool IMPL>
+template <int AMODE, int BMODE, bool VEC>
 hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -372,16 +486,16 @@ hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
     dim3 grid(tiles, 1, p.splits);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm_kernel<2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<2, 2, 2, 2, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm_kernel<2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<2, 2, 1, 1, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm_kernel<1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<1, 4, 1, 1, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm_kernel<1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<1, 4, 3, 1, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;  // tile shape not built for f32
@@ -389,26 +503,17 @@ hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <class DT, bool A_KC, bool B_KC, bool IMPL = false>
-hipError_t launch_gemm_layout(int cfg, const GemmParams &p, hipStream_t s)
+// VEC covers the plainly strided operands (OP_ROWS / OP_KC); the gathered
+// ones (OP_IMPL, OP_NCHW) load single elements either way.
+template <int AMODE, int BMODE>
+hipError_t launch_gemm32_modes(int cfg, const GemmParams &p, hipStream_t s)
 {
-    static_assert(DT::ID == DT_F32, "f32 kernel");
-    const bool vec = IMPL ? (p.a_vec != 0) : (p.a_vec && p.b_vec);
+    const bool a_plain = AMODE == OP_ROWS || AMODE == OP_KC;
+    const bool b_plain = BMODE == OP_ROWS || BMODE == OP_KC;
+    const bool vec = (!a_plain || p.a_vec) && (!b_plain || p.b_vec);
     if (vec)
-        return launch_gemm32_vec<A_KC, B_KC, true, IMPL>(cfg, p, s);
-    return launch_gemm32_vec<A_KC, B_KC, false, IMPL>(cfg, p, s);
-}
-
-template <class DT>
-hipError_t launch_gemm_dt(int cfg, bool a_kc, bool b_kc, const GemmParams &p, hipStream_t s)
-{
-    if (a_kc && b_kc)
-        return launch_gemm_layout<DT, true, true>(cfg, p, s);
-    if (a_kc && !b_kc)
-        return launch_gemm_layout<DT, true, false>(cfg, p, s);
-    if (!a_kc && b_kc)
-        return launch_gemm_layout<DT, false, true>(cfg, p, s);
-    return launch_gemm_layout<DT, false, false>(cfg, p, s);
+        return launch_gemm32_vec<AMODE, BMODE, true>(cfg, p, s);
+    return launch_gemm32_vec<AMODE, BMODE, false>(cfg, p, s);
 }
 
 }  // namespace d4r

@@ -65,10 +65,19 @@ struct ConvGeom {
     int N;    // B*P
 };
 
+// How a GEMM operand is laid out in memory.  Operand "rows" are m for A and
+// n for B.
+enum OperandMode : int {
+    OP_ROWS = 0,  // row index contiguous: A[k*lda + m], B[k*ldb + n]
+    OP_KC = 1,    // k contiguous: A[m*lda + k], B[n*ldb + k]
+    OP_IMPL = 2,  // B only: op(B) = im2col(x), gathered from x (geometry p.g)
+    OP_NCHW = 3   // an NCHW gradient dy[b][o][pix] (geometry p.g) whose
+                  // (image, pixel) pair n = b*P + pix is the k index of A
+                  // (A[o][n]) or the column index of B (B[o][n]); o is the row
+                  // of A or the k of B.  Element address b*O*P + o*P + pix.
+};
+
 // C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
-// Operand "rows" are m for A and n for B.  a_kc / b_kc: the operand is
-// stored with k contiguous (A[m*lda + k], B[n*ldb + k]); otherwise the row
-// index is contiguous (A[k*lda + m], B[k*ldb + n]).
 struct GemmParams {
     const void *A;
     const void *B;
@@ -82,14 +91,13 @@ struct GemmParams {
     int splits;
     long long c_split_stride;
     int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned)
-    ConvGeom g;         // implicit B operand: B = x and op(B)[kc][n] = im2col(x)
+    ConvGeom g;         // OP_IMPL and OP_NCHW operands
 };
 
-hipError_t launch_gemm(int dt, int cfg, bool a_kc, bool b_kc, const GemmParams &p,
-                       hipStream_t s);
-// Forward GEMM whose B operand is the im2col of x (p.B = x, geometry p.g),
-// gathered into LDS by the loader: A = Wmat (k contiguous), NCHW epilogue.
-hipError_t launch_gemm_implicit(int dt, int cfg, const GemmParams &p, hipStream_t s);
+// Supported (A, B) modes: every pair of OP_ROWS / OP_KC, (OP_KC, OP_IMPL),
+// and for f32 also (OP_ROWS, OP_NCHW) and (OP_NCHW, OP_KC).  Others return
+// hipErrorInvalidValue.
+hipError_t launch_gemm(int dt, int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s);
 int gemm_bk(int dt);  // K depth of one LDS stage, in elements
 
 

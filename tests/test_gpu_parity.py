@@ -348,6 +348,36 @@ def test_gemm_every_tile_config(dt, tile, flags, monkeypatch):
         assert err < TOL[dt], (tile, M, K, N, err)
 
 
+# f32 conv passes with every tile and both ways of taking dy in the gradient
+# GEMMs (read in place by the NCHW operand loaders, or copied first), over
+# odd pixel counts whose images straddle tiles, with and without 16-byte
+# vector loads on the other operand (Kc % 4).
+CONV_TILE_SHAPES = [
+    (5, 5, 9, 9, 37, 3, 3, 1, 1),     # P = 81, Kc = 45, N = 405
+    (7, 8, 13, 13, 40, 3, 3, 2, 1),   # P = 49, Kc = 72, N = 343
+    (3, 4, 11, 10, 130, 1, 1, 1, 0),  # P = 110, Kc = 4, O > 128
+]
+
+
+@pytest.mark.parametrize("path", ["inplace", "copy"])
+@pytest.mark.parametrize("tile", TILES["f32"])
+@pytest.mark.parametrize("t", CONV_TILE_SHAPES, ids=str)
+def test_conv_f32_every_tile(tile, t, path, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    monkeypatch.setenv("D4R_GRAD_PATH", path)
+    sh = _shape(t)
+    _check_whole(sh, "f32", wl.random_conv(sh, "f32", seed=sum(t) + 3), f"tile {tile}")
+
+
+@pytest.mark.parametrize("li", [0, 1, 2])
+def test_conv_c4_f32_gradients_in_place(li, monkeypatch):
+    # conv3-5 take the copy path by default; force the in-place loaders
+    monkeypatch.setenv("D4R_GRAD_PATH", "inplace")
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[li].shape.with_batch(3)
+    _check_whole(sh, "f32", wl.conv_inputs(w, li, "f32", batch=3), f"c4/{w.layers[li].name}/b3/inplace")
+
+
 @pytest.mark.parametrize("tile", ["128x128", "128x256", "256x128"])
 def test_conv_bf16_every_big_tile(tile, monkeypatch):
     monkeypatch.setenv("D4R_GEMM_TILE", tile)
