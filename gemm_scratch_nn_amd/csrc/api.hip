@@ -78,6 +78,7 @@ int wg_per_cu(int cfg, int dt)
     case TILE_64x64: return h ? 3 : 4;
     case TILE_32x128: return 3;
     case TILE_96x128: return 2;
+    case TILE_128x64: return 2;  // f32 only
     default: return 1;  // 128x256, 256x128 (16-bit only)
     }
 }
@@ -96,6 +97,8 @@ int tile_from_env(int dt)
     for (int c = 0; c < TILE_COUNT; ++c) {
         if (dt == DT_F32 && (c == TILE_128x256 || c == TILE_256x128))
             continue;
+        if (dt != DT_F32 && c == TILE_128x64)
+            continue;
         TileShape ts = tile_shape(c);
         char buf[32];
         snprintf(buf, sizeof buf, "%dx%d", ts.bm, ts.bn);
@@ -107,17 +110,21 @@ int tile_from_env(int dt)
 
 GemmPlan plan_gemm(int M, int N, int K, int dt)
 {
-    TileCand cands[4];
+    TileCand cands[6];
     int nc = 0;
     if (M <= 32) {
         cands[nc++] = {TILE_32x128, 1.0};
     } else if (M <= 64 || N <= 64) {
         cands[nc++] = {TILE_64x64, 1.0};
     } else if (dt == DT_F32) {
-        if (M % 128 != 0 && M % 96 == 0 && M <= 192)
+        if (M % 128 != 0 && M % 96 == 0 && M <= 192) {
             cands[nc++] = {TILE_96x128, 1.0};
-        else
+        } else {
+            // 128x64 fills the chip without split-K where 128x128 tiles
+            // would half-fill it (measured 8% slower per flop otherwise)
             cands[nc++] = {TILE_128x128, 1.0};
+            cands[nc++] = {TILE_128x64, 0.92};
+        }
     } else {
         cands[nc++] = {TILE_128x128, 0.85};
         cands[nc++] = {TILE_128x256, 1.0};

@@ -499,8 +499,10 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
 
 // ---------------------------------------------------------------------------
 // Bias gradient.  Pass 1: block (s, o) sums images [s*per, (s+1)*per) of
-// channel o; the block reduces through a fixed wave-shuffle tree and LDS.
-// Pass 2: one thread per channel adds the partials in split order.
+// channel o: its threads stride through the flattened (image, pixel) range
+// of those planes, four elements in flight per thread, then the block
+// reduces through a fixed wave-shuffle tree and LDS.  Pass 2: one thread per
+// channel adds the partials in split order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v)
 {
@@ -517,23 +519,50 @@ __global__ __launch_bounds__(NT) void bias_partial_kernel(const T *__restrict__ 
 {
     __shared__ float red[NT / 64];
     const int s = blockIdx.x, o = blockIdx.y;
-    const int b0 = s * per, b1 = min(g.B, b0 + per);
-    float acc = 0.0f;
-    for (int b = b0; b < b1; ++b) {
-        const T *plane = dy + ((long long)b * g.O + o) * g.P;
-        for (int t = threadIdx.x; t < g.P; t += NT)
-            acc += to_f32(plane[t], dt);
+    const int b0 = s * per, nb = min(g.B, b0 + per) - b0;
+    const int total = nb * g.P;  // elements of this block
+    const long long plane = (long long)g.O * g.P;
+    const T *base = dy + ((long long)b0 * g.O + o) * g.P;
+    // element i = b*P + pix of the block sits at base[b*O*P + pix]
+    int b = threadIdx.x / g.P, pix = threadIdx.x - (threadIdx.x / g.P) * g.P;
+    const int step_b = NT / g.P, step_p = NT - (NT / g.P) * g.P;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int i = threadIdx.x;
+    for (; i + 3 * NT < total; i += 4 * NT) {
+        T v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = base[b * plane + pix];
+            pix += step_p;
+            b += step_b;
+            if (pix >= g.P) {
+                pix -= g.P;
+                ++b;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc[u] += to_f32(v[u], dt);
     }
-    acc = wave_sum(acc);
+    for (; i < total; i += NT) {
+        acc[0] += to_f32(base[b * plane + pix], dt);
+        pix += step_p;
+        b += step_b;
+        if (pix >= g.P) {
+            pix -= g.P;
+            ++b;
+        }
+    }
+    float tot = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
     if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = acc;
+        red[threadIdx.x >> 6] = tot;
     __syncthreads();
     if (threadIdx.x == 0) {
-        float tot = 0.0f;
+        float t = 0.0f;
 #pragma unroll
         for (int w = 0; w < NT / 64; ++w)
-            tot += red[w];
-        partial[o * splits + s] = tot;
+            t += red[w];
+        partial[o * splits + s] = t;
     }
 }
 
@@ -722,8 +751,9 @@ hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, vo
 
 int bias_grad_splits(const ConvGeom &g)
 {
-    // enough blocks to cover the chip (>= ~2048), at most one image per block
-    int want = (2048 + g.O - 1) / g.O;
+    // enough blocks to cover the chip several times (>= ~4096), at least one
+    // image per block
+    int want = (4096 + g.O - 1) / g.O;
     if (want > g.B)
         want = g.B;
     if (want < 1)

@@ -25,7 +25,13 @@
 //    contiguous is kept as [row][k] (row pitch padded by 16 bytes so the
 //    16-byte fragment reads of 8 consecutive rows hit distinct banks); an
 //    operand stored row-contiguous is kept as [k][row] and read one element
-//    per lane per k.
+//    per lane per k.  (Loading row-contiguous operands one element per lane
+//    into [row][k] instead measured slower: four times the load
+//    instructions.)
+//  * When both layouts are [row][k], scheduling-group hints read both k
+//    groups' fragments up front and spread the next stage's LDS stores
+//    through the MFMAs; with [k][row] layouts the compiler's own schedule
+//    measured faster.
 //  * Only the sum over k matters to the result, so lane-half h of a
 //    fragment takes k = 8h..8h+7 of each 16-wide k group, the same mapping
 //    for A and B.
@@ -36,6 +42,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 
@@ -323,6 +330,31 @@ __device__ __forceinline__ void frag_f32(const float *lds, int row, int kg, int 
     }
 }
 
+// Scheduling hints for one stage (fragment reads, MFMAs and the LDS stores
+// of the next stage): both k groups' fragments are read up front, then the
+// next stage's LDS stores are spread evenly through the MFMAs.  Masks:
+// 0x008 MFMA, 0x100 LDS read, 0x200 LDS write.
+template <int STEP, int... W>
+__device__ __forceinline__ void sched_spread_writes(std::integer_sequence<int, W...>)
+{
+    ((__builtin_amdgcn_sched_group_barrier(0x008, STEP + 0 * W, 0),
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0)),
+     ...);
+}
+
+template <int RD_KG, int MF_KG, int WR>
+__device__ __forceinline__ void sched_stage()
+{
+    constexpr int LEAD = 2;
+    constexpr int REST = 2 * MF_KG - LEAD;
+    constexpr int STEP = REST / (WR + 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD_KG, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD_KG, 0);
+    sched_spread_writes<STEP>(std::make_integer_sequence<int, WR>{});
+    __builtin_amdgcn_sched_group_barrier(0x008, REST - STEP * WR, 0);
+}
+
 template <int NWM, int NWN, int TM, int TN, int AMODE, int BMODE, bool VEC>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 {
@@ -394,25 +426,35 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     auto compute = [&](const char *buf) {
         const float *fa = (const float *)buf;
         const float *fb = (const float *)(buf + TA::LDS_BYTES);
+        // all fragment reads of the stage first, so the LDS latency is paid
+        // once per stage rather than once per 16-wide k group
+        constexpr int KG = BK / 16;
+        float af[KG][TM][8], bf[KG][TN][8];
 #pragma unroll
-        for (int kg = 0; kg < BK / 16; ++kg) {
-            float af[TM][8], bf[TN][8];
+        for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                frag_f32<A_KC, TA::PITCH>(fa, (wm * TM + i) * 32 + l32, kg, h, af[i]);
+                frag_f32<A_KC, TA::PITCH>(fa, (wm * TM + i) * 32 + l32, kg, h, af[kg][i]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                frag_f32<B_KC, TB::PITCH>(fb, (wn * TN + j) * 32 + l32, kg, h, bf[j]);
+                frag_f32<B_KC, TB::PITCH>(fb, (wn * TN + j) * 32 + l32, kg, h, bf[kg][j]);
+        }
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][t], bf[j][t], acc[i][j], 0,
-                                                                         0, 0);
-        }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[kg][i][t], bf[kg][j][t], acc[i][j],
+                                                                         0, 0, 0);
     };
+
+    // instruction counts of one stage, for the scheduling hints
+    constexpr int RD_KG = (A_KC ? 2 : 8) * TM + (B_KC ? 2 : 8) * TN;  // LDS reads per k group
+    constexpr int MF_KG = 8 * TM * TN;                               // MFMAs per k group
+    constexpr int WR = TA::PER + TB::PER;                            // LDS stores per stage
 
     if (nk > 0) {
         // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
@@ -432,11 +474,17 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
         for (; t + 1 < nk; t += 2) {
             compute(smem);
             store(ta1, tb1, smem + STAGE);
+            if constexpr (A_KC && B_KC)
+                sched_stage<RD_KG, MF_KG, WR>();
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             load(ta1, tb1, kbeg + (t + 3) * BK);
             __builtin_amdgcn_sched_barrier(0);
             compute(smem + STAGE);
             store(ta0, tb0, smem);
+            if constexpr (A_KC && B_KC)
+                sched_stage<RD_KG, MF_KG, WR>();
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             load(ta0, tb0, kbeg + (t + 4) * BK);
             __builtin_amdgcn_sched_barrier(0);
@@ -496,6 +544,9 @@ hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
         break;
     case TILE_96x128:
         hipLaunchKernelGGL((gemm_kernel<1, 4, 3, 1, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
+        break;
+    case TILE_128x64:
+        hipLaunchKernelGGL((gemm_kernel<2, 2, 2, 1, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;  // tile shape not built for f32

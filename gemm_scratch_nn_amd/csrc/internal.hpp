@@ -21,7 +21,8 @@ enum TileCfg : int {
     TILE_96x128 = 3,   // 1x4 waves, 3x1 blocks (M = 96)
     TILE_128x256 = 4,  // 2x2 waves, 2x4 blocks (16-bit operands only)
     TILE_256x128 = 5,  // 2x2 waves, 4x2 blocks (16-bit operands only)
-    TILE_COUNT = 6
+    TILE_128x64 = 6,   // 2x2 waves, 2x1 blocks (f32 operands only)
+    TILE_COUNT = 7
 };
 
 struct TileShape { int bm, bn; };
@@ -33,6 +34,7 @@ inline TileShape tile_shape(int cfg)
     case TILE_32x128: return {32, 128};
     case TILE_96x128: return {96, 128};
     case TILE_128x256: return {128, 256};
+    case TILE_128x64: return {128, 64};
     default: return {256, 128};
     }
 }

@@ -328,7 +328,7 @@ def test_forward_without_bias():
 # every GEMM tile configuration on ragged shapes (planner override)
 # ---------------------------------------------------------------------------
 
-TILES = {"f32": ["128x128", "64x64", "32x128", "96x128"],
+TILES = {"f32": ["128x128", "64x64", "32x128", "96x128", "128x64"],
          "f16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"],
          "bf16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"]}
 
