@@ -79,7 +79,7 @@ int wg_per_cu(int cfg, int dt)
     case TILE_32x128: return 3;
     case TILE_96x128: return 2;
     case TILE_128x64: return 2;  // f32 only
-    default: return 1;  // 128x256, 256x128 (16-bit only)
+    default: return 1;  // 128x256, 256x128 (16-bit only, 8 waves)
     }
 }
 

@@ -16,6 +16,9 @@
 //    are loaded as 4 k-rows x 8 rows per thread (four 16-byte loads), turned
 //    into 8 rows x 4 k in registers (16 half-word permutes) and stored as
 //    8-byte LDS writes, so fragment reads are 16-byte reads for every layout.
+//  * The 128x256 and 256x128 tiles run eight wavefronts (two per SIMD, one
+//    workgroup per CU by LDS), so one wavefront's waits are covered by the
+//    other's MFMAs; the smaller tiles run four.
 //  * Workgroups are renumbered so that consecutive tiles land on the same
 //    XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each
 //    with its own L2): the M tiles that share a B panel then share one L2.
@@ -46,10 +49,10 @@ __device__ __forceinline__ f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c)
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// One operand tile of BR rows x 64 k, 16-bit elements.
-template <int BR, bool KC>
+// One operand tile of BR rows x 64 k, 16-bit elements, loaded by NT threads.
+template <int BR, bool KC, int NT_ = 256>
 struct Tile16 {
-    static constexpr int NT = 256;
+    static constexpr int NT = NT_;
     static constexpr int BK = 64;
     static constexpr int LDS_BYTES = BR * 128;
     // k-contiguous: one 16-byte chunk per slot, 8 slots per row
@@ -194,13 +197,16 @@ struct Tile16 {
 // offsets and window origins are decoded once.
 // Image offsets and window origins of a thread's 8 columns (fixed for the
 // whole K loop, shared by both register sets).
-template <int BR>
+template <int BR, int NT>
 struct ImplicitCols16 {
     int nb[8], nh[8], nw[8];  // image offset (-1 past N or unused), window origin
 
     __device__ __forceinline__ void setup(const ConvGeom &g, int n_blk, int tid)
     {
-        constexpr int RGH = Tile16<BR, false>::RGH;
+        // a thread's row group is the same in every slot: id = s*NT + tid and
+        // NT/16 is a multiple of RGH
+        constexpr int RGH = Tile16<BR, false, NT>::RGH;
+        static_assert((NT / 16) % RGH == 0, "fixed columns per thread");
         const int rg = ((tid >> 4) % RGH) * 8 + (tid & 7);
         const int n0 = n_blk + rg * 8;
         int b = n0 / g.P;
@@ -223,16 +229,16 @@ struct ImplicitCols16 {
     }
 };
 
-template <int BR>
-struct ImplicitTile16 : Tile16<BR, false> {
-    using Base = Tile16<BR, false>;
+template <int BR, int NT_>
+struct ImplicitTile16 : Tile16<BR, false, NT_> {
+    using Base = Tile16<BR, false, NT_>;
     using Base::NT;
     using Base::PER;
     using Base::SLOTS;
     using Base::r;
 
     __device__ __forceinline__ void gather(const uint16_t *__restrict__ x, const ConvGeom &g,
-                                           const ImplicitCols16<BR> &cols, int K, int k0, int tid)
+                                           const ImplicitCols16<BR, NT_> &cols, int K, int k0, int tid)
     {
         const int *nb = cols.nb, *nh = cols.nh, *nw = cols.nw;
         const int khw = g.kH * g.kW;
@@ -281,13 +287,14 @@ __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h
 }
 
 template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
-__global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
+__global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 {
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = 64;
-    static_assert(NWM * NWN == 4, "four wavefronts per workgroup");
+    constexpr int NT = NWM * NWN * 64;
+    static_assert(NWM * NWN == 4 || NWM * NWN == 8, "four or eight wavefronts per workgroup");
     static_assert(!IMPL || !B_KC, "implicit B uses the row-contiguous path");
-    using TA = Tile16<BM, A_KC>;
-    using TB = std::conditional_t<IMPL, ImplicitTile16<BN>, Tile16<BN, B_KC>>;
+    using TA = Tile16<BM, A_KC, NT>;
+    using TB = std::conditional_t<IMPL, ImplicitTile16<BN, NT>, Tile16<BN, B_KC, NT>>;
     constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemmParams p)
     TA ta0, ta1;
     TB tb0, tb1;
 
-    ImplicitCols16<BN> cols;
+    ImplicitCols16<BN, NT> cols;
     if constexpr (IMPL)
         cols.setup(p.g, n_blk, tid);
     auto load_b = [&](TB &t, int k0) {
@@ -425,25 +432,27 @@ hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
-    const dim3 grid(tiles, 1, p.splits), block(256);
+    const dim3 grid(tiles, 1, p.splits), b4(256), b8(512);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
         break;
+    // the large tiles run eight wavefronts, two per SIMD, so one wave's
+    // waits are covered by the other's MFMAs
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 4, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 4, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b8, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 4, 2, A_KC, B_KC, VEC, IMPL>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 4, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b8, 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;

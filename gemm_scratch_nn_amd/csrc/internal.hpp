@@ -19,8 +19,8 @@ enum TileCfg : int {
     TILE_64x64 = 1,    // 2x2 waves, 1x1 block
     TILE_32x128 = 2,   // 1x4 waves, 1x1 block (M <= 32)
     TILE_96x128 = 3,   // 1x4 waves, 3x1 blocks (M = 96)
-    TILE_128x256 = 4,  // 2x2 waves, 2x4 blocks (16-bit operands only)
-    TILE_256x128 = 5,  // 2x2 waves, 4x2 blocks (16-bit operands only)
+    TILE_128x256 = 4,  // 2x4 waves, 2x2 blocks (16-bit operands only)
+    TILE_256x128 = 5,  // 4x2 waves, 2x2 blocks (16-bit operands only)
     TILE_128x64 = 6,   // 2x2 waves, 2x1 blocks (f32 operands only)
     TILE_COUNT = 7
 };
