@@ -286,6 +286,44 @@ __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h
     return *(const u32x4_t *)(lds + row * 128 + ((ch ^ swz(row)) << 4));
 }
 
+// Epilogue of a wavefront's TM x TN accumulator blocks, whose top-left
+// output is (m0, n0): accumulator element e of a 32x32 block is row
+// 8*(e/4) + 4*h + (e%4), column l32.  Row-major store (split-K partials at
+// blockIdx.z) or the NCHW store with bias.
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&acc)[TM][TN], int m0, int n0,
+                                          int h, int l32)
+{
+    float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n0 + j * 32 + l32;
+        if (n >= p.N)
+            continue;
+        long long col_off;
+        if (p.epi == EPI_NCHW) {
+            const int b = n / p.P;
+            col_off = (long long)b * p.M * p.P + (n - b * p.P);
+        } else {
+            col_off = n;
+        }
+        const long long row_stride = (p.epi == EPI_NCHW) ? p.P : p.ldc;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < p.M) {
+                    float v = acc[i][j][e];
+                    if (p.epi == EPI_NCHW && p.bias)
+                        v += p.bias[m];
+                    C[col_off + (long long)m * row_stride] = v;
+                }
+            }
+        }
+    }
+}
+
 template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 {
@@ -395,36 +433,182 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
             compute(smem, smem + TA::LDS_BYTES);
     }
 
-    // Epilogue: accumulator element e of a 32x32 block is row
-    // 8*(e/4) + 4*h + (e%4), column l32.
-    float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for two k-contiguous operands (the filter-gradient
+// product and other NT/NN-with-transposed-A shapes).  Each 16-byte chunk
+// goes from global memory straight into LDS (global_load_lds_dwordx4: lane
+// i of a wavefront writes bytes [16i, 16i+16) after the wavefront's LDS
+// base), so no registers stage the tiles and no LDS store instructions are
+// issued.  A stage of BK k is one LDS row of BK*2 bytes per tile row; chunk
+// c of row r sits at position c ^ dl_swz(r), which the loading lane realises
+// by fetching the permuted global chunk, so the 16-byte fragment reads of 8
+// consecutive rows hit distinct banks.  A ring of NBUF LDS stages keeps
+// NBUF-1 stages of loads in flight; one barrier per stage.
+// Requirements (checked by the launcher): 16-byte aligned rows, every split
+// a whole number of stages.  Rows past M or N load a clamped row; they only
+// reach outputs that the epilogue masks.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// chunk position of chunk c in row r: c ^ dl_swz<CH>(r) for CH chunks per row
+template <int CH>
+__device__ __forceinline__ int dl_swz(int row)
+{
+    return CH == 4 ? ((row >> 1) & 3) : ((row ^ (row >> 3)) & 7);
+}
+
+template <int DTID, int NWM, int NWN, int TM, int TN, int BK, int NBUF>
+__global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
+{
+    constexpr int NW = NWM * NWN;
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
+    constexpr int ROWB = BK * 2;      // bytes per LDS row
+    constexpr int CH = ROWB / 16;     // 16-byte chunks per row
+    constexpr int RPL = 64 / CH;      // rows per wavefront load (1 KB)
+    constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+    constexpr int A_LD = BM / (RPL * NW), B_LD = BN / (RPL * NW);  // loads per wavefront per stage
+    static_assert(CH == 4 || CH == 8, "32- or 64-deep stages");
+    static_assert(BM % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "whole load groups");
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % NWM, wn = wave / NWM;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const int mt = (p.M + BM - 1) / BM;
+    const int tile = xcd_tile(blockIdx.x, mt * ((p.N + BN - 1) / BN));
+    const int m_blk = (tile % mt) * BM;
+    const int n_blk = (tile / mt) * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg) / BK;
+
+    // This lane's load rows and chunks: load j of a wavefront covers tile
+    // rows [(j*NW + wave)*RPL, +RPL); lane -> row lane/CH, LDS position
+    // lane%CH.
+    const uint16_t *A = (const uint16_t *)p.A;
+    const uint16_t *B = (const uint16_t *)p.B;
+    long long a_off[A_LD], b_off[B_LD];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n_blk + (wn * TN + j) * 32 + l32;
-        if (n >= p.N)
-            continue;
-        long long col_off;
-        if (p.epi == EPI_NCHW) {
-            const int b = n / p.P;
-            col_off = (long long)b * p.M * p.P + (n - b * p.P);
-        } else {
-            col_off = n;
-        }
-        const long long row_stride = (p.epi == EPI_NCHW) ? p.P : p.ldc;
+    for (int j = 0; j < A_LD; ++j) {
+        const int r = (j * NW + wave) * RPL + lane / CH;
+        const int gr = min(m_blk + r, p.M - 1);
+        a_off[j] = (long long)gr * p.lda + ((lane % CH) ^ dl_swz<CH>(r)) * 8;
+    }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < B_LD; ++j) {
+        const int r = (j * NW + wave) * RPL + lane / CH;
+        const int gr = min(n_blk + r, p.N - 1);
+        b_off[j] = (long long)gr * p.ldb + ((lane % CH) ^ dl_swz<CH>(r)) * 8;
+    }
+    // stage s (clamped to the first stage past the end: its buffer is never
+    // read) into ring slot s % NBUF
+    auto issue = [&](int s) {
+        const int k0 = kbeg + (s < nk ? s : 0) * BK;
+        char *base = smem + (s % NBUF) * STAGE;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m_blk + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < p.M) {
-                    float v = acc[i][j][e];
-                    if (p.epi == EPI_NCHW && p.bias)
-                        v += p.bias[m];
-                    C[col_off + (long long)m * row_stride] = v;
-                }
-            }
+        for (int j = 0; j < A_LD; ++j)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(A + a_off[j] + k0),
+                                             (lds_void_t *)(base + (j * NW + wave) * RPL * ROWB), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < B_LD; ++j)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(B + b_off[j] + k0),
+                                             (lds_void_t *)(base + A_BYTES + (j * NW + wave) * RPL * ROWB), 16,
+                                             0, 0);
+    };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    auto frag = [&](const char *lds, int row, int q) {
+        const int c = 2 * q + h;
+        return *(const u32x4_t *)(lds + row * ROWB + ((c ^ dl_swz<CH>(row)) << 4));
+    };
+
+    // NBUF-1 stages are issued ahead; at the top of iteration t the loads of
+    // stages t+1 .. t+NBUF-2 may still be in flight, stage t's must be done
+    constexpr int LPS = A_LD + B_LD;
+    constexpr int VM = (NBUF - 2) * LPS;
+    static_assert(VM < 64, "vmcnt range");
+    constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+
+#pragma unroll
+    for (int s0 = 0; s0 < NBUF - 1; ++s0)
+        issue(s0);
+    for (int t = 0; t < nk; ++t) {
+        // Stage t has landed (this wavefront's share; the barrier makes it
+        // everyone's) and every wavefront is done reading slot (t+3) % NBUF.
+        // A plain s_barrier: the workgroup fence of __syncthreads would wait
+        // for all loads in flight, LDS-bound ones included.  The empty asm
+        // keeps the compiler from moving LDS accesses across it.
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(t + NBUF - 1);
+        const char *la = smem + (t % NBUF) * STAGE;
+        const char *lb = la + A_BYTES;
+#pragma unroll
+        for (int q = 0; q < BK / 16; ++q) {
+            u32x4_t af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = frag(la, (wm * TM + i) * 32 + l32, q);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bf[j] = frag(lb, (wn * TN + j) * 32 + l32, q);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = mfma16<DTID>(af[i], bf[j], acc[i][j]);
         }
     }
+    // drain the loads of the stages past the end before the workgroup exits
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32);
+}
+
+// The direct-to-LDS kernel applies to two k-contiguous operands with
+// 16-byte aligned rows whose splits are whole stages.
+// 64-deep stages in a ring of three (two stages of loads in flight):
+// measured level with 32-deep stages in a ring of four, with half the
+// barriers.
+constexpr int kDlBK = 64, kDlBuf = 3;
+inline bool dl_applies(int amode, int bmode, const GemmParams &p)
+{
+    return amode == OP_KC && bmode == OP_KC && p.a_vec && p.b_vec && p.K % kDlBK == 0 &&
+           p.k_per_split % kDlBK == 0;
+}
+
+template <int DTID>
+hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
+{
+    TileShape ts = tile_shape(cfg);
+    const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
+    const dim3 grid(tiles, 1, p.splits), b8(512);
+    switch (cfg) {
+    case TILE_128x256:
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBK, kDlBuf>), grid, b8, 0, s, p);
+        break;
+    case TILE_256x128:
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBK, kDlBuf>), grid, b8, 0, s, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int DTID, bool A_KC, bool B_KC, bool VEC, bool IMPL = false>
@@ -483,6 +667,8 @@ hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hip
     if (!a_ok || !b_ok)
         return hipErrorInvalidValue;
     const bool a_kc = amode == OP_KC, b_kc = bmode == OP_KC;
+    if ((cfg == TILE_128x256 || cfg == TILE_256x128) && dl_applies(amode, bmode, p))
+        return launch_gemm16_dl<DTID>(cfg, p, s);
     if (a_kc && b_kc)
         return launch_gemm16_layout<DTID, true, true>(cfg, p, s);
     if (a_kc && !b_kc)
