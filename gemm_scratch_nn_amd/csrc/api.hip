@@ -121,9 +121,12 @@ GemmPlan plan_gemm(int M, int N, int K, int dt)
             cands[nc++] = {TILE_96x128, 1.0};
         } else {
             // 128x64 fills the chip without split-K where 128x128 tiles
-            // would half-fill it (measured 8% slower per flop otherwise)
+            // would not make one full wave; elsewhere it measured 4-8%
+            // slower per flop, more than the model's wave rounding shows
             cands[nc++] = {TILE_128x128, 1.0};
-            cands[nc++] = {TILE_128x64, 0.92};
+            const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
+            if (t128 < (long long)kComputeUnits * wg_per_cu(TILE_128x128, dt))
+                cands[nc++] = {TILE_128x64, 0.92};
         }
     } else {
         cands[nc++] = {TILE_128x128, 0.85};

@@ -475,6 +475,9 @@ __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ 
 // ---------------------------------------------------------------------------
 // Batched transpose out[b][c][r] = in[b][r][c] through a 64x64 LDS tile
 // (one extra column of padding so the column reads hit distinct banks).
+// Each wavefront reads 64 consecutive elements of a row and writes 64
+// consecutive elements of an output row; a thread's 16 loads are all issued
+// before the first is used.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in, T *__restrict__ out,
@@ -484,16 +487,24 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
     const long long base = (long long)blockIdx.z * R * Cc;
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int rr = ty; rr < 64; rr += 4) {
-        int r = r0 + rr, c = c0 + tx;
-        if (r < R && c < Cc)
-            tile[rr][tx] = in[base + (long long)r * Cc + c];
+    constexpr int ROWS = 64 / (NT / 64);
+    T v[ROWS];
+    const bool cin = c0 + tx < Cc;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = r0 + ty + i * (NT / 64);
+        v[i] = (cin && r < R) ? in[base + (long long)r * Cc + c0 + tx] : (T)0;
     }
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+        tile[ty + i * (NT / 64)][tx] = v[i];
     __syncthreads();
-    for (int cc = ty; cc < 64; cc += 4) {
-        int c = c0 + cc, r = r0 + tx;
-        if (r < R && c < Cc)
-            out[base + (long long)c * R + r] = tile[tx][cc];
+    const bool rin = r0 + tx < R;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int c = c0 + ty + i * (NT / 64);
+        if (rin && c < Cc)
+            out[base + (long long)c * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
     }
 }
 
