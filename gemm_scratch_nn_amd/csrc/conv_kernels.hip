@@ -590,22 +590,21 @@ __global__ __launch_bounds__(NT) void bias_final_kernel(const float *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduction: C = sum_{s} part[s] in split order, then the GEMM
-// epilogue (row-major store, or NCHW store with bias).
+// Split-K reduction: C = sum_{s} part[s], then the GEMM epilogue (row-major
+// store, or NCHW store with bias).  Two fixed summation orders:
+//  * vector path (N and the split stride multiples of 4): a thread owns four
+//    consecutive outputs, loads four splits ahead and adds them in split
+//    order;
+//  * grouped path (anything else, and few outputs over many splits): a block
+//    owns 64 consecutive outputs; its four wavefronts sum contiguous quarters
+//    of the split range (lanes along the outputs, so loads coalesce) and the
+//    four partial sums are added in quarter order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float *__restrict__ part, int splits,
-                                                           int M, int N, long long stride, int epi,
-                                                           float *__restrict__ C, int ldc,
-                                                           const float *__restrict__ bias, int P)
+__device__ __forceinline__ void splitk_store(float acc, long long idx, int M, int N, int epi, float *C,
+                                             int ldc, const float *bias, int P)
 {
-    const long long idx = (long long)blockIdx.x * NT + threadIdx.x;
-    if (idx >= (long long)M * N)
-        return;
     const int m = (int)(idx / N);
     const int n = (int)(idx - (long long)m * N);
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s)
-        acc += part[s * stride + idx];
     if (epi == EPI_NCHW) {
         if (bias)
             acc += bias[m];
@@ -613,6 +612,81 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float *__restri
         C[((long long)b * M + m) * P + pix] = acc;
     } else {
         C[(long long)m * ldc + n] = acc;
+    }
+}
+
+__global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__restrict__ part, int splits,
+                                                               int M, int N, long long stride, int epi,
+                                                               float *__restrict__ C, int ldc,
+                                                               const float *__restrict__ bias, int P)
+{
+    const long long total = (long long)M * N;
+    const long long i0 = ((long long)blockIdx.x * NT + threadIdx.x) * 4;
+    if (i0 >= total)
+        return;
+    // i0 .. i0+3 lie in one row and inside the matrix (N % 4 == 0)
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int sp = 0;
+    for (; sp + 4 <= splits; sp += 4) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = *(const float4 *)(part + (sp + u) * stride + i0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc[0] += v[u].x;
+            acc[1] += v[u].y;
+            acc[2] += v[u].z;
+            acc[3] += v[u].w;
+        }
+    }
+    for (; sp < splits; ++sp) {
+        const float4 v = *(const float4 *)(part + sp * stride + i0);
+        acc[0] += v.x;
+        acc[1] += v.y;
+        acc[2] += v.z;
+        acc[3] += v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        splitk_store(acc[e], i0 + e, M, N, epi, C, ldc, bias, P);
+}
+
+__global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__restrict__ part, int splits,
+                                                                 int M, int N, long long stride, int epi,
+                                                                 float *__restrict__ C, int ldc,
+                                                                 const float *__restrict__ bias, int P)
+{
+    constexpr int G = NT / 64;  // split groups per block
+    __shared__ float red[G][64];
+    const long long total = (long long)M * N;
+    const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    const long long idx = (long long)blockIdx.x * 64 + lane;
+    const int per = (splits + G - 1) / G;
+    const int s0 = grp * per, s1 = min(splits, s0 + per);
+    float acc = 0.0f;
+    if (idx < total) {
+        int sp = s0;
+        for (; sp + 4 <= s1; sp += 4) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = part[(sp + u) * stride + idx];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc += v[u];
+        }
+        for (; sp < s1; ++sp)
+            acc += part[sp * stride + idx];
+    }
+    red[grp][lane] = acc;
+    __syncthreads();
+    if (grp == 0 && idx < total) {
+        float t = red[0][lane];
+#pragma unroll
+        for (int g2 = 1; g2 < G; ++g2)
+            t += red[g2][lane];
+        splitk_store(t, idx, M, N, epi, C, ldc, bias, P);
     }
 }
 
@@ -796,8 +870,15 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, lon
                                 int epi, float *C, int ldc, const float *bias, int P, hipStream_t s)
 {
     const long long total = (long long)M * N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + NT - 1) / NT)), dim3(NT), 0, s,
-                       part, splits, M, N, split_stride, epi, C, ldc, bias, P);
+    const long long vthreads = (total + 3) / 4;
+    const bool vec = (N % 4) == 0 && (split_stride % 4) == 0 && ((uintptr_t)part % 16) == 0;
+    // the vector path needs enough threads to fill the chip
+    if (vec && vthreads >= 64LL * 1024)
+        hipLaunchKernelGGL(splitk_reduce_vec_kernel, dim3((unsigned)((vthreads + NT - 1) / NT)), dim3(NT), 0,
+                           s, part, splits, M, N, split_stride, epi, C, ldc, bias, P);
+    else
+        hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3((unsigned)((total + 63) / 64)), dim3(NT), 0, s,
+                           part, splits, M, N, split_stride, epi, C, ldc, bias, P);
     return hipGetLastError();
 }
 
