@@ -333,8 +333,9 @@ struct d4r_conv {
     int es;
     GemmPlan fwd, bwd_data, bwd_filter;
     int bias_splits;
-    size_t off_g, off_bias, off_big, ws_bytes;
-    GradPath dgrad, wgrad;  // how the gradient GEMMs take dy and W
+    size_t off_g, off_wt, off_bias, off_big, ws_bytes;
+    GradPath dgrad, wgrad;  // how the gradient GEMMs take dy
+    bool dgrad_wt;          // data gradient reads a k-contiguous copy of W^T
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -462,6 +463,13 @@ void choose_grad_paths(d4r_conv *h)
     }
     h->dgrad = gp;
     h->wgrad = gp;
+    // With dy copied, a transposed copy of W (small next to dy) lets the
+    // data-gradient GEMM read both operands k-contiguous: 1% faster per
+    // step on AlexNet conv3-5 (f32 and bf16) than reading W row-contiguous.
+    // D4R_DGRAD_WT=0|1 overrides (experiments, tests).
+    h->dgrad_wt = h->dgrad == GP_COPY;
+    if (const char *e = getenv("D4R_DGRAD_WT"))
+        h->dgrad_wt = h->dgrad == GP_COPY && e[0] == '1';
 }
 
 }  // namespace
@@ -528,6 +536,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->off_g = off;
     if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
         off += align_up((size_t)y_el * h->es);
+    h->off_wt = off;
+    if (h->dgrad_wt)
+        off += align_up((size_t)w_el * h->es);
     h->off_bias = off;
     off += align_up((size_t)outC * h->bias_splits * sizeof(float));
     h->off_big = off;
@@ -683,7 +694,17 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, f
     } else {
         void *gt = wsb + h->off_g;
         D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad transpose");
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_KC, w, g.Kc, gt, g.O, g.Kc, g.N, g.O,
+        const void *a = w;
+        int amode = OP_ROWS, lda = g.Kc;
+        if (h->dgrad_wt) {
+            // Wt[kc][o] = W[o][kc]
+            void *wt = wsb + h->off_wt;
+            D4R_LAUNCH(step_transpose(h, 1, g.O, g.Kc, w, wt, s, "dgrad_w"), "filter transpose");
+            a = wt;
+            amode = OP_KC;
+            lda = g.O;
+        }
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, amode, OP_KC, a, lda, gt, g.O, g.Kc, g.N, g.O,
                             EPI_ROWMAJOR, dcol, g.N, nullptr, 0, partial, s, "dgrad"),
                    "data-gradient GEMM");
     }

@@ -381,6 +381,16 @@ def test_conv_c4_f32_gradients_in_place(li, monkeypatch):
     _check_whole(sh, "f32", wl.conv_inputs(w, li, "f32", batch=3), f"c4/{w.layers[li].name}/b3/inplace")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_conv_data_gradient_w_row_contiguous(dt, monkeypatch):
+    # the copy path transposes W for the data gradient by default; force the
+    # GEMM that reads W row-contiguous instead
+    monkeypatch.setenv("D4R_DGRAD_WT", "0")
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[2].shape.with_batch(3)
+    _check_whole(sh, dt, wl.conv_inputs(w, 2, dt, batch=3), f"c4/conv5/b3/w-rows")
+
+
 @pytest.mark.parametrize("tile", ["128x128", "128x256", "256x128"])
 def test_conv_bf16_every_big_tile(tile, monkeypatch):
     monkeypatch.setenv("D4R_GEMM_TILE", tile)
