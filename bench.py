@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--forward", choices=("explicit", "implicit"), default="explicit",
                     help="explicit: im2col + GEMM (col saved for the filter gradient); "
                          "implicit: implicit-GEMM forward, im2col redone in the filter gradient")
+    ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="explicit",
+                    help="explicit: GEMM to dcol + col2im; implicit: implicit-GEMM data gradient "
+                         "(stride-1 square-kernel layers; others stay explicit)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph (stream capture) and time its replays; "
                          "per-kernel event timing is then unavailable")
@@ -173,6 +176,8 @@ def main() -> int:
         del src, dst
 
     implicit = args.forward == "implicit"
+    dgrad_fn = (d4r.d4r_conv_backward_data_implicit if args.dgrad == "implicit"
+                else d4r.d4r_conv_backward_data)
 
     def step(stream=stream):
         for layer, pl, t in layers:
@@ -181,7 +186,7 @@ def main() -> int:
                                               stream)
             else:
                 d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
-            d4r.d4r_conv_backward_data(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
+            dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
             d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
                                          0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
 
@@ -294,7 +299,8 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "forward": args.forward, "hip_graph": bool(args.graph),
+                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad,
+                   "hip_graph": bool(args.graph),
                    "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],
         "gemm_TFLOPs": gemm_tf,

@@ -74,6 +74,8 @@ _c = {
     "d4r_conv_forward_implicit": _sig("d4r_conv_forward_implicit",
                                       [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_data": _sig("d4r_conv_backward_data", [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_conv_backward_data_implicit": _sig("d4r_conv_backward_data_implicit",
+                                            [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_filter": _sig("d4r_conv_backward_filter",
                                      [_vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "d4r_conv_im2col": _sig("d4r_conv_im2col", [_vp, _vp, _vp, _vp]),
@@ -201,6 +203,13 @@ def d4r_conv_backward_data(h, w, dy, dx, ws, ws_bytes=None, stream=None) -> None
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_conv_backward_data", _c["d4r_conv_backward_data"](h, _ptr(w), _ptr(dy), _ptr(dx),
                                                                   _ptr(ws), nb, _stream(stream)))
+
+
+def d4r_conv_backward_data_implicit(h, w, dy, dx, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_conv_backward_data_implicit",
+           _c["d4r_conv_backward_data_implicit"](h, _ptr(w), _ptr(dy), _ptr(dx), _ptr(ws), nb,
+                                                 _stream(stream)))
 
 
 def d4r_conv_backward_filter(h, x, dy, dw, db, reuse_col, ws, ws_bytes=None, stream=None) -> None:
@@ -348,6 +357,15 @@ class ConvPlan:
         if dx is None:
             dx = torch.empty(self.x_shape, dtype=torch.float32, device=dy.device)
         d4r_conv_backward_data(self.h, w, dy, dx, self.ws, self.ws_bytes)
+        return dx
+
+    def backward_data_implicit(self, w, dy, dx=None):
+        import torch
+        _require(w, "w", self.dtype, self.w_shape)
+        _require(dy, "dy", self.dtype, self.y_shape)
+        if dx is None:
+            dx = torch.empty(self.x_shape, dtype=torch.float32, device=dy.device)
+        d4r_conv_backward_data_implicit(self.h, w, dy, dx, self.ws, self.ws_bytes)
         return dx
 
     def backward_filter(self, x, dy, reuse_col=False, want_bias=True, dw=None, db=None):

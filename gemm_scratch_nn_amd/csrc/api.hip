@@ -333,9 +333,14 @@ struct d4r_conv {
     int es;
     GemmPlan fwd, bwd_data, bwd_filter;
     int bias_splits;
-    size_t off_g, off_wt, off_bias, off_big, ws_bytes;
+    size_t off_g, off_wt, off_wflip, off_bias, off_big, ws_bytes;
     GradPath dgrad, wgrad;  // how the gradient GEMMs take dy
     bool dgrad_wt;          // data gradient reads a k-contiguous copy of W^T
+    // implicit data gradient (stride 1, square kernel): dx is the forward
+    // convolution of dy with the flipped filter, geometry gd
+    bool dgrad_impl;
+    ConvGeom gd;
+    GemmPlan bwd_data_impl;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -513,6 +518,18 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->fwd = plan_gemm(g.O, g.N, g.Kc, dtype);
     h->bwd_data = plan_gemm(g.Kc, g.N, g.O, dtype);
     h->bwd_filter = plan_gemm(g.O, g.Kc, g.N, dtype);
+    // For stride 1, dx[b,c,h,w] = sum_{o,u,v} W[o,c,u,v] dy[b,o,h+p-u,w+p-v]
+    // is a stride-1 convolution of dy (O channels, OH x OW, padding kH-1-p)
+    // with Wf[c,o,u,v] = W[o,c,kH-1-u,kW-1-v], whose output is exactly H x W.
+    // One padding value serves both axes, so the kernel must be square.
+    h->dgrad_impl = stride == 1 && kH == kW;
+    if (h->dgrad_impl) {
+        ConvGeom &d = h->gd;
+        d.B = batch; d.C = outC; d.H = g.OH; d.W = g.OW; d.O = inC; d.kH = kH; d.kW = kW;
+        d.s = 1; d.p = kH - 1 - padding; d.OH = inH; d.OW = inW;
+        d.P = inH * inW; d.Kc = outC * kH * kW; d.N = batch * d.P;
+        h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
+    }
     h->bias_splits = bias_grad_splits(g);
     {
         // sum over output rows i of the taps u that land inside the image
@@ -539,6 +556,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->off_wt = off;
     if (h->dgrad_wt)
         off += align_up((size_t)w_el * h->es);
+    h->off_wflip = off;
+    if (h->dgrad_impl)
+        off += align_up((size_t)w_el * h->es);
     h->off_bias = off;
     off += align_up((size_t)outC * h->bias_splits * sizeof(float));
     h->off_big = off;
@@ -549,6 +569,11 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     size_t wf = plan_partial_bytes(h->bwd_filter, g.O, g.Kc);
     if (wf > big)
         big = wf;
+    if (h->dgrad_impl) {
+        size_t di = plan_partial_bytes(h->bwd_data_impl, h->gd.O, h->gd.N);
+        if (di > big)
+            big = di;
+    }
     h->ws_bytes = off + align_up(big);
     *out = h;
     return ok();
@@ -670,16 +695,11 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
     return ok();
 }
 
-d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws,
-                                  size_t ws_bytes, void *hip_stream)
+namespace {
+
+// dx = col2im(Wmat^T * G): the page's data gradient
+d4r_status dgrad_explicit(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws, hipStream_t s)
 {
-    if (!h)
-        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
-    D4R_TRY(check_tensor(w, "w"));
-    D4R_TRY(check_tensor(dy, "dy"));
-    D4R_TRY(check_tensor(dx, "dx"));
-    D4R_TRY(check_ws(h, ws, ws_bytes));
-    hipStream_t s = (hipStream_t)hip_stream;
     const ConvGeom &g = h->g;
     char *wsb = (char *)ws;
     float *dcol = (float *)(wsb + h->off_big);
@@ -709,6 +729,50 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, f
                    "data-gradient GEMM");
     }
     D4R_LAUNCH(step_col2im(h, dcol, dx, s, "dgrad"), "col2im");
+    return ok();
+}
+
+}  // namespace
+
+d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws,
+                                  size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    return dgrad_explicit(h, w, dy, dx, ws, (hipStream_t)hip_stream);
+}
+
+d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const void *dy, float *dx,
+                                           void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (!h->dgrad_impl)
+        return dgrad_explicit(h, w, dy, dx, ws, s);
+    const ConvGeom &g = h->g, &d = h->gd;
+    char *wsb = (char *)ws;
+    void *wf = wsb + h->off_wflip;
+    float *partial = (float *)(wsb + h->off_big);
+    {
+        ProfScope ps(s, std::string("flip_filter_") + dt_name(h->dt) + ":dgrad", 0.0,
+                     2.0 * h->es * (double)g.O * g.Kc);
+        hipError_t e = launch_flip_filter(h->dt, g, w, wf, s);
+        ps.done();
+        D4R_LAUNCH(e, "filter flip");
+    }
+    // dx = Wf(C x O*kH*kW) * im2col_d(dy), NCHW epilogue over the H x W map
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_data_impl, OP_KC, OP_IMPL, wf, d.Kc, dy, 0, d.O, d.N, d.Kc, EPI_NCHW,
+                        dx, 0, nullptr, d.P, partial, s, "dgrad", &d),
+               "implicit data-gradient GEMM");
     return ok();
 }
 

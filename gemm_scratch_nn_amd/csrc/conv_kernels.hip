@@ -690,6 +690,27 @@ __global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Filter for the implicit data gradient: Wf[c][o][u][v] = W[o][c][kH-1-u][kW-1-v]
+// (output channels and input channels swapped, taps rotated by 180 degrees).
+// One thread per output element; writes coalesced.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void flip_filter_kernel(const T *__restrict__ w, T *__restrict__ wf, int O,
+                                                         int C, int kH, int kW)
+{
+    const long long total = (long long)O * C * kH * kW;
+    const long long i = (long long)blockIdx.x * NT + threadIdx.x;
+    if (i >= total)
+        return;
+    const int khw = kH * kW;
+    const int t = (int)(i % khw);
+    const long long co = i / khw;  // c*O + o
+    const int o = (int)(co % O), c = (int)(co / O);
+    const int u = t / kW, v = t - (t / kW) * kW;
+    wf[i] = w[((long long)o * C + c) * khw + (kH - 1 - u) * kW + (kW - 1 - v)];
+}
+
 inline dim3 grid2(long long x, long long y)
 {
     return dim3((unsigned)x, (unsigned)(y < 65535 ? y : 65535), 1);
@@ -863,6 +884,19 @@ hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db
         return e;
     hipLaunchKernelGGL(bias_final_kernel, dim3((g.O + NT - 1) / NT), dim3(NT), 0, s, partial, db, g.O,
                        splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf, hipStream_t s)
+{
+    const long long total = (long long)g.O * g.C * g.kH * g.kW;
+    const dim3 grid((unsigned)((total + NT - 1) / NT));
+    if (dt == DT_F32)
+        hipLaunchKernelGGL(flip_filter_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)w,
+                           (uint32_t *)wf, g.O, g.C, g.kH, g.kW);
+    else
+        hipLaunchKernelGGL(flip_filter_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w,
+                           (uint16_t *)wf, g.O, g.C, g.kH, g.kW);
     return hipGetLastError();
 }
 

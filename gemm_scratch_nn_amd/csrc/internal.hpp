@@ -115,6 +115,8 @@ hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, vo
 hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db,
                             float *partial, int splits, hipStream_t s);
 int bias_grad_splits(const ConvGeom &g);
+// wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v] (the implicit data gradient's filter)
+hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf, hipStream_t s);
 // out = sum over s of part[s] (fixed order) with the GEMM epilogue
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,

@@ -149,6 +149,23 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy,
                                   void *hip_stream);
 
 /*
+ * Data gradient without the dcol matrix.  The directcompute-nn page lists a
+ * fused direct input-gradient kernel among the shaders the im2col path
+ * replaced ("HLSL Shader Reference", "Legacy / Unused Shaders"); the
+ * mlvc.cpp design page runs dense spatial convolution as an implicit GEMM
+ * ("Driver-only AOT cubin direction").  For stride 1 and a square kernel,
+ * dx is the stride-1 convolution of dy (padding kH-1-p) with the filter
+ * Wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v]; it runs as the implicit-GEMM
+ * forward on that geometry: no dcol, no col2im.  Other shapes run the
+ * explicit path of d4r_conv_backward_data.  Same arguments, result equal up
+ * to summation order; ws holds Wf and split-K partials, and the col region
+ * is left untouched (reuse_col stays valid).
+ */
+d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w,
+                                           const void *dy, float *dx, void *ws,
+                                           size_t ws_bytes, void *hip_stream);
+
+/*
  * Filter and bias gradients (page: Filter gradients = grad_reshaped x
  * im2col_matrix^T, reusing the saved im2col; Bias gradients = per-channel
  * sum of grad_reshaped): dw = G * col^T (float32, OIHW), db[o] = sum over

@@ -14,7 +14,7 @@ def test_every_declared_symbol_is_exported():
     names = d4r.declared_functions()
     expected = {"d4r_conv_create", "d4r_conv_destroy", "d4r_conv_output_dims",
                 "d4r_conv_workspace_size", "d4r_conv_forward", "d4r_conv_forward_implicit",
-                "d4r_conv_backward_data",
+                "d4r_conv_backward_data", "d4r_conv_backward_data_implicit",
                 "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
                 "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
                 "d4r_status_string", "d4r_last_error", "d4r_profile_enable",
@@ -121,6 +121,17 @@ def test_forward_implicit_argument_errors(handle):
     with pytest.raises(D4RError) as e:
         d4r.d4r_conv_forward_implicit(handle, FAKE, FAKE, None, FAKE, FAKE, ws - 1, stream=0)
     assert e.value.status == WORKSPACE
+
+
+def test_backward_data_implicit_argument_errors(handle):
+    ws = _ws(handle)
+    for args, code in [((None, FAKE, FAKE, FAKE, ws), INVALID), ((FAKE, None, FAKE, FAKE, ws), INVALID),
+                       ((FAKE, FAKE, None, FAKE, ws), INVALID), ((FAKE, FAKE, FAKE, None, ws), WORKSPACE),
+                       ((FAKE, FAKE, FAKE, FAKE, ws - 1), WORKSPACE),
+                       ((FAKE, MISALIGNED, FAKE, FAKE, ws), INVALID)]:
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_backward_data_implicit(handle, *args, stream=0)
+        assert e.value.status == code, args
 
 
 def test_backward_argument_errors(handle):

@@ -453,3 +453,82 @@ def test_implicit_forward_every_tile(dt, tile, monkeypatch):
     _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=11), f"tile {tile}")
     sh = _shape((2, 17, 12, 12, 130, 3, 3, 1, 1))
     _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=12), f"tile {tile}")
+
+
+# ---------------------------------------------------------------------------
+# implicit-GEMM data gradient (stride 1, square kernel: no dcol, no col2im;
+# other shapes take the explicit path through the same entry point)
+# ---------------------------------------------------------------------------
+
+def _check_dgrad_implicit(sh, dt, ops, tag, sample=False):
+    _say("implicit dgrad", tag, sh, dt)
+    pl = _plan(sh, dt)
+    w, g = dev(ops["w"]), dev(ops["g"])
+    dx = pl.backward_data_implicit(w, g)
+    dx2 = pl.backward_data(w, g)
+    torch.cuda.synchronize()
+    s, p = sh.stride, sh.padding
+    if sample:
+        bs = _sample_idx(sh.batch, 2)
+        cs = _sample_idx(sh.inC, 6)
+        ref = oracle.conv_backward_data(ops["g"].exact[bs], ops["w"].exact[:, cs],
+                                        (len(bs), len(cs), sh.inH, sh.inW), s, p)
+        got = host(dx)[np.ix_(bs, cs)]
+    else:
+        ref = oracle.conv_backward_data(ops["g"].exact, ops["w"].exact, sh.x_shape(), s, p)
+        got = host(dx)
+    err = rel_err(got, ref)
+    _say("  rel err", err, "vs explicit", rel_err(host(dx), host(dx2)))
+    assert err < TOL[dt], (tag, err)
+
+
+# stride 1 with padding below, at and above kH - 1 (negative flipped padding)
+DGRAD_TINY = TINY + [
+    (2, 3, 8, 7, 4, 3, 3, 1, 0),
+    (2, 3, 8, 7, 4, 3, 3, 1, 2),
+    (1, 2, 6, 6, 3, 2, 2, 1, 3),
+    (2, 4, 9, 11, 5, 5, 5, 1, 2),
+    (3, 5, 7, 7, 6, 1, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("t", DGRAD_TINY, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_implicit_dgrad_tiny(t, dt):
+    sh = _shape(t)
+    _check_dgrad_implicit(sh, dt, wl.random_conv(sh, dt, seed=sum(t) + 17), "tiny")
+
+
+@pytest.mark.parametrize("key,li,dt,batch", _config_cases(REDUCED), ids=str)
+def test_implicit_dgrad_configs(key, li, dt, batch):
+    w = wl.WORKLOADS[key]
+    sh = w.layers[li].shape.with_batch(batch)
+    _check_dgrad_implicit(sh, dt, wl.conv_inputs(w, li, dt, batch=batch), f"{key}/{w.layers[li].name}/b{batch}")
+
+
+@pytest.mark.parametrize("key,li,dt", [(k, li, dt) for k, w in wl.WORKLOADS.items() if k in ("c4", "c5")
+                                       for li in range(len(w.layers)) for dt in w.dtypes], ids=str)
+def test_implicit_dgrad_full_size_sampled(key, li, dt):
+    w = wl.WORKLOADS[key]
+    _check_dgrad_implicit(w.layers[li].shape, dt, wl.conv_inputs(w, li, dt), f"{key}/full", sample=True)
+
+
+@pytest.mark.parametrize("dt,tile", [(d, t) for d in TILES for t in TILES[d]])
+def test_implicit_dgrad_every_tile(dt, tile, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    sh = _shape((3, 37, 9, 10, 21, 3, 3, 1, 1))
+    _check_dgrad_implicit(sh, dt, wl.random_conv(sh, dt, seed=23), f"tile {tile}")
+
+
+def test_implicit_dgrad_keeps_saved_col():
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[0].shape.with_batch(2)
+    ops = wl.conv_inputs(w, 0, "f32", batch=2)
+    pl = _plan(sh, "f32")
+    x, wt, g = dev(ops["x"]), dev(ops["w"]), dev(ops["g"])
+    pl.forward(x, wt, dev(ops["bias"]))
+    pl.backward_data_implicit(wt, g)   # must not disturb the saved col
+    dw1, db1 = pl.backward_filter(None, g, reuse_col=True)
+    dw2, db2 = pl.backward_filter(x, g, reuse_col=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2) and torch.equal(db1, db2)
