@@ -437,16 +437,18 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant for two k-contiguous operands (the filter-gradient
-// product and other NT/NN-with-transposed-A shapes).  Each 16-byte chunk
-// goes from global memory straight into LDS (global_load_lds_dwordx4: lane
-// i of a wavefront writes bytes [16i, 16i+16) after the wavefront's LDS
-// base), so no registers stage the tiles and no LDS store instructions are
-// issued.  A stage of BK k is one LDS row of BK*2 bytes per tile row; chunk
-// c of row r sits at position c ^ dl_swz(r), which the loading lane realises
-// by fetching the permuted global chunk, so the 16-byte fragment reads of 8
-// consecutive rows hit distinct banks.  A ring of NBUF LDS stages keeps
-// NBUF-1 stages of loads in flight; one barrier per stage.
+// Direct-to-LDS variant for two k-contiguous operands (128x256 and 256x128
+// tiles, eight wavefronts).  Every 16-byte chunk goes from global memory
+// straight into LDS (global_load_lds_dwordx4: lane i of a wavefront writes
+// bytes [16i, 16i+16) after the wavefront's LDS base), so no registers stage
+// the tiles and no LDS store instructions are issued.  A stage is 64 k deep:
+// LDS [row][k] with 128-byte rows, chunk c of row r at position c ^ swz(r);
+// the loading lane fetches the permuted global chunk, so the swizzle costs
+// nothing and a fragment is one conflict-free 16-byte read.  A ring of NBUF
+// LDS stages keeps NBUF-1 stages of loads in flight; one barrier per stage.
+// (Row-contiguous operands loaded the same way as [k][row] and read with
+// ds_read_b64_tr_b16 measured 5-15% slower than the register-transpose
+// path: twice the LDS read instructions per fragment, more waits.)
 // Requirements (checked by the launcher): 16-byte aligned rows, every split
 // a whole number of stages.  Rows past M or N load a clamped row; they only
 // reach outputs that the epilogue masks.
@@ -454,25 +456,54 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// chunk position of chunk c in row r: c ^ dl_swz<CH>(r) for CH chunks per row
-template <int CH>
-__device__ __forceinline__ int dl_swz(int row)
-{
-    return CH == 4 ? ((row >> 1) & 3) : ((row ^ (row >> 3)) & 7);
-}
+constexpr int kDlBK = 64;  // k per stage
 
-template <int DTID, int NWM, int NWN, int TM, int TN, int BK, int NBUF>
+// Per-lane load offsets of one k-contiguous operand (BR rows of the tile,
+// NW wavefronts): a wavefront load covers 8 rows of 128 bytes.
+template <int BR, int NW>
+struct DlOperand {
+    static constexpr int ROWB = kDlBK * 2;          // bytes per LDS row
+    static constexpr int LPL = 8;                   // rows per wavefront load
+    static constexpr int LD = BR / (LPL * NW);      // loads per wavefront per stage
+    static constexpr int BYTES = BR * ROWB;
+    static_assert(BR % (LPL * NW) == 0, "whole load groups");
+
+    long long off[LD];  // element offset of this lane's chunk, k0 excluded
+
+    __device__ __forceinline__ void setup(int r0, int R, int ld, int wave, int lane)
+    {
+#pragma unroll
+        for (int j = 0; j < LD; ++j) {
+            const int lr = (j * NW + wave) * LPL + lane / 8;  // tile row
+            const int gr = min(r0 + lr, R - 1);
+            off[j] = (long long)gr * ld + ((lane % 8) ^ swz(lr)) * 8;
+        }
+    }
+
+    // stage starting at k0 into LDS stage base `lds`
+    __device__ __forceinline__ void issue(const uint16_t *X, int k0, char *lds, int wave) const
+    {
+#pragma unroll
+        for (int j = 0; j < LD; ++j)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(X + off[j] + k0),
+                                             (lds_void_t *)(lds + (j * NW + wave) * LPL * ROWB), 16, 0, 0);
+    }
+
+    // 16-byte fragment: row `row` of the tile, k = 16q + 8h .. +7
+    __device__ __forceinline__ static u32x4_t frag(const char *lds, int row, int q, int h)
+    {
+        return *(const u32x4_t *)(lds + row * ROWB + (((2 * q + h) ^ swz(row)) << 4));
+    }
+};
+
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
 {
     constexpr int NW = NWM * NWN;
-    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
-    constexpr int ROWB = BK * 2;      // bytes per LDS row
-    constexpr int CH = ROWB / 16;     // 16-byte chunks per row
-    constexpr int RPL = 64 / CH;      // rows per wavefront load (1 KB)
-    constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
-    constexpr int A_LD = BM / (RPL * NW), B_LD = BN / (RPL * NW);  // loads per wavefront per stage
-    static_assert(CH == 4 || CH == 8, "32- or 64-deep stages");
-    static_assert(BM % (RPL * NW) == 0 && BN % (RPL * NW) == 0, "whole load groups");
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = kDlBK;
+    using OA = DlOperand<BM, NW>;
+    using OB = DlOperand<BN, NW>;
+    constexpr int STAGE = OA::BYTES + OB::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
     const int tid = threadIdx.x;
@@ -488,38 +519,19 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg) / BK;
 
-    // This lane's load rows and chunks: load j of a wavefront covers tile
-    // rows [(j*NW + wave)*RPL, +RPL); lane -> row lane/CH, LDS position
-    // lane%CH.
     const uint16_t *A = (const uint16_t *)p.A;
     const uint16_t *B = (const uint16_t *)p.B;
-    long long a_off[A_LD], b_off[B_LD];
-#pragma unroll
-    for (int j = 0; j < A_LD; ++j) {
-        const int r = (j * NW + wave) * RPL + lane / CH;
-        const int gr = min(m_blk + r, p.M - 1);
-        a_off[j] = (long long)gr * p.lda + ((lane % CH) ^ dl_swz<CH>(r)) * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j) {
-        const int r = (j * NW + wave) * RPL + lane / CH;
-        const int gr = min(n_blk + r, p.N - 1);
-        b_off[j] = (long long)gr * p.ldb + ((lane % CH) ^ dl_swz<CH>(r)) * 8;
-    }
-    // stage s (clamped to the first stage past the end: its buffer is never
+    OA oa;
+    OB ob;
+    oa.setup(m_blk, p.M, p.lda, wave, lane);
+    ob.setup(n_blk, p.N, p.ldb, wave, lane);
+    // stage s (clamped to the first stage past the end: its slot is never
     // read) into ring slot s % NBUF
     auto issue = [&](int s) {
         const int k0 = kbeg + (s < nk ? s : 0) * BK;
         char *base = smem + (s % NBUF) * STAGE;
-#pragma unroll
-        for (int j = 0; j < A_LD; ++j)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(A + a_off[j] + k0),
-                                             (lds_void_t *)(base + (j * NW + wave) * RPL * ROWB), 16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < B_LD; ++j)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(B + b_off[j] + k0),
-                                             (lds_void_t *)(base + A_BYTES + (j * NW + wave) * RPL * ROWB), 16,
-                                             0, 0);
+        oa.issue(A, k0, base, wave);
+        ob.issue(B, k0, base + OA::BYTES, wave);
     };
 
     f32x16_t acc[TM][TN];
@@ -531,14 +543,9 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.0f;
 
-    auto frag = [&](const char *lds, int row, int q) {
-        const int c = 2 * q + h;
-        return *(const u32x4_t *)(lds + row * ROWB + ((c ^ dl_swz<CH>(row)) << 4));
-    };
-
     // NBUF-1 stages are issued ahead; at the top of iteration t the loads of
     // stages t+1 .. t+NBUF-2 may still be in flight, stage t's must be done
-    constexpr int LPS = A_LD + B_LD;
+    constexpr int LPS = OA::LD + OB::LD;
     constexpr int VM = (NBUF - 2) * LPS;
     static_assert(VM < 64, "vmcnt range");
     constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -548,25 +555,26 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
         issue(s0);
     for (int t = 0; t < nk; ++t) {
         // Stage t has landed (this wavefront's share; the barrier makes it
-        // everyone's) and every wavefront is done reading slot (t+3) % NBUF.
-        // A plain s_barrier: the workgroup fence of __syncthreads would wait
-        // for all loads in flight, LDS-bound ones included.  The empty asm
-        // keeps the compiler from moving LDS accesses across it.
+        // everyone's) and every wavefront is done reading slot
+        // (t+NBUF-1) % NBUF.  A plain s_barrier: the workgroup fence of
+        // __syncthreads would wait for all loads in flight, LDS-bound ones
+        // included.  The empty asm keeps the compiler from moving LDS
+        // accesses across it.
         __builtin_amdgcn_s_waitcnt(WAIT);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         issue(t + NBUF - 1);
         const char *la = smem + (t % NBUF) * STAGE;
-        const char *lb = la + A_BYTES;
+        const char *lb = la + OA::BYTES;
 #pragma unroll
         for (int q = 0; q < BK / 16; ++q) {
             u32x4_t af[TM], bf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = frag(la, (wm * TM + i) * 32 + l32, q);
+                af[i] = OA::frag(la, (wm * TM + i) * 32 + l32, q, h);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bf[j] = frag(lb, (wn * TN + j) * 32 + l32, q);
+                bf[j] = OB::frag(lb, (wn * TN + j) * 32 + l32, q, h);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -580,12 +588,13 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32);
 }
 
-// The direct-to-LDS kernel applies to two k-contiguous operands with
-// 16-byte aligned rows whose splits are whole stages.
 // 64-deep stages in a ring of three (two stages of loads in flight):
 // measured level with 32-deep stages in a ring of four, with half the
 // barriers.
-constexpr int kDlBK = 64, kDlBuf = 3;
+constexpr int kDlBuf = 3;
+
+// The direct-to-LDS kernel applies to two k-contiguous operands with
+// 16-byte aligned rows (the VEC condition) whose splits are whole stages.
 inline bool dl_applies(int amode, int bmode, const GemmParams &p)
 {
     return amode == OP_KC && bmode == OP_KC && p.a_vec && p.b_vec && p.K % kDlBK == 0 &&
@@ -600,10 +609,10 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
     const dim3 grid(tiles, 1, p.splits), b8(512);
     switch (cfg) {
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBK, kDlBuf>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf>), grid, b8, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBK, kDlBuf>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf>), grid, b8, 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -338,9 +338,9 @@ TILES = {"f32": ["128x128", "64x64", "32x128", "96x128", "128x64"],
 def test_gemm_every_tile_config(dt, tile, flags, monkeypatch):
     monkeypatch.setenv("D4R_GEMM_TILE", tile)
     # K % 64 == 0 shapes take the direct-to-LDS 16-bit kernel for flags 2 on
-    # the 128x256 / 256x128 tiles; (200, 4096, 300) also splits K
+    # the 128x256 / 256x128 tiles; (200, 4096, 304) also splits K
     for (M, K, N) in [(300, 200, 333), (97, 1000, 65), (257, 136, 520), (300, 256, 333), (129, 64, 520),
-                      (200, 4096, 300)]:
+                      (296, 256, 336), (136, 64, 520), (200, 4096, 304)]:
         rng = np.random.default_rng(M + K + N + flags)
         a = wl.quantize(rng.normal(size=(K, M) if flags & 1 else (M, K)), dt)
         b = wl.quantize(rng.normal(size=(N, K) if flags & 2 else (K, N)), dt)
