@@ -15,6 +15,7 @@
 //                    partial sums reduced in a fixed order; db by reduction
 #include <mutex>
 #include <new>
+#include <algorithm>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -397,12 +398,23 @@ hipError_t step_transpose(const d4r_conv *h, int batch, int R, int C, const void
     return e;
 }
 
-hipError_t step_grad_reshape(const d4r_conv *h, const void *dy, void *G, hipStream_t s)
+// With bias_part set, the reshape also produces the bias gradient's partial
+// sums, which step_bias_final then adds up.
+hipError_t step_grad_reshape(const d4r_conv *h, const void *dy, void *G, float *bias_part, hipStream_t s)
 {
     const ConvGeom &g = h->g;
-    ProfScope ps(s, std::string("grad_reshape_") + dt_name(h->dt) + ":wgrad", 0.0,
-                 2.0 * h->es * (double)g.O * g.N);
-    hipError_t e = launch_grad_reshape(h->dt, g, dy, G, s);
+    ProfScope ps(s, std::string(bias_part ? "grad_reshape_bias_" : "grad_reshape_") + dt_name(h->dt) + ":wgrad",
+                 0.0, 2.0 * h->es * (double)g.O * g.N);
+    hipError_t e = launch_grad_reshape(h->dt, g, dy, G, bias_part, s);
+    ps.done();
+    return e;
+}
+
+hipError_t step_bias_final(const d4r_conv *h, const float *partial, float *db, hipStream_t s)
+{
+    const int splits = grad_reshape_blocks(h->dt, h->g);
+    ProfScope ps(s, "bias_final:wgrad", 0.0, 4.0 * h->g.O * (splits + 1.0));
+    hipError_t e = launch_bias_final(partial, db, h->g.O, splits, s);
     ps.done();
     return e;
 }
@@ -531,6 +543,8 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
     h->bias_splits = bias_grad_splits(g);
+    // bias partials: the bias kernel's splits, or the fused reshape's blocks
+    const int bias_part_cols = std::max(h->bias_splits, grad_reshape_blocks(dtype, g));
     {
         // sum over output rows i of the taps u that land inside the image
         long long rows = 0, cols = 0;
@@ -560,7 +574,7 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     if (h->dgrad_impl)
         off += align_up((size_t)w_el * h->es);
     h->off_bias = off;
-    off += align_up((size_t)outC * h->bias_splits * sizeof(float));
+    off += align_up((size_t)outC * bias_part_cols * sizeof(float));
     h->off_big = off;
     size_t big = plan_partial_bytes(h->fwd, g.O, g.N);
     size_t dd = align_up((size_t)col_el * sizeof(float)) + plan_partial_bytes(h->bwd_data, g.Kc, g.N);
@@ -805,11 +819,16 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
                             EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g),
                    "filter-gradient GEMM");
     } else {
+        // the reshape's pass over dy also yields the bias partial sums
         void *G = wsb + h->off_g;
-        D4R_LAUNCH(step_grad_reshape(h, dy, G, s), "grad reshape");
+        float *bias_part = db ? (float *)(wsb + h->off_bias) : nullptr;
+        D4R_LAUNCH(step_grad_reshape(h, dy, G, bias_part, s), "grad reshape");
         D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N,
                             EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad"),
                    "filter-gradient GEMM");
+        if (db)
+            D4R_LAUNCH(step_bias_final(h, bias_part, db, s), "bias gradient");
+        return ok();
     }
     if (db)
         D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s),

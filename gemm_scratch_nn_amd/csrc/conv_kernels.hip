@@ -435,39 +435,73 @@ __global__ __launch_bounds__(NT) void col2im_lds_kernel(const float *__restrict_
     }
 }
 
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // conv_grad_reshape: G[o][n] = dy[b][o][pix], n = b*P + pix.  Thread per VW
 // consecutive n of one row o: consecutive lanes read consecutive pixels of
-// an image plane and write consecutive columns of G.
+// an image plane and write consecutive columns of G.  With bias_part set,
+// the same pass also yields the bias gradient's first level: block (x, o)
+// sums its elements (fixed wave-shuffle tree, then LDS in wave order) into
+// bias_part[o * gridDim.x + x].
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ dy, T *__restrict__ G,
-                                                          ConvGeom g, int vec_store)
+                                                          ConvGeom g, int vec_store,
+                                                          float *__restrict__ bias_part, int dt)
 {
     constexpr int VW = Vec16<T>::N;
+    __shared__ float red[NT / 64];
     const int n0 = (blockIdx.x * NT + threadIdx.x) * VW;
-    if (n0 >= g.N)
-        return;
+    const bool live = n0 < g.N;
     for (int o = blockIdx.y; o < g.O; o += gridDim.y) {
-        int b = n0 / g.P;
-        int pix = n0 - b * g.P;
-        typename Vec16<T>::type out;
+        float sum = 0.0f;
+        if (live) {
+            int b = n0 / g.P;
+            int pix = n0 - b * g.P;
+            typename Vec16<T>::type out;
 #pragma unroll
-        for (int e = 0; e < VW; ++e) {
-            out[e] = (b < g.B) ? dy[((long long)b * g.O + o) * g.P + pix] : (T)0;
-            if (++pix == g.P) {
-                pix = 0;
-                ++b;
+            for (int e = 0; e < VW; ++e) {
+                out[e] = (b < g.B) ? dy[((long long)b * g.O + o) * g.P + pix] : (T)0;
+                if (++pix == g.P) {
+                    pix = 0;
+                    ++b;
+                }
+            }
+            T *dst = G + (long long)o * g.N + n0;
+            if (vec_store) {
+                *(typename Vec16<T>::type *)dst = out;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    if (n0 + e < g.N)
+                        dst[e] = out[e];
+            }
+            if (bias_part) {
+#pragma unroll
+                for (int e = 0; e < VW; ++e)
+                    sum += to_f32(out[e], dt);  // zero past N
             }
         }
-        T *dst = G + (long long)o * g.N + n0;
-        if (vec_store) {
-            *(typename Vec16<T>::type *)dst = out;
-        } else {
+        if (bias_part) {  // uniform across the block
+            sum = wave_sum(sum);
+            if ((threadIdx.x & 63) == 0)
+                red[threadIdx.x >> 6] = sum;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float t = 0.0f;
 #pragma unroll
-            for (int e = 0; e < VW; ++e)
-                if (n0 + e < g.N)
-                    dst[e] = out[e];
+                for (int w = 0; w < NT / 64; ++w)
+                    t += red[w];
+                bias_part[(long long)o * gridDim.x + blockIdx.x] = t;
+            }
+            __syncthreads();
         }
     }
 }
@@ -515,14 +549,6 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
 // reduces through a fixed wave-shuffle tree and LDS.  Pass 2: one thread per
 // channel adds the partials in split order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 template <typename T>
 __global__ __launch_bounds__(NT) void bias_partial_kernel(const T *__restrict__ dy,
                                                           float *__restrict__ partial, ConvGeom g,
@@ -828,18 +854,31 @@ hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_grad_reshape(int dt, const ConvGeom &g, const void *dy, void *G, hipStream_t s)
+int grad_reshape_blocks(int dt, const ConvGeom &g)
 {
     const int VW = dt == DT_F32 ? 4 : 8;
     const long long threads = (g.N + VW - 1) / VW;
-    dim3 grid = grid2((threads + NT - 1) / NT, g.O);
+    return (int)((threads + NT - 1) / NT);
+}
+
+hipError_t launch_grad_reshape(int dt, const ConvGeom &g, const void *dy, void *G, float *bias_part,
+                               hipStream_t s)
+{
+    const int VW = dt == DT_F32 ? 4 : 8;
+    dim3 grid = grid2(grad_reshape_blocks(dt, g), g.O);
     const int vec = (g.N % VW) == 0;
     if (dt == DT_F32)
         hipLaunchKernelGGL(grad_reshape_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)dy,
-                           (uint32_t *)G, g, vec);
+                           (uint32_t *)G, g, vec, bias_part, dt);
     else
         hipLaunchKernelGGL(grad_reshape_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)dy,
-                           (uint16_t *)G, g, vec);
+                           (uint16_t *)G, g, vec, bias_part, dt);
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_final(const float *partial, float *db, int O, int splits, hipStream_t s)
+{
+    hipLaunchKernelGGL(bias_final_kernel, dim3((O + NT - 1) / NT), dim3(NT), 0, s, partial, db, O, splits);
     return hipGetLastError();
 }
 

@@ -106,8 +106,14 @@ int gemm_bk(int dt);  // K depth of one LDS stage, in elements
 
 hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s);
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s);
-// G[o][n] = dy[b][o][pix], n = b*P + pix  (O x N row-major)
-hipError_t launch_grad_reshape(int dt, const ConvGeom &g, const void *dy, void *G, hipStream_t s);
+// G[o][n] = dy[b][o][pix], n = b*P + pix  (O x N row-major); with bias_part
+// set, also the bias gradient's per-block partial sums, O x
+// grad_reshape_blocks() floats (finish with launch_bias_final)
+hipError_t launch_grad_reshape(int dt, const ConvGeom &g, const void *dy, void *G, float *bias_part,
+                               hipStream_t s);
+int grad_reshape_blocks(int dt, const ConvGeom &g);
+// db[o] = sum over s < splits of partial[o*splits + s], in order
+hipError_t launch_bias_final(const float *partial, float *db, int O, int splits, hipStream_t s);
 // out[b][c][r] = in[b][r][c] for a batch of R x Cc matrices of dt elements
 hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, void *out,
                             hipStream_t s);

@@ -314,6 +314,22 @@ def test_reuse_col_matches_fresh_im2col():
     assert torch.equal(dw1, dw2) and torch.equal(db1, db2)
 
 
+@pytest.mark.parametrize("path", ["inplace", "copy"])
+def test_filter_gradient_without_bias(path, monkeypatch):
+    # db = NULL skips the bias gradient on both ways of taking dy (the copy
+    # path otherwise folds the bias partial sums into its reshape)
+    monkeypatch.setenv("D4R_GRAD_PATH", path)
+    sh = _shape((3, 5, 9, 9, 37, 3, 3, 1, 1))
+    ops = wl.random_conv(sh, "f32", seed=5)
+    pl = _plan(sh, "f32")
+    pl.forward(dev(ops["x"]), dev(ops["w"]), dev(ops["bias"]))
+    dw, db = pl.backward_filter(None, dev(ops["g"]), reuse_col=True, want_bias=False)
+    torch.cuda.synchronize()
+    assert db is None
+    ref = oracle.conv_backward_filter(ops["x"].exact, ops["g"].exact, sh.w_shape(), 1, 1)
+    assert rel_err(host(dw), ref) < 1e-5
+
+
 def test_forward_without_bias():
     sh = _shape((2, 3, 9, 9, 4, 3, 3, 1, 1))
     ops = wl.random_conv(sh, "f32", seed=3)
