@@ -7,12 +7,16 @@
 // Approach"):
 //   forward          im2col(x) -> col;  GEMM NN  Wmat[O x Kc] * col[Kc x N]
 //                    with the conv_reshape + bias store fused in its epilogue
-//   backward_data    dy -> Gt[N x O] (reshape, transposed), W -> Wt[Kc x O];
-//                    GEMM dcol[Kc x N] = Wmat^T * G, both operands read with
-//                    k contiguous; col2im(dcol) -> dx
-//   backward_filter  [im2col(x) -> col]; dy -> G[O x N];
-//                    GEMM NT  dW[O x Kc] = G * col^T, split over k with
-//                    partial sums reduced in a fixed order; db by reduction
+//   backward_data    GEMM dcol[Kc x N] = Wmat^T * G, then col2im(dcol) -> dx.
+//                    G is dy read in place (f32, small Kc) or copied as
+//                    Gt[N x O] with W copied as Wt[Kc x O], so both operands
+//                    stream k-contiguous
+//   backward_filter  [im2col(x) -> col]; GEMM NT dW[O x Kc] = G * col^T,
+//                    split over k with partial sums reduced in a fixed order;
+//                    G is dy read in place or reshaped to G[O x N] (that pass
+//                    also yields the bias partial sums); db by reduction
+//   backward_data_implicit  (stride 1, square kernel) the implicit-GEMM
+//                    forward of dy with the flipped filter; no dcol
 #include <mutex>
 #include <new>
 #include <algorithm>
@@ -208,7 +212,7 @@ Profiler &prof()
 
 // Brackets one launch.  Constructed before the launch, finished after it.
 struct ProfScope {
-    ProfRec *rec = nullptr;
+    long long idx = -1;  // index into recs (the vector may grow under another thread)
     hipStream_t s;
     ProfScope(hipStream_t st, const std::string &name, double flops, double bytes) : s(st)
     {
@@ -235,16 +239,20 @@ struct ProfScope {
                 return;
             P.recs.push_back(r);
         }
-        rec = &P.recs[P.used++];
-        rec->key = key;
-        rec->flops = flops;
-        rec->bytes = bytes;
-        (void)hipEventRecord(rec->a, s);
+        idx = (long long)P.used++;
+        ProfRec &rec = P.recs[idx];
+        rec.key = key;
+        rec.flops = flops;
+        rec.bytes = bytes;
+        (void)hipEventRecord(rec.a, s);
     }
     void done()
     {
-        if (rec)
-            (void)hipEventRecord(rec->b, s);
+        if (idx < 0)
+            return;
+        Profiler &P = prof();
+        std::lock_guard<std::mutex> lk(P.mu);
+        (void)hipEventRecord(P.recs[idx].b, s);
     }
 };
 
