@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
         return LIB_PATH
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           "-Wall", "-Wextra", "-o", tmp, SRC_PATH]
+           "-Wall", "-Wextra", "-o", tmp, SRC_PATH, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
@@ -58,6 +58,19 @@ def _load() -> ctypes.CDLL:
         lib.oracle_num_threads.argtypes = []
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_num_threads.restype = None
+        I32 = ctypes.POINTER(ctypes.c_int32)
+        D = ctypes.c_double
+        lib.oracle_relu.argtypes = [P, P, L]
+        lib.oracle_relu_grad.argtypes = [P, P, P, L]
+        lib.oracle_maxpool_forward.argtypes = [P, P, I32] + [L] * 6
+        lib.oracle_maxpool_backward.argtypes = [P, I32, P] + [L] * 6
+        lib.oracle_add_bias_rows.argtypes = [P, P, P, L, L]
+        lib.oracle_bias_grad_rows.argtypes = [P, P, L, L]
+        lib.oracle_softmax.argtypes = [P, P, L, L]
+        lib.oracle_softmax_ce_grad.argtypes = [P, I32, P, L, L]
+        lib.oracle_ce_loss.argtypes = [P, I32, ctypes.POINTER(D), L, L]
+        lib.oracle_sgd.argtypes = [P, P, L, D, D]
+        lib.oracle_grad_accum.argtypes = [P, P, L]
         _lib = lib
     return _lib
 
@@ -186,3 +199,116 @@ def col2im_spec(col, x_shape, kH: int, kW: int, stride: int, padding: int) -> np
         raise ValueError("oracle_col2im_spec rejected the shape")
     return dx
 
+
+
+# ---------------------------------------------------------------------------
+# the rest of a training step ("HLSL Shader Reference": activation / loss,
+# pooling and utility shaders of the directcompute-nn page)
+# ---------------------------------------------------------------------------
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle_{what} rejected its arguments")
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def relu(x) -> np.ndarray:
+    x = _f64(x)
+    y = np.empty_like(x)
+    _check(_load().oracle_relu(_ptr(x), _ptr(y), x.size), "relu")
+    return y
+
+
+def relu_grad(x, dy) -> np.ndarray:
+    x, dy = _f64(x), _f64(dy)
+    dx = np.empty_like(x)
+    _check(_load().oracle_relu_grad(_ptr(x), _ptr(dy), _ptr(dx), x.size), "relu_grad")
+    return dx
+
+
+def pool_dims(H: int, W: int, k: int, s: int) -> Tuple[int, int]:
+    return (H - k) // s + 1, (W - k) // s + 1
+
+
+def maxpool_forward(x, k: int, s: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(y, idx): idx is the offset h*W + w of the maximum inside its plane."""
+    x = _f64(x)
+    B, C, H, W = x.shape
+    OH, OW = pool_dims(H, W, k, s)
+    y = np.empty((B, C, OH, OW))
+    idx = np.empty((B, C, OH, OW), dtype=np.int32)
+    _check(_load().oracle_maxpool_forward(_ptr(x), _ptr(y), _iptr(idx), B, C, H, W, k, s),
+           "maxpool_forward")
+    return y, idx
+
+
+def maxpool_backward(dy, idx, x_shape, k: int, s: int) -> np.ndarray:
+    dy, idx = _f64(dy), _i32(idx)
+    B, C, H, W = x_shape
+    dx = np.empty((B, C, H, W))
+    _check(_load().oracle_maxpool_backward(_ptr(dy), _iptr(idx), _ptr(dx), B, C, H, W, k, s),
+           "maxpool_backward")
+    return dx
+
+
+def add_bias_rows(x, bias) -> np.ndarray:
+    x, bias = _f64(x), _f64(bias)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_add_bias_rows(_ptr(x), _ptr(bias), _ptr(y), rows, cols), "add_bias_rows")
+    return y
+
+
+def bias_grad_rows(dy) -> np.ndarray:
+    dy = _f64(dy)
+    rows, cols = dy.shape
+    db = np.empty(cols)
+    _check(_load().oracle_bias_grad_rows(_ptr(dy), _ptr(db), rows, cols), "bias_grad_rows")
+    return db
+
+
+def softmax(z) -> np.ndarray:
+    z = _f64(z)
+    rows, classes = z.shape
+    p = np.empty_like(z)
+    _check(_load().oracle_softmax(_ptr(z), _ptr(p), rows, classes), "softmax")
+    return p
+
+
+def softmax_ce_grad(z, labels) -> np.ndarray:
+    z, labels = _f64(z), _i32(labels)
+    rows, classes = z.shape
+    dz = np.empty_like(z)
+    _check(_load().oracle_softmax_ce_grad(_ptr(z), _iptr(labels), _ptr(dz), rows, classes),
+           "softmax_ce_grad")
+    return dz
+
+
+def ce_loss(z, labels) -> float:
+    z, labels = _f64(z), _i32(labels)
+    rows, classes = z.shape
+    out = ctypes.c_double()
+    _check(_load().oracle_ce_loss(_ptr(z), _iptr(labels), ctypes.byref(out), rows, classes), "ce_loss")
+    return out.value
+
+
+def sgd(param, grad, lr: float, clip: float) -> np.ndarray:
+    """Returns the updated parameter (the input array is not modified)."""
+    p = _f64(param).copy()
+    g = _f64(grad)
+    _check(_load().oracle_sgd(_ptr(p), _ptr(g), p.size, float(lr), float(clip)), "sgd")
+    return p
+
+
+def grad_accum(acc, grad) -> np.ndarray:
+    a = _f64(acc).copy()
+    g = _f64(grad)
+    _check(_load().oracle_grad_accum(_ptr(a), _ptr(g), a.size), "grad_accum")
+    return a

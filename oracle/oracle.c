@@ -36,6 +36,7 @@
  */
 #include <stddef.h>
 #include <stdint.h>
+#include <math.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -335,5 +336,210 @@ int oracle_col2im_spec(const double *col, double *dx, i64 B, i64 C, i64 H,
             }
         }
     }
+    return 0;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * The rest of a training step (directcompute-nn page, "HLSL Shader
+ * Reference": "Activation / Loss Shaders", "Pooling Shaders", "Utility
+ * Shaders"), as plain double-precision definitions.
+ *
+ * Readings where the page is silent:
+ *   - ReLU gradient passes dy where x > 0 (strictly) and 0 elsewhere.
+ *   - Max pooling has no padding, one window size k and one stride s for
+ *     both axes, output extent floor((in - k)/s) + 1.  The saved argmax is
+ *     the offset h*W + w inside the (b, c) plane of the first maximum met in
+ *     the scan order u ascending, then v ascending (strictly greater wins).
+ *     Its backward adds each dy element to dx at the saved position, scanning
+ *     outputs i ascending, then j ascending (overlapping windows add up).
+ *   - Bias add for row-major rows x cols: y[i][j] = x[i][j] + bias[j]; its
+ *     gradient sums over the rows.
+ *   - Softmax-cross-entropy gradient: softmax(z) - one_hot(label) per row,
+ *     as the page states it (no 1/rows factor); the loss is the mean over the
+ *     rows of -log softmax(z)[label].  Softmax subtracts the row maximum.
+ *   - SGD: param -= lr * clamp(grad, -clip, clip).
+ * ---------------------------------------------------------------------------
+ */
+int oracle_relu(const double *x, double *y, i64 n)
+{
+    if (n < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i)
+        y[i] = x[i] > 0.0 ? x[i] : 0.0;
+    return 0;
+}
+
+int oracle_relu_grad(const double *x, const double *dy, double *dx, i64 n)
+{
+    if (n < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i)
+        dx[i] = x[i] > 0.0 ? dy[i] : 0.0;
+    return 0;
+}
+
+static int bad_pool(i64 B, i64 C, i64 H, i64 W, i64 k, i64 s, i64 *OH, i64 *OW)
+{
+    if (B < 1 || C < 1 || H < 1 || W < 1 || k < 1 || s < 1 || k > H || k > W)
+        return 1;
+    *OH = (H - k) / s + 1;
+    *OW = (W - k) / s + 1;
+    return 0;
+}
+
+int oracle_maxpool_forward(const double *x, double *y, int32_t *idx, i64 B, i64 C,
+                           i64 H, i64 W, i64 k, i64 s)
+{
+    i64 OH, OW;
+    if (bad_pool(B, C, H, W, k, s, &OH, &OW))
+        return -1;
+    i64 BC = B * C;
+#pragma omp parallel for schedule(static)
+    for (i64 bc = 0; bc < BC; ++bc) {
+        const double *xp = x + bc * H * W;
+        for (i64 i = 0; i < OH; ++i)
+            for (i64 j = 0; j < OW; ++j) {
+                i64 best = (i * s) * W + j * s;
+                for (i64 u = 0; u < k; ++u)
+                    for (i64 v = 0; v < k; ++v) {
+                        i64 at = (i * s + u) * W + (j * s + v);
+                        if (xp[at] > xp[best])
+                            best = at;
+                    }
+                y[(bc * OH + i) * OW + j] = xp[best];
+                idx[(bc * OH + i) * OW + j] = (int32_t)best;
+            }
+    }
+    return 0;
+}
+
+int oracle_maxpool_backward(const double *dy, const int32_t *idx, double *dx, i64 B,
+                            i64 C, i64 H, i64 W, i64 k, i64 s)
+{
+    i64 OH, OW;
+    if (bad_pool(B, C, H, W, k, s, &OH, &OW))
+        return -1;
+    i64 BC = B * C;
+#pragma omp parallel for schedule(static)
+    for (i64 bc = 0; bc < BC; ++bc) {
+        double *dp = dx + bc * H * W;
+        for (i64 t = 0; t < H * W; ++t)
+            dp[t] = 0.0;
+        for (i64 i = 0; i < OH; ++i)
+            for (i64 j = 0; j < OW; ++j) {
+                i64 o = (bc * OH + i) * OW + j;
+                dp[idx[o]] += dy[o];
+            }
+    }
+    return 0;
+}
+
+int oracle_add_bias_rows(const double *x, const double *bias, double *y, i64 rows, i64 cols)
+{
+    if (rows < 1 || cols < 1)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < rows; ++i)
+        for (i64 j = 0; j < cols; ++j)
+            y[i * cols + j] = x[i * cols + j] + bias[j];
+    return 0;
+}
+
+int oracle_bias_grad_rows(const double *dy, double *db, i64 rows, i64 cols)
+{
+    if (rows < 1 || cols < 1)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 j = 0; j < cols; ++j) {
+        double acc = 0.0;
+        for (i64 i = 0; i < rows; ++i)
+            acc += dy[i * cols + j];
+        db[j] = acc;
+    }
+    return 0;
+}
+
+int oracle_softmax(const double *z, double *prob, i64 rows, i64 classes)
+{
+    if (rows < 1 || classes < 1)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < rows; ++i) {
+        const double *zr = z + i * classes;
+        double m = zr[0];
+        for (i64 j = 1; j < classes; ++j)
+            if (zr[j] > m)
+                m = zr[j];
+        double sum = 0.0;
+        for (i64 j = 0; j < classes; ++j)
+            sum += exp(zr[j] - m);
+        for (i64 j = 0; j < classes; ++j)
+            prob[i * classes + j] = exp(zr[j] - m) / sum;
+    }
+    return 0;
+}
+
+int oracle_softmax_ce_grad(const double *z, const int32_t *label, double *dz, i64 rows,
+                           i64 classes)
+{
+    if (oracle_softmax(z, dz, rows, classes))
+        return -1;
+    for (i64 i = 0; i < rows; ++i) {
+        if (label[i] < 0 || label[i] >= classes)
+            return -1;
+        dz[i * classes + label[i]] -= 1.0;
+    }
+    return 0;
+}
+
+/* mean over the rows of -log softmax(z)[label] */
+int oracle_ce_loss(const double *z, const int32_t *label, double *loss, i64 rows, i64 classes)
+{
+    if (rows < 1 || classes < 1)
+        return -1;
+    double total = 0.0;
+    for (i64 i = 0; i < rows; ++i) {
+        const double *zr = z + i * classes;
+        if (label[i] < 0 || label[i] >= classes)
+            return -1;
+        double m = zr[0];
+        for (i64 j = 1; j < classes; ++j)
+            if (zr[j] > m)
+                m = zr[j];
+        double sum = 0.0;
+        for (i64 j = 0; j < classes; ++j)
+            sum += exp(zr[j] - m);
+        total += log(sum) + m - zr[label[i]];
+    }
+    *loss = total / (double)rows;
+    return 0;
+}
+
+int oracle_sgd(double *param, const double *grad, i64 n, double lr, double clip)
+{
+    if (n < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i) {
+        double g = grad[i];
+        if (g > clip)
+            g = clip;
+        if (g < -clip)
+            g = -clip;
+        param[i] -= lr * g;
+    }
+    return 0;
+}
+
+int oracle_grad_accum(double *acc, const double *grad, i64 n)
+{
+    if (n < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i)
+        acc[i] += grad[i];
     return 0;
 }

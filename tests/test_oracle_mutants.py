@@ -14,6 +14,7 @@ import subprocess
 import pytest
 
 import test_oracle_pins as pins
+import test_oracle_train_pins as tpins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
@@ -55,6 +56,20 @@ MUTANTS = [
     ("col2im skips the stride test", "oracle_col2im_spec",
      "if (ti < 0 || ti % s != 0 || ti / s >= OH)",
      "if (ti < 0 || ti / s >= OH)"),
+    ("ReLU gradient passes at zero", "oracle_relu_grad",
+     "dx[i] = x[i] > 0.0 ? dy[i] : 0.0;", "dx[i] = x[i] >= 0.0 ? dy[i] : 0.0;"),
+    ("max pooling keeps the last tied maximum", "oracle_maxpool_forward",
+     "if (xp[at] > xp[best])", "if (xp[at] >= xp[best])"),
+    ("max-pool backward overwrites overlapping windows", "oracle_maxpool_backward",
+     "dp[idx[o]] += dy[o];", "dp[idx[o]] = dy[o];"),
+    ("bias-row gradient reads the next column", "oracle_bias_grad_rows",
+     "acc += dy[i * cols + j];", "acc += dy[i * cols + (j + 1) % cols];"),
+    ("softmax-CE gradient adds the one-hot", "oracle_softmax_ce_grad",
+     "dz[i * classes + label[i]] -= 1.0;", "dz[i * classes + label[i]] += 1.0;"),
+    ("CE loss sums instead of averaging", "oracle_ce_loss",
+     "*loss = total / (double)rows;", "*loss = total;"),
+    ("SGD clips only from above", "oracle_sgd",
+     "if (g < -clip)\n            g = -clip;", "if (g < -clip)\n            g = g;"),
 ]
 
 
@@ -93,6 +108,16 @@ def _run_pins(orc) -> list:
     for name in sorted(os.listdir(pins.GOLDEN)):
         if name.startswith("conv_") and name.endswith(".json"):
             checks.append((name, lambda n=name: pins.test_golden_conv_fixture(orc, n)))
+    for name in dir(tpins):
+        if name.startswith("test_"):
+            fn = getattr(tpins, name)
+            if hasattr(fn, "pytestmark"):  # parametrized: run its first case set
+                for mark in fn.pytestmark:
+                    if mark.name == "parametrize":
+                        for case in mark.args[1]:
+                            checks.append((f"{name} {case}", lambda f=fn, c=case: f(orc, *c)))
+            else:
+                checks.append((name, lambda f=fn: f(orc)))
     for label, fn in checks:
         try:
             fn()
@@ -103,7 +128,7 @@ def _run_pins(orc) -> list:
 
 def test_unmutated_copy_passes(tmp_path):
     so = tmp_path / "liboracle_copy.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(so), SRC],
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(so), SRC, "-lm"],
                    check=True)
     assert _run_pins(_bind(str(so), "copy")) == []
 
@@ -115,7 +140,7 @@ def test_planted_mistake_is_caught(tmp_path, name, func, old, new):
     c_path = tmp_path / "oracle_mutant.c"
     c_path.write_text(_mutate(src, func, old, new))
     so = tmp_path / "liboracle_mutant.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-w", "-o", str(so), str(c_path)],
-                   check=True)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-w", "-o", str(so), str(c_path),
+                    "-lm"], check=True)
     failed = _run_pins(_bind(str(so), func))
     assert failed, f"no pin caught: {name}"
