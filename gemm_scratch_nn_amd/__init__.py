@@ -55,6 +55,8 @@ if len(_hip_runtimes()) > 1:
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
+_ll = ctypes.c_longlong
+_f = ctypes.c_float
 _st = ctypes.c_int
 
 
@@ -83,6 +85,16 @@ _c = {
     "d4r_conv_bias_grad": _sig("d4r_conv_bias_grad", [_vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_gemm_workspace_size": _sig("d4r_gemm_workspace_size", [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "d4r_gemm": _sig("d4r_gemm", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_relu_forward": _sig("d4r_relu_forward", [_vp, _vp, _ll, _vp]),
+    "d4r_relu_backward": _sig("d4r_relu_backward", [_vp, _vp, _vp, _ll, _vp]),
+    "d4r_maxpool_forward": _sig("d4r_maxpool_forward", [_vp, _vp, _vp] + [_i] * 6 + [_vp]),
+    "d4r_maxpool_backward": _sig("d4r_maxpool_backward", [_vp, _vp, _vp] + [_i] * 6 + [_vp]),
+    "d4r_add_bias_rows": _sig("d4r_add_bias_rows", [_vp, _vp, _vp, _i, _i, _vp]),
+    "d4r_bias_grad_rows": _sig("d4r_bias_grad_rows", [_vp, _vp, _i, _i, _vp]),
+    "d4r_softmax": _sig("d4r_softmax", [_vp, _vp, _i, _i, _vp]),
+    "d4r_softmax_ce_grad": _sig("d4r_softmax_ce_grad", [_vp, _vp, _vp, _vp, _i, _i, _vp]),
+    "d4r_sgd_update": _sig("d4r_sgd_update", [_vp, _vp, _ll, _f, _f, _vp]),
+    "d4r_grad_accum": _sig("d4r_grad_accum", [_vp, _vp, _ll, _vp]),
     "d4r_profile_enable": _sig("d4r_profile_enable", [_i]),
     "d4r_profile_reset": _sig("d4r_profile_reset", []),
     "d4r_status_string": _sig("d4r_status_string", [_i], ctypes.c_char_p),
@@ -243,6 +255,50 @@ def d4r_gemm(M, K, N, flags, dtype, A, B, C, ws=None, ws_bytes=None, stream=None
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_gemm", _c["d4r_gemm"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(C), _ptr(ws), nb,
                                       _stream(stream)))
+
+
+def d4r_relu_forward(x, y, n, stream=None) -> None:
+    _check("d4r_relu_forward", _c["d4r_relu_forward"](_ptr(x), _ptr(y), n, _stream(stream)))
+
+
+def d4r_relu_backward(x, dy, dx, n, stream=None) -> None:
+    _check("d4r_relu_backward", _c["d4r_relu_backward"](_ptr(x), _ptr(dy), _ptr(dx), n, _stream(stream)))
+
+
+def d4r_maxpool_forward(x, y, idx, batch, channels, H, W, k, stride, stream=None) -> None:
+    _check("d4r_maxpool_forward", _c["d4r_maxpool_forward"](_ptr(x), _ptr(y), _ptr(idx), batch, channels, H, W,
+                                                            k, stride, _stream(stream)))
+
+
+def d4r_maxpool_backward(dy, idx, dx, batch, channels, H, W, k, stride, stream=None) -> None:
+    _check("d4r_maxpool_backward", _c["d4r_maxpool_backward"](_ptr(dy), _ptr(idx), _ptr(dx), batch, channels,
+                                                              H, W, k, stride, _stream(stream)))
+
+
+def d4r_add_bias_rows(x, bias, y, rows, cols, stream=None) -> None:
+    _check("d4r_add_bias_rows", _c["d4r_add_bias_rows"](_ptr(x), _ptr(bias), _ptr(y), rows, cols,
+                                                        _stream(stream)))
+
+
+def d4r_bias_grad_rows(dy, db, rows, cols, stream=None) -> None:
+    _check("d4r_bias_grad_rows", _c["d4r_bias_grad_rows"](_ptr(dy), _ptr(db), rows, cols, _stream(stream)))
+
+
+def d4r_softmax(z, p, rows, classes, stream=None) -> None:
+    _check("d4r_softmax", _c["d4r_softmax"](_ptr(z), _ptr(p), rows, classes, _stream(stream)))
+
+
+def d4r_softmax_ce_grad(z, labels, dz, loss, rows, classes, stream=None) -> None:
+    _check("d4r_softmax_ce_grad", _c["d4r_softmax_ce_grad"](_ptr(z), _ptr(labels), _ptr(dz), _ptr(loss), rows,
+                                                            classes, _stream(stream)))
+
+
+def d4r_sgd_update(param, grad, n, lr, clip, stream=None) -> None:
+    _check("d4r_sgd_update", _c["d4r_sgd_update"](_ptr(param), _ptr(grad), n, lr, clip, _stream(stream)))
+
+
+def d4r_grad_accum(acc, grad, n, stream=None) -> None:
+    _check("d4r_grad_accum", _c["d4r_grad_accum"](_ptr(acc), _ptr(grad), n, _stream(stream)))
 
 
 def d4r_profile_enable(on: bool) -> None:

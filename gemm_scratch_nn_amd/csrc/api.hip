@@ -935,6 +935,230 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
     return ok();
 }
 
+/* ---- the rest of a training step (f32) ---- */
+
+namespace {
+
+d4r_status check_count(long long n, const char *name)
+{
+    if (n < 0)
+        return fail(D4R_ERR_INVALID_ARG, "%s = %lld is negative", name, n);
+    return D4R_OK;
+}
+
+// Profiled launch of one training-step kernel: name, algorithmic bytes
+extern "C++" template <class F>
+d4r_status run_step(hipStream_t s, const char *name, double bytes, const char *what, F &&launch)
+{
+    ProfScope ps(s, name, 0.0, bytes);
+    hipError_t e = launch();
+    ps.done();
+    if (e != hipSuccess)
+        return launched(e, what);
+    return ok();
+}
+
+}  // namespace
+
+d4r_status d4r_relu_forward(const float *x, float *y, long long n, void *hip_stream)
+{
+    D4R_TRY(check_count(n, "n"));
+    if (n == 0)
+        return ok();
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(y, "y"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "relu_fwd", 8.0 * n, "ReLU", [&] { return launch_relu_forward(x, y, n, s); });
+}
+
+d4r_status d4r_relu_backward(const float *x, const float *dy, float *dx, long long n, void *hip_stream)
+{
+    D4R_TRY(check_count(n, "n"));
+    if (n == 0)
+        return ok();
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    if (dx == x && dx != dy)
+        return fail(D4R_ERR_INVALID_ARG, "dx may be dy but not x");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "relu_bwd", 12.0 * n, "ReLU gradient",
+                    [&] { return launch_relu_backward(x, dy, dx, n, s); });
+}
+
+namespace {
+
+d4r_status check_pool(int batch, int channels, int H, int W, int k, int stride, long long *planes, int *OH,
+                      int *OW)
+{
+    if (batch < 0 || channels < 0)
+        return fail(D4R_ERR_INVALID_ARG, "batch = %d, channels = %d must be >= 0", batch, channels);
+    if (k < 1 || stride < 1)
+        return fail(D4R_ERR_INVALID_ARG, "k = %d, stride = %d must be >= 1", k, stride);
+    if (H < k || W < k)
+        return fail(D4R_ERR_INVALID_ARG, "plane %dx%d is smaller than the %dx%d window", H, W, k, k);
+    *OH = (H - k) / stride + 1;
+    *OW = (W - k) / stride + 1;
+    *planes = (long long)batch * channels;
+    if ((long long)H * W > kMaxElems)
+        return fail(D4R_ERR_INVALID_ARG, "plane %dx%d has 2^31 or more elements", H, W);
+    return D4R_OK;
+}
+
+}  // namespace
+
+d4r_status d4r_maxpool_forward(const float *x, float *y, int *idx, int batch, int channels, int H, int W, int k,
+                               int stride, void *hip_stream)
+{
+    long long planes;
+    int OH, OW;
+    D4R_TRY(check_pool(batch, channels, H, W, k, stride, &planes, &OH, &OW));
+    if (planes == 0)
+        return ok();
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(y, "y"));
+    D4R_TRY(check_tensor(idx, "idx"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const double outs = (double)planes * OH * OW;
+    return run_step(s, "maxpool_fwd", 4.0 * planes * H * W + 8.0 * outs, "max pooling", [&] {
+        return launch_maxpool_forward(x, y, (int32_t *)idx, planes, H, W, OH, OW, k, stride, s);
+    });
+}
+
+d4r_status d4r_maxpool_backward(const float *dy, const int *idx, float *dx, int batch, int channels, int H, int W,
+                                int k, int stride, void *hip_stream)
+{
+    long long planes;
+    int OH, OW;
+    D4R_TRY(check_pool(batch, channels, H, W, k, stride, &planes, &OH, &OW));
+    if (planes == 0)
+        return ok();
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(idx, "idx"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const double outs = (double)planes * OH * OW;
+    return run_step(s, "maxpool_bwd", 8.0 * outs + 4.0 * planes * H * W, "max-pool gradient", [&] {
+        return launch_maxpool_backward(dy, (const int32_t *)idx, dx, planes, H, W, OH, OW, k, stride, s);
+    });
+}
+
+d4r_status d4r_add_bias_rows(const float *x, const float *bias, float *y, int rows, int cols, void *hip_stream)
+{
+    if (rows < 0 || cols < 1)
+        return fail(D4R_ERR_INVALID_ARG, "rows = %d must be >= 0 and cols = %d >= 1", rows, cols);
+    if ((long long)rows * cols > kMaxElems)
+        return fail(D4R_ERR_INVALID_ARG, "rows * cols has 2^31 or more elements");
+    if (rows == 0)
+        return ok();
+    D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(y, "y"));
+    if (!bias)
+        return fail(D4R_ERR_INVALID_ARG, "bias is NULL");
+    D4R_TRY(check_vec(bias, "bias"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "add_bias_rows", 8.0 * rows * cols + 4.0 * cols, "bias add",
+                    [&] { return launch_add_bias_rows(x, bias, y, rows, cols, s); });
+}
+
+d4r_status d4r_bias_grad_rows(const float *dy, float *db, int rows, int cols, void *hip_stream)
+{
+    if (rows < 0 || cols < 1)
+        return fail(D4R_ERR_INVALID_ARG, "rows = %d must be >= 0 and cols = %d >= 1", rows, cols);
+    if ((long long)rows * cols > kMaxElems)
+        return fail(D4R_ERR_INVALID_ARG, "rows * cols has 2^31 or more elements");
+    if (rows > 0)
+        D4R_TRY(check_tensor(dy, "dy"));  // rows == 0 reads no dy (db = 0)
+    if (!db)
+        return fail(D4R_ERR_INVALID_ARG, "db is NULL");
+    D4R_TRY(check_vec(db, "db"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "bias_grad_rows", 4.0 * rows * cols + 4.0 * cols, "bias gradient",
+                    [&] { return launch_bias_grad_rows(dy, db, rows, cols, s); });
+}
+
+namespace {
+
+d4r_status check_rows(int rows, int classes)
+{
+    if (rows < 1 || classes < 1)
+        return fail(D4R_ERR_INVALID_ARG, "rows = %d and classes = %d must be >= 1", rows, classes);
+    if ((long long)rows * classes > kMaxElems)
+        return fail(D4R_ERR_INVALID_ARG, "rows * classes has 2^31 or more elements");
+    return D4R_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+d4r_status d4r_softmax(const float *z, float *p, int rows, int classes, void *hip_stream)
+{
+    D4R_TRY(check_rows(rows, classes));
+    D4R_TRY(check_tensor(z, "z"));
+    D4R_TRY(check_tensor(p, "p"));
+    const size_t bytes = 4ull * rows * classes;
+    if (overlaps(z, bytes, p, bytes))
+        return fail(D4R_ERR_INVALID_ARG, "p overlaps z");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "softmax", 8.0 * rows * classes, "softmax",
+                    [&] { return launch_softmax_rows(z, nullptr, p, nullptr, rows, classes, s); });
+}
+
+d4r_status d4r_softmax_ce_grad(const float *z, const int *labels, float *dz, float *loss, int rows, int classes,
+                               void *hip_stream)
+{
+    D4R_TRY(check_rows(rows, classes));
+    D4R_TRY(check_tensor(z, "z"));
+    D4R_TRY(check_tensor(dz, "dz"));
+    if (!labels)
+        return fail(D4R_ERR_INVALID_ARG, "labels is NULL");
+    D4R_TRY(check_vec(labels, "labels"));
+    D4R_TRY(check_vec(loss, "loss"));
+    const size_t bytes = 4ull * rows * classes;
+    if (overlaps(z, bytes, dz, bytes))
+        return fail(D4R_ERR_INVALID_ARG, "dz overlaps z");
+    if (loss && (overlaps(loss, 4, z, bytes) || overlaps(loss, 4, dz, bytes)))
+        return fail(D4R_ERR_INVALID_ARG, "loss overlaps z or dz");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "softmax_ce_grad", 8.0 * rows * classes + 4.0 * rows, "softmax-CE gradient", [&] {
+        return launch_softmax_rows(z, (const int32_t *)labels, dz, loss, rows, classes, s);
+    });
+}
+
+d4r_status d4r_sgd_update(float *param, const float *grad, long long n, float lr, float clip, void *hip_stream)
+{
+    D4R_TRY(check_count(n, "n"));
+    if (!(clip >= 0.0f))
+        return fail(D4R_ERR_INVALID_ARG, "clip must be >= 0 (got %g)", (double)clip);
+    if (n == 0)
+        return ok();
+    D4R_TRY(check_tensor(param, "param"));
+    D4R_TRY(check_tensor(grad, "grad"));
+    if (overlaps(param, 4ull * n, grad, 4ull * n))
+        return fail(D4R_ERR_INVALID_ARG, "grad overlaps param");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "sgd", 12.0 * n, "SGD update", [&] { return launch_sgd(param, grad, n, lr, clip, s); });
+}
+
+d4r_status d4r_grad_accum(float *acc, const float *grad, long long n, void *hip_stream)
+{
+    D4R_TRY(check_count(n, "n"));
+    if (n == 0)
+        return ok();
+    D4R_TRY(check_tensor(acc, "acc"));
+    D4R_TRY(check_tensor(grad, "grad"));
+    if (overlaps(acc, 4ull * n, grad, 4ull * n))
+        return fail(D4R_ERR_INVALID_ARG, "grad overlaps acc");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "grad_accum", 12.0 * n, "gradient accumulation",
+                    [&] { return launch_grad_accum(acc, grad, n, s); });
+}
+
 d4r_status d4r_profile_enable(int on)
 {
     Profiler &P = prof();

@@ -128,4 +128,23 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,
                                 const float *bias, int P, hipStream_t s);
 
+// The rest of a training step (f32; train_kernels.hip).  Elementwise
+// kernels take 16-byte aligned pointers; n may be 0.
+hipError_t launch_relu_forward(const float *x, float *y, long long n, hipStream_t s);
+hipError_t launch_relu_backward(const float *x, const float *dy, float *dx, long long n, hipStream_t s);
+// planes = batch * channels of H x W; output OH x OW; idx = plane offsets
+hipError_t launch_maxpool_forward(const float *x, float *y, int32_t *idx, long long planes, int H, int W,
+                                  int OH, int OW, int k, int st, hipStream_t s);
+hipError_t launch_maxpool_backward(const float *dy, const int32_t *idx, float *dx, long long planes, int H,
+                                   int W, int OH, int OW, int k, int st, hipStream_t s);
+hipError_t launch_add_bias_rows(const float *x, const float *bias, float *y, long long rows, int cols,
+                                hipStream_t s);
+hipError_t launch_bias_grad_rows(const float *dy, float *db, long long rows, int cols, hipStream_t s);
+// label NULL: out = softmax(z); else out = softmax(z) - one_hot(label) and
+// *loss (if loss != NULL) = mean cross-entropy
+hipError_t launch_softmax_rows(const float *z, const int32_t *label, float *out, float *loss, int rows,
+                               int classes, hipStream_t s);
+hipError_t launch_sgd(float *p, const float *g, long long n, float lr, float clip, hipStream_t s);
+hipError_t launch_grad_accum(float *acc, const float *g, long long n, hipStream_t s);
+
 }  // namespace d4r

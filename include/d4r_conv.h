@@ -219,6 +219,80 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
                     void *hip_stream);
 
 /*
+ * The rest of a training step around the convolutions (directcompute-nn
+ * page, "HLSL Shader Reference": "Activation / Loss Shaders", "Pooling
+ * Shaders", "Utility Shaders"; the page's framework composes them with the
+ * convolutions and matmuls into LeNet and AlexNet training, "Layer Stack"
+ * and "File Structure").  All float32 (labels and argmax indices int32), all device
+ * pointers owned by the caller, 16-byte aligned except bias, db, labels and
+ * loss (4-byte).  Counts n, batch*channels and rows may be 0: nothing is
+ * enqueued and the pointers are not examined (except d4r_bias_grad_rows,
+ * which still writes db = 0 when rows is 0).  Every result is
+ * run-to-run deterministic (fixed summation orders, no atomics).
+ *
+ * d4r_relu_forward: y = max(x, 0) elementwise; y may be x.
+ * d4r_relu_backward: dx = dy where x > 0 (strictly), else 0; dx may be dy,
+ *   not x.
+ */
+d4r_status d4r_relu_forward(const float *x, float *y, long long n, void *hip_stream);
+d4r_status d4r_relu_backward(const float *x, const float *dy, float *dx, long long n,
+                             void *hip_stream);
+
+/*
+ * Max pooling with argmax, window k x k, stride `stride` on both axes, no
+ * padding: x (batch, channels, H, W) -> y (batch, channels, OH, OW), OH =
+ * (H - k)/stride + 1, OW likewise (H, W >= k).  idx[b][c][i][j] = h*W + w,
+ * the position of the maximum inside its (b, c) plane: the first strictly
+ * greater value met scanning the window row by row.  The backward writes
+ * every dx element: the sum of the dy entries whose saved index is that
+ * element (overlapping windows add up, windows in row-major order), 0 where
+ * none chose it (a gather, so dx needs no clearing first, unlike the page's
+ * scatter after a buffer clear, "How the Engine Works").  idx must come from
+ * the forward with the same geometry.
+ * y, idx and dx must not overlap the other arguments.
+ */
+d4r_status d4r_maxpool_forward(const float *x, float *y, int *idx, int batch, int channels,
+                               int H, int W, int k, int stride, void *hip_stream);
+d4r_status d4r_maxpool_backward(const float *dy, const int *idx, float *dx, int batch,
+                                int channels, int H, int W, int k, int stride,
+                                void *hip_stream);
+
+/*
+ * Linear-layer bias on row-major rows x cols (the page's add_bias:
+ * out[i] = A[i] + B[i mod cols]): y[r][c] = x[r][c] + bias[c]; y may be x.
+ * d4r_bias_grad_rows: db[c] = sum over r of dy[r][c].  Use d4r_gemm for the layer's matmuls (x * W^T is flags 2, the data
+ * gradient dy * W flags 0, the weight gradient dy^T * x flags 1).
+ */
+d4r_status d4r_add_bias_rows(const float *x, const float *bias, float *y, int rows, int cols,
+                             void *hip_stream);
+d4r_status d4r_bias_grad_rows(const float *dy, float *db, int rows, int cols, void *hip_stream);
+
+/*
+ * Row softmax of z (rows x classes, row-major), the row maximum subtracted
+ * before exponentiation: p = softmax(z).  p must not overlap z.
+ *
+ * d4r_softmax_ce_grad: dz = softmax(z) - one_hot(labels) per row (no 1/rows
+ * factor), and, when loss is not NULL, *loss = the mean over rows of
+ * -log softmax(z)[label] (one float).  A label outside [0, classes) cannot be
+ * rejected without a host synchronisation: that row of dz and the loss
+ * become NaN.  With a loss the kernel runs as one workgroup (a fixed-order
+ * mean); without, one wavefront per row.  dz and loss must not overlap z.
+ */
+d4r_status d4r_softmax(const float *z, float *p, int rows, int classes, void *hip_stream);
+d4r_status d4r_softmax_ce_grad(const float *z, const int *labels, float *dz, float *loss,
+                               int rows, int classes, void *hip_stream);
+
+/*
+ * d4r_sgd_update: param -= lr * clamp(grad, -clip, clip), elementwise, in
+ * place (clip >= 0; +infinity disables clipping).
+ * d4r_grad_accum: acc += grad, in place (a tensor that receives gradients
+ * along several paths).  grad must not overlap param / acc.
+ */
+d4r_status d4r_sgd_update(float *param, const float *grad, long long n, float lr, float clip,
+                          void *hip_stream);
+d4r_status d4r_grad_accum(float *acc, const float *grad, long long n, void *hip_stream);
+
+/*
  * Kernel timing (measurement aid).  While enabled, every kernel launch made
  * by the calls above is bracketed by a pair of HIP events recorded on the
  * call's stream, and tagged with the launch's algorithmic work: flops for

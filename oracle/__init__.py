@@ -312,3 +312,69 @@ def grad_accum(acc, grad) -> np.ndarray:
     g = _f64(grad)
     _check(_load().oracle_grad_accum(_ptr(a), _ptr(g), a.size), "grad_accum")
     return a
+
+
+# ---------------------------------------------------------------------------
+# One LeNet-5 training step composed from the functions above
+# ---------------------------------------------------------------------------
+
+def lenet_step(inp: dict, lr: float, clip: float) -> dict:
+    """Forward, backward and SGD update of LeNet-5 on one batch, in float64.
+
+    The network is the directcompute-nn page's LeNet ("File Structure":
+    1->6->16 conv, 256->120->84->10 FC) on 1x28x28 images: conv 5x5 without
+    padding, ReLU, max pool 2x2 stride 2, twice; flatten (NCHW order) to 256;
+    linear 256->120, ReLU, 120->84, ReLU, 84->10; softmax-cross-entropy.
+    Each layer follows the page's autograd ("Autograd"; "Convolution: The
+    im2col Approach" for the conv gradients, "Transpose via Flags" for the
+    linear ones): a linear layer y = x W^T + b (W stored out x in) is the
+    matmul with flags 2; its data gradient dy W is flags 0 and its weight
+    gradient dy^T x is flags 1.  The loss gradient is softmax - one_hot (no
+    1/batch factor); the first convolution's data gradient is not needed.
+    Every parameter then takes param -= lr * clamp(grad, -clip, clip).
+
+    ``inp`` holds x, labels and the parameters named in workloads.LENET_PARAMS.
+    Returns the loss, every activation, every gradient (key "d" + name) and
+    every updated parameter (key "new_" + name).
+    """
+    f = {k: _f64(v) if k != "labels" else np.asarray(v) for k, v in inp.items()}
+    B = f["x"].shape[0]
+    r = {}
+    # forward
+    r["a1"] = relu(conv_forward(f["x"], f["conv1_w"], f["conv1_b"], 1, 0))          # B,6,24,24
+    r["p1"], r["idx1"] = maxpool_forward(r["a1"], 2, 2)                              # B,6,12,12
+    r["a2"] = relu(conv_forward(r["p1"], f["conv2_w"], f["conv2_b"], 1, 0))         # B,16,8,8
+    r["p2"], r["idx2"] = maxpool_forward(r["a2"], 2, 2)                              # B,16,4,4
+    flat = r["p2"].reshape(B, 256)
+    r["pre1"] = add_bias_rows(gemm(flat, f["fc1_w"], B, 256, 120, 2), f["fc1_b"])
+    r["h1"] = relu(r["pre1"])
+    r["pre2"] = add_bias_rows(gemm(r["h1"], f["fc2_w"], B, 120, 84, 2), f["fc2_b"])
+    r["h2"] = relu(r["pre2"])
+    r["z"] = add_bias_rows(gemm(r["h2"], f["fc3_w"], B, 84, 10, 2), f["fc3_b"])
+    r["loss"] = ce_loss(r["z"], f["labels"])
+    # backward
+    dz = softmax_ce_grad(r["z"], f["labels"])
+    r["dz"] = dz
+    r["dfc3_w"] = gemm(dz, r["h2"], 10, B, 84, 1)
+    r["dfc3_b"] = bias_grad_rows(dz)
+    dh2 = relu_grad(r["pre2"], gemm(dz, f["fc3_w"], B, 10, 84, 0))
+    r["dfc2_w"] = gemm(dh2, r["h1"], 84, B, 120, 1)
+    r["dfc2_b"] = bias_grad_rows(dh2)
+    dh1 = relu_grad(r["pre1"], gemm(dh2, f["fc2_w"], B, 84, 120, 0))
+    r["dfc1_w"] = gemm(dh1, flat, 120, B, 256, 1)
+    r["dfc1_b"] = bias_grad_rows(dh1)
+    dflat = gemm(dh1, f["fc1_w"], B, 120, 256, 0)
+    da2 = maxpool_backward(dflat.reshape(r["p2"].shape), r["idx2"], r["a2"].shape, 2, 2)
+    g2 = relu_grad(r["a2"], da2)
+    r["dconv2_w"] = conv_backward_filter(r["p1"], g2, f["conv2_w"].shape, 1, 0)
+    r["dconv2_b"] = conv_backward_bias(g2)
+    dp1 = conv_backward_data(g2, f["conv2_w"], r["p1"].shape, 1, 0)
+    da1 = maxpool_backward(dp1, r["idx1"], r["a1"].shape, 2, 2)
+    g1 = relu_grad(r["a1"], da1)
+    r["dconv1_w"] = conv_backward_filter(f["x"], g1, f["conv1_w"].shape, 1, 0)
+    r["dconv1_b"] = conv_backward_bias(g1)
+    # update
+    for name in ("conv1_w", "conv1_b", "conv2_w", "conv2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b",
+                 "fc3_w", "fc3_b"):
+        r["new_" + name] = sgd(f[name], r["d" + name], lr, clip)
+    return r

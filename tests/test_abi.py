@@ -18,7 +18,10 @@ def test_every_declared_symbol_is_exported():
                 "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
                 "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
                 "d4r_status_string", "d4r_last_error", "d4r_profile_enable",
-                "d4r_profile_reset", "d4r_profile_read"}
+                "d4r_profile_reset", "d4r_profile_read", "d4r_relu_forward", "d4r_relu_backward",
+                "d4r_maxpool_forward", "d4r_maxpool_backward", "d4r_add_bias_rows",
+                "d4r_bias_grad_rows", "d4r_softmax", "d4r_softmax_ce_grad", "d4r_sgd_update",
+                "d4r_grad_accum"}
     assert expected <= set(names)
     for n in names:
         assert d4r.exported(n), n
@@ -212,3 +215,68 @@ def test_profile_recorder_host_side():
     d4r.d4r_profile_enable(True)
     d4r.d4r_profile_enable(False)
     assert d4r.d4r_profile_read() == []
+
+
+# ---- the rest of a training step: validation only (no kernel runs here) ----
+
+TRAIN_ERRORS = [
+    ("relu_forward negative n", lambda: d4r.d4r_relu_forward(FAKE, FAKE, -1, stream=0)),
+    ("relu_forward x NULL", lambda: d4r.d4r_relu_forward(None, FAKE, 8, stream=0)),
+    ("relu_forward y misaligned", lambda: d4r.d4r_relu_forward(FAKE, MISALIGNED, 8, stream=0)),
+    ("relu_backward dy NULL", lambda: d4r.d4r_relu_backward(FAKE, None, FAKE, 8, stream=0)),
+    ("relu_backward dx is x", lambda: d4r.d4r_relu_backward(FAKE, FAKE + 4096, FAKE, 8, stream=0)),
+    ("maxpool_forward window > plane", lambda: d4r.d4r_maxpool_forward(FAKE, FAKE, FAKE, 1, 1, 3, 8, 4, 1,
+                                                                       stream=0)),
+    ("maxpool_forward k 0", lambda: d4r.d4r_maxpool_forward(FAKE, FAKE, FAKE, 1, 1, 8, 8, 0, 1, stream=0)),
+    ("maxpool_forward stride 0", lambda: d4r.d4r_maxpool_forward(FAKE, FAKE, FAKE, 1, 1, 8, 8, 2, 0,
+                                                                 stream=0)),
+    ("maxpool_forward batch < 0", lambda: d4r.d4r_maxpool_forward(FAKE, FAKE, FAKE, -1, 1, 8, 8, 2, 2,
+                                                                  stream=0)),
+    ("maxpool_forward idx NULL", lambda: d4r.d4r_maxpool_forward(FAKE, FAKE, None, 1, 1, 8, 8, 2, 2, stream=0)),
+    ("maxpool_backward dx misaligned", lambda: d4r.d4r_maxpool_backward(FAKE, FAKE, MISALIGNED, 1, 1, 8, 8, 2, 2,
+                                                                        stream=0)),
+    ("add_bias_rows cols 0", lambda: d4r.d4r_add_bias_rows(FAKE, FAKE, FAKE, 4, 0, stream=0)),
+    ("add_bias_rows bias NULL", lambda: d4r.d4r_add_bias_rows(FAKE, None, FAKE, 4, 4, stream=0)),
+    ("add_bias_rows 2^31", lambda: d4r.d4r_add_bias_rows(FAKE, FAKE, FAKE, 1 << 16, 1 << 15, stream=0)),
+    ("bias_grad_rows db NULL", lambda: d4r.d4r_bias_grad_rows(FAKE, None, 4, 4, stream=0)),
+    ("bias_grad_rows db misaligned", lambda: d4r.d4r_bias_grad_rows(FAKE, FAKE + 2, 4, 4, stream=0)),
+    ("softmax rows 0", lambda: d4r.d4r_softmax(FAKE, FAKE + 4096, 0, 10, stream=0)),
+    ("softmax p overlaps z", lambda: d4r.d4r_softmax(FAKE, FAKE + 16, 4, 10, stream=0)),
+    ("softmax_ce labels NULL", lambda: d4r.d4r_softmax_ce_grad(FAKE, None, FAKE + 4096, None, 4, 10, stream=0)),
+    ("softmax_ce classes 0", lambda: d4r.d4r_softmax_ce_grad(FAKE, FAKE, FAKE + 4096, None, 4, 0, stream=0)),
+    ("softmax_ce dz is z", lambda: d4r.d4r_softmax_ce_grad(FAKE, FAKE + 8192, FAKE, None, 4, 10, stream=0)),
+    ("softmax_ce loss inside dz", lambda: d4r.d4r_softmax_ce_grad(FAKE, FAKE + 8192, FAKE + 4096, FAKE + 4100,
+                                                                  4, 10, stream=0)),
+    ("softmax_ce loss misaligned", lambda: d4r.d4r_softmax_ce_grad(FAKE, FAKE + 8192, FAKE + 4096, FAKE + 16386,
+                                                                   4, 10, stream=0)),
+    ("sgd negative clip", lambda: d4r.d4r_sgd_update(FAKE, FAKE + 4096, 8, 0.1, -1.0, stream=0)),
+    ("sgd NaN clip", lambda: d4r.d4r_sgd_update(FAKE, FAKE + 4096, 8, 0.1, float("nan"), stream=0)),
+    ("sgd grad overlaps param", lambda: d4r.d4r_sgd_update(FAKE, FAKE + 16, 8, 0.1, 1.0, stream=0)),
+    ("sgd negative n", lambda: d4r.d4r_sgd_update(FAKE, FAKE + 4096, -8, 0.1, 1.0, stream=0)),
+    ("grad_accum grad NULL", lambda: d4r.d4r_grad_accum(FAKE, None, 8, stream=0)),
+    ("grad_accum overlap", lambda: d4r.d4r_grad_accum(FAKE, FAKE, 8, stream=0)),
+]
+
+
+@pytest.mark.parametrize("name,call", TRAIN_ERRORS, ids=[t[0] for t in TRAIN_ERRORS])
+def test_training_step_argument_errors(name, call):
+    with pytest.raises(D4RError) as e:
+        call()
+    assert e.value.status == INVALID, name
+    assert d4r.d4r_last_error()
+
+
+def test_training_step_empty_calls_enqueue_nothing():
+    # n = 0 / zero planes / zero rows return before any HIP call; the
+    # pointers (an empty tensor has none) are not examined
+    d4r.d4r_relu_forward(None, None, 0, stream=0)
+    d4r.d4r_relu_backward(None, None, None, 0, stream=0)
+    d4r.d4r_maxpool_forward(None, None, None, 0, 3, 8, 8, 2, 2, stream=0)
+    d4r.d4r_maxpool_backward(None, None, None, 2, 0, 8, 8, 2, 2, stream=0)
+    d4r.d4r_add_bias_rows(None, None, None, 0, 10, stream=0)
+    d4r.d4r_sgd_update(None, None, 0, 0.1, 1.0, stream=0)
+    d4r.d4r_grad_accum(None, None, 0, stream=0)
+    with pytest.raises(D4RError):  # geometry is still checked
+        d4r.d4r_maxpool_forward(None, None, None, 0, 3, 8, 8, 9, 2, stream=0)
+    with pytest.raises(D4RError):
+        d4r.d4r_sgd_update(None, None, 0, 0.1, -1.0, stream=0)

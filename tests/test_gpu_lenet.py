@@ -1,0 +1,119 @@
+"""A whole LeNet-5 training step on the GPU against the oracle's step.
+
+The step (gemm_scratch_nn_amd.lenet.LeNetStep) issues only library calls:
+two im2col + GEMM convolutions with their filter, data and bias gradients,
+ReLU, max pooling with argmax, three linear layers (matmul flags + row
+bias), the softmax-cross-entropy gradient and one SGD launch over all
+parameters.  The oracle (oracle.lenet_step) composes its float64 routines
+in the same order.
+
+Inputs (workloads.lenet_step_inputs): the image and the conv parameters are
+small dyadic rationals, so both convolutions, their ReLUs and poolings are
+exact in float32 and must match bit for bit, ties in the pooling windows
+included.  The linear layers are continuous; their ReLU decisions agree
+because every pre-activation is far from 0 compared to float32 rounding
+(checked on the oracle's values below).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+LR, CLIP = 0.01, 0.05
+
+
+def _setup(batch, seed):
+    from gemm_scratch_nn_amd.lenet import LeNetStep
+    inp = wl.lenet_step_inputs(batch, seed)
+    net = LeNetStep(batch)
+    net.load({n: torch.from_numpy(inp[n]).cuda() for n, _ in wl.LENET_PARAMS})
+    x = torch.from_numpy(inp["x"]).cuda()
+    lab = torch.from_numpy(inp["labels"]).cuda()
+    return inp, net, x, lab
+
+
+def _decision_margin(r):
+    """Smallest |pre-activation| of the linear layers over their RMS."""
+    return min(np.min(np.abs(r[k])) / np.sqrt(np.mean(r[k] ** 2)) for k in ("pre1", "pre2"))
+
+
+@pytest.mark.parametrize("batch,seed", [(64, 0), (5, 3)])
+def test_lenet_step_matches_oracle(batch, seed):
+    inp, net, x, lab = _setup(batch, seed)
+    lr = float(np.float32(LR))
+    r = oracle.lenet_step(inp, lr, CLIP)
+    # float32 rounding of the linear layers is ~1e-6 of their RMS: a margin
+    # 20x larger keeps every ReLU decision the same on both sides
+    assert _decision_margin(r) > 2e-5, "seed gives a near-zero pre-activation"
+    old = net.flat.clone()
+    net.forward_backward(x, lab)
+    torch.cuda.synchronize()
+    # convolution part: exact
+    for k, t in (("a1", net.a1), ("p1", net.p1), ("a2", net.a2), ("p2", net.p2)):
+        assert np.array_equal(host(t), r[k]), k
+    assert np.array_equal(net.idx1.cpu().numpy(), r["idx1"])
+    assert np.array_equal(net.idx2.cpu().numpy(), r["idx2"])
+    # linear part and the loss
+    for k, t in (("h1", net.h1), ("h2", net.h2), ("z", net.z), ("dz", net.dz)):
+        assert rel_err(host(t), r[k]) <= TOL, k
+    assert abs(net.loss.item() - r["loss"]) <= TOL * abs(r["loss"])
+    for name, _ in wl.LENET_PARAMS:
+        assert rel_err(host(net.g[name]), r["d" + name]) <= TOL, name
+    # the gaps between parameters in the gradient buffer stay zero
+    mask = torch.ones_like(net.flat_grad, dtype=torch.bool)
+    for name, shape in wl.LENET_PARAMS:
+        o = net.offsets[name]
+        mask[o:o + int(np.prod(shape))] = False
+    assert not net.flat_grad[mask].any()
+    # the update
+    net.update(lr, CLIP)
+    torch.cuda.synchronize()
+    assert torch.equal(net.flat[mask], old[mask])
+    for name, _ in wl.LENET_PARAMS:
+        got = host(net.p[name])
+        ref = r["new_" + name]
+        assert rel_err(got, ref) <= 1e-6, name
+        # the step itself, p_new - p_old: float32 rounding of p - lr*c is up to
+        # 2^-24 |p|, and |p| / |lr * c| reaches ~10^3 here
+        step_ref = ref - inp[name].astype(np.float64)
+        step_got = got - inp[name].astype(np.float64)
+        assert rel_err(step_got, step_ref) <= 1e-3, name
+
+
+def test_lenet_steps_graph_replay_matches_eager():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    inp, eager, x, lab = _setup(64, 1)
+    _, graphed, _, _ = _setup(64, 1)
+    gx, glab = x.clone(), lab.clone()
+    graphed.step(gx, glab, LR, CLIP)  # warm up outside capture
+    eager.step(x, lab, LR, CLIP)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed.step(gx, glab, LR, CLIP)
+    torch.cuda.synchronize()
+    for i in range(4):
+        # eager work between replays: a new batch, in place
+        x.copy_(torch.roll(x, shifts=1 + i, dims=3))
+        lab.copy_(torch.remainder(lab + 3, 10))
+        gx.copy_(x)
+        glab.copy_(lab)
+        torch.cuda.synchronize()
+        graph.replay()
+        eager.step(x, lab, LR, CLIP)
+        torch.cuda.synchronize()
+        assert torch.equal(graphed.flat, eager.flat), i
+        assert torch.equal(graphed.loss, eager.loss), i
+    # training moved the loss of a repeated batch down
+    first = eager.loss.item()
+    for _ in range(20):
+        eager.step(x, lab, LR, CLIP)
+    torch.cuda.synchronize()
+    assert eager.loss.item() < first

@@ -172,3 +172,43 @@ def test_sgd_clips_both_sides(orc):
 
 def test_grad_accum_adds(orc):
     assert np.array_equal(orc.grad_accum([1.0, -2.0, 0.5], [0.25, 2.0, -0.5]), [1.25, 0.0, 0.0])
+
+
+# ---------------------------------------------------- a whole LeNet-5 step
+def _lenet_torch_f64(inp, lr, clip):
+    """The same network in torch float64 autograd (independent operators)."""
+    p = {k: _t(v).requires_grad_() for k, v in inp.items() if k not in ("x", "labels")}
+    x = _t(inp["x"])
+    a = F.max_pool2d(F.relu(F.conv2d(x, p["conv1_w"], p["conv1_b"])), 2, 2)
+    a = F.max_pool2d(F.relu(F.conv2d(a, p["conv2_w"], p["conv2_b"])), 2, 2)
+    h = a.reshape(a.shape[0], -1)
+    h = F.relu(F.linear(h, p["fc1_w"], p["fc1_b"]))
+    h = F.relu(F.linear(h, p["fc2_w"], p["fc2_b"]))
+    z = F.linear(h, p["fc3_w"], p["fc3_b"])
+    lab = torch.tensor(inp["labels"], dtype=torch.long)
+    # the page's loss gradient is softmax - one_hot per row: the gradient of
+    # the summed (not averaged) cross-entropy
+    F.cross_entropy(z, lab, reduction="sum").backward()
+    loss = F.cross_entropy(z, lab).item()
+    new = {k: (v - lr * torch.clamp(v.grad, -clip, clip)).detach().numpy() for k, v in p.items()}
+    return loss, {k: v.grad.numpy() for k, v in p.items()}, new
+
+
+@pytest.mark.parametrize("batch,seed", [(8, 0), (3, 1)])
+def test_lenet_step_matches_torch_autograd(orc, batch, seed):
+    import workloads as wl
+    rng = np.random.default_rng((880, seed))
+    inp = {"x": rng.uniform(0.0, 1.0, size=(batch, 1, 28, 28)),
+           "labels": rng.integers(0, 10, size=batch).astype(np.int32)}
+    for name, shape in wl.LENET_PARAMS:  # continuous values: no max-pool ties
+        inp[name] = rng.normal(0.0, 0.3, size=shape)
+    lr, clip = 0.05, 0.02
+    r = orc.lenet_step(inp, lr, clip)
+    loss, grads, new = _lenet_torch_f64(inp, lr, clip)
+    assert abs(r["loss"] - loss) <= 1e-12 * max(1.0, abs(loss))
+    for name, g in grads.items():
+        assert np.allclose(r["d" + name], g, rtol=1e-10, atol=1e-12), name
+        assert np.allclose(r["new_" + name], new[name], rtol=1e-12, atol=1e-14), name
+    # the clip acted on some gradients and not on others
+    d = np.concatenate([np.abs(g).ravel() for g in grads.values()])
+    assert (d > clip).any() and (d < clip).any()

@@ -195,6 +195,10 @@ def draw(dist: tuple, shape, seed: tuple) -> np.ndarray:
         v = np.arange(1, int(np.prod(shape)) + 1, dtype=np.float64).reshape(shape)
     elif kind == "small_int":
         v = rng.integers(-dist[1], dist[1] + 1, size=shape).astype(np.float64)
+    elif kind == "dyadic":
+        # integers in [lo, hi] scaled by 2^-frac: exact in float32, and so are
+        # short sums and products of them
+        v = rng.integers(dist[1], dist[2] + 1, size=shape).astype(np.float64) * 2.0 ** -dist[3]
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return v
@@ -277,3 +281,47 @@ def random_conv(shape: ConvShape, dtype: str, seed: int,
     g = draw(("normal", 1.0), shape.y_shape(), (9000 + seed, 0, TID_G))
     return {"x": quantize(x, dtype), "w": quantize(w, dtype),
             "bias": quantize(b, "f32"), "g": quantize(g, dtype)}
+
+
+# ----------------------------------------------------------------------------
+# The rest of a training step: activations, labels, a LeNet-5 step
+# ----------------------------------------------------------------------------
+
+def f32_array(dist: tuple, shape, seed: tuple) -> np.ndarray:
+    """``draw`` rounded to float32 (the storage of every training-step op)."""
+    return draw(dist, shape, seed).astype(np.float32)
+
+
+def labels(rows: int, classes: int, seed: tuple) -> np.ndarray:
+    """Uniform class labels in [0, classes), int32."""
+    return np.random.default_rng(seed).integers(0, classes, size=rows).astype(np.int32)
+
+
+# LeNet-5 of the directcompute-nn page ("File Structure": 1->6->16 conv,
+# 256->120->84->10 FC) on 1x28x28 inputs: conv 5x5 (no padding), ReLU, max
+# pool 2x2 stride 2, twice, then three linear layers with ReLU between.
+LENET_PARAMS = (("conv1_w", (6, 1, 5, 5)), ("conv1_b", (6,)),
+                ("conv2_w", (16, 6, 5, 5)), ("conv2_b", (16,)),
+                ("fc1_w", (120, 256)), ("fc1_b", (120,)),
+                ("fc2_w", (84, 120)), ("fc2_b", (84,)),
+                ("fc3_w", (10, 84)), ("fc3_b", (10,)))
+
+
+def lenet_step_inputs(batch: int, seed: int) -> Dict[str, np.ndarray]:
+    """Seeded float32 inputs of one LeNet-5 training step.
+
+    The image and the convolution parameters are small dyadic rationals, so
+    the convolutions, ReLUs and poolings are exact in float32 and every
+    max-pool choice (ties included) is the same in any precision.  Linear
+    layers are Kaiming-normal, biases small normal.  x is a binarised digit
+    stand-in (values 0 or 1 on a 28x28 plane); labels are uniform in 0..9.
+    """
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = f32_array(("dyadic", 0, 1, 0), (batch, 1, 28, 28), (900 + seed, 0))
+    out["labels"] = labels(batch, 10, (900 + seed, 1))
+    dists = {"conv1_w": ("dyadic", -2, 2, 2), "conv1_b": ("dyadic", -1, 1, 2),
+             "conv2_w": ("dyadic", -2, 2, 4), "conv2_b": ("dyadic", -1, 1, 4),
+             "fc1_w": _kaiming(256), "fc2_w": _kaiming(120), "fc3_w": _kaiming(84)}
+    for t, (name, shape) in enumerate(LENET_PARAMS):
+        out[name] = f32_array(dists.get(name, ("normal", 0.01)), shape, (900 + seed, 2 + t))
+    return out
