@@ -41,7 +41,10 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", help="c1..c5")
+    ap.add_argument("--workload", default="c4",
+                    help="c1..c5, or lenet: one whole LeNet-5 training step (conv, ReLU, pooling, "
+                         "linear layers, softmax-CE, SGD) at --batch")
+    ap.add_argument("--batch", type=int, default=64, help="batch of the lenet workload")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -126,12 +129,138 @@ def cpu_baseline(wl, dtype: str, target_s: float) -> dict:
             "seconds": t}
 
 
+def kernel_table(stats, peak_tf):
+    """Per kernel symbol: launches, average time, share, TFLOP/s or GB/s."""
+    by_kernel = {}
+    for s in stats:
+        k = s["name"].split(":")[0]
+        a = by_kernel.setdefault(k, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        for f in ("launches", "ms", "flops", "bytes"):
+            a[f] += s[f]
+    total = max(1e-12, sum(v["ms"] for v in by_kernel.values()))
+    kernels = {}
+    for k, a in by_kernel.items():
+        e = {"launches": a["launches"], "avg_us": 1e3 * a["ms"] / a["launches"], "share": a["ms"] / total}
+        if a["flops"] > 0:
+            e["TFLOPs"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
+            e["frac_mfma"] = e["TFLOPs"] / peak_tf
+        else:
+            e["GBps"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+            e["frac_hbm"] = e["GBps"] / HBM_PEAK_GBPS
+        kernels[k] = e
+    return by_kernel, kernels
+
+
+def roofline_of(by_kernel, dom, peak_tf):
+    d = by_kernel[dom]
+    if d["flops"] > 0:
+        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        return {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": achieved / peak_tf, "traffic": None,
+                "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
+    achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+    return {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
+
+
+def bench_lenet(args) -> int:
+    """Whole LeNet-5 training steps (forward, backward, SGD) at --batch, fp32."""
+    import torch
+
+    import workloads as W
+    from gemm_scratch_nn_amd.lenet import LeNetStep
+
+    B = args.batch
+    lr, clip = 0.01, 0.05
+    inp = W.lenet_step_inputs(B, 0)
+    net = LeNetStep(B)
+    net.load({n: torch.from_numpy(inp[n]).cuda() for n, _ in W.LENET_PARAMS})
+    x = torch.from_numpy(inp["x"]).cuda()
+    lab = torch.from_numpy(inp["labels"]).cuda()
+
+    def step():
+        net.step(x, lab, lr, clip)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is None:
+            step()
+        else:
+            graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    import gemm_scratch_nn_amd as d4r
+    d4r.d4r_profile_reset()
+    d4r.d4r_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    d4r.d4r_profile_enable(False)
+    by_kernel, kernels = kernel_table(d4r.d4r_profile_read(), MFMA_PEAK["f32"])
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
+    ms = elapsed * 1e3 / args.steps
+    busy_ms = sum(v["ms"] for v in by_kernel.values()) / args.steps
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        if not os.path.exists(oracle.LIB_PATH):
+            oracle.build()
+        n, t = 0, 0.0
+        while t < args.cpu_seconds and n < 1000:
+            t1 = time.perf_counter()
+            oracle.lenet_step(inp, lr, clip)
+            t += time.perf_counter() - t1
+            n += 1
+        cpu = {"value": n * B / t, "unit": "images/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{n} whole LeNet-5 steps at batch {B} (float64); {t:.2f} s"}
+    line = {
+        "metric": "LeNet-5 training throughput (images/s): forward, backward and SGD update",
+        "value": B / (ms * 1e-3),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded dyadic images and conv weights, Kaiming linear weights, uniform labels)",
+        "config": {"workload": f"LeNet-5 1x28x28: conv 5x5 1->6, pool 2, conv 5x5 6->16, pool 2, "
+                               f"linear 256->120->84->10, softmax-CE, SGD lr {lr} clip {clip}",
+                   "batch": B, "hip_graph": bool(args.graph)},
+        "kernel_busy_ms_per_step": busy_ms,
+        "launches_per_step": sum(v["launches"] for v in by_kernel.values()) / args.steps,
+        "roofline": roofline_of(by_kernel, dom, MFMA_PEAK["f32"]),
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
               "multi-GPU batch sharding is a design note only", file=sys.stderr)
         return 2
+
+    if args.workload == "lenet":
+        return bench_lenet(args)
 
     import torch
 
@@ -230,35 +359,10 @@ def main() -> int:
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     # per kernel symbol (the part before ':' is one template instantiation)
-    by_kernel = {}
-    for s in stats:
-        k = s["name"].split(":")[0]
-        a = by_kernel.setdefault(k, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-        for f in ("launches", "ms", "flops", "bytes"):
-            a[f] += s[f]
-    kernels = {}
-    for k, a in by_kernel.items():
-        e = {"launches": a["launches"], "avg_us": 1e3 * a["ms"] / a["launches"],
-             "share": a["ms"] / max(1e-12, sum(v["ms"] for v in by_kernel.values()))}
-        if a["flops"] > 0:
-            e["TFLOPs"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
-            e["frac_mfma"] = e["TFLOPs"] / MFMA_PEAK[dtype]
-        else:
-            e["GBps"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
-            e["frac_hbm"] = e["GBps"] / HBM_PEAK_GBPS
-        kernels[k] = e
+    by_kernel, kernels = kernel_table(stats, MFMA_PEAK[dtype])
     dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
     d = by_kernel[dom]
-    if d["flops"] > 0:
-        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK[dtype],
-                "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK[dtype], "traffic": None,
-                "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
-    else:
-        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                "avg_launch_us": 1e3 * d["ms"] / d["launches"], "launches": d["launches"]}
+    roof = roofline_of(by_kernel, dom, MFMA_PEAK[dtype])
 
     tr = recorded_traffic(dom)
     if tr is not None:

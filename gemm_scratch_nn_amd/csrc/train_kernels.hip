@@ -137,104 +137,138 @@ __global__ __launch_bounds__(NT) void add_bias_rows_kernel(const float *x, const
         y[e] = x[e] + bias[e % cols];
 }
 
-// db[j] = sum over rows of dy[i][j].  A block owns 64 columns; its wave w
-// sums rows [w*rows/4, (w+1)*rows/4) ascending with lane = column (one
-// 256-byte row segment per load), then the four partial sums are added in
-// wave order.
-__global__ __launch_bounds__(NT) void bias_grad_rows_kernel(const float *__restrict__ dy,
-                                                            float *__restrict__ db, long long rows, int cols)
+// db[j] = sum over rows of dy[i][j].  A block of kBgWaves wavefronts owns
+// 64 columns; wave w sums the rows [w*rows/kBgWaves, (w+1)*rows/kBgWaves)
+// ascending with lane = column (one 256-byte row segment per load, eight
+// loads in flight), then the partial sums are added in wave order.
+constexpr int kBgWaves = 16;
+
+__global__ __launch_bounds__(kBgWaves * 64) void bias_grad_rows_kernel(const float *__restrict__ dy,
+                                                                       float *__restrict__ db, long long rows,
+                                                                       int cols)
 {
-    __shared__ float part[NT / 64][64];
+    __shared__ float part[kBgWaves][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int j = blockIdx.x * 64 + lane;
-    const long long r0 = rows * wv / (NT / 64), r1 = rows * (wv + 1) / (NT / 64);
+    const long long r0 = rows * wv / kBgWaves, r1 = rows * (wv + 1) / kBgWaves;
     float acc = 0.0f;
-    if (j < cols)
-        for (long long i = r0; i < r1; ++i)
-            acc += dy[i * cols + j];
+    if (j < cols) {
+        const float *col = dy + j;
+        long long i = r0;
+        for (; i + 8 <= r1; i += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = col[(i + u) * cols];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                acc += v[u];
+        }
+        for (; i < r1; ++i)
+            acc += col[i * cols];
+    }
     part[wv][lane] = acc;
     __syncthreads();
     if (wv == 0 && j < cols) {
         float t = part[0][lane];
 #pragma unroll
-        for (int w = 1; w < NT / 64; ++w)
+        for (int w = 1; w < kBgWaves; ++w)
             t += part[w][lane];
         db[j] = t;
     }
 }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Butterfly sum / max over aligned groups of G lanes (G a power of two <= 64)
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int off = G / 2; off >= 1; off >>= 1)
         v += __shfl_xor(v, off, 64);
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v)
+template <int G>
+__device__ __forceinline__ float group_max(float v)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int off = G / 2; off >= 1; off >>= 1)
         v = fmaxf(v, __shfl_xor(v, off, 64));
     return v;
 }
 
 constexpr int kSmWaves = 16;  // waves per softmax block
 
-// Row softmax, one wave per row (lanes stride over the classes; max and sum
-// by fixed butterfly trees, the row maximum subtracted before exp).
+// Row softmax by groups of G lanes (G = the class count rounded up to a
+// power of two, at most 64; lanes stride over the classes), 64/G rows per
+// wavefront at a time; max and sum by fixed butterfly trees, the row
+// maximum subtracted before exp.
 //   label == NULL: out = softmax(z)
 //   label != NULL: out = softmax(z) - one_hot(label), and when loss != NULL
 //                  *loss = mean over rows of log(sum) + max - z[label]
-// With a loss the launch is one block: lane 0 of each wave adds its rows'
-// losses in row order, then thread 0 adds the waves' sums in wave order, so
-// the loss is run-to-run deterministic.  A label outside [0, classes) makes
-// that row of out and the loss NaN.  out must not overlap z.
+// With a loss the launch is one block: the first lane of each group adds its
+// rows' losses in row order, the groups of a wave are added by a fixed
+// tree, then thread 0 adds the waves' sums in wave order, so the loss is
+// run-to-run deterministic.  A label outside [0, classes) makes that row of
+// out and the loss NaN.  out must not overlap z.
+template <int G>
 __global__ __launch_bounds__(kSmWaves * 64) void softmax_rows_kernel(const float *__restrict__ z,
                                                                      const int32_t *__restrict__ label,
                                                                      float *__restrict__ out,
                                                                      float *__restrict__ loss, int rows,
                                                                      int classes)
 {
+    constexpr int RPW = 64 / G;  // rows per wavefront pass
     __shared__ float red[kSmWaves];
     const int lane = threadIdx.x & 63;
+    const int gl = lane % G;  // lane within the group
     const int wave = blockIdx.x * kSmWaves + (threadIdx.x >> 6);
-    const int nwaves = gridDim.x * kSmWaves;
+    const int nrows = gridDim.x * kSmWaves * RPW;
     float lsum = 0.0f;
-    for (int r = wave; r < rows; r += nwaves) {
-        const float *zr = z + (long long)r * classes;
-        float *orow = out + (long long)r * classes;
+    for (int r0 = wave * RPW; r0 < rows; r0 += nrows) {
+        const int r = r0 + lane / G;
+        const bool live = r < rows;  // uniform within a group
+        const int rr = live ? r : r0;
+        const float *zr = z + (long long)rr * classes;
+        float *orow = out + (long long)rr * classes;
         float m = -__builtin_inff();
-        for (int j = lane; j < classes; j += 64)
+        for (int j = gl; j < classes; j += G)
             m = fmaxf(m, zr[j]);
-        m = wave_max(m);
+        m = group_max<G>(m);
         float sum = 0.0f;
-        for (int j = lane; j < classes; j += 64)
+        for (int j = gl; j < classes; j += G)
             sum += expf(zr[j] - m);
-        sum = wave_sum(sum);
+        sum = group_sum<G>(sum);
+        if (!live)
+            continue;
         const float inv = 1.0f / sum;
         if (!label) {
-            for (int j = lane; j < classes; j += 64)
+            for (int j = gl; j < classes; j += G)
                 orow[j] = expf(zr[j] - m) * inv;
             continue;
         }
         const int lab = label[r];
         const bool ok = lab >= 0 && lab < classes;
-        for (int j = lane; j < classes; j += 64)
+        for (int j = gl; j < classes; j += G)
             orow[j] = ok ? expf(zr[j] - m) * inv - (j == lab ? 1.0f : 0.0f) : __builtin_nanf("");
         const float zl = zr[ok ? lab : 0];  // never read outside the row
         lsum += ok ? logf(sum) + m - zl : __builtin_nanf("");
     }
     if (!loss)
         return;
+    // the group leaders hold the row sums; add the wave's groups in order
+    float w = 0.0f;
+#pragma unroll
+    for (int g = 0; g < RPW; ++g)
+        w += __shfl(lsum, g * G, 64);
     if (lane == 0)
-        red[threadIdx.x >> 6] = lsum;
+        red[threadIdx.x >> 6] = w;
     __syncthreads();
     if (threadIdx.x == 0) {
         float t = red[0];
 #pragma unroll
-        for (int w = 1; w < kSmWaves; ++w)
-            t += red[w];
+        for (int v = 1; v < kSmWaves; ++v)
+            t += red[v];
         *loss = t / (float)rows;
     }
 }
@@ -322,18 +356,40 @@ hipError_t launch_add_bias_rows(const float *x, const float *bias, float *y, lon
 
 hipError_t launch_bias_grad_rows(const float *dy, float *db, long long rows, int cols, hipStream_t s)
 {
-    hipLaunchKernelGGL(bias_grad_rows_kernel, dim3((cols + 63) / 64), dim3(NT), 0, s, dy, db, rows, cols);
+    hipLaunchKernelGGL(bias_grad_rows_kernel, dim3((cols + 63) / 64), dim3(kBgWaves * 64), 0, s, dy, db, rows,
+                       cols);
+    return hipGetLastError();
+}
+
+template <int G>
+static hipError_t softmax_launch(const float *z, const int32_t *label, float *out, float *loss, int rows,
+                                 int classes, hipStream_t s)
+{
+    // with a loss: one block (fixed-order mean); else enough blocks for one
+    // pass over the rows
+    const int per_block = kSmWaves * (64 / G);
+    const int blocks = loss ? 1 : std::min((rows + per_block - 1) / per_block, 65535);
+    hipLaunchKernelGGL(softmax_rows_kernel<G>, dim3(blocks), dim3(kSmWaves * 64), 0, s, z, label, out, loss,
+                       rows, classes);
     return hipGetLastError();
 }
 
 hipError_t launch_softmax_rows(const float *z, const int32_t *label, float *out, float *loss, int rows,
                                int classes, hipStream_t s)
 {
-    // with a loss: one block (fixed-order mean); else one wave per row
-    const int blocks = loss ? 1 : std::min((rows + kSmWaves - 1) / kSmWaves, 65535);
-    hipLaunchKernelGGL(softmax_rows_kernel, dim3(blocks), dim3(kSmWaves * 64), 0, s, z, label, out, loss, rows,
-                       classes);
-    return hipGetLastError();
+    if (classes <= 1)
+        return softmax_launch<1>(z, label, out, loss, rows, classes, s);
+    if (classes <= 2)
+        return softmax_launch<2>(z, label, out, loss, rows, classes, s);
+    if (classes <= 4)
+        return softmax_launch<4>(z, label, out, loss, rows, classes, s);
+    if (classes <= 8)
+        return softmax_launch<8>(z, label, out, loss, rows, classes, s);
+    if (classes <= 16)
+        return softmax_launch<16>(z, label, out, loss, rows, classes, s);
+    if (classes <= 32)
+        return softmax_launch<32>(z, label, out, loss, rows, classes, s);
+    return softmax_launch<64>(z, label, out, loss, rows, classes, s);
 }
 
 hipError_t launch_sgd(float *p, const float *g, long long n, float lr, float clip, hipStream_t s)
