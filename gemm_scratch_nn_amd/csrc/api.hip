@@ -137,6 +137,12 @@ GemmPlan plan_gemm(int M, int N, int K, int dt)
         cands[nc++] = {TILE_128x128, 0.85};
         cands[nc++] = {TILE_128x256, 1.0};
         cands[nc++] = {TILE_256x128, 1.0};
+        // small products (a 1x1 layer on the 46x80 map): when the large
+        // tiles leave most CUs idle, 64x64 tiles at three per CU hide the
+        // load latency better than split-K (measured 12 against 22 us)
+        const long long tbig = (long long)((M + 127) / 128) * ((N + 255) / 256);
+        if (tbig < kComputeUnits)
+            cands[nc++] = {TILE_64x64, 0.5};
         if (M % 128 != 0 && M % 96 == 0 && M <= 192)
             cands[nc++] = {TILE_96x128, 0.8};
     }
@@ -263,7 +269,7 @@ std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
 {
     TileShape ts = tile_shape(cfg);
     const char a = amode == OP_KC ? 'k' : (amode == OP_NCHW ? 'g' : 'm');
-    const char b = (bmode == OP_KC) ? 'k' : (bmode == OP_NCHW ? 'g' : 'n');
+    const char b = (bmode == OP_KC) ? 'k' : (bmode == OP_NCHW ? 'g' : (bmode == OP_NCHW_K ? 'c' : 'n'));
     return std::string("gemm_") + dt_name(dt) + "_" + std::to_string(ts.bm) + "x" + std::to_string(ts.bn) +
            "_" + a + b + (bmode == OP_IMPL ? "_implicit" : "");
 }
@@ -271,11 +277,12 @@ std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
 
 // Runs one planned GEMM (split-K partials + reduction when the plan splits).
 // Operand forms follow OperandMode; OP_IMPL (B = x, op(B) = im2col(x)) and
-// OP_NCHW (the gradient dy read in place) take their geometry from `geom`.
+// the NCHW forms take their geometry from `geom`; a_ch / b_ch are the channel
+// counts of NCHW operands (default: geom->O, the gradient dy).
 hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
                     const float *bias, int P, float *partial, hipStream_t s, const char *pass,
-                    const ConvGeom *geom = nullptr)
+                    const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0)
 {
     const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
@@ -299,6 +306,13 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
         p.g = *geom;
     else
         memset(&p.g, 0, sizeof p.g);
+    p.a_ch = a_ch ? a_ch : p.g.O;
+    p.b_ch = b_ch ? b_ch : p.g.O;
+    // an NCHW operand takes whole vectors when they cannot straddle images
+    if (amode == OP_NCHW)
+        p.a_vec = geom && geom->P % vw == 0;
+    if (bmode == OP_NCHW || bmode == OP_NCHW_K)
+        p.b_vec = geom && geom->P % vw == 0;
     if (pl.splits > 1) {
         p.C = partial;
         p.ldc = N;
@@ -350,6 +364,10 @@ struct d4r_conv {
     bool dgrad_impl;
     ConvGeom gd;
     GemmPlan bwd_data_impl;
+    // 1x1 kernel, stride 1, no padding: col is x with the batch folded into
+    // its columns, so the GEMMs can read x and dy in place (no im2col, no
+    // dcol, no col2im)
+    bool pointwise;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -550,6 +568,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         d.P = inH * inW; d.Kc = outC * kH * kW; d.N = batch * d.P;
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
+    h->pointwise = kH == 1 && kW == 1 && stride == 1 && padding == 0;
+    if (const char *e = getenv("D4R_POINTWISE"))  // experiments, tests: 0 = im2col path
+        h->pointwise = h->pointwise && e[0] != '0';
     h->bias_splits = bias_grad_splits(g);
     // bias partials: the bias kernel's splits, or the fused reshape's blocks
     const int bias_part_cols = std::max(h->bias_splits, grad_reshape_blocks(dtype, g));
@@ -711,6 +732,13 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
     hipStream_t s = (hipStream_t)hip_stream;
     const ConvGeom &g = h->g;
     float *partial = (float *)((char *)ws + h->off_big);
+    if (h->pointwise) {
+        // 1x1: y[b] = Wmat * x[b] with x read in place (C channels)
+        D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_NCHW, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
+                            bias, g.P, partial, s, "fwd", &g, 0, g.C),
+                   "pointwise forward GEMM");
+        return ok();
+    }
     D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_IMPL, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0, bias,
                         g.P, partial, s, "fwd", &g),
                "implicit forward GEMM");
@@ -724,6 +752,13 @@ d4r_status dgrad_explicit(d4r_conv_t h, const void *w, const void *dy, float *dx
 {
     const ConvGeom &g = h->g;
     char *wsb = (char *)ws;
+    if (h->pointwise) {
+        // 1x1: dx[b] = Wmat^T * dy[b], stored NCHW by the GEMM (dcol is dx)
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_NCHW, w, g.Kc, dy, 0, g.Kc, g.N, g.O, EPI_NCHW,
+                            dx, 0, nullptr, g.P, (float *)(wsb + h->off_big), s, "dgrad", &g, 0, g.O),
+                   "pointwise data-gradient GEMM");
+        return ok();
+    }
     float *dcol = (float *)(wsb + h->off_big);
     float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
     // dcol = Wmat^T * G with A = Wmat (O x Kc) read row-contiguous as
@@ -778,7 +813,7 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     D4R_TRY(check_tensor(dx, "dx"));
     D4R_TRY(check_ws(h, ws, ws_bytes));
     hipStream_t s = (hipStream_t)hip_stream;
-    if (!h->dgrad_impl)
+    if (!h->dgrad_impl || h->pointwise)
         return dgrad_explicit(h, w, dy, dx, ws, s);
     const ConvGeom &g = h->g, &d = h->gd;
     char *wsb = (char *)ws;
@@ -818,6 +853,15 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     char *wsb = (char *)ws;
     void *col = wsb;
     float *partial = (float *)(wsb + h->off_big);
+    if (h->pointwise && !reuse_col) {
+        // 1x1: dW = sum_b dy[b] * x[b]^T with dy and x read in place
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_NCHW, OP_NCHW_K, dy, 0, x, 0, g.O, g.Kc, g.N,
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g, g.O, g.C),
+                   "pointwise filter-gradient GEMM");
+        if (db)
+            D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s), "bias gradient");
+        return ok();
+    }
     if (!reuse_col)
         D4R_LAUNCH(step_im2col(h, x, col, s, "wgrad"), "im2col");
     // dW = G * col^T: A = G (O x N), read from dy in place or reshaped;

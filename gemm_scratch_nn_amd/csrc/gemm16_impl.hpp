@@ -80,14 +80,32 @@ struct Tile16 {
         kq = kqh * 2 + b3;
     }
 
-    // VEC: the operand's leading dimension and K are multiples of 8, so every
-    // 16-byte vector is either wholly inside or wholly outside the matrix.
-    // Then each load is issued unconditionally (from offset 0 when outside)
-    // and zeroed by a select: no branches, so the compiler can count the
-    // loads in flight and wait only for the register set it stores next.
-    template <bool VEC>
+    // Element offset of (row rr, k kk).  Plain operands: rr*ld + kk
+    // (k-contiguous) or kk*ld + rr (row-contiguous).  NC (an NCHW tensor
+    // t[b][c][pix], nch channels, P pixels): the (image, pixel) index is k
+    // for a k-contiguous operand (rows = c) and the row for a row-contiguous
+    // one (k = c), at b*nch*P + c*P + pix.
+    template <bool NC>
+    __device__ __forceinline__ static long long offset(int rr, int kk, int ld, int nch, int P)
+    {
+        if constexpr (NC) {
+            const int n = KC ? kk : rr, c = KC ? rr : kk;
+            const int b = n / P;
+            return ((long long)b * nch + c) * P + (n - b * P);
+        } else {
+            return KC ? (long long)rr * ld + kk : (long long)kk * ld + rr;
+        }
+    }
+
+    // VEC: the operand's leading dimension and K are multiples of 8 (NC: P
+    // is), so every 16-byte vector is either wholly inside or wholly outside
+    // the matrix (NC: inside one image).  Then each load is issued
+    // unconditionally (from offset 0 when outside) and zeroed by a select:
+    // no branches, so the compiler can count the loads in flight and wait
+    // only for the register set it stores next.
+    template <bool VEC, bool NC = false>
     __device__ __forceinline__ void load(const uint16_t *__restrict__ X, int ld, int R, int K, int r0,
-                                         int k0, int tid)
+                                         int k0, int tid, int nch = 0, int P = 1)
     {
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
@@ -97,15 +115,15 @@ struct Tile16 {
                 const int rr = r0 + row, kk = k0 + ch * 8;
                 const bool ok = id < SLOTS && rr < R && kk < K;
                 if constexpr (VEC) {
-                    const long long off = ok ? (long long)rr * ld + kk : 0;
+                    const long long off = ok ? offset<NC>(rr, kk, ld, nch, P) : 0;
                     r[s] = *(const u32x4_t *)(X + off);
                     okmask = (s == 0 ? 0u : okmask) | ((ok ? 1u : 0u) << s);
                 } else {
                     u32x4_t v = {0u, 0u, 0u, 0u};
-                    const long long off = (long long)rr * ld + kk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        uint32_t hv = (ok && kk + e < K) ? (uint32_t)X[off + e] : 0u;
+                        const bool in = ok && kk + e < K;
+                        uint32_t hv = in ? (uint32_t)X[offset<NC>(rr, in ? kk + e : 0, ld, nch, P)] : 0u;
                         v[e >> 1] |= hv << (16 * (e & 1));
                     }
                     r[s] = v;
@@ -121,15 +139,15 @@ struct Tile16 {
                     const int kk = k0 + kq * 4 + i;
                     const bool ok = live && kk < K && rr < R;
                     if constexpr (VEC) {
-                        const long long off = ok ? (long long)kk * ld + rr : 0;
+                        const long long off = ok ? offset<NC>(rr, kk, ld, nch, P) : 0;
                         r[4 * s + i] = *(const u32x4_t *)(X + off);
                         okmask = (s == 0 && i == 0 ? 0u : okmask) | ((ok ? 1u : 0u) << (4 * s + i));
                     } else {
                         u32x4_t v = {0u, 0u, 0u, 0u};
-                        const long long off = (long long)kk * ld + rr;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            uint32_t hv = (ok && rr + e < R) ? (uint32_t)X[off + e] : 0u;
+                            const bool in = ok && rr + e < R;
+                            uint32_t hv = in ? (uint32_t)X[offset<NC>(in ? rr + e : 0, kk, ld, nch, P)] : 0u;
                             v[e >> 1] |= hv << (16 * (e & 1));
                         }
                         r[4 * s + i] = v;
@@ -324,7 +342,10 @@ __device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&
     }
 }
 
-template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL>
+// A_NC / B_NC: the operand is an NCHW tensor (OP_NCHW, or OP_NCHW_K for a
+// k-contiguous B), addressed through p.a_ch / p.b_ch and p.g.P.
+template <int DTID, int NWM, int NWN, int TM, int TN, bool A_KC, bool B_KC, bool VEC, bool IMPL,
+          bool A_NC = false, bool B_NC = false>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 {
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = 64;
@@ -368,11 +389,14 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
     ImplicitCols16<BN, NT> cols;
     if constexpr (IMPL)
         cols.setup(p.g, n_blk, tid);
+    auto load_a = [&](TA &t, int k0) {
+        t.template load<VEC, A_NC>(A, p.lda, p.M, kend, m_blk, k0, tid, p.a_ch, p.g.P);
+    };
     auto load_b = [&](TB &t, int k0) {
         if constexpr (IMPL)
             t.gather(B, p.g, cols, kend, k0, tid);
         else
-            t.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
+            t.template load<VEC, B_NC>(B, p.ldb, p.N, kend, n_blk, k0, tid, p.b_ch, p.g.P);
     };
 
     auto compute = [&](const char *la, const char *lb) {
@@ -395,14 +419,14 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 
     if (nk > 0) {
         // prologue: stages 0 and 1 in flight, stage 0 into LDS buffer 0
-        ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg, tid);
+        load_a(ta0, kbeg);
         load_b(tb0, kbeg);
-        ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + BK, tid);
+        load_a(ta1, kbeg + BK);
         load_b(tb1, kbeg + BK);
         ta0.template store<VEC>(smem, tid);
         tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
         __syncthreads();
-        ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + 2 * BK, tid);
+        load_a(ta0, kbeg + 2 * BK);
         load_b(tb0, kbeg + 2 * BK);
         // Stage t is computed from LDS buffer t&1.  Register set (t+1)&1 holds
         // stage t+1 and is stored into LDS buffer (t+1)&1 after the compute;
@@ -418,14 +442,14 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
             ta1.template store<VEC>(smem + STAGE, tid);
             tb1.template store<VEC>(smem + STAGE + TA::LDS_BYTES, tid);
             __syncthreads();
-            ta1.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 3) * BK, tid);
+            load_a(ta1, kbeg + (t + 3) * BK);
             load_b(tb1, kbeg + (t + 3) * BK);
             __builtin_amdgcn_sched_barrier(0);
             compute(smem + STAGE, smem + STAGE + TA::LDS_BYTES);
             ta0.template store<VEC>(smem, tid);
             tb0.template store<VEC>(smem + TA::LDS_BYTES, tid);
             __syncthreads();
-            ta0.template load<VEC>(A, p.lda, p.M, kend, m_blk, kbeg + (t + 4) * BK, tid);
+            load_a(ta0, kbeg + (t + 4) * BK);
             load_b(tb0, kbeg + (t + 4) * BK);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -620,7 +644,7 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int DTID, bool A_KC, bool B_KC, bool VEC, bool IMPL = false>
+template <int DTID, bool A_KC, bool B_KC, bool VEC, bool IMPL = false, bool A_NC = false, bool B_NC = false>
 hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -628,24 +652,30 @@ hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
     const dim3 grid(tiles, 1, p.splits), b4(256), b8(512);
     switch (cfg) {
     case TILE_128x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b4, 0, s,
+                           p);
         break;
     case TILE_64x64:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 1, 1, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b4, 0, s,
+                           p);
         break;
     case TILE_32x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 1, 1, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b4, 0, s,
+                           p);
         break;
     case TILE_96x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC, IMPL>), grid, b4, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 1, 4, 3, 1, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b4, 0, s,
+                           p);
         break;
     // the large tiles run eight wavefronts, two per SIMD, so one wave's
     // waits are covered by the other's MFMAs
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 4, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 4, 2, 2, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b8, 0, s,
+                           p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_kernel<DTID, 4, 2, 2, 2, A_KC, B_KC, VEC, IMPL>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_kernel<DTID, 4, 2, 2, 2, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b8, 0, s,
+                           p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -653,16 +683,18 @@ hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int DTID, bool A_KC, bool B_KC>
+template <int DTID, bool A_KC, bool B_KC, bool A_NC = false, bool B_NC = false>
 hipError_t launch_gemm16_layout(int cfg, const GemmParams &p, hipStream_t s)
 {
     if (p.a_vec && p.b_vec)
-        return launch_gemm16_vec<DTID, A_KC, B_KC, true>(cfg, p, s);
-    return launch_gemm16_vec<DTID, A_KC, B_KC, false>(cfg, p, s);
+        return launch_gemm16_vec<DTID, A_KC, B_KC, true, false, A_NC, B_NC>(cfg, p, s);
+    return launch_gemm16_vec<DTID, A_KC, B_KC, false, false, A_NC, B_NC>(cfg, p, s);
 }
 
-// Supported (A, B) modes: every pair of OP_ROWS / OP_KC, and (OP_KC,
-// OP_IMPL) for the implicit forward (VEC then covers A only).
+// Supported (A, B) modes: every pair of OP_ROWS / OP_KC, (OP_KC, OP_IMPL)
+// for the implicit forward (VEC then covers A only), and the NCHW pairs of
+// a 1x1 stride-1 unpadded convolution: (OP_KC, OP_NCHW) forward, (OP_ROWS,
+// OP_NCHW) data gradient, (OP_NCHW, OP_NCHW_K) filter gradient.
 template <int DTID>
 hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
@@ -671,6 +703,12 @@ hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hip
             return launch_gemm16_vec<DTID, true, false, true, true>(cfg, p, s);
         return launch_gemm16_vec<DTID, true, false, false, true>(cfg, p, s);
     }
+    if (amode == OP_KC && bmode == OP_NCHW)
+        return launch_gemm16_layout<DTID, true, false, false, true>(cfg, p, s);
+    if (amode == OP_ROWS && bmode == OP_NCHW)
+        return launch_gemm16_layout<DTID, false, false, false, true>(cfg, p, s);
+    if (amode == OP_NCHW && bmode == OP_NCHW_K)
+        return launch_gemm16_layout<DTID, true, true, true, true>(cfg, p, s);
     const bool a_ok = amode == OP_ROWS || amode == OP_KC;
     const bool b_ok = bmode == OP_ROWS || bmode == OP_KC;
     if (!a_ok || !b_ok)

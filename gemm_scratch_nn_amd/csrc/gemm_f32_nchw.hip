@@ -1,7 +1,8 @@
 // Instantiation of the gfx950 MFMA GEMM for f32 operands whose A or B is an
-// NCHW gradient read in place: the data-gradient product (A = Wmat read
+// NCHW tensor read in place: the data-gradient product (A = Wmat read
 // row-contiguous, B = dy) and the filter-gradient product (A = dy, B = col
-// read k-contiguous).
+// read k-contiguous), and for 1x1 stride-1 unpadded convolutions the forward
+// (A = Wmat, B = x) and the filter gradient (A = dy, B = x).
 #include "gemm_impl.hpp"
 
 namespace d4r {
@@ -12,6 +13,10 @@ hipError_t launch_gemm_f32_nchw(int cfg, int amode, int bmode, const GemmParams 
         return launch_gemm32_modes<OP_ROWS, OP_NCHW>(cfg, p, s);
     if (amode == OP_NCHW && bmode == OP_KC)
         return launch_gemm32_modes<OP_NCHW, OP_KC>(cfg, p, s);
+    if (amode == OP_KC && bmode == OP_NCHW)
+        return launch_gemm32_modes<OP_KC, OP_NCHW>(cfg, p, s);
+    if (amode == OP_NCHW && bmode == OP_NCHW_K)
+        return launch_gemm32_modes<OP_NCHW, OP_NCHW_K>(cfg, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -213,9 +213,10 @@ struct ImplicitTileF32 {
     }
 };
 
-// A operand read straight from an NCHW gradient dy[b][o][pix]: row m = o,
-// k = b*P + pix, so op(A)[m][k] = dy[(k / P)*O*P + m*P + k % P].  Kept in LDS
-// as [m][k] like a k-contiguous operand.  The 32 lanes of a half-wave take
+// Operand read straight from an NCHW tensor t[b][c][pix] (ch channels) with
+// row r = c and k = b*P + pix, so op[r][k] = t[(k / P)*ch*P + r*P + k % P]:
+// A = dy of the filter gradient, or B = x of a 1x1 filter gradient.  Kept in
+// LDS as [r][k] like a k-contiguous operand.  The 32 lanes of a half-wave take
 // 32 consecutive k of one row (pixel runs, split at most once per image
 // boundary), so each load instruction reads whole 128-byte runs; a thread
 // decodes its k once per stage.  Loads are unconditional (offset 0 when
@@ -231,12 +232,12 @@ struct NchwKTile {
     uint32_t reg[PER];
     uint32_t okmask;
 
-    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g, int R, int K,
-                                         int r0, int k0, int tid)
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g, int ch, int R,
+                                         int K, int r0, int k0, int tid)
     {
         const int k = k0 + tid % BK;
         const int b = k / g.P;
-        const long long base = (long long)b * g.O * g.P + (k - b * g.P);
+        const long long base = (long long)b * ch * g.P + (k - b * g.P);
         const bool kok = k < K;
         okmask = 0u;
 #pragma unroll
@@ -258,20 +259,21 @@ struct NchwKTile {
     }
 };
 
-// B operand read straight from an NCHW gradient dy[b][o][pix]: k = o,
-// column n = b*P + pix, so op(B)[k][n] = dy[(n / P)*O*P + k*P + n % P].  Kept
-// in LDS as [k][n] like a row-contiguous operand.  Each thread owns one
+// B operand read straight from an NCHW tensor t[b][c][pix] (ch channels):
+// k = c, column n = b*P + pix, so op(B)[k][n] = t[(n / P)*ch*P + k*P + n % P]
+// (dy of the data gradient, or x of a 1x1 forward).  Kept in LDS as [k][n]
+// like a row-contiguous operand.  Each thread owns one
 // column for the whole K loop (decoded once, in NchwCol); consecutive lanes
 // take consecutive columns, so a load instruction reads pixel runs.
 struct NchwCol {
     long long off;  // element offset of (b, o = 0, pix)
     bool ok;        // n < N
 
-    __device__ __forceinline__ void setup(const ConvGeom &g, int n)
+    __device__ __forceinline__ void setup(const ConvGeom &g, int ch, int n)
     {
         ok = n < g.N;
         const int b = n / g.P;
-        off = (long long)b * g.O * g.P + (n - b * g.P);
+        off = (long long)b * ch * g.P + (n - b * g.P);
     }
 };
 
@@ -365,11 +367,12 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     // LDS layouts: [m][k] unless A is row-contiguous; [n][k] only for a
     // k-contiguous B
     constexpr bool A_KC = AMODE != OP_ROWS;
-    constexpr bool B_KC = BMODE == OP_KC;
+    constexpr bool B_KC = BMODE == OP_KC || BMODE == OP_NCHW_K;
     using TA = std::conditional_t<AMODE == OP_NCHW, NchwKTile<BM, NT>, OperandTile<BM, A_KC, NT>>;
     using TB = std::conditional_t<
         BMODE == OP_IMPL, ImplicitTileF32<BN, NT>,
-        std::conditional_t<BMODE == OP_NCHW, NchwNTile<BN, NT>, OperandTile<BN, B_KC, NT>>>;
+        std::conditional_t<BMODE == OP_NCHW, NchwNTile<BN, NT>,
+                           std::conditional_t<BMODE == OP_NCHW_K, NchwKTile<BN, NT>, OperandTile<BN, B_KC, NT>>>>;
     constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -405,17 +408,19 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
         cols.setup(p.g, n_blk, tid);
     NchwCol ncol;
     if constexpr (BMODE == OP_NCHW)
-        ncol.setup(p.g, n_blk + tid % BN);
+        ncol.setup(p.g, p.b_ch, n_blk + tid % BN);
     // K bound for this split: the loaders zero-fill k >= kend.
     auto load = [&](TA &a, TB &b, int k0) {
         if constexpr (AMODE == OP_NCHW)
-            a.load(A, p.g, p.M, kend, m_blk, k0, tid);
+            a.load(A, p.g, p.a_ch, p.M, kend, m_blk, k0, tid);
         else
             a.template load<VEC>(A, p.lda, p.M, kend, m_blk, k0, tid);
         if constexpr (BMODE == OP_IMPL)
             b.gather(B, p.g, cols, kend, k0, tid);
         else if constexpr (BMODE == OP_NCHW)
             b.load(B, p.g, ncol, kend, k0, tid);
+        else if constexpr (BMODE == OP_NCHW_K)
+            b.load(B, p.g, p.b_ch, p.N, kend, n_blk, k0, tid);
         else
             b.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
     };

@@ -73,10 +73,16 @@ enum OperandMode : int {
     OP_ROWS = 0,  // row index contiguous: A[k*lda + m], B[k*ldb + n]
     OP_KC = 1,    // k contiguous: A[m*lda + k], B[n*ldb + k]
     OP_IMPL = 2,  // B only: op(B) = im2col(x), gathered from x (geometry p.g)
-    OP_NCHW = 3   // an NCHW gradient dy[b][o][pix] (geometry p.g) whose
-                  // (image, pixel) pair n = b*P + pix is the k index of A
-                  // (A[o][n]) or the column index of B (B[o][n]); o is the row
-                  // of A or the k of B.  Element address b*O*P + o*P + pix.
+    OP_NCHW = 3,  // an NCHW tensor t[b][c][pix] with ch channels (p.a_ch /
+                  // p.b_ch) and P = p.g.P pixels, whose (image, pixel) pair
+                  // n = b*P + pix is the k index of A (A[c][n]) or the
+                  // column index of B (B[c][n]); c is the row of A or the k
+                  // of B.  Element address b*ch*P + c*P + pix.  (dy read in
+                  // place; x or dy of a 1x1 stride-1 unpadded convolution.)
+    OP_NCHW_K = 4 // B only: an NCHW tensor whose channel c is the row n of
+                  // B and whose (image, pixel) pair is the k index:
+                  // op(B)[k][c] = t[k / P][c][k % P] (x in the filter
+                  // gradient of a 1x1 stride-1 unpadded convolution)
 };
 
 // C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
@@ -92,12 +98,15 @@ struct GemmParams {
     int k_per_split;    // multiple of the tile's K depth
     int splits;
     long long c_split_stride;
-    int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned)
+    int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned;
+                        // NCHW operands: P a multiple of the vector width)
+    int a_ch, b_ch;     // channel counts of OP_NCHW / OP_NCHW_K operands
     ConvGeom g;         // OP_IMPL and OP_NCHW operands
 };
 
 // Supported (A, B) modes: every pair of OP_ROWS / OP_KC, (OP_KC, OP_IMPL),
-// and for f32 also (OP_ROWS, OP_NCHW) and (OP_NCHW, OP_KC).  Others return
+// (OP_KC, OP_NCHW), (OP_ROWS, OP_NCHW), (OP_NCHW, OP_NCHW_K), and for f32
+// also (OP_NCHW, OP_KC).  Others return
 // hipErrorInvalidValue.
 hipError_t launch_gemm(int dt, int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s);
 int gemm_bk(int dt);  // K depth of one LDS stage, in elements

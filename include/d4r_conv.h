@@ -119,6 +119,22 @@ d4r_status d4r_conv_output_dims(d4r_conv_t h, int *outH, int *outW);
 d4r_status d4r_conv_workspace_size(d4r_conv_t h, size_t *bytes);
 
 /*
+ * 1x1 convolutions.  When kH = kW = 1, stride = 1 and padding = 0, col is x
+ * itself with the batch folded into its columns, so three calls read x and
+ * dy in place instead of going through col (the mlvc.cpp design page runs
+ * dense pointwise convolution as a direct matrix-core GEMM, "Driver-only
+ * AOT cubin direction"):
+ *   d4r_conv_forward_implicit          y[b] = Wmat * x[b] + bias
+ *   d4r_conv_backward_data(_implicit)  dx[b] = Wmat^T * dy[b], stored NCHW
+ *                                      by the GEMM (no dcol, no col2im)
+ *   d4r_conv_backward_filter, reuse_col = 0
+ *                                      dw = sum_b dy[b] * x[b]^T (no im2col;
+ *                                      the col region of ws is untouched)
+ * d4r_conv_forward still writes col (for reuse_col = 1).  Results equal the
+ * general path up to summation order.
+ */
+
+/*
  * Forward (page: im2col -> matmul flags 0 -> conv_reshape with bias):
  * y = conv(x; w) + bias.  x, w in the handle's dtype; bias float32 or NULL
  * (no bias); y float32.  Leaves col at the start of ws.
