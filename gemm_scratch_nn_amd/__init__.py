@@ -360,8 +360,11 @@ class ConvPlan:
     def __del__(self):
         h = getattr(self, "h", None)
         if h:
-            d4r_conv_destroy(h)
             self.h = None
+            try:
+                d4r_conv_destroy(h)
+            except Exception:  # interpreter shutdown: the binding may be gone
+                pass
 
     @property
     def x_shape(self):
