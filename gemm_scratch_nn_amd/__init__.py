@@ -78,6 +78,10 @@ _c = {
     "d4r_conv_backward_data": _sig("d4r_conv_backward_data", [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_data_implicit": _sig("d4r_conv_backward_data_implicit",
                                             [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_conv_packed_filter_size": _sig("d4r_conv_packed_filter_size", [_vp, ctypes.POINTER(_sz)]),
+    "d4r_conv_pack_filter": _sig("d4r_conv_pack_filter", [_vp, _vp, _vp, _vp]),
+    "d4r_conv_backward_data_packed": _sig("d4r_conv_backward_data_packed",
+                                          [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_filter": _sig("d4r_conv_backward_filter",
                                      [_vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "d4r_conv_im2col": _sig("d4r_conv_im2col", [_vp, _vp, _vp, _vp]),
@@ -222,6 +226,22 @@ def d4r_conv_backward_data_implicit(h, w, dy, dx, ws, ws_bytes=None, stream=None
     _check("d4r_conv_backward_data_implicit",
            _c["d4r_conv_backward_data_implicit"](h, _ptr(w), _ptr(dy), _ptr(dx), _ptr(ws), nb,
                                                  _stream(stream)))
+
+
+def d4r_conv_packed_filter_size(h) -> int:
+    n = _sz()
+    _check("d4r_conv_packed_filter_size", _c["d4r_conv_packed_filter_size"](h, ctypes.byref(n)))
+    return n.value
+
+
+def d4r_conv_pack_filter(h, w, wp, stream=None) -> None:
+    _check("d4r_conv_pack_filter", _c["d4r_conv_pack_filter"](h, _ptr(w), _ptr(wp), _stream(stream)))
+
+
+def d4r_conv_backward_data_packed(h, wp, dy, dx, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_conv_backward_data_packed",
+           _c["d4r_conv_backward_data_packed"](h, _ptr(wp), _ptr(dy), _ptr(dx), _ptr(ws), nb, _stream(stream)))
 
 
 def d4r_conv_backward_filter(h, x, dy, dw, db, reuse_col, ws, ws_bytes=None, stream=None) -> None:
@@ -425,6 +445,24 @@ class ConvPlan:
         if dx is None:
             dx = torch.empty(self.x_shape, dtype=torch.float32, device=dy.device)
         d4r_conv_backward_data_implicit(self.h, w, dy, dx, self.ws, self.ws_bytes)
+        return dx
+
+    def pack_filter(self, w, wp=None):
+        """The data gradient's packed filter (Kc x O) for backward_data_packed."""
+        import torch
+        _require(w, "w", self.dtype, self.w_shape)
+        if wp is None:
+            wp = torch.empty((self.Kc, self.shape[8]), dtype=w.dtype, device=w.device)
+        d4r_conv_pack_filter(self.h, w, wp)
+        return wp
+
+    def backward_data_packed(self, wp, dy, dx=None):
+        import torch
+        _require(wp, "wp", self.dtype, (self.Kc, self.shape[8]))
+        _require(dy, "dy", self.dtype, self.y_shape)
+        if dx is None:
+            dx = torch.empty(self.x_shape, dtype=torch.float32, device=dy.device)
+        d4r_conv_backward_data_packed(self.h, wp, dy, dx, self.ws, self.ws_bytes)
         return dx
 
     def backward_filter(self, x, dy, reuse_col=False, want_bias=True, dw=None, db=None):

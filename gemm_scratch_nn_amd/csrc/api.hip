@@ -747,41 +747,47 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
 
 namespace {
 
-// dx = col2im(Wmat^T * G): the page's data gradient
-d4r_status dgrad_explicit(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws, hipStream_t s)
+// dx = col2im(Wmat^T * G): the page's data gradient.  wt, when given, is
+// the caller's packed filter Wt[kc][o] = W[o][kc] (d4r_conv_pack_filter),
+// read k-contiguous; otherwise W is read row-contiguous or transposed here.
+d4r_status dgrad_explicit(d4r_conv_t h, const void *w, const void *wt_packed, const void *dy, float *dx,
+                          void *ws, hipStream_t s)
 {
     const ConvGeom &g = h->g;
     char *wsb = (char *)ws;
+    const void *a = wt_packed ? wt_packed : w;
+    const int amode = wt_packed ? OP_KC : OP_ROWS;
+    const int lda = wt_packed ? g.O : g.Kc;
     if (h->pointwise) {
         // 1x1: dx[b] = Wmat^T * dy[b], stored NCHW by the GEMM (dcol is dx)
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_NCHW, w, g.Kc, dy, 0, g.Kc, g.N, g.O, EPI_NCHW,
-                            dx, 0, nullptr, g.P, (float *)(wsb + h->off_big), s, "dgrad", &g, 0, g.O),
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, amode, OP_NCHW, a, lda, dy, 0, g.Kc, g.N, g.O, EPI_NCHW, dx, 0,
+                            nullptr, g.P, (float *)(wsb + h->off_big), s, "dgrad", &g, 0, g.O),
                    "pointwise data-gradient GEMM");
         return ok();
     }
     float *dcol = (float *)(wsb + h->off_big);
     float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
     // dcol = Wmat^T * G with A = Wmat (O x Kc) read row-contiguous as
-    // op(A) = Wmat^T and B = G (O x N) read from dy in place or from its
-    // transpose Gt[b*P + pix][o] = dy[b][o][pix]
+    // op(A) = Wmat^T (or its packed transpose) and B = G (O x N) read from
+    // dy in place or from its transpose Gt[b*P + pix][o] = dy[b][o][pix]
     if (h->dgrad == GP_INPLACE) {
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, OP_ROWS, OP_NCHW, w, g.Kc, dy, 0, g.Kc, g.N, g.O,
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, amode, OP_NCHW, a, lda, dy, 0, g.Kc, g.N, g.O,
                             EPI_ROWMAJOR, dcol, g.N, nullptr, 0, partial, s, "dgrad", &g),
                    "data-gradient GEMM");
     } else {
         void *gt = wsb + h->off_g;
         D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad transpose");
-        const void *a = w;
-        int amode = OP_ROWS, lda = g.Kc;
-        if (h->dgrad_wt) {
+        const void *aa = a;
+        int am = amode, ld = lda;
+        if (!wt_packed && h->dgrad_wt) {
             // Wt[kc][o] = W[o][kc]
             void *wt = wsb + h->off_wt;
             D4R_LAUNCH(step_transpose(h, 1, g.O, g.Kc, w, wt, s, "dgrad_w"), "filter transpose");
-            a = wt;
-            amode = OP_KC;
-            lda = g.O;
+            aa = wt;
+            am = OP_KC;
+            ld = g.O;
         }
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, amode, OP_KC, a, lda, gt, g.O, g.Kc, g.N, g.O,
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, am, OP_KC, aa, ld, gt, g.O, g.Kc, g.N, g.O,
                             EPI_ROWMAJOR, dcol, g.N, nullptr, 0, partial, s, "dgrad"),
                    "data-gradient GEMM");
     }
@@ -800,7 +806,42 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, f
     D4R_TRY(check_tensor(dy, "dy"));
     D4R_TRY(check_tensor(dx, "dx"));
     D4R_TRY(check_ws(h, ws, ws_bytes));
-    return dgrad_explicit(h, w, dy, dx, ws, (hipStream_t)hip_stream);
+    return dgrad_explicit(h, w, nullptr, dy, dx, ws, (hipStream_t)hip_stream);
+}
+
+d4r_status d4r_conv_packed_filter_size(d4r_conv_t h, size_t *bytes)
+{
+    if (!h || !bytes)
+        return fail(D4R_ERR_INVALID_ARG, "NULL argument");
+    *bytes = (size_t)h->g.O * h->g.Kc * h->es;
+    return ok();
+}
+
+d4r_status d4r_conv_pack_filter(d4r_conv_t h, const void *w, void *wp, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(wp, "wp"));
+    const size_t bytes = (size_t)h->g.O * h->g.Kc * h->es;
+    const char *a = (const char *)w, *b = (const char *)wp;
+    if (a < b + bytes && b < a + bytes)
+        return fail(D4R_ERR_INVALID_ARG, "wp overlaps w");
+    D4R_LAUNCH(step_transpose(h, 1, h->g.O, h->g.Kc, w, wp, (hipStream_t)hip_stream, "pack_w"),
+               "filter pack");
+    return ok();
+}
+
+d4r_status d4r_conv_backward_data_packed(d4r_conv_t h, const void *wp, const void *dy, float *dx, void *ws,
+                                         size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    D4R_TRY(check_tensor(wp, "wp"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    return dgrad_explicit(h, nullptr, wp, dy, dx, ws, (hipStream_t)hip_stream);
 }
 
 d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const void *dy, float *dx,
@@ -814,7 +855,7 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     D4R_TRY(check_ws(h, ws, ws_bytes));
     hipStream_t s = (hipStream_t)hip_stream;
     if (!h->dgrad_impl || h->pointwise)
-        return dgrad_explicit(h, w, dy, dx, ws, s);
+        return dgrad_explicit(h, w, nullptr, dy, dx, ws, s);
     const ConvGeom &g = h->g, &d = h->gd;
     char *wsb = (char *)ws;
     void *wf = wsb + h->off_wflip;

@@ -182,6 +182,27 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w,
                                            size_t ws_bytes, void *hip_stream);
 
 /*
+ * Pre-packed filter for the data gradient.  The data-gradient GEMM reads
+ * Wmat^T; d4r_conv_pack_filter writes it once as wp[kc][o] = w[o][kc] (Kc x
+ * O, row-major, the handle's dtype, d4r_conv_packed_filter_size() bytes), and
+ * d4r_conv_backward_data_packed then reads wp k-contiguous instead of
+ * transposing or striding through w on every call -- for callers that run
+ * several data gradients per weight update (gradient accumulation over
+ * micro-batches).  Same result as d4r_conv_backward_data up to summation
+ * order.  (The d4r engine page packs its weights once as [K/16][N/16]
+ * [N16][K16] tiles so that its matrix-core loads become plain row loads,
+ * "The network on the native HIP layers".  Here the forward already reads
+ * w's rows as contiguous 16-byte runs, so only the transposed copy for the
+ * data gradient is worth keeping.)  wp must not overlap w; it stays valid
+ * while w is unchanged.
+ */
+d4r_status d4r_conv_packed_filter_size(d4r_conv_t h, size_t *bytes);
+d4r_status d4r_conv_pack_filter(d4r_conv_t h, const void *w, void *wp, void *hip_stream);
+d4r_status d4r_conv_backward_data_packed(d4r_conv_t h, const void *wp, const void *dy,
+                                         float *dx, void *ws, size_t ws_bytes,
+                                         void *hip_stream);
+
+/*
  * Filter and bias gradients (page: Filter gradients = grad_reshaped x
  * im2col_matrix^T, reusing the saved im2col; Bias gradients = per-channel
  * sum of grad_reshaped): dw = G * col^T (float32, OIHW), db[o] = sum over

@@ -17,6 +17,7 @@ def test_every_declared_symbol_is_exported():
                 "d4r_conv_backward_data", "d4r_conv_backward_data_implicit",
                 "d4r_conv_backward_filter", "d4r_conv_im2col", "d4r_conv_col2im",
                 "d4r_conv_bias_grad", "d4r_gemm_workspace_size", "d4r_gemm",
+                "d4r_conv_packed_filter_size", "d4r_conv_pack_filter", "d4r_conv_backward_data_packed",
                 "d4r_status_string", "d4r_last_error", "d4r_profile_enable",
                 "d4r_profile_reset", "d4r_profile_read", "d4r_relu_forward", "d4r_relu_backward",
                 "d4r_maxpool_forward", "d4r_maxpool_backward", "d4r_add_bias_rows",
@@ -280,3 +281,19 @@ def test_training_step_empty_calls_enqueue_nothing():
         d4r.d4r_maxpool_forward(None, None, None, 0, 3, 8, 8, 9, 2, stream=0)
     with pytest.raises(D4RError):
         d4r.d4r_sgd_update(None, None, 0, 0.1, -1.0, stream=0)
+
+
+def test_packed_filter_size_and_argument_errors(handle):
+    # handle: (2, 3, 9, 9) -> 4 filters 3x3, f32 (Kc = 27)
+    assert d4r.d4r_conv_packed_filter_size(handle) == 4 * 27 * 4
+    ws = _ws(handle)
+    for args, code in [((None, FAKE + (1 << 16)), INVALID), ((FAKE, None), INVALID),
+                       ((FAKE, MISALIGNED), INVALID), ((FAKE, FAKE + 16), INVALID)]:  # overlap
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_pack_filter(handle, *args, stream=0)
+        assert e.value.status == code, args
+    for args, code in [((None, FAKE, FAKE, FAKE, ws), INVALID), ((FAKE, FAKE, FAKE, None, ws), WORKSPACE),
+                       ((FAKE, FAKE, FAKE, FAKE, ws - 1), WORKSPACE), ((FAKE, MISALIGNED, FAKE, FAKE, ws), INVALID)]:
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_backward_data_packed(handle, *args, stream=0)
+        assert e.value.status == code, args
