@@ -357,9 +357,14 @@ __device__ __forceinline__ void sched_stage()
     __builtin_amdgcn_sched_group_barrier(0x008, REST - STEP * WR, 0);
 }
 
-template <int NWM, int NWN, int TM, int TN, int AMODE, int BMODE, bool VEC>
+// VEC: bit 0 lets a plainly strided A take 16-byte vector loads, bit 1 a
+// plainly strided B (the other operand forms ignore their bit).  Separate
+// bits, because one misaligned operand (a filter with Kc % 4 != 0) must not
+// cost the other one its vector loads.
+template <int NWM, int NWN, int TM, int TN, int AMODE, int BMODE, int VEC>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 {
+    constexpr bool VA = (VEC & 1) != 0, VB = (VEC & 2) != 0;
     constexpr int NT = NWM * NWN * 64;
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
     constexpr int BK = kBK32;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
         if constexpr (AMODE == OP_NCHW)
             a.load(A, p.g, p.a_ch, p.M, kend, m_blk, k0, tid);
         else
-            a.template load<VEC>(A, p.lda, p.M, kend, m_blk, k0, tid);
+            a.template load<VA>(A, p.lda, p.M, kend, m_blk, k0, tid);
         if constexpr (BMODE == OP_IMPL)
             b.gather(B, p.g, cols, kend, k0, tid);
         else if constexpr (BMODE == OP_NCHW)
@@ -422,11 +427,11 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
         else if constexpr (BMODE == OP_NCHW_K)
             b.load(B, p.g, p.b_ch, p.N, kend, n_blk, k0, tid);
         else
-            b.template load<VEC>(B, p.ldb, p.N, kend, n_blk, k0, tid);
+            b.template load<VB>(B, p.ldb, p.N, kend, n_blk, k0, tid);
     };
     auto store = [&](const TA &a, const TB &b, char *buf) {
-        a.template store<VEC>(buf, tid);
-        b.template store<VEC>(buf + TA::LDS_BYTES, tid);
+        a.template store<VA>(buf, tid);
+        b.template store<VB>(buf + TA::LDS_BYTES, tid);
     };
     auto compute = [&](const char *buf) {
         const float *fa = (const float *)buf;
@@ -514,6 +519,37 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     // Epilogue.  Accumulator element e of a 32x32 block sits at
     // row 8*(e/4) + 4*h + (e%4), column l32.
     float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+
+    // Row-major output (split-K partials, dcol, dW, plain GEMMs) with rows
+    // of 16-byte aligned columns: the tile goes through LDS, so every lane
+    // stores 16-byte vectors of 4 consecutive columns instead of one float
+    // per element (a quarter of the store instructions; the short-K data
+    // gradient of AlexNet conv1 is bound by its 140 MB of dcol stores).
+    constexpr int CP = BN + 4;  // LDS row pitch of the staged tile (floats)
+    if constexpr (BM * CP * 4 <= 2 * STAGE) {
+        if (p.epi == EPI_ROWMAJOR && (p.ldc & 3) == 0 && (p.N & 3) == 0 && (p.c_split_stride & 3) == 0) {
+            float *cs = (float *)smem;
+            __syncthreads();  // every wavefront is done reading the stages
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ml = (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                        cs[ml * CP + (wn * TN + j) * 32 + l32] = acc[i][j][e];
+                    }
+            __syncthreads();
+            constexpr int QR = BN / 4;  // 16-byte vectors per tile row
+            for (int q = tid; q < BM * QR; q += NT) {
+                const int r = q / QR, c = (q - r * QR) * 4;
+                const int m = m_blk + r, n = n_blk + c;
+                if (m < p.M && n < p.N)
+                    *(float4 *)(C + (long long)m * p.ldc + n) = *(const float4 *)(cs + r * CP + c);
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int n = n_blk + (wn * TN + j) * 32 + l32;
@@ -544,7 +580,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     }
 }
 
-template <int AMODE, int BMODE, bool VEC>
+template <int AMODE, int BMODE, int VEC>
 hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -572,17 +608,28 @@ hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-// VEC covers the plainly strided operands (OP_ROWS / OP_KC); the gathered
-// ones (OP_IMPL, OP_NCHW) load single elements either way.
+// The vector bits cover the plainly strided operands (OP_ROWS / OP_KC); the
+// gathered ones (OP_IMPL, OP_NCHW, OP_NCHW_K) load single elements either
+// way, so their bit is fixed at 1 (no extra instantiations).
 template <int AMODE, int BMODE>
 hipError_t launch_gemm32_modes(int cfg, const GemmParams &p, hipStream_t s)
 {
-    const bool a_plain = AMODE == OP_ROWS || AMODE == OP_KC;
-    const bool b_plain = BMODE == OP_ROWS || BMODE == OP_KC;
-    const bool vec = (!a_plain || p.a_vec) && (!b_plain || p.b_vec);
-    if (vec)
-        return launch_gemm32_vec<AMODE, BMODE, true>(cfg, p, s);
-    return launch_gemm32_vec<AMODE, BMODE, false>(cfg, p, s);
+    constexpr bool a_plain = AMODE == OP_ROWS || AMODE == OP_KC;
+    constexpr bool b_plain = BMODE == OP_ROWS || BMODE == OP_KC;
+    const bool va = !a_plain || p.a_vec, vb = !b_plain || p.b_vec;
+    if (va && vb)
+        return launch_gemm32_vec<AMODE, BMODE, 3>(cfg, p, s);
+    if constexpr (a_plain && b_plain) {
+        if (va)
+            return launch_gemm32_vec<AMODE, BMODE, 1>(cfg, p, s);
+        if (vb)
+            return launch_gemm32_vec<AMODE, BMODE, 2>(cfg, p, s);
+        return launch_gemm32_vec<AMODE, BMODE, 0>(cfg, p, s);
+    } else if constexpr (a_plain) {
+        return launch_gemm32_vec<AMODE, BMODE, 2>(cfg, p, s);  // A scalar
+    } else {
+        return launch_gemm32_vec<AMODE, BMODE, 1>(cfg, p, s);  // B scalar
+    }
 }
 
 }  // namespace d4r
