@@ -56,6 +56,10 @@ def parse_args():
     ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="explicit",
                     help="explicit: GEMM to dcol + col2im; implicit: implicit-GEMM data gradient "
                          "(stride-1 square-kernel layers; others stay explicit)")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
+                    help="2: the forwards and filter gradients on one stream, the data gradients "
+                         "(own workspace) on a second one after the forwards, joined at the step's "
+                         "end -- the two gradients of a layer only share dy, so they may overlap")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph (stream capture) and time its replays; "
                          "per-kernel event timing is then unavailable")
@@ -308,16 +312,38 @@ def main() -> int:
     dgrad_fn = (d4r.d4r_conv_backward_data_implicit if args.dgrad == "implicit"
                 else d4r.d4r_conv_backward_data)
 
-    def step(stream=stream):
+    def forward(layer, pl, t, stream):
+        if implicit:
+            d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
+        else:
+            d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
+
+    def wgrad(layer, pl, t, stream):
+        d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
+                                     0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
+
+    if args.streams == 2:
+        aux = torch.cuda.Stream()  # default priority
+        for _, pl, t in layers:
+            t["ws2"] = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(stream=stream, streams=args.streams):
+        if streams == 1:
+            for layer, pl, t in layers:
+                forward(layer, pl, t, stream)
+                dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
+                wgrad(layer, pl, t, stream)
+            return
+        # forwards, then per layer (last first, as a backward pass runs) the
+        # filter gradient on this stream and the data gradient on the other
+        cur = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
         for layer, pl, t in layers:
-            if implicit:
-                d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes,
-                                              stream)
-            else:
-                d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
-            dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
-            d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
-                                         0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
+            forward(layer, pl, t, stream)
+        aux.wait_stream(cur)
+        for layer, pl, t in reversed(layers):
+            dgrad_fn(pl.h, t["w"], t["g"], t["dx"], t["ws2"], pl.ws_bytes, aux.cuda_stream)
+            wgrad(layer, pl, t, stream)
+        cur.wait_stream(aux)
 
     for _ in range(args.warmup):
         step()
@@ -344,12 +370,13 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Kernel timing: the same K steps again, eager, with the library's HIP
-    # event pair around every launch on its stream.
+    # Kernel timing: the same K steps again, eager and on one stream (so no
+    # kernel shares the GPU with another), with the library's HIP event pair
+    # around every launch on its stream.
     d4r.d4r_profile_reset()
     d4r.d4r_profile_enable(True)
     for _ in range(args.steps):
-        step()
+        step(streams=1)
     torch.cuda.synchronize()
     d4r.d4r_profile_enable(False)
     stats = d4r.d4r_profile_read()
@@ -403,7 +430,7 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad,
+                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad, "streams": args.streams,
                    "hip_graph": bool(args.graph),
                    "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],
@@ -413,7 +440,8 @@ def main() -> int:
         "col2im": stage("col2im"),
         "roofline": roof,
         "kernel_timing": "HIP event pair per launch, recorded by the library on its launch stream "
-                         "during a second pass of the same steps (step time from an event-free pass)",
+                         "during a second, single-stream pass of the same steps (step time from an "
+                         "event-free pass)",
         "cpu_baseline": cpu,
         "kernels": kernels,
     }

@@ -55,7 +55,10 @@
  *
  * Streams.  hip_stream is a hipStream_t (NULL = the null stream).  Calls
  * only enqueue kernels on it: no host synchronisation, no allocation.
- * Results are deterministic: no atomics, fixed summation orders.
+ * Results are deterministic: no atomics, fixed summation orders.  Calls
+ * that may run at the same time on different streams must not share a
+ * workspace: e.g. a layer's data gradient may overlap its filter gradient
+ * (both only read w and dy) when given a workspace of its own.
  *
  * Errors.  Every call returns a d4r_status.  All argument validation runs
  * before any HIP call, so an invalid call enqueues nothing.  A kernel launch

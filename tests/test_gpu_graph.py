@@ -61,3 +61,31 @@ def test_graph_replay_matches_eager(key, li, dt, batch):
         torch.cuda.synchronize()
         for k in got:
             assert torch.equal(got[k], t[k]), (r, k)
+
+
+@pytest.mark.parametrize("key,li,dt,batch", [("c4", 1, "f32", 4), ("c4", 2, "bf16", 4), ("c5", 1, "f16", 1)])
+def test_gradients_on_two_streams_match_one_stream(key, li, dt, batch):
+    # the data gradient (its own workspace) on a second stream, overlapping
+    # the filter gradient that reuses the forward's col: results equal the
+    # one-stream sequence bit for bit (the library only enqueues; nothing is
+    # shared between the two besides the read-only w and dy)
+    pl, t = _setup(key, li, dt, batch)
+    main = torch.cuda.current_stream()
+    _step(pl, t, main.cuda_stream)
+    torch.cuda.synchronize()
+    ref = {k: t[k].clone() for k in ("y", "dx", "dw", "db")}
+    for k in ("y", "dx", "dw", "db"):
+        t[k].fill_(float("nan"))
+    ws2 = torch.empty(pl.ws_bytes, dtype=torch.uint8, device="cuda")
+    aux = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, main.cuda_stream)
+        aux.wait_stream(main)
+        d4r.d4r_conv_backward_data(pl.h, t["w"], t["g"], t["dx"], ws2, pl.ws_bytes, aux.cuda_stream)
+        d4r.d4r_conv_backward_filter(pl.h, None, t["g"], t["dw"], t["db"], 1, pl.ws, pl.ws_bytes,
+                                     main.cuda_stream)
+        main.wait_stream(aux)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(ref[k], t[k]), k
