@@ -3,9 +3,10 @@
 
 One step = the whole hot path over one batch of seeded synthetic input, for
 every conv layer of the workload: forward (im2col -> GEMM NN with the
-conv_reshape + bias epilogue), data gradient (reshape dy, GEMM, col2im) and
-filter + bias gradients (reshape dy, split-K GEMM NT on the saved col,
-reduction, bias row sum).  Inputs are resident in HBM before timing starts.
+conv_reshape + bias epilogue), data gradient (by default the implicit GEMM
+over dy, no dcol; --dgrad explicit: GEMM to dcol, col2im) and filter + bias
+gradients (reshape dy, split-K GEMM NT on the saved col, reduction, bias
+row sum).  Inputs are resident in HBM before timing starts.
 
 Default workload: the AlexNet conv3-5 stack (batch 64, 256x13x13 -> 384 ->
 384 -> 256 filters 3x3 pad 1) in fp32, the largest GEMM-dominated
@@ -53,9 +54,9 @@ def parse_args():
     ap.add_argument("--forward", choices=("explicit", "implicit"), default="explicit",
                     help="explicit: im2col + GEMM (col saved for the filter gradient); "
                          "implicit: implicit-GEMM forward, im2col redone in the filter gradient")
-    ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="explicit",
-                    help="explicit: GEMM to dcol + col2im; implicit: implicit-GEMM data gradient "
-                         "(stride-1 square-kernel layers; others stay explicit)")
+    ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="implicit",
+                    help="implicit: implicit-GEMM data gradient, no dcol (stride-1 square-kernel "
+                         "layers; others run explicit); explicit: the page's GEMM to dcol + col2im")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the forwards and filter gradients on one stream, the data gradients "
                          "(own workspace) on a second one after the forwards, joined at the step's "

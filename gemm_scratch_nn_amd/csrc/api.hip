@@ -113,11 +113,15 @@ int tile_from_env(int dt)
     return -1;
 }
 
-GemmPlan plan_gemm(int M, int N, int K, int dt)
+// dl16: only the tiles of the 16-bit direct-to-LDS kernel (OP_IMPL_T).
+GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false)
 {
     TileCand cands[6];
     int nc = 0;
-    if (M <= 32) {
+    if (dl16) {
+        cands[nc++] = {TILE_128x256, 1.0};
+        cands[nc++] = {TILE_256x128, 1.0};
+    } else if (M <= 32) {
         cands[nc++] = {TILE_32x128, 1.0};
     } else if (M <= 64 || N <= 64) {
         cands[nc++] = {TILE_64x64, 1.0};
@@ -271,7 +275,7 @@ std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
     const char a = amode == OP_KC ? 'k' : (amode == OP_NCHW ? 'g' : 'm');
     const char b = (bmode == OP_KC) ? 'k' : (bmode == OP_NCHW ? 'g' : (bmode == OP_NCHW_K ? 'c' : 'n'));
     return std::string("gemm_") + dt_name(dt) + "_" + std::to_string(ts.bm) + "x" + std::to_string(ts.bn) +
-           "_" + a + b + (bmode == OP_IMPL ? "_implicit" : "");
+           "_" + a + b + (bmode == OP_IMPL ? "_implicit" : (bmode == OP_IMPL_T ? "_nhwc" : ""));
 }
 
 
@@ -282,7 +286,7 @@ std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
 hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
                     const float *bias, int P, float *partial, hipStream_t s, const char *pass,
-                    const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0)
+                    const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0, const void *zero = nullptr)
 {
     const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
@@ -306,6 +310,7 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
         p.g = *geom;
     else
         memset(&p.g, 0, sizeof p.g);
+    p.zero = zero;
     p.a_ch = a_ch ? a_ch : p.g.O;
     p.b_ch = b_ch ? b_ch : p.g.O;
     // an NCHW operand takes whole vectors when they cannot straddle images
@@ -325,7 +330,8 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
         p.c_split_stride = 0;
     }
     const int es = dt_size(dt);
-    const double b_bytes = implicit ? (double)geom->B * geom->C * geom->H * geom->W : (double)K * N;
+    const double b_bytes = (implicit || bmode == OP_IMPL_T) ? (double)geom->B * geom->C * geom->H * geom->W
+                                                             : (double)K * N;
     ProfScope ps(s, gemm_kernel_name(dt, pl.cfg, amode, bmode) + ":" + pass, 2.0 * M * N * K,
                  (double)es * ((double)M * K + b_bytes) + 4.0 * M * N);
     hipError_t e = launch_gemm(dt, pl.cfg, amode, bmode, p, s);
@@ -368,6 +374,11 @@ struct d4r_conv {
     // its columns, so the GEMMs can read x and dy in place (no im2col, no
     // dcol, no col2im)
     bool pointwise;
+    // implicit data gradient from dy read as NHWC (its transpose Gt): filter
+    // wd[c][u][v][o], a zero page (16-bit direct-to-LDS loads of padding)
+    bool dgrad_nhwc;
+    GemmPlan bwd_data_nhwc;
+    size_t off_zero;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -568,6 +579,13 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         d.P = inH * inW; d.Kc = outC * kH * kW; d.N = batch * d.P;
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
+    // the NHWC form needs whole GEMM stages of dy (32 f32 / 64 16-bit
+    // channels) within one tap
+    h->dgrad_nhwc = h->dgrad_impl && outC % gemm_bk(dtype) == 0;
+    if (const char *e = getenv("D4R_DGRAD_NHWC"))  // experiments, tests: 0 = gathered path
+        h->dgrad_nhwc = h->dgrad_nhwc && e[0] != '0';
+    if (h->dgrad_nhwc)
+        h->bwd_data_nhwc = plan_gemm(h->gd.O, h->gd.N, h->gd.Kc, dtype, dtype != D4R_F32);
     h->pointwise = kH == 1 && kW == 1 && stride == 1 && padding == 0;
     if (const char *e = getenv("D4R_POINTWISE"))  // experiments, tests: 0 = im2col path
         h->pointwise = h->pointwise && e[0] != '0';
@@ -594,7 +612,7 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->col_bytes = (size_t)col_el * h->es;
     size_t off = align_up(h->col_bytes);
     h->off_g = off;
-    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
+    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE || h->dgrad_nhwc)
         off += align_up((size_t)y_el * h->es);
     h->off_wt = off;
     if (h->dgrad_wt)
@@ -602,6 +620,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->off_wflip = off;
     if (h->dgrad_impl)
         off += align_up((size_t)w_el * h->es);
+    h->off_zero = off;
+    if (h->dgrad_nhwc)
+        off += align_up(256);
     h->off_bias = off;
     off += align_up((size_t)outC * bias_part_cols * sizeof(float));
     h->off_big = off;
@@ -616,6 +637,11 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         size_t di = plan_partial_bytes(h->bwd_data_impl, h->gd.O, h->gd.N);
         if (di > big)
             big = di;
+    }
+    if (h->dgrad_nhwc) {
+        size_t dn = plan_partial_bytes(h->bwd_data_nhwc, h->gd.O, h->gd.N);
+        if (dn > big)
+            big = dn;
     }
     h->ws_bytes = off + align_up(big);
     *out = h;
@@ -860,6 +886,24 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     char *wsb = (char *)ws;
     void *wf = wsb + h->off_wflip;
     float *partial = (float *)(wsb + h->off_big);
+    if (h->dgrad_nhwc) {
+        // dx = Wd(C x kH*kW*O) * im2col(dy as NHWC): dy transposed to
+        // Gt[b][pix][o], the filter flipped with k ordered (u, v, o)
+        void *gt = wsb + h->off_g;
+        void *zero = wsb + h->off_zero;
+        D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad transpose");
+        {
+            ProfScope ps(s, std::string("flip_filter_nhwc_") + dt_name(h->dt) + ":dgrad", 0.0,
+                         2.0 * h->es * (double)g.O * g.Kc);
+            hipError_t e = launch_flip_filter_nhwc(h->dt, g, w, wf, zero, s);
+            ps.done();
+            D4R_LAUNCH(e, "filter flip");
+        }
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_data_nhwc, OP_KC, OP_IMPL_T, wf, d.Kc, gt, 0, d.O, d.N, d.Kc,
+                            EPI_NCHW, dx, 0, nullptr, d.P, partial, s, "dgrad", &d, 0, 0, zero),
+                   "implicit data-gradient GEMM");
+        return ok();
+    }
     {
         ProfScope ps(s, std::string("flip_filter_") + dt_name(h->dt) + ":dgrad", 0.0,
                      2.0 * h->es * (double)g.O * g.Kc);

@@ -513,11 +513,16 @@ __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ 
 // consecutive elements of an output row; a thread's 16 loads are all issued
 // before the first is used.
 // ---------------------------------------------------------------------------
+// flip > 0 (the data gradient's filter for an NHWC dy): the columns come in
+// groups of flip taps and output row c takes input column c with its tap
+// reversed inside the group; block 0 also clears 256 bytes at `zero`.
 template <typename T>
 __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in, T *__restrict__ out,
-                                                       int R, int Cc)
+                                                       int R, int Cc, int flip, uint32_t *__restrict__ zero)
 {
     __shared__ T tile[64][65];
+    if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
+        zero[threadIdx.x] = 0u;
     const long long base = (long long)blockIdx.z * R * Cc;
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -537,8 +542,9 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int c = c0 + ty + i * (NT / 64);
+        const int oc = flip > 0 ? c - c % flip + (flip - 1 - c % flip) : c;
         if (rin && c < Cc)
-            out[base + (long long)c * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
+            out[base + (long long)oc * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
     }
 }
 
@@ -887,10 +893,10 @@ hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, vo
     dim3 grid((Cc + 63) / 64, (R + 63) / 64, batch);
     if (dt == DT_F32)
         hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)in,
-                           (uint32_t *)out, R, Cc);
+                           (uint32_t *)out, R, Cc, 0, nullptr);
     else
         hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)in,
-                           (uint16_t *)out, R, Cc);
+                           (uint16_t *)out, R, Cc, 0, nullptr);
     return hipGetLastError();
 }
 
@@ -936,6 +942,22 @@ hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf
     else
         hipLaunchKernelGGL(flip_filter_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w,
                            (uint16_t *)wf, g.O, g.C, g.kH, g.kW);
+    return hipGetLastError();
+}
+
+// wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v]: W (O x Kc) transposed through
+// LDS tiles, each output row's tap reversed (rows come in groups of kH*kW
+// taps); plus the zero page.
+hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, void *wd, void *zero, hipStream_t s)
+{
+    const int R = g.O, Cc = g.C * g.kH * g.kW, khw = g.kH * g.kW;
+    dim3 grid((Cc + 63) / 64, (R + 63) / 64, 1);
+    if (dt == DT_F32)
+        hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)w, (uint32_t *)wd,
+                           R, Cc, khw, (uint32_t *)zero);
+    else
+        hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w, (uint16_t *)wd,
+                           R, Cc, khw, (uint32_t *)zero);
     return hipGetLastError();
 }
 

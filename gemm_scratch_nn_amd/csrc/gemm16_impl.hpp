@@ -520,13 +520,69 @@ struct DlOperand {
     }
 };
 
-template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF>
+// B operand of the implicit GEMM over an NHWC tensor t[b][h][w][c] (OP_IMPL_T,
+// geometry g, stride 1): tile row n = (b, i, j) is an output pixel and a
+// 64-deep stage covers channels c0 .. c0+63 of one tap (u, v), so each row's
+// stage is one contiguous 128-byte run of t at (b, i-p+u, j-p+v, c0), or the
+// zero page when that position is in the padding.  The same lane-to-LDS
+// mapping and swizzle as DlOperand; a lane decodes its rows' pixels once
+// and each stage's tap once.
+template <int BR, int NW>
+struct DlImplNhwc {
+    static constexpr int ROWB = kDlBK * 2;
+    static constexpr int LPL = 8;
+    static constexpr int LD = BR / (LPL * NW);
+    static constexpr int BYTES = BR * ROWB;
+    static_assert(BR % (LPL * NW) == 0, "whole load groups");
+
+    int b[LD], h0[LD], w0[LD], chk[LD];  // b < 0: row past N
+
+    __device__ __forceinline__ void setup(int n0, const ConvGeom &g, int wave, int lane)
+    {
+#pragma unroll
+        for (int j = 0; j < LD; ++j) {
+            const int lr = (j * NW + wave) * LPL + lane / 8;
+            const int n = n0 + lr;
+            chk[j] = (lane % 8) ^ swz(lr);
+            const int bb = n / g.P, r = n - (n / g.P) * g.P;
+            const int i = r / g.OW;
+            b[j] = n < g.N ? bb : -1;
+            h0[j] = i - g.p;
+            w0[j] = r - i * g.OW - g.p;
+        }
+    }
+
+    __device__ __forceinline__ void issue(const uint16_t *X, const uint16_t *zero, int k0, char *lds, int wave,
+                                          const ConvGeom &g) const
+    {
+        const int tap = k0 / g.C, c0 = k0 - tap * g.C;
+        const int u = tap / g.kW, v = tap - (tap / g.kW) * g.kW;
+#pragma unroll
+        for (int j = 0; j < LD; ++j) {
+            const int hh = h0[j] + u, ww = w0[j] + v;
+            const bool ok = b[j] >= 0 && (unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W;
+            const uint16_t *src = ok ? X + (((long long)b[j] * g.H + hh) * g.W + ww) * g.C + c0 + chk[j] * 8
+                                     : zero + chk[j] * 8;
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)(lds + (j * NW + wave) * LPL * ROWB),
+                                             16, 0, 0);
+        }
+    }
+
+    // the LDS layout is DlOperand's
+    __device__ __forceinline__ static u32x4_t frag(const char *lds, int row, int q, int h)
+    {
+        return DlOperand<BR, NW>::frag(lds, row, q, h);
+    }
+};
+
+// BI: B is OP_IMPL_T (DlImplNhwc) instead of a k-contiguous matrix.
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
 {
     constexpr int NW = NWM * NWN;
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = kDlBK;
     using OA = DlOperand<BM, NW>;
-    using OB = DlOperand<BN, NW>;
+    using OB = std::conditional_t<BI, DlImplNhwc<BN, NW>, DlOperand<BN, NW>>;
     constexpr int STAGE = OA::BYTES + OB::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
@@ -548,14 +604,20 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     OA oa;
     OB ob;
     oa.setup(m_blk, p.M, p.lda, wave, lane);
-    ob.setup(n_blk, p.N, p.ldb, wave, lane);
+    if constexpr (BI)
+        ob.setup(n_blk, p.g, wave, lane);
+    else
+        ob.setup(n_blk, p.N, p.ldb, wave, lane);
     // stage s (clamped to the first stage past the end: its slot is never
     // read) into ring slot s % NBUF
     auto issue = [&](int s) {
         const int k0 = kbeg + (s < nk ? s : 0) * BK;
         char *base = smem + (s % NBUF) * STAGE;
         oa.issue(A, k0, base, wave);
-        ob.issue(B, k0, base + OA::BYTES, wave);
+        if constexpr (BI)
+            ob.issue(B, (const uint16_t *)p.zero, k0, base + OA::BYTES, wave, p.g);
+        else
+            ob.issue(B, k0, base + OA::BYTES, wave);
     };
 
     f32x16_t acc[TM][TN];
@@ -625,7 +687,7 @@ inline bool dl_applies(int amode, int bmode, const GemmParams &p)
            p.k_per_split % kDlBK == 0;
 }
 
-template <int DTID>
+template <int DTID, bool BI = false>
 hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
@@ -633,10 +695,10 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
     const dim3 grid(tiles, 1, p.splits), b8(512);
     switch (cfg) {
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -698,6 +760,14 @@ hipError_t launch_gemm16_layout(int cfg, const GemmParams &p, hipStream_t s)
 template <int DTID>
 hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
+    if (bmode == OP_IMPL_T) {
+        // direct-to-LDS only: a k-contiguous A, whole 64-deep stages, each
+        // inside one tap
+        if (amode != OP_KC || !p.a_vec || p.K % kDlBK != 0 || p.k_per_split % kDlBK != 0 || p.g.C % kDlBK != 0 ||
+            p.g.s != 1 || !p.zero)
+            return hipErrorInvalidValue;
+        return launch_gemm16_dl<DTID, true>(cfg, p, s);
+    }
     if (amode == OP_KC && bmode == OP_IMPL) {
         if (p.a_vec)
             return launch_gemm16_vec<DTID, true, false, true, true>(cfg, p, s);

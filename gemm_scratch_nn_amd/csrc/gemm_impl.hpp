@@ -126,6 +126,60 @@ struct OperandTile {
     }
 };
 
+// B operand: the im2col of an NHWC tensor t[b][h][w][c] (OP_IMPL_T, stride
+// 1, C % 32 == 0) with k ordered (u, v, c): op(B)[k][n] = t[b][i-p+u][j-p+v][c]
+// for n = (b, i, j).  A 32-deep stage lies inside one tap, so every 16-byte
+// slot is 4 consecutive channels of one pixel; loads are unconditional (offset
+// 0 in the padding or past N) and zeroed at the LDS store, the layout [n][k]
+// of a k-contiguous operand.  The slots' pixels are the same in every stage:
+// decoded once into NhwcRows (shared by both register sets).
+template <int BR, int NT>
+struct NhwcRows {
+    using T = OperandTile<BR, true, NT>;
+    int b[T::PER], h0[T::PER], w0[T::PER];  // b < 0: no such row
+
+    __device__ __forceinline__ void setup(const ConvGeom &g, int n0, int tid)
+    {
+#pragma unroll
+        for (int s = 0; s < T::PER; ++s) {
+            const int id = s * NT + tid;
+            const bool live = T::NV % NT == 0 || id < T::NV;
+            int row, kk;
+            T::slot(live ? id : 0, row, kk);
+            const int n = n0 + row;
+            const int bb = n / g.P, r = n - (n / g.P) * g.P;
+            const int i = r / g.OW;
+            b[s] = (live && n < g.N) ? bb : -1;
+            h0[s] = i - g.p;
+            w0[s] = r - i * g.OW - g.p;
+        }
+    }
+};
+
+template <int BR, int NT>
+struct ImplNhwcTileF32 : OperandTile<BR, true, NT> {
+    using T = OperandTile<BR, true, NT>;
+
+    __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g,
+                                         const NhwcRows<BR, NT> &rows, int K, int k0, int tid)
+    {
+        const int tap = k0 / g.C, c0 = k0 - tap * g.C;
+        const int u = tap / g.kW, v = tap - (tap / g.kW) * g.kW;
+#pragma unroll
+        for (int s = 0; s < T::PER; ++s) {
+            const int id = s * NT + tid;
+            int row, kk;
+            T::slot(id, row, kk);
+            const int hh = rows.h0[s] + u, ww = rows.w0[s] + v;
+            const bool ok = rows.b[s] >= 0 && k0 + kk < K && (unsigned)hh < (unsigned)g.H &&
+                            (unsigned)ww < (unsigned)g.W;
+            const long long off = (((long long)rows.b[s] * g.H + hh) * g.W + ww) * g.C + c0 + kk;
+            this->reg[s] = *(const u32x4 *)(X + (ok ? off : 0));
+            this->okmask = (s == 0 ? 0u : this->okmask) | ((ok ? 1u : 0u) << s);
+        }
+    }
+};
+
 // Forward-GEMM B operand gathered straight from x (the implicit GEMM):
 // op(B)[kc][n] = xt(b, c, i*s - p + u, j*s - p + v), kc = (c*kH + u)*kW + v,
 // n = (b*OH + i)*OW + j, stored in the same [k][n] LDS layout as a
@@ -372,12 +426,15 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     // LDS layouts: [m][k] unless A is row-contiguous; [n][k] only for a
     // k-contiguous B
     constexpr bool A_KC = AMODE != OP_ROWS;
-    constexpr bool B_KC = BMODE == OP_KC || BMODE == OP_NCHW_K;
+    constexpr bool B_KC = BMODE == OP_KC || BMODE == OP_NCHW_K || BMODE == OP_IMPL_T;
     using TA = std::conditional_t<AMODE == OP_NCHW, NchwKTile<BM, NT>, OperandTile<BM, A_KC, NT>>;
     using TB = std::conditional_t<
         BMODE == OP_IMPL, ImplicitTileF32<BN, NT>,
-        std::conditional_t<BMODE == OP_NCHW, NchwNTile<BN, NT>,
-                           std::conditional_t<BMODE == OP_NCHW_K, NchwKTile<BN, NT>, OperandTile<BN, B_KC, NT>>>>;
+        std::conditional_t<
+            BMODE == OP_NCHW, NchwNTile<BN, NT>,
+            std::conditional_t<BMODE == OP_NCHW_K, NchwKTile<BN, NT>,
+                               std::conditional_t<BMODE == OP_IMPL_T, ImplNhwcTileF32<BN, NT>,
+                                                  OperandTile<BN, B_KC, NT>>>>>;
     constexpr int STAGE = TA::LDS_BYTES + TB::LDS_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -414,6 +471,9 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     NchwCol ncol;
     if constexpr (BMODE == OP_NCHW)
         ncol.setup(p.g, p.b_ch, n_blk + tid % BN);
+    NhwcRows<BN, NT> nrows;
+    if constexpr (BMODE == OP_IMPL_T)
+        nrows.setup(p.g, n_blk, tid);
     // K bound for this split: the loaders zero-fill k >= kend.
     auto load = [&](TA &a, TB &b, int k0) {
         if constexpr (AMODE == OP_NCHW)
@@ -426,6 +486,8 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
             b.load(B, p.g, ncol, kend, k0, tid);
         else if constexpr (BMODE == OP_NCHW_K)
             b.load(B, p.g, p.b_ch, p.N, kend, n_blk, k0, tid);
+        else if constexpr (BMODE == OP_IMPL_T)
+            b.load(B, p.g, nrows, kend, k0, tid);
         else
             b.template load<VB>(B, p.ldb, p.N, kend, n_blk, k0, tid);
     };
@@ -615,7 +677,8 @@ template <int AMODE, int BMODE>
 hipError_t launch_gemm32_modes(int cfg, const GemmParams &p, hipStream_t s)
 {
     constexpr bool a_plain = AMODE == OP_ROWS || AMODE == OP_KC;
-    constexpr bool b_plain = BMODE == OP_ROWS || BMODE == OP_KC;
+    constexpr bool b_plain = BMODE == OP_ROWS || BMODE == OP_KC;  // OP_IMPL_T keeps bit 1: its
+                                                                  // store applies the zero mask
     const bool va = !a_plain || p.a_vec, vb = !b_plain || p.b_vec;
     if (va && vb)
         return launch_gemm32_vec<AMODE, BMODE, 3>(cfg, p, s);

@@ -79,10 +79,15 @@ enum OperandMode : int {
                   // column index of B (B[c][n]); c is the row of A or the k
                   // of B.  Element address b*ch*P + c*P + pix.  (dy read in
                   // place; x or dy of a 1x1 stride-1 unpadded convolution.)
-    OP_NCHW_K = 4 // B only: an NCHW tensor whose channel c is the row n of
+    OP_NCHW_K = 4,// B only: an NCHW tensor whose channel c is the row n of
                   // B and whose (image, pixel) pair is the k index:
                   // op(B)[k][c] = t[k / P][c][k % P] (x in the filter
                   // gradient of a 1x1 stride-1 unpadded convolution)
+    OP_IMPL_T = 5 // B only, 16-bit direct-to-LDS GEMM: the im2col of an
+                  // NHWC tensor t[b][h][w][c] (geometry p.g, stride 1) with k
+                  // ordered (u, v, c), c fastest: op(B)[k][n] =
+                  // t[b][i-p+u][j-p+v][c] for n = (b, i, j), or 0 in the
+                  // padding (read from p.zero).  Needs p.g.C % 64 == 0.
 };
 
 // C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
@@ -101,6 +106,7 @@ struct GemmParams {
     int a_vec, b_vec;   // 16-byte vector loads allowed (ld and base aligned;
                         // NCHW operands: P a multiple of the vector width)
     int a_ch, b_ch;     // channel counts of OP_NCHW / OP_NCHW_K operands
+    const void *zero;   // OP_IMPL_T: 256 zero bytes, 16-byte aligned
     ConvGeom g;         // OP_IMPL and OP_NCHW operands
 };
 
@@ -132,6 +138,10 @@ hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db
 int bias_grad_splits(const ConvGeom &g);
 // wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v] (the implicit data gradient's filter)
 hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf, hipStream_t s);
+// wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v] (the same, k ordered for an NHWC
+// dy), and 256 zero bytes at `zero`
+hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, void *wd, void *zero,
+                                   hipStream_t s);
 // out = sum over s of part[s] (fixed order) with the GEMM epilogue
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,

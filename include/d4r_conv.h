@@ -174,11 +174,16 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy,
  * mlvc.cpp design page runs dense spatial convolution as an implicit GEMM
  * ("Driver-only AOT cubin direction").  For stride 1 and a square kernel,
  * dx is the stride-1 convolution of dy (padding kH-1-p) with the filter
- * Wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v]; it runs as the implicit-GEMM
- * forward on that geometry: no dcol, no col2im.  Other shapes run the
- * explicit path of d4r_conv_backward_data.  Same arguments, result equal up
- * to summation order; ws holds Wf and split-K partials, and the col region
- * is left untouched (reuse_col stays valid).
+ * Wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v]; it runs as an implicit GEMM on
+ * that geometry: no dcol, no col2im.  When outC is a multiple of 32 (f32)
+ * or 64 (f16, bf16), dy is first transposed to NHWC and the filter flipped
+ * with k ordered (u, v, o), so that every GEMM stage reads contiguous
+ * channel runs of dy (16-byte loads; straight into LDS for 16-bit);
+ * otherwise the GEMM gathers im2col(dy) element by element.  1x1 stride-1
+ * unpadded convolutions take their direct path, other shapes the explicit
+ * path of d4r_conv_backward_data.  Same arguments, result equal up to
+ * summation order; ws holds dy^T, the flipped filter and split-K partials,
+ * and the col region is left untouched (reuse_col stays valid).
  */
 d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w,
                                            const void *dy, float *dx, void *ws,

@@ -548,3 +548,37 @@ def test_implicit_dgrad_keeps_saved_col():
     dw2, db2 = pl.backward_filter(x, g, reuse_col=False)
     torch.cuda.synchronize()
     assert torch.equal(dw1, dw2) and torch.equal(db1, db2)
+
+
+# implicit data gradient from dy read as NHWC (dy channels a multiple of the
+# GEMM stage: 32 f32, 64 16-bit, the latter through the direct-to-LDS
+# kernel): padding below, at and above kH - 1, pixel counts that leave
+# ragged tiles, input channels that do not fill a tile row, and split K
+DGRAD_NHWC = [
+    (2, 3, 8, 7, 64, 3, 3, 1, 1),
+    (3, 40, 9, 11, 128, 3, 3, 1, 0),
+    (2, 130, 7, 7, 64, 3, 3, 1, 2),
+    (1, 16, 6, 6, 192, 5, 5, 1, 2),
+    (2, 8, 13, 13, 64, 3, 3, 1, 3),
+    (4, 24, 5, 9, 256, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("t", DGRAD_NHWC, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_dgrad_implicit_nhwc(t, dt, monkeypatch):
+    sh = _shape(t)
+    ops = wl.random_conv(sh, dt, seed=sum(t) + 21)
+    _check_dgrad_implicit(sh, dt, ops, "nhwc")
+    # the gathered implicit path agrees
+    monkeypatch.setenv("D4R_DGRAD_NHWC", "0")
+    _check_dgrad_implicit(sh, dt, ops, "gathered")
+
+
+@pytest.mark.parametrize("key,li,dt", [("c4", 0, "bf16"), ("c4", 1, "bf16"), ("c4", 2, "bf16"), ("c5", 0, "f16"),
+                                       ("c4", 1, "f32")])
+def test_dgrad_implicit_nhwc_full_size(key, li, dt):
+    w = wl.WORKLOADS[key]
+    sh = w.layers[li].shape
+    ops = wl.conv_inputs(w, li, dt)
+    _check_dgrad_implicit(sh, dt, ops, f"{key}/{w.layers[li].name}/nhwc", sample=True)
