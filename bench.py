@@ -61,6 +61,10 @@ def parse_args():
                     help="2: the forwards and filter gradients on one stream, the data gradients "
                          "(own workspace) on a second one after the forwards, joined at the step's "
                          "end -- the two gradients of a layer only share dy, so they may overlap")
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="cycle through this many independent copies of every input, output and "
+                         "workspace, so that a step's operands are not left in the 256 MB MALL by "
+                         "the previous step (cold-cache timing)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph (stream capture) and time its replays; "
                          "per-kernel event timing is then unavailable")
@@ -284,19 +288,29 @@ def main() -> int:
             return torch.from_numpy(op.stored).to(dev)
         return torch.from_numpy(op.stored.view(np.int16)).to(dev).view(tdt)
 
-    layers = []
-    for li, layer in enumerate(wl.layers):
-        sh = layer.shape
-        ops = W.conv_inputs(wl, li, dtype)
-        pl = d4r.ConvPlan(sh.batch, sh.inC, sh.inH, sh.inW, sh.kH, sh.kW, sh.stride, sh.padding,
-                          sh.outC, code, device=dev)
-        t = {k: to_dev(ops[k]) for k in ("x", "w", "g")}
-        t["bias"] = torch.from_numpy(ops["bias"].stored).to(dev)
-        t["y"] = torch.empty(sh.y_shape(), dtype=torch.float32, device=dev)
-        t["dx"] = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
-        t["dw"] = torch.empty(sh.w_shape(), dtype=torch.float32, device=dev)
-        t["db"] = torch.empty((sh.outC,), dtype=torch.float32, device=dev)
-        layers.append((layer, pl, t))
+    if args.rotate < 1 or (args.rotate > 1 and args.graph):
+        print("bench.py: --rotate must be >= 1 and cannot be combined with --graph", file=sys.stderr)
+        return 2
+
+    def build_layers():
+        out = []
+        for li, layer in enumerate(wl.layers):
+            sh = layer.shape
+            ops = W.conv_inputs(wl, li, dtype)
+            pl = d4r.ConvPlan(sh.batch, sh.inC, sh.inH, sh.inW, sh.kH, sh.kW, sh.stride, sh.padding,
+                              sh.outC, code, device=dev)
+            t = {k: to_dev(ops[k]) for k in ("x", "w", "g")}
+            t["bias"] = torch.from_numpy(ops["bias"].stored).to(dev)
+            t["y"] = torch.empty(sh.y_shape(), dtype=torch.float32, device=dev)
+            t["dx"] = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
+            t["dw"] = torch.empty(sh.w_shape(), dtype=torch.float32, device=dev)
+            t["db"] = torch.empty((sh.outC,), dtype=torch.float32, device=dev)
+            out.append((layer, pl, t))
+        return out
+
+    sets = [build_layers() for _ in range(args.rotate)]
+    layers = sets[0]
+    n_step = [0]
 
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -325,10 +339,13 @@ def main() -> int:
 
     if args.streams == 2:
         aux = torch.cuda.Stream()  # default priority
-        for _, pl, t in layers:
-            t["ws2"] = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=dev)
+        for st in sets:
+            for _, pl, t in st:
+                t["ws2"] = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=dev)
 
     def step(stream=stream, streams=args.streams):
+        layers = sets[n_step[0] % len(sets)]
+        n_step[0] += 1
         if streams == 1:
             for layer, pl, t in layers:
                 forward(layer, pl, t, stream)
@@ -432,7 +449,7 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
                    "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad, "streams": args.streams,
-                   "hip_graph": bool(args.graph),
+                   "rotate": args.rotate, "hip_graph": bool(args.graph),
                    "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],
         "gemm_TFLOPs": gemm_tf,
