@@ -75,6 +75,7 @@ _c = {
     "d4r_conv_forward": _sig("d4r_conv_forward", [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_forward_implicit": _sig("d4r_conv_forward_implicit",
                                       [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_conv_forward_ex": _sig("d4r_conv_forward_ex", [_vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "d4r_conv_backward_data": _sig("d4r_conv_backward_data", [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_data_implicit": _sig("d4r_conv_backward_data_implicit",
                                             [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -89,6 +90,7 @@ _c = {
     "d4r_conv_bias_grad": _sig("d4r_conv_bias_grad", [_vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_gemm_workspace_size": _sig("d4r_gemm_workspace_size", [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "d4r_gemm": _sig("d4r_gemm", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_gemm_bias_act": _sig("d4r_gemm_bias_act", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "d4r_relu_forward": _sig("d4r_relu_forward", [_vp, _vp, _ll, _vp]),
     "d4r_relu_backward": _sig("d4r_relu_backward", [_vp, _vp, _vp, _ll, _vp]),
     "d4r_maxpool_forward": _sig("d4r_maxpool_forward", [_vp, _vp, _vp] + [_i] * 6 + [_vp]),
@@ -215,6 +217,16 @@ def d4r_conv_forward_implicit(h, x, w, bias, y, ws, ws_bytes=None, stream=None) 
                                            _stream(stream)))
 
 
+D4R_FWD_RELU, D4R_FWD_IMPLICIT = 1, 2
+
+
+def d4r_conv_forward_ex(h, x, w, bias, y, flags, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_conv_forward_ex",
+           _c["d4r_conv_forward_ex"](h, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), int(flags), _ptr(ws), nb,
+                                     _stream(stream)))
+
+
 def d4r_conv_backward_data(h, w, dy, dx, ws, ws_bytes=None, stream=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_conv_backward_data", _c["d4r_conv_backward_data"](h, _ptr(w), _ptr(dy), _ptr(dx),
@@ -275,6 +287,14 @@ def d4r_gemm(M, K, N, flags, dtype, A, B, C, ws=None, ws_bytes=None, stream=None
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_gemm", _c["d4r_gemm"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(C), _ptr(ws), nb,
                                       _stream(stream)))
+
+
+def d4r_gemm_bias_act(M, K, N, flags, dtype, A, B, bias, relu, C, ws=None, ws_bytes=None,
+                      stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_gemm_bias_act",
+           _c["d4r_gemm_bias_act"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(bias), int(relu), _ptr(C),
+                                   _ptr(ws), nb, _stream(stream)))
 
 
 def d4r_relu_forward(x, y, n, stream=None) -> None:
@@ -427,6 +447,19 @@ class ConvPlan:
         if y is None:
             y = torch.empty(self.y_shape, dtype=torch.float32, device=x.device)
         d4r_conv_forward_implicit(self.h, x, w, bias, y, self.ws, self.ws_bytes)
+        return y
+
+    def forward_relu(self, x, w, bias=None, y=None, implicit=False):
+        """y = relu(conv(x; w) + bias) in one GEMM epilogue (d4r_conv_forward_ex)."""
+        import torch
+        _require(x, "x", self.dtype, self.x_shape)
+        _require(w, "w", self.dtype, self.w_shape)
+        if bias is not None:
+            _require(bias, "bias", D4R_F32, (self.shape[8],))
+        if y is None:
+            y = torch.empty(self.y_shape, dtype=torch.float32, device=x.device)
+        d4r_conv_forward_ex(self.h, x, w, bias, y, D4R_FWD_RELU | (D4R_FWD_IMPLICIT if implicit else 0),
+                            self.ws, self.ws_bytes)
         return y
 
     def backward_data(self, w, dy, dx=None):

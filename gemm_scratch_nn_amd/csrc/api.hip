@@ -168,7 +168,9 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false)
         const long long slots = (long long)kComputeUnits * wg_per_cu(cands[ci].cfg, dt);
         // seconds per K stage of one workgroup when every slot is busy
         const double t_stage = 2.0 * ts.bm * ts.bn * bk / (peak * cands[ci].eff / (double)slots);
-        const long long smax = ktiles < 256 ? ktiles : 256;
+        long long smax = ktiles < 256 ? ktiles : 256;
+    if (const char *e = getenv("D4R_GEMM_MAX_SPLITS"))  // experiments: cap split-K
+        smax = std::max(1LL, std::min(smax, atoll(e)));
         for (long long sp = 1; sp <= smax; ++sp) {
             const long long per = (ktiles + sp - 1) / sp;
             const long long se = (ktiles + per - 1) / per;
@@ -282,11 +284,14 @@ std::string gemm_kernel_name(int dt, int cfg, int amode, int bmode)
 // Runs one planned GEMM (split-K partials + reduction when the plan splits).
 // Operand forms follow OperandMode; OP_IMPL (B = x, op(B) = im2col(x)) and
 // the NCHW forms take their geometry from `geom`; a_ch / b_ch are the channel
-// counts of NCHW operands (default: geom->O, the gradient dy).
+// counts of NCHW operands (default: geom->O, the gradient dy).  The epilogue
+// adds bias (per row m for EPI_NCHW, per column n for EPI_ROWMAJOR) and then
+// applies ReLU when relu is set; with split K both happen in the reduction.
 hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void *A, int lda,
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
                     const float *bias, int P, float *partial, hipStream_t s, const char *pass,
-                    const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0, const void *zero = nullptr)
+                    const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0, const void *zero = nullptr,
+                    int relu = 0)
 {
     const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
@@ -319,15 +324,19 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
     if (bmode == OP_NCHW || bmode == OP_NCHW_K)
         p.b_vec = geom && geom->P % vw == 0;
     if (pl.splits > 1) {
+        // raw partial sums: bias and ReLU wait for the reduction
         p.C = partial;
         p.ldc = N;
         p.epi = EPI_ROWMAJOR;
         p.c_split_stride = (long long)M * N;
+        p.bias = nullptr;
+        p.relu = 0;
     } else {
         p.C = C;
         p.ldc = ldc;
         p.epi = epi;
         p.c_split_stride = 0;
+        p.relu = relu;
     }
     const int es = dt_size(dt);
     const double b_bytes = (implicit || bmode == OP_IMPL_T) ? (double)geom->B * geom->C * geom->H * geom->W
@@ -340,7 +349,7 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
         return e;
     ProfScope pr(s, std::string("splitk_reduce:") + pass, 0.0,
                  4.0 * (double)M * N * (pl.splits + 1));
-    e = launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, s);
+    e = launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, relu, s);
     pr.done();
     return e;
 }
@@ -723,30 +732,13 @@ d4r_status launched(hipError_t e, const char *what)
 
 }  // namespace
 
-d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const float *bias, float *y,
-                            void *ws, size_t ws_bytes, void *hip_stream)
-{
-    if (!h)
-        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
-    D4R_TRY(check_tensor(x, "x"));
-    D4R_TRY(check_tensor(w, "w"));
-    D4R_TRY(check_tensor(y, "y"));
-    D4R_TRY(check_vec(bias, "bias"));
-    D4R_TRY(check_ws(h, ws, ws_bytes));
-    hipStream_t s = (hipStream_t)hip_stream;
-    const ConvGeom &g = h->g;
-    char *wsb = (char *)ws;
-    void *col = wsb;
-    float *partial = (float *)(wsb + h->off_big);
-    D4R_LAUNCH(step_im2col(h, x, col, s, "fwd"), "im2col");
-    D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_ROWS, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
-                        bias, g.P, partial, s, "fwd"),
-               "forward GEMM");
-    return ok();
-}
+namespace {
 
-d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w, const float *bias,
-                                     float *y, void *ws, size_t ws_bytes, void *hip_stream)
+// The forward in both forms: im2col + GEMM (col left at the start of ws) or
+// the implicit GEMM (1x1 convolutions read x in place); the GEMM's epilogue
+// adds the bias and, with relu, applies ReLU before storing y.
+d4r_status conv_forward(d4r_conv_t h, const void *x, const void *w, const float *bias, float *y,
+                        void *ws, size_t ws_bytes, void *hip_stream, bool implicit, int relu)
 {
     if (!h)
         return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
@@ -758,17 +750,46 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
     hipStream_t s = (hipStream_t)hip_stream;
     const ConvGeom &g = h->g;
     float *partial = (float *)((char *)ws + h->off_big);
-    if (h->pointwise) {
+    if (!implicit) {
+        void *col = ws;
+        D4R_LAUNCH(step_im2col(h, x, col, s, "fwd"), "im2col");
+        D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_ROWS, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y,
+                            0, bias, g.P, partial, s, "fwd", nullptr, 0, 0, nullptr, relu),
+                   "forward GEMM");
+    } else if (h->pointwise) {
         // 1x1: y[b] = Wmat * x[b] with x read in place (C channels)
         D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_NCHW, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
-                            bias, g.P, partial, s, "fwd", &g, 0, g.C),
+                            bias, g.P, partial, s, "fwd", &g, 0, g.C, nullptr, relu),
                    "pointwise forward GEMM");
-        return ok();
+    } else {
+        D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_IMPL, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
+                            bias, g.P, partial, s, "fwd", &g, 0, 0, nullptr, relu),
+                   "implicit forward GEMM");
     }
-    D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_IMPL, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0, bias,
-                        g.P, partial, s, "fwd", &g),
-               "implicit forward GEMM");
     return ok();
+}
+
+}  // namespace
+
+d4r_status d4r_conv_forward(d4r_conv_t h, const void *x, const void *w, const float *bias, float *y,
+                            void *ws, size_t ws_bytes, void *hip_stream)
+{
+    return conv_forward(h, x, w, bias, y, ws, ws_bytes, hip_stream, false, 0);
+}
+
+d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w, const float *bias,
+                                     float *y, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    return conv_forward(h, x, w, bias, y, ws, ws_bytes, hip_stream, true, 0);
+}
+
+d4r_status d4r_conv_forward_ex(d4r_conv_t h, const void *x, const void *w, const float *bias, float *y,
+                               int flags, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (flags & ~(D4R_FWD_RELU | D4R_FWD_IMPLICIT))
+        return fail(D4R_ERR_INVALID_ARG, "flags %d has bits outside D4R_FWD_RELU | D4R_FWD_IMPLICIT", flags);
+    return conv_forward(h, x, w, bias, y, ws, ws_bytes, hip_stream, (flags & D4R_FWD_IMPLICIT) != 0,
+                        (flags & D4R_FWD_RELU) ? 1 : 0);
 }
 
 namespace {
@@ -1035,8 +1056,11 @@ d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dty
     return ok();
 }
 
-d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
-                    float *C, void *ws, size_t ws_bytes, void *hip_stream)
+namespace {
+
+d4r_status gemm_call(const char *what, int M, int K, int N, int flags, d4r_dtype dtype, const void *A,
+                     const void *B, const float *bias, int relu, float *C, void *ws, size_t ws_bytes,
+                     void *hip_stream)
 {
     D4R_TRY(check_gemm_args(M, K, N, flags, dtype));
     D4R_TRY(check_tensor(A, "A"));
@@ -1058,10 +1082,27 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
     const int bmode = (flags & 2) ? OP_KC : OP_ROWS;
     const int lda = amode == OP_KC ? K : M;
     const int ldb = bmode == OP_KC ? K : N;
-    D4R_LAUNCH(run_gemm(dtype, pl, amode, bmode, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
-                        (float *)ws, (hipStream_t)hip_stream, "gemm"),
+    D4R_LAUNCH(run_gemm(dtype, pl, amode, bmode, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, bias, 0,
+                        (float *)ws, (hipStream_t)hip_stream, what, nullptr, 0, 0, nullptr, relu),
                "GEMM");
     return ok();
+}
+
+}  // namespace
+
+d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
+                    float *C, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    return gemm_call("gemm", M, K, N, flags, dtype, A, B, nullptr, 0, C, ws, ws_bytes, hip_stream);
+}
+
+d4r_status d4r_gemm_bias_act(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
+                             const float *bias, int relu, float *C, void *ws, size_t ws_bytes,
+                             void *hip_stream)
+{
+    D4R_TRY(check_vec(bias, "bias"));
+    return gemm_call("gemm_bias", M, K, N, flags, dtype, A, B, bias, relu ? 1 : 0, C, ws, ws_bytes,
+                     hip_stream);
 }
 
 /* ---- the rest of a training step (f32) ---- */

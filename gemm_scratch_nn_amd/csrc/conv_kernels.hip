@@ -633,24 +633,23 @@ __global__ __launch_bounds__(NT) void bias_final_kernel(const float *__restrict_
 //    four partial sums are added in quarter order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void splitk_store(float acc, long long idx, int M, int N, int epi, float *C,
-                                             int ldc, const float *bias, int P)
+                                             int ldc, const float *bias, int P, int relu)
 {
     const int m = (int)(idx / N);
     const int n = (int)(idx - (long long)m * N);
+    const float v = epi_value(acc, bias, relu, epi, m, n);
     if (epi == EPI_NCHW) {
-        if (bias)
-            acc += bias[m];
         const int b = n / P, pix = n - b * P;
-        C[((long long)b * M + m) * P + pix] = acc;
+        C[((long long)b * M + m) * P + pix] = v;
     } else {
-        C[(long long)m * ldc + n] = acc;
+        C[(long long)m * ldc + n] = v;
     }
 }
 
 __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__restrict__ part, int splits,
                                                                int M, int N, long long stride, int epi,
                                                                float *__restrict__ C, int ldc,
-                                                               const float *__restrict__ bias, int P)
+                                                               const float *__restrict__ bias, int P, int relu)
 {
     const long long total = (long long)M * N;
     const long long i0 = ((long long)blockIdx.x * NT + threadIdx.x) * 4;
@@ -681,13 +680,13 @@ __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__re
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        splitk_store(acc[e], i0 + e, M, N, epi, C, ldc, bias, P);
+        splitk_store(acc[e], i0 + e, M, N, epi, C, ldc, bias, P, relu);
 }
 
 __global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__restrict__ part, int splits,
                                                                  int M, int N, long long stride, int epi,
                                                                  float *__restrict__ C, int ldc,
-                                                                 const float *__restrict__ bias, int P)
+                                                                 const float *__restrict__ bias, int P, int relu)
 {
     constexpr int G = NT / 64;  // split groups per block
     __shared__ float red[G][64];
@@ -718,7 +717,7 @@ __global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__
 #pragma unroll
         for (int g2 = 1; g2 < G; ++g2)
             t += red[g2][lane];
-        splitk_store(t, idx, M, N, epi, C, ldc, bias, P);
+        splitk_store(t, idx, M, N, epi, C, ldc, bias, P, relu);
     }
 }
 
@@ -962,7 +961,8 @@ hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, voi
 }
 
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long split_stride,
-                                int epi, float *C, int ldc, const float *bias, int P, hipStream_t s)
+                                int epi, float *C, int ldc, const float *bias, int P, int relu,
+                                hipStream_t s)
 {
     const long long total = (long long)M * N;
     const long long vthreads = (total + 3) / 4;
@@ -970,10 +970,10 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, lon
     // the vector path needs enough threads to fill the chip
     if (vec && vthreads >= 64LL * 1024)
         hipLaunchKernelGGL(splitk_reduce_vec_kernel, dim3((unsigned)((vthreads + NT - 1) / NT)), dim3(NT), 0,
-                           s, part, splits, M, N, split_stride, epi, C, ldc, bias, P);
+                           s, part, splits, M, N, split_stride, epi, C, ldc, bias, P, relu);
     else
         hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3((unsigned)((total + 63) / 64)), dim3(NT), 0, s,
-                           part, splits, M, N, split_stride, epi, C, ldc, bias, P);
+                           part, splits, M, N, split_stride, epi, C, ldc, bias, P, relu);
     return hipGetLastError();
 }
 

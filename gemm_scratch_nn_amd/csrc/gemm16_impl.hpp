@@ -307,7 +307,7 @@ __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h
 // Epilogue of a wavefront's TM x TN accumulator blocks, whose top-left
 // output is (m0, n0): accumulator element e of a 32x32 block is row
 // 8*(e/4) + 4*h + (e%4), column l32.  Row-major store (split-K partials at
-// blockIdx.z) or the NCHW store with bias.
+// blockIdx.z) or the NCHW store, bias and ReLU as p says (epi_value).
 template <int TM, int TN>
 __device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&acc)[TM][TN], int m0, int n0,
                                           int h, int l32)
@@ -331,12 +331,8 @@ __device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < p.M) {
-                    float v = acc[i][j][e];
-                    if (p.epi == EPI_NCHW && p.bias)
-                        v += p.bias[m];
-                    C[col_off + (long long)m * row_stride] = v;
-                }
+                if (m < p.M)
+                    C[col_off + (long long)m * row_stride] = epi_value(acc[i][j][e], p.bias, p.relu, p.epi, m, n);
             }
         }
     }

@@ -606,8 +606,16 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
             for (int q = tid; q < BM * QR; q += NT) {
                 const int r = q / QR, c = (q - r * QR) * 4;
                 const int m = m_blk + r, n = n_blk + c;
-                if (m < p.M && n < p.N)
-                    *(float4 *)(C + (long long)m * p.ldc + n) = *(const float4 *)(cs + r * CP + c);
+                if (m < p.M && n < p.N) {
+                    float4 v = *(const float4 *)(cs + r * CP + c);
+                    if (p.bias || p.relu) {
+                        v.x = epi_value(v.x, p.bias, p.relu, EPI_ROWMAJOR, m, n);
+                        v.y = epi_value(v.y, p.bias, p.relu, EPI_ROWMAJOR, m, n + 1);
+                        v.z = epi_value(v.z, p.bias, p.relu, EPI_ROWMAJOR, m, n + 2);
+                        v.w = epi_value(v.w, p.bias, p.relu, EPI_ROWMAJOR, m, n + 3);
+                    }
+                    *(float4 *)(C + (long long)m * p.ldc + n) = v;
+                }
             }
             return;
         }
@@ -631,12 +639,8 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 int m = m_blk + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < p.M) {
-                    float v = acc[i][j][e];
-                    if (p.epi == EPI_NCHW && p.bias)
-                        v += p.bias[m];
-                    C[col_off + (long long)m * row_stride] = v;
-                }
+                if (m < p.M)
+                    C[col_off + (long long)m * row_stride] = epi_value(acc[i][j][e], p.bias, p.relu, p.epi, m, n);
             }
         }
     }

@@ -55,10 +55,22 @@ __device__ __forceinline__ int xcd_tile(int pid, int n)
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// Store of a GEMM result v = acc (+ bias) (then max(v, 0) with p.relu):
 enum Epilogue : int {
-    EPI_ROWMAJOR = 0,  // C[m*ldc + n] (+ blockIdx.z * c_split_stride)
-    EPI_NCHW = 1       // y[((n/P)*M + m)*P + n%P] = acc + bias[m]
+    EPI_ROWMAJOR = 0,  // C[m*ldc + n] (+ blockIdx.z * c_split_stride); bias per column n
+    EPI_NCHW = 1       // y[((n/P)*M + m)*P + n%P]; bias per row m (the output channel)
 };
+
+// The epilogue's value: bias (per row for EPI_NCHW, per column otherwise)
+// and ReLU (x > 0 ? x : 0, so NaN gives 0 like the ReLU kernel).
+__device__ __forceinline__ float epi_value(float v, const float *bias, int relu, int epi, int m, int n)
+{
+    if (bias)
+        v += bias[epi == EPI_NCHW ? m : n];
+    if (relu)
+        v = v > 0.0f ? v : 0.0f;
+    return v;
+}
 
 struct ConvGeom {
     int B, C, H, W, O, kH, kW, s, p, OH, OW;
@@ -100,6 +112,7 @@ struct GemmParams {
     int lda, ldb, ldc;
     int P;              // EPI_NCHW: pixels per image
     int epi;
+    int relu;           // apply ReLU after the bias
     int k_per_split;    // multiple of the tile's K depth
     int splits;
     long long c_split_stride;
@@ -145,7 +158,7 @@ hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, voi
 // out = sum over s of part[s] (fixed order) with the GEMM epilogue
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,
-                                const float *bias, int P, hipStream_t s);
+                                const float *bias, int P, int relu, hipStream_t s);
 
 // The rest of a training step (f32; train_kernels.hip).  Elementwise
 // kernels take 16-byte aligned pointers; n may be 0.

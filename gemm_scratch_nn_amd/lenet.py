@@ -9,6 +9,10 @@ im2col Approach"): conv gradients by im2col + GEMM (the saved col matrix is
 reused for the filter gradient), linear gradients by the matmul flags, the
 loss gradient softmax - one_hot.
 
+Each layer's bias and ReLU run in the epilogue of its GEMM (conv forward
+with D4R_FWD_RELU, linear layers through d4r_gemm_bias_act), so the
+activations are stored once.
+
 Marshalling and sequencing only: every value is computed by a library
 kernel.  torch provides the device buffers (allocated once, in the
 constructor) and the stream, so a whole step can be captured in a HIP graph
@@ -23,9 +27,9 @@ from typing import Dict
 
 import torch
 
-from . import (ConvPlan, D4R_F32, d4r_add_bias_rows, d4r_bias_grad_rows, d4r_gemm,
+from . import (ConvPlan, D4R_F32, d4r_bias_grad_rows, d4r_gemm, d4r_gemm_bias_act,
                d4r_gemm_workspace_size, d4r_maxpool_backward, d4r_maxpool_forward,
-               d4r_relu_backward, d4r_relu_forward, d4r_sgd_update, d4r_softmax_ce_grad)
+               d4r_relu_backward, d4r_sgd_update, d4r_softmax_ce_grad)
 
 PARAMS = (("conv1_w", (6, 1, 5, 5)), ("conv1_b", (6,)),
           ("conv2_w", (16, 6, 5, 5)), ("conv2_b", (16,)),
@@ -105,6 +109,10 @@ class LeNetStep:
     def _gemm(self, M, K, N, flags, A, Bm, C):
         d4r_gemm(M, K, N, flags, D4R_F32, A, Bm, C, self.gws, self.gws_bytes)
 
+    def _linear(self, M, K, N, x, w, b, relu, out):
+        # out = x * w^T + b (then ReLU): matmul flags 2 with the fused epilogue
+        d4r_gemm_bias_act(M, K, N, 2, D4R_F32, x, w, b, relu, out, self.gws, self.gws_bytes)
+
     def forward_backward(self, x: torch.Tensor, labels: torch.Tensor) -> None:
         """Loss, every gradient (into flat_grad) for one batch; no update."""
         B, p, g = self.batch, self.p, self.g
@@ -112,21 +120,14 @@ class LeNetStep:
             raise ValueError("x must be float32 of shape (batch, 1, 28, 28)")
         if tuple(labels.shape) != (B,) or labels.dtype != torch.int32:
             raise ValueError("labels must be int32 of shape (batch,)")
-        # forward
-        self.c1.forward(x, p["conv1_w"], p["conv1_b"], y=self.a1)
-        d4r_relu_forward(self.a1, self.a1, self.a1.numel())
+        # forward (the conv forwards keep col in their workspaces)
+        self.c1.forward_relu(x, p["conv1_w"], p["conv1_b"], y=self.a1)
         d4r_maxpool_forward(self.a1, self.p1, self.idx1, B, 6, 24, 24, 2, 2)
-        self.c2.forward(self.p1, p["conv2_w"], p["conv2_b"], y=self.a2)
-        d4r_relu_forward(self.a2, self.a2, self.a2.numel())
+        self.c2.forward_relu(self.p1, p["conv2_w"], p["conv2_b"], y=self.a2)
         d4r_maxpool_forward(self.a2, self.p2, self.idx2, B, 16, 8, 8, 2, 2)
-        self._gemm(B, 256, 120, 2, self.p2, p["fc1_w"], self.h1)
-        d4r_add_bias_rows(self.h1, p["fc1_b"], self.h1, B, 120)
-        d4r_relu_forward(self.h1, self.h1, self.h1.numel())
-        self._gemm(B, 120, 84, 2, self.h1, p["fc2_w"], self.h2)
-        d4r_add_bias_rows(self.h2, p["fc2_b"], self.h2, B, 84)
-        d4r_relu_forward(self.h2, self.h2, self.h2.numel())
-        self._gemm(B, 84, 10, 2, self.h2, p["fc3_w"], self.z)
-        d4r_add_bias_rows(self.z, p["fc3_b"], self.z, B, 10)
+        self._linear(B, 256, 120, self.p2, p["fc1_w"], p["fc1_b"], 1, self.h1)
+        self._linear(B, 120, 84, self.h1, p["fc2_w"], p["fc2_b"], 1, self.h2)
+        self._linear(B, 84, 10, self.h2, p["fc3_w"], p["fc3_b"], 0, self.z)
         # loss gradient
         d4r_softmax_ce_grad(self.z, labels, self.dz, self.loss, B, 10)
         # fc3, fc2, fc1 (ReLU masks from the stored ReLU outputs)

@@ -159,6 +159,29 @@ d4r_status d4r_conv_forward_implicit(d4r_conv_t h, const void *x, const void *w,
                                      size_t ws_bytes, void *hip_stream);
 
 /*
+ * Forward with the layer's activation fused (the directcompute-nn page
+ * trains LeNet-5 and AlexNet, "File Structure", whose hidden convolutions
+ * are followed by ReLU, the page's relu shader, "Activation / Loss
+ * Shaders"):
+ * y = relu(conv(x; w) + bias) when flags has D4R_FWD_RELU, where relu(v) =
+ * v if v > 0 else 0 (NaN gives 0, as d4r_relu_forward).  The GEMM's
+ * epilogue (or the split-K reduction) applies it before the only store of
+ * y, so y equals d4r_conv_forward followed by d4r_relu_forward bit for bit
+ * without a second pass over y.  D4R_FWD_IMPLICIT selects the implicit
+ * GEMM of d4r_conv_forward_implicit (ws then does not hold col); without it
+ * col is left at the start of ws as by d4r_conv_forward.  flags = 0 is
+ * d4r_conv_forward.  The ReLU backward needs the stored y (dx = dy where
+ * y > 0), so y is what d4r_relu_backward takes as x.
+ * Errors: those of d4r_conv_forward, and D4R_ERR_INVALID_ARG for other
+ * flag bits.
+ */
+#define D4R_FWD_RELU 1
+#define D4R_FWD_IMPLICIT 2
+d4r_status d4r_conv_forward_ex(d4r_conv_t h, const void *x, const void *w,
+                               const float *bias, float *y, int flags, void *ws,
+                               size_t ws_bytes, void *hip_stream);
+
+/*
  * Data gradient (page: Input gradients = filters^T x grad_reshaped, then
  * col2im): dx = col2im(Wmat^T * G).  w, dy in the handle's dtype; dx
  * float32, fully overwritten.  dcol is float32 in ws, after the col region.
@@ -262,6 +285,24 @@ d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dty
 d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void *A,
                     const void *B, float *C, void *ws, size_t ws_bytes,
                     void *hip_stream);
+
+/*
+ * A linear layer's forward in one call: C = op(A) * op(B) + bias, then
+ * ReLU when relu != 0 (the directcompute-nn page's fully connected layer is
+ * matmul then add_bias, x * W^T being flags 2, "Matmul Shaders" and
+ * "Utility Shaders"; hidden layers of its LeNet-5 and AlexNet apply ReLU
+ * next, "File Structure").
+ * bias has N float32 entries, added per column: C[m][n] = sum + bias[n];
+ * NULL adds nothing.  The epilogue applies both before the one store of C
+ * (the split-K reduction does when the GEMM splits K), so C equals d4r_gemm,
+ * then d4r_add_bias_rows, then d4r_relu_forward, bit for bit.  Workspace
+ * as d4r_gemm_workspace_size gives for the same M, K, N, flags, dtype.
+ * Errors: those of d4r_gemm; bias misaligned (4 bytes).
+ */
+d4r_status d4r_gemm_bias_act(int M, int K, int N, int flags, d4r_dtype dtype,
+                             const void *A, const void *B, const float *bias,
+                             int relu, float *C, void *ws, size_t ws_bytes,
+                             void *hip_stream);
 
 /*
  * The rest of a training step around the convolutions (directcompute-nn

@@ -127,6 +127,24 @@ def test_forward_implicit_argument_errors(handle):
     assert e.value.status == WORKSPACE
 
 
+def test_forward_ex_argument_errors(handle):
+    ws = _ws(handle)
+    for flags in (4, -1, 8 | d4r.D4R_FWD_RELU):
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_forward_ex(handle, FAKE, FAKE, None, FAKE, flags, FAKE, ws, stream=0)
+        assert e.value.status == INVALID, flags
+    for flags in (0, 1, 2, 3):
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_forward_ex(handle, FAKE, FAKE, FAKE + 2, FAKE, flags, FAKE, ws, stream=0)
+        assert e.value.status == INVALID, flags  # bias misaligned
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_conv_forward_ex(handle, FAKE, FAKE, None, FAKE, flags, FAKE, ws - 1, stream=0)
+        assert e.value.status == WORKSPACE, flags
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_forward_ex(None, FAKE, FAKE, None, FAKE, 1, FAKE, ws, stream=0)
+    assert e.value.status == INVALID
+
+
 def test_backward_data_implicit_argument_errors(handle):
     ws = _ws(handle)
     for args, code in [((None, FAKE, FAKE, FAKE, ws), INVALID), ((FAKE, None, FAKE, FAKE, ws), INVALID),
@@ -208,6 +226,23 @@ def test_gemm_pointer_and_workspace_errors():
     assert e.value.status == WORKSPACE
     with pytest.raises(D4RError) as e:
         d4r.d4r_gemm(96, 96800, 363, 2, D4R_F32, FAKE, FAKE, FAKE, FAKE, need - 4, stream=0)
+    assert e.value.status == WORKSPACE
+
+
+def test_gemm_bias_act_argument_errors():
+    for args in [(0, 4, 4, 0, D4R_F32), (4, 4, 4, 4, D4R_F32), (4, 4, 4, 0, 9)]:
+        with pytest.raises(D4RError) as e:
+            d4r.d4r_gemm_bias_act(*args, FAKE, FAKE, FAKE, 1, FAKE, None, 0, stream=0)
+        assert e.value.status == INVALID, args
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm_bias_act(64, 256, 120, 2, D4R_F32, FAKE, FAKE, FAKE + 2, 1, FAKE, None, 0, stream=0)
+    assert e.value.status == INVALID  # bias misaligned
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm_bias_act(64, 256, 120, 2, D4R_F32, FAKE, None, FAKE, 0, FAKE, None, 0, stream=0)
+    assert e.value.status == INVALID
+    need = d4r.d4r_gemm_workspace_size(96, 96800, 363, 2, D4R_F32)
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_gemm_bias_act(96, 96800, 363, 2, D4R_F32, FAKE, FAKE, None, 1, FAKE, FAKE, need - 4, stream=0)
     assert e.value.status == WORKSPACE
 
 

@@ -1,10 +1,10 @@
 """A whole LeNet-5 training step on the GPU against the oracle's step.
 
 The step (gemm_scratch_nn_amd.lenet.LeNetStep) issues only library calls:
-two im2col + GEMM convolutions with their filter, data and bias gradients,
-ReLU, max pooling with argmax, three linear layers (matmul flags + row
-bias), the softmax-cross-entropy gradient and one SGD launch over all
-parameters.  The oracle (oracle.lenet_step) composes its float64 routines
+two im2col + GEMM convolutions (bias and ReLU in the GEMM epilogue) with
+their filter, data and bias gradients, the ReLU gradient, max pooling with
+argmax, three linear layers (matmul flags, bias and ReLU in the epilogue),
+the softmax-cross-entropy gradient and one SGD launch over all parameters.  The oracle (oracle.lenet_step) composes its float64 routines
 in the same order.
 
 Inputs (workloads.lenet_step_inputs): the image and the conv parameters are
