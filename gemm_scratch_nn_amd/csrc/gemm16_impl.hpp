@@ -306,13 +306,13 @@ __device__ __forceinline__ u32x4_t frag16(const char *lds, int row, int q, int h
 
 // Epilogue of a wavefront's TM x TN accumulator blocks, whose top-left
 // output is (m0, n0): accumulator element e of a 32x32 block is row
-// 8*(e/4) + 4*h + (e%4), column l32.  Row-major store (split-K partials at
-// blockIdx.z) or the NCHW store, bias and ReLU as p says (epi_value).
+// 8*(e/4) + 4*h + (e%4), column l32.  Row-major store (the partials of
+// split `split`) or the NCHW store, bias and ReLU as p says (epi_value).
 template <int TM, int TN>
 __device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&acc)[TM][TN], int m0, int n0,
-                                          int h, int l32)
+                                          int h, int l32, int split)
 {
-    float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+    float *C = p.C + (long long)split * p.c_split_stride;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int n = n0 + j * 32 + l32;
@@ -359,12 +359,11 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
     const int h = lane >> 5, l32 = lane & 31;
 
     const int mt = (p.M + BM - 1) / BM;
-    const int ntiles = mt * ((p.N + BN - 1) / BN);
-    const int tile = xcd_tile(blockIdx.x, ntiles);
-    const int m_blk = (tile % mt) * BM;
-    const int n_blk = (tile / mt) * BN;
+    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
+    const int m_blk = (wi.tile % mt) * BM;
+    const int n_blk = (wi.tile / mt) * BN;
 
-    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kbeg = wi.split * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg + BK - 1) / BK;
 
@@ -453,7 +452,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
             compute(smem, smem + TA::LDS_BYTES);
     }
 
-    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32);
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, wi.split);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,10 +587,10 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     const int h = lane >> 5, l32 = lane & 31;
 
     const int mt = (p.M + BM - 1) / BM;
-    const int tile = xcd_tile(blockIdx.x, mt * ((p.N + BN - 1) / BN));
-    const int m_blk = (tile % mt) * BM;
-    const int n_blk = (tile / mt) * BN;
-    const int kbeg = blockIdx.z * p.k_per_split;
+    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
+    const int m_blk = (wi.tile % mt) * BM;
+    const int n_blk = (wi.tile / mt) * BN;
+    const int kbeg = wi.split * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg) / BK;
 
@@ -667,7 +666,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     // drain the loads of the stages past the end before the workgroup exits
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
-    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32);
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, wi.split);
 }
 
 // 64-deep stages in a ring of three (two stages of loads in flight):
@@ -688,7 +687,7 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
-    const dim3 grid(tiles, 1, p.splits), b8(512);
+    const dim3 grid(tiles * p.splits), b8(512);
     switch (cfg) {
     case TILE_128x256:
         hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
@@ -707,7 +706,7 @@ hipError_t launch_gemm16_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
-    const dim3 grid(tiles, 1, p.splits), b4(256), b8(512);
+    const dim3 grid(tiles * p.splits), b4(256), b8(512);
     switch (cfg) {
     case TILE_128x128:
         hipLaunchKernelGGL((gemm16_kernel<DTID, 2, 2, 2, 2, A_KC, B_KC, VEC, IMPL, A_NC, B_NC>), grid, b4, 0, s,

@@ -444,11 +444,11 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
     const int h = lane >> 5, l32 = lane & 31;
 
     const int mt = (p.M + BM - 1) / BM;
-    const int tile = xcd_tile(blockIdx.x, mt * ((p.N + BN - 1) / BN));
-    const int m_blk = (tile % mt) * BM;
-    const int n_blk = (tile / mt) * BN;
+    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
+    const int m_blk = (wi.tile % mt) * BM;
+    const int n_blk = (wi.tile / mt) * BN;
 
-    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kbeg = wi.split * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg + BK - 1) / BK;
 
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_kernel(GemmParams p)
 
     // Epilogue.  Accumulator element e of a 32x32 block sits at
     // row 8*(e/4) + 4*h + (e%4), column l32.
-    float *C = p.C + (long long)blockIdx.z * p.c_split_stride;
+    float *C = p.C + (long long)wi.split * p.c_split_stride;
 
     // Row-major output (split-K partials, dcol, dW, plain GEMMs) with rows
     // of 16-byte aligned columns: the tile goes through LDS, so every lane
@@ -651,7 +651,7 @@ hipError_t launch_gemm32_vec(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
-    dim3 grid(tiles, 1, p.splits);
+    dim3 grid(tiles * p.splits);
     switch (cfg) {
     case TILE_128x128:
         hipLaunchKernelGGL((gemm_kernel<2, 2, 2, 2, AMODE, BMODE, VEC>), grid, dim3(256), 0, s, p);

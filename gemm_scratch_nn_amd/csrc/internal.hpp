@@ -55,6 +55,20 @@ __device__ __forceinline__ int xcd_tile(int pid, int n)
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// Work item of workgroup `pid` in a GEMM's 1-D grid of tiles x splits.  The
+// XCD renumbering runs over all work items with the split outermost, so the
+// contiguous range one XCD receives covers one or two K ranges (split-K
+// slices) of the operands instead of a share of every slice: each XCD's L2
+// then fetches the operand rows of its own K ranges only.
+struct WorkItem {
+    int tile, split;
+};
+__device__ __forceinline__ WorkItem xcd_work(int pid, int tiles, int splits)
+{
+    const int w = xcd_tile(pid, tiles * splits);
+    return {w % tiles, w / tiles};
+}
+
 // Store of a GEMM result v = acc (+ bias) (then max(v, 0) with p.relu):
 enum Epilogue : int {
     EPI_ROWMAJOR = 0,  // C[m*ldc + n] (+ blockIdx.z * c_split_stride); bias per column n
