@@ -589,8 +589,11 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
     // the NHWC form needs whole GEMM stages of dy (32 f32 / 64 16-bit
-    // channels) within one tap
-    h->dgrad_nhwc = h->dgrad_impl && outC % gemm_bk(dtype) == 0;
+    // channels) within one tap; the 16-bit loader decodes a stage's tap
+    // with small_div, exact for stage indices below 2^20 and divisors <= 1024
+    h->dgrad_nhwc = h->dgrad_impl && outC % gemm_bk(dtype) == 0 &&
+                    (long long)h->gd.Kc / gemm_bk(dtype) < (1 << 20) && outC / gemm_bk(dtype) <= 1024 &&
+                    kW <= 1024;
     if (const char *e = getenv("D4R_DGRAD_NHWC"))  // experiments, tests: 0 = gathered path
         h->dgrad_nhwc = h->dgrad_nhwc && e[0] != '0';
     if (h->dgrad_nhwc)

@@ -550,8 +550,11 @@ struct DlImplNhwc {
     __device__ __forceinline__ void issue(const uint16_t *X, const uint16_t *zero, int k0, char *lds, int wave,
                                           const ConvGeom &g) const
     {
-        const int tap = k0 / g.C, c0 = k0 - tap * g.C;
-        const int u = tap / g.kW, v = tap - (tap / g.kW) * g.kW;
+        // k0 is a whole stage (kDlBK channels of one tap); divisor
+        // C / kDlBK <= 1024 and stage index < 2^20 (checked by the host)
+        const int ks = k0 / kDlBK, cb = g.C / kDlBK;
+        const int tap = small_div(ks, cb), c0 = (ks - tap * cb) * kDlBK;
+        const int u = small_div(tap, g.kW), v = tap - u * g.kW;
 #pragma unroll
         for (int j = 0; j < LD; ++j) {
             const int hh = h0[j] + u, ww = w0[j] + v;

@@ -55,6 +55,16 @@ __device__ __forceinline__ int xcd_tile(int pid, int n)
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// floor(n / d) for 0 <= n < 2^20 and 1 <= d <= 1024, from the hardware
+// reciprocal (v_rcp_f32, within 1 ulp) instead of an integer division
+// sequence: (n + 0.5) / d lies at least 0.5 / d from an integer, more than
+// the float error over that range (checked exhaustively on the host with
+// the reciprocal rounded either way).  Callers guarantee the ranges.
+__device__ __forceinline__ int small_div(int n, int d)
+{
+    return (int)(((float)n + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
 // Work item of workgroup `pid` in a GEMM's 1-D grid of tiles x splits.  The
 // XCD renumbering runs over all work items with the split outermost, so the
 // contiguous range one XCD receives covers one or two K ranges (split-K

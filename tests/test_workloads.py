@@ -65,3 +65,4 @@ def test_gemm_case_storage(key):
             assert ops["A"].stored.shape == (c.K, c.M)
         if c.flags & 2:
             assert ops["B"].stored.shape == (c.N, c.K)
+
