@@ -530,7 +530,12 @@ struct DlImplNhwc {
     static constexpr int BYTES = BR * ROWB;
     static_assert(BR % (LPL * NW) == 0, "whole load groups");
 
-    int b[LD], h0[LD], w0[LD], chk[LD];  // b < 0: row past N
+    // per load: window origin (h0 far negative for rows past N, so no tap
+    // is ever in range) and the element offset of the origin's channel
+    // chunk, ((b*H + h0)*W + w0)*C + chunk*8; a stage adds its tap's
+    // uniform offset (u*W + v)*C + c0
+    int h0[LD], w0[LD];
+    long long base[LD];
 
     __device__ __forceinline__ void setup(int n0, const ConvGeom &g, int wave, int lane)
     {
@@ -538,12 +543,12 @@ struct DlImplNhwc {
         for (int j = 0; j < LD; ++j) {
             const int lr = (j * NW + wave) * LPL + lane / 8;
             const int n = n0 + lr;
-            chk[j] = (lane % 8) ^ swz(lr);
+            const int chk = (lane % 8) ^ swz(lr);
             const int bb = n / g.P, r = n - (n / g.P) * g.P;
             const int i = r / g.OW;
-            b[j] = n < g.N ? bb : -1;
-            h0[j] = i - g.p;
+            h0[j] = n < g.N ? i - g.p : -(1 << 30);
             w0[j] = r - i * g.OW - g.p;
+            base[j] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[j]) * g.C + chk * 8;
         }
     }
 
@@ -555,12 +560,11 @@ struct DlImplNhwc {
         const int ks = k0 / kDlBK, cb = g.C / kDlBK;
         const int tap = small_div(ks, cb), c0 = (ks - tap * cb) * kDlBK;
         const int u = small_div(tap, g.kW), v = tap - u * g.kW;
+        const long long toff = ((long long)u * g.W + v) * g.C + c0;
 #pragma unroll
         for (int j = 0; j < LD; ++j) {
-            const int hh = h0[j] + u, ww = w0[j] + v;
-            const bool ok = b[j] >= 0 && (unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W;
-            const uint16_t *src = ok ? X + (((long long)b[j] * g.H + hh) * g.W + ww) * g.C + c0 + chk[j] * 8
-                                     : zero + chk[j] * 8;
+            const bool ok = (unsigned)(h0[j] + u) < (unsigned)g.H && (unsigned)(w0[j] + v) < (unsigned)g.W;
+            const uint16_t *src = ok ? X + base[j] + toff : zero + (base[j] & 63);
             __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)(lds + (j * NW + wave) * LPL * ROWB),
                                              16, 0, 0);
         }
