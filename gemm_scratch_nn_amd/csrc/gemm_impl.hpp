@@ -136,7 +136,11 @@ struct OperandTile {
 template <int BR, int NT>
 struct NhwcRows {
     using T = OperandTile<BR, true, NT>;
-    int b[T::PER], h0[T::PER], w0[T::PER];  // b < 0: no such row
+    // per slot: window origin (h0 far negative for a slot past N, so no tap
+    // is ever in range) and the element offset ((b*H + h0)*W + w0)*C + kk;
+    // a stage adds its tap's uniform offset (u*W + v)*C + c0
+    int h0[T::PER], w0[T::PER];
+    long long base[T::PER];
 
     __device__ __forceinline__ void setup(const ConvGeom &g, int n0, int tid)
     {
@@ -149,9 +153,9 @@ struct NhwcRows {
             const int n = n0 + row;
             const int bb = n / g.P, r = n - (n / g.P) * g.P;
             const int i = r / g.OW;
-            b[s] = (live && n < g.N) ? bb : -1;
-            h0[s] = i - g.p;
+            h0[s] = (live && n < g.N) ? i - g.p : -(1 << 30);
             w0[s] = r - i * g.OW - g.p;
+            base[s] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[s]) * g.C + kk;
         }
     }
 };
@@ -165,16 +169,15 @@ struct ImplNhwcTileF32 : OperandTile<BR, true, NT> {
     {
         const int tap = k0 / g.C, c0 = k0 - tap * g.C;
         const int u = tap / g.kW, v = tap - (tap / g.kW) * g.kW;
+        const long long toff = ((long long)u * g.W + v) * g.C + c0;
 #pragma unroll
         for (int s = 0; s < T::PER; ++s) {
             const int id = s * NT + tid;
             int row, kk;
             T::slot(id, row, kk);
-            const int hh = rows.h0[s] + u, ww = rows.w0[s] + v;
-            const bool ok = rows.b[s] >= 0 && k0 + kk < K && (unsigned)hh < (unsigned)g.H &&
-                            (unsigned)ww < (unsigned)g.W;
-            const long long off = (((long long)rows.b[s] * g.H + hh) * g.W + ww) * g.C + c0 + kk;
-            this->reg[s] = *(const u32x4 *)(X + (ok ? off : 0));
+            const bool ok = k0 + kk < K && (unsigned)(rows.h0[s] + u) < (unsigned)g.H &&
+                            (unsigned)(rows.w0[s] + v) < (unsigned)g.W;
+            this->reg[s] = *(const u32x4 *)(X + (ok ? rows.base[s] + toff : 0));
             this->okmask = (s == 0 ? 0u : this->okmask) | ((ok ? 1u : 0u) << s);
         }
     }
