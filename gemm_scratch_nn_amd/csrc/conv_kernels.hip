@@ -145,34 +145,46 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
     const int h_org = i0 * g.s - g.p, w_org = -g.p;
 
     // Fill: a thread keeps one window column q and walks the window rows
-    // (rows_per_pass of them are filled per pass), so no per-element division.
+    // (rows_per_pass of them are filled per pass), so no per-element
+    // division.  Loads go out FB at a time before their LDS stores, so a
+    // thread waits for one batch instead of once per row.
     {
+        constexpr int FB = 8;
         const int rpp = Wl <= NT ? NT / Wl : 1;
         const int r_off = Wl <= NT ? threadIdx.x / Wl : 0;
         const int q0 = Wl <= NT ? threadIdx.x - r_off * Wl : threadIdx.x;
+        const int qstep = Wl <= NT ? Wl : NT;
         const int total_rows = nbb * Rl;
         if (r_off < rpp) {
-            int bb = 0, r = r_off;
-            while (r >= Rl) {
-                r -= Rl;
-                ++bb;
-            }
-            for (int rr = r_off; rr < total_rows; rr += rpp) {
-                const int hh = h_org + r;
-                const bool row_ok = hh >= 0 && hh < g.H;
-                const long long xrow = (((long long)(b0 + bb) * g.C + c) * g.H + hh) * g.W;
-                const int drow = (bb * Rl + r) * Wl;
-                for (int q = q0; q < Wl; q += (Wl <= NT ? Wl : NT)) {
-                    const int ww = w_org + q;
-                    T val = 0;
-                    if (row_ok && ww >= 0 && ww < g.W)
-                        val = x[xrow + ww];
-                    lds[lds_pad<T>(drow + q)] = val;
-                }
-                r += rpp;
-                while (r >= Rl) {
-                    r -= Rl;
-                    ++bb;
+            for (int q = q0; q < Wl; q += qstep) {
+                const int ww = w_org + q;
+                const bool col_ok = ww >= 0 && ww < g.W;
+                // (bb, r) of window row rr = bb*Rl + r, stepped by rpp
+                // (small_div: r + rpp < 2^20 and Rl <= 1024, checked by the
+                // host); out-of-window loads read x[0] and are discarded,
+                // so the batch has no branches to wait at
+                int bb = small_div(r_off, Rl), r = r_off - bb * Rl;
+                for (int rr = r_off; rr < total_rows; rr += FB * rpp) {
+                    T val[FB];
+                    int dst[FB];
+#pragma unroll
+                    for (int k = 0; k < FB; ++k) {
+                        const bool live = rr + k * rpp < total_rows;
+                        const int hh = h_org + r;
+                        const bool ok = live && col_ok && (unsigned)hh < (unsigned)g.H;
+                        const long long a = (((long long)(b0 + bb) * g.C + c) * g.H + hh) * g.W + ww;
+                        const T v = x[ok ? a : 0];
+                        val[k] = ok ? v : (T)0;
+                        dst[k] = live ? (bb * Rl + r) * Wl + q : -1;
+                        r += rpp;
+                        const int wr = small_div(r, Rl);
+                        r -= wr * Rl;
+                        bb += wr;
+                    }
+#pragma unroll
+                    for (int k = 0; k < FB; ++k)
+                        if (dst[k] >= 0)
+                            lds[lds_pad<T>(dst[k])] = val[k];
                 }
             }
         }
@@ -753,14 +765,21 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
 {
     const int VW = dt == DT_F32 ? 4 : 8;
     const int es = dt == DT_F32 ? 4 : 2;
-    // LDS-staged path: a block covers ~16K col elements (whole images of one
-    // channel when an image is small, else a range of output rows) and its
-    // input window must fit in 48 KB; otherwise the direct gather below.
+    // LDS-staged path: a block covers up to ~128K col elements (whole images
+    // of one channel when an image is small, else a range of output rows),
+    // halved until the grid has 2048 blocks, and its input window must fit
+    // in 48 KB; otherwise the direct gather below.  (Measured against 16K
+    // and 1024 blocks: C4 bf16 im2col 25.3 -> 22.1 us, others level.)
     {
         const int khw = g.kH * g.kW;
         const int Wl = (g.OW - 1) * g.s + g.kW;
         const long long per_img = (long long)khw * g.OH * g.OW;
-        const long long target = 16384;
+        long long target = 131072;
+        long long min_blocks = 2048;
+        if (const char *e = getenv("D4R_IM2COL_TARGET"))  // experiments
+            target = atoll(e);
+        if (const char *e = getenv("D4R_IM2COL_MINBLK"))  // experiments
+            min_blocks = atoll(e);
         int RB = g.OH, BB = 1;
         if (per_img >= target) {
             RB = (int)(target / ((long long)khw * g.OW));
@@ -773,9 +792,9 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
         auto blocks = [&](int rb, int bb) {
             return (long long)((g.OH + rb - 1) / rb) * g.C * ((g.B + bb - 1) / bb);
         };
-        while (BB > 1 && blocks(RB, BB) < 1024)
+        while (BB > 1 && blocks(RB, BB) < min_blocks)
             BB = (BB + 1) / 2;
-        while (RB > 1 && blocks(RB, BB) < 1024)
+        while (RB > 1 && blocks(RB, BB) < min_blocks)
             RB = (RB + 1) / 2;
         int Rl = (RB - 1) * g.s + g.kH;
         while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
@@ -787,7 +806,7 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
         const long long win_elems = (long long)BB * Rl * Wl;
         const size_t shm = (size_t)(es == 4 ? lds_padded_elems<uint32_t>(win_elems)
                                             : lds_padded_elems<uint16_t>(win_elems)) * es;
-        if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535) {
+        if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535 && Rl <= 1024) {
             dim3 grid((g.OH + RB - 1) / RB, g.C, (g.B + BB - 1) / BB);
             const int vec = (g.N % VW) == 0;
             if (dt == DT_F32)
