@@ -683,16 +683,41 @@ __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__re
             acc[3] += v[u].w;
         }
     }
-    for (; sp < splits; ++sp) {
-        const float4 v = *(const float4 *)(part + sp * stride + i0);
-        acc[0] += v.x;
-        acc[1] += v.y;
-        acc[2] += v.z;
-        acc[3] += v.w;
-    }
+    if (sp < splits) {
+        // the last 1-3 slabs: all loads issued together (a slab past the
+        // end re-reads the last one and is not added), added in order
+        float4 v[3];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        splitk_store(acc[e], i0 + e, M, N, epi, C, ldc, bias, P, relu);
+        for (int u = 0; u < 3; ++u)
+            v[u] = *(const float4 *)(part + (long long)min(sp + u, splits - 1) * stride + i0);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            if (sp + u < splits) {
+                acc[0] += v[u].x;
+                acc[1] += v[u].y;
+                acc[2] += v[u].z;
+                acc[3] += v[u].w;
+            }
+        }
+    }
+    // one row m for all four; the NCHW position decoded once and stepped
+    const int m = (int)(i0 / N);
+    const int n0 = (int)(i0 - (long long)m * N);
+    if (epi == EPI_NCHW) {
+        int b = n0 / P, pix = n0 - b * P;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            C[((long long)b * M + m) * P + pix] = epi_value(acc[e], bias, relu, epi, m, n0 + e);
+            if (++pix == P) {
+                pix = 0;
+                ++b;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            C[(long long)m * ldc + n0 + e] = epi_value(acc[e], bias, relu, epi, m, n0 + e);
+    }
 }
 
 __global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__restrict__ part, int splits,
