@@ -291,7 +291,7 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
                     const void *B, int ldb, int M, int N, int K, int epi, float *C, int ldc,
                     const float *bias, int P, float *partial, hipStream_t s, const char *pass,
                     const ConvGeom *geom = nullptr, int a_ch = 0, int b_ch = 0, const void *zero = nullptr,
-                    int relu = 0)
+                    int relu = 0, const BiasSum *bsum = nullptr)
 {
     const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
@@ -345,11 +345,22 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
                  (double)es * ((double)M * K + b_bytes) + 4.0 * M * N);
     hipError_t e = launch_gemm(dt, pl.cfg, amode, bmode, p, s);
     ps.done();
-    if (e != hipSuccess || pl.splits == 1)
+    if (e != hipSuccess)
         return e;
+    const BiasSum none{nullptr, nullptr, 0, 0};
+    const BiasSum &bs = bsum ? *bsum : none;
+    if (pl.splits == 1) {
+        if (!bs.db)
+            return hipSuccess;
+        ProfScope pb(s, std::string("bias_final:") + pass, 0.0, 4.0 * bs.O * (bs.parts + 1.0));
+        e = launch_bias_final(bs.partial, bs.db, bs.O, bs.parts, s);
+        pb.done();
+        return e;
+    }
+    // the reduction's extra blocks finish the bias sum, if any
     ProfScope pr(s, std::string("splitk_reduce:") + pass, 0.0,
-                 4.0 * (double)M * N * (pl.splits + 1));
-    e = launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, relu, s);
+                 4.0 * (double)M * N * (pl.splits + 1) + (bs.db ? 4.0 * bs.O * (bs.parts + 1.0) : 0.0));
+    e = launch_splitk_reduce(partial, pl.splits, M, N, (long long)M * N, epi, C, ldc, bias, P, relu, bs, s);
     pr.done();
     return e;
 }
@@ -445,22 +456,13 @@ hipError_t step_transpose(const d4r_conv *h, int batch, int R, int C, const void
 }
 
 // With bias_part set, the reshape also produces the bias gradient's partial
-// sums, which step_bias_final then adds up.
+// sums (one per reshape block and channel), which a BiasSum adds up.
 hipError_t step_grad_reshape(const d4r_conv *h, const void *dy, void *G, float *bias_part, hipStream_t s)
 {
     const ConvGeom &g = h->g;
     ProfScope ps(s, std::string(bias_part ? "grad_reshape_bias_" : "grad_reshape_") + dt_name(h->dt) + ":wgrad",
                  0.0, 2.0 * h->es * (double)g.O * g.N);
     hipError_t e = launch_grad_reshape(h->dt, g, dy, G, bias_part, s);
-    ps.done();
-    return e;
-}
-
-hipError_t step_bias_final(const d4r_conv *h, const float *partial, float *db, hipStream_t s)
-{
-    const int splits = grad_reshape_blocks(h->dt, h->g);
-    ProfScope ps(s, "bias_final:wgrad", 0.0, 4.0 * h->g.O * (splits + 1.0));
-    hipError_t e = launch_bias_final(partial, db, h->g.O, splits, s);
     ps.done();
     return e;
 }
@@ -984,11 +986,12 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
         void *G = wsb + h->off_g;
         float *bias_part = db ? (float *)(wsb + h->off_bias) : nullptr;
         D4R_LAUNCH(step_grad_reshape(h, dy, G, bias_part, s), "grad reshape");
+        // the bias sum rides on the GEMM's split-K reduction (or follows it)
+        const BiasSum bs{bias_part, db, g.O, grad_reshape_blocks(h->dt, g)};
         D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N,
-                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad"),
-                   "filter-gradient GEMM");
-        if (db)
-            D4R_LAUNCH(step_bias_final(h, bias_part, db, s), "bias gradient");
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", nullptr, 0, 0, nullptr, 0,
+                            db ? &bs : nullptr),
+                   "filter-gradient GEMM and bias gradient");
         return ok();
     }
     if (db)

@@ -633,6 +633,19 @@ __global__ __launch_bounds__(NT) void bias_final_kernel(const float *__restrict_
     db[o] = tot;
 }
 
+// The same per-channel sum as bias_final_kernel, run by extra blocks of a
+// split-K reduction (block j of the job covers channels j*NT ..).
+__device__ __forceinline__ void bias_sum_job(const BiasSum &bs, int j)
+{
+    const int o = j * NT + threadIdx.x;
+    if (o >= bs.O)
+        return;
+    float tot = 0.0f;
+    for (int s = 0; s < bs.parts; ++s)
+        tot += bs.partial[o * bs.parts + s];
+    bs.db[o] = tot;
+}
+
 // ---------------------------------------------------------------------------
 // Split-K reduction: C = sum_{s} part[s], then the GEMM epilogue (row-major
 // store, or NCHW store with bias).  Two fixed summation orders:
@@ -661,8 +674,13 @@ __device__ __forceinline__ void splitk_store(float acc, long long idx, int M, in
 __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__restrict__ part, int splits,
                                                                int M, int N, long long stride, int epi,
                                                                float *__restrict__ C, int ldc,
-                                                               const float *__restrict__ bias, int P, int relu)
+                                                               const float *__restrict__ bias, int P, int relu,
+                                                               int rblocks, BiasSum bs)
 {
+    if ((int)blockIdx.x >= rblocks) {
+        bias_sum_job(bs, (int)blockIdx.x - rblocks);
+        return;
+    }
     const long long total = (long long)M * N;
     const long long i0 = ((long long)blockIdx.x * NT + threadIdx.x) * 4;
     if (i0 >= total)
@@ -723,8 +741,13 @@ __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__re
 __global__ __launch_bounds__(NT) void splitk_reduce_group_kernel(const float *__restrict__ part, int splits,
                                                                  int M, int N, long long stride, int epi,
                                                                  float *__restrict__ C, int ldc,
-                                                                 const float *__restrict__ bias, int P, int relu)
+                                                                 const float *__restrict__ bias, int P, int relu,
+                                                                 int rblocks, BiasSum bs)
 {
+    if ((int)blockIdx.x >= rblocks) {  // uniform per block: no barrier below is split
+        bias_sum_job(bs, (int)blockIdx.x - rblocks);
+        return;
+    }
     constexpr int G = NT / 64;  // split groups per block
     __shared__ float red[G][64];
     const long long total = (long long)M * N;
@@ -1006,18 +1029,22 @@ hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, voi
 
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long split_stride,
                                 int epi, float *C, int ldc, const float *bias, int P, int relu,
-                                hipStream_t s)
+                                const BiasSum &bs, hipStream_t s)
 {
     const long long total = (long long)M * N;
     const long long vthreads = (total + 3) / 4;
     const bool vec = (N % 4) == 0 && (split_stride % 4) == 0 && ((uintptr_t)part % 16) == 0;
+    const int bblocks = bs.db ? (bs.O + NT - 1) / NT : 0;
     // the vector path needs enough threads to fill the chip
-    if (vec && vthreads >= 64LL * 1024)
-        hipLaunchKernelGGL(splitk_reduce_vec_kernel, dim3((unsigned)((vthreads + NT - 1) / NT)), dim3(NT), 0,
-                           s, part, splits, M, N, split_stride, epi, C, ldc, bias, P, relu);
-    else
-        hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3((unsigned)((total + 63) / 64)), dim3(NT), 0, s,
-                           part, splits, M, N, split_stride, epi, C, ldc, bias, P, relu);
+    if (vec && vthreads >= 64LL * 1024) {
+        const int rb = (int)((vthreads + NT - 1) / NT);
+        hipLaunchKernelGGL(splitk_reduce_vec_kernel, dim3((unsigned)(rb + bblocks)), dim3(NT), 0, s, part, splits,
+                           M, N, split_stride, epi, C, ldc, bias, P, relu, rb, bs);
+    } else {
+        const int rb = (int)((total + 63) / 64);
+        hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3((unsigned)(rb + bblocks)), dim3(NT), 0, s, part,
+                           splits, M, N, split_stride, epi, C, ldc, bias, P, relu, rb, bs);
+    }
     return hipGetLastError();
 }
 

@@ -179,10 +179,19 @@ hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf
 // dy), and 256 zero bytes at `zero`
 hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, void *wd, void *zero,
                                    hipStream_t s);
-// out = sum over s of part[s] (fixed order) with the GEMM epilogue
+// A per-channel sum db[o] = sum over k < parts of partial[o*parts + k] (in k
+// order) that a split-K reduction can run in extra blocks; db NULL: none.
+struct BiasSum {
+    const float *partial;
+    float *db;
+    int O, parts;
+};
+
+// out = sum over s of part[s] (fixed order) with the GEMM epilogue, plus the
+// bias sum bs when bs.db is set
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,
-                                const float *bias, int P, int relu, hipStream_t s);
+                                const float *bias, int P, int relu, const BiasSum &bs, hipStream_t s);
 
 // The rest of a training step (f32; train_kernels.hip).  Elementwise
 // kernels take 16-byte aligned pointers; n may be 0.
