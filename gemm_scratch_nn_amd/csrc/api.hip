@@ -917,13 +917,16 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
         // Gt[b][pix][o], the filter flipped with k ordered (u, v, o)
         void *gt = wsb + h->off_g;
         void *zero = wsb + h->off_zero;
-        D4R_LAUNCH(step_transpose(h, g.B, g.O, g.P, dy, gt, s, "dgrad_dy"), "grad transpose");
         {
-            ProfScope ps(s, std::string("flip_filter_nhwc_") + dt_name(h->dt) + ":dgrad", 0.0,
-                         2.0 * h->es * (double)g.O * g.Kc);
-            hipError_t e = launch_flip_filter_nhwc(h->dt, g, w, wf, zero, s);
+            // one launch: dy -> Gt per image, and the filter (O x C*kH*kW)
+            // transposed with its taps reversed, clearing the zero page
+            ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":dgrad_dy_w", 0.0,
+                         2.0 * h->es * ((double)g.B * g.O * g.P + (double)g.O * g.Kc));
+            const TransposeJob jdy{dy, gt, g.O, g.P, g.B, 0, nullptr, 0};
+            const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0};
+            hipError_t e = launch_transpose_pair(h->dt, jdy, jw, s);
             ps.done();
-            D4R_LAUNCH(e, "filter flip");
+            D4R_LAUNCH(e, "grad transpose and filter flip");
         }
         D4R_LAUNCH(run_gemm(h->dt, h->bwd_data_nhwc, OP_KC, OP_IMPL_T, wf, d.Kc, gt, 0, d.O, d.N, d.Kc,
                             EPI_NCHW, dx, 0, nullptr, d.P, partial, s, "dgrad", &d, 0, 0, zero),

@@ -529,14 +529,12 @@ __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ 
 // groups of flip taps and output row c takes input column c with its tap
 // reversed inside the group; block 0 also clears 256 bytes at `zero`.
 template <typename T>
-__global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in, T *__restrict__ out,
-                                                       int R, int Cc, int flip, uint32_t *__restrict__ zero)
+__device__ __forceinline__ void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int R, int Cc,
+                                               int flip, int bx, int by, int bz)
 {
     __shared__ T tile[64][65];
-    if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
-        zero[threadIdx.x] = 0u;
-    const long long base = (long long)blockIdx.z * R * Cc;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const long long base = (long long)bz * R * Cc;
+    const int r0 = by * 64, c0 = bx * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     constexpr int ROWS = 64 / (NT / 64);
     T v[ROWS];
@@ -558,6 +556,30 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
         if (rin && c < Cc)
             out[base + (long long)oc * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in, T *__restrict__ out,
+                                                       int R, int Cc, int flip, uint32_t *__restrict__ zero)
+{
+    if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
+        zero[threadIdx.x] = 0u;
+    transpose_tile<T>(in, out, R, Cc, flip, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Two independent batched transposes in one launch: blocks [0, a.blocks)
+// run job a, the rest job b (the choice is uniform per block).
+template <typename T>
+__global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob a, TransposeJob b)
+{
+    const bool first = (int)blockIdx.x < a.blocks;
+    const TransposeJob &j = first ? a : b;
+    const int local = first ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
+    const int gx = (j.Cc + 63) / 64, gy = (j.R + 63) / 64;
+    if (j.zero && local == 0 && threadIdx.x < 64)
+        j.zero[threadIdx.x] = 0u;
+    transpose_tile<T>((const T *)j.in, (T *)j.out, j.R, j.Cc, j.flip, local % gx, (local / gx) % gy,
+                      local / (gx * gy));
 }
 
 // ---------------------------------------------------------------------------
@@ -1014,16 +1036,20 @@ hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf
 // wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v]: W (O x Kc) transposed through
 // LDS tiles, each output row's tap reversed (rows come in groups of kH*kW
 // taps); plus the zero page.
-hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, void *wd, void *zero, hipStream_t s)
+hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s)
 {
-    const int R = g.O, Cc = g.C * g.kH * g.kW, khw = g.kH * g.kW;
-    dim3 grid((Cc + 63) / 64, (R + 63) / 64, 1);
+    auto blocks = [](const TransposeJob &j) {
+        return (long long)((j.Cc + 63) / 64) * ((j.R + 63) / 64) * j.batch;
+    };
+    const long long na = blocks(a), nb = blocks(b);
+    if (na + nb > INT32_MAX)
+        return hipErrorInvalidValue;
+    a.blocks = (int)na;
+    b.blocks = (int)nb;
     if (dt == DT_F32)
-        hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)w, (uint32_t *)wd,
-                           R, Cc, khw, (uint32_t *)zero);
+        hipLaunchKernelGGL(transpose2_kernel<uint32_t>, dim3((unsigned)(na + nb)), dim3(NT), 0, s, a, b);
     else
-        hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w, (uint16_t *)wd,
-                           R, Cc, khw, (uint32_t *)zero);
+        hipLaunchKernelGGL(transpose2_kernel<uint16_t>, dim3((unsigned)(na + nb)), dim3(NT), 0, s, a, b);
     return hipGetLastError();
 }
 

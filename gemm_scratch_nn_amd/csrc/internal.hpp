@@ -175,10 +175,6 @@ hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db
 int bias_grad_splits(const ConvGeom &g);
 // wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v] (the implicit data gradient's filter)
 hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf, hipStream_t s);
-// wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v] (the same, k ordered for an NHWC
-// dy), and 256 zero bytes at `zero`
-hipError_t launch_flip_filter_nhwc(int dt, const ConvGeom &g, const void *w, void *wd, void *zero,
-                                   hipStream_t s);
 // A per-channel sum db[o] = sum over k < parts of partial[o*parts + k] (in k
 // order) that a split-K reduction can run in extra blocks; db NULL: none.
 struct BiasSum {
@@ -186,6 +182,22 @@ struct BiasSum {
     float *db;
     int O, parts;
 };
+
+// One batched transpose out[z][c'][r] = in[z][r][c] (batch z, R x Cc): with
+// flip > 0 the columns come in groups of flip taps and c' reverses the tap
+// inside its group; zero, when set, gets 256 bytes cleared.  `blocks` is
+// filled in by launch_transpose_pair.
+struct TransposeJob {
+    const void *in;
+    void *out;
+    int R, Cc, batch, flip;
+    uint32_t *zero;
+    int blocks;
+};
+
+// jobs a and b in one launch (each 64x64 tile a block; the jobs must not
+// overlap in memory)
+hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s);
 
 // out = sum over s of part[s] (fixed order) with the GEMM epilogue, plus the
 // bias sum bs when bs.db is set
