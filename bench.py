@@ -57,6 +57,10 @@ def parse_args():
     ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="implicit",
                     help="implicit: implicit-GEMM data gradient, no dcol (stride-1 square-kernel "
                          "layers; others run explicit); explicit: the page's GEMM to dcol + col2im")
+    ap.add_argument("--backward", choices=("combined", "separate"), default="combined",
+                    help="combined: one d4r_conv_backward call per layer (dy prepared once for both "
+                         "gradients where the layer allows); separate: the data-gradient call, then "
+                         "the filter-gradient call (always with --streams 2 or --dgrad explicit)")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the forwards and filter gradients on one stream, the data gradients "
                          "(own workspace) on a second one after the forwards, joined at the step's "
@@ -343,14 +347,21 @@ def main() -> int:
             for _, pl, t in st:
                 t["ws2"] = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=dev)
 
+    combined = args.backward == "combined" and args.dgrad == "implicit"
+
     def step(stream=stream, streams=args.streams):
         layers = sets[n_step[0] % len(sets)]
         n_step[0] += 1
         if streams == 1:
             for layer, pl, t in layers:
                 forward(layer, pl, t, stream)
-                dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
-                wgrad(layer, pl, t, stream)
+                if combined:
+                    d4r.d4r_conv_backward(pl.h, t["x"] if implicit else None, t["w"], t["g"], t["dx"],
+                                          t["dw"], t["db"], 0 if implicit else 1, pl.ws, pl.ws_bytes,
+                                          stream)
+                else:
+                    dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
+                    wgrad(layer, pl, t, stream)
             return
         # forwards, then per layer (last first, as a backward pass runs) the
         # filter gradient on this stream and the data gradient on the other
@@ -448,7 +459,9 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad, "streams": args.streams,
+                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad,
+                   "backward": "combined" if combined and args.streams == 1 else "separate",
+                   "streams": args.streams,
                    "rotate": args.rotate, "hip_graph": bool(args.graph),
                    "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / MFMA_PEAK[dtype],

@@ -85,6 +85,7 @@ _c = {
                                           [_vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_backward_filter": _sig("d4r_conv_backward_filter",
                                      [_vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "d4r_conv_backward": _sig("d4r_conv_backward", [_vp] * 7 + [_i, _vp, _sz, _vp]),
     "d4r_conv_im2col": _sig("d4r_conv_im2col", [_vp, _vp, _vp, _vp]),
     "d4r_conv_col2im": _sig("d4r_conv_col2im", [_vp, _vp, _vp, _vp]),
     "d4r_conv_bias_grad": _sig("d4r_conv_bias_grad", [_vp, _vp, _vp, _vp, _sz, _vp]),
@@ -261,6 +262,13 @@ def d4r_conv_backward_filter(h, x, dy, dw, db, reuse_col, ws, ws_bytes=None, str
     _check("d4r_conv_backward_filter",
            _c["d4r_conv_backward_filter"](h, _ptr(x), _ptr(dy), _ptr(dw), _ptr(db), int(reuse_col),
                                           _ptr(ws), nb, _stream(stream)))
+
+
+def d4r_conv_backward(h, x, w, dy, dx, dw, db, reuse_col, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check("d4r_conv_backward",
+           _c["d4r_conv_backward"](h, _ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db), int(reuse_col),
+                                   _ptr(ws), nb, _stream(stream)))
 
 
 def d4r_conv_im2col(h, x, col, stream=None) -> None:
@@ -510,6 +518,23 @@ class ConvPlan:
         d4r_conv_backward_filter(self.h, None if reuse_col else x, dy, dw, db if want_bias else None,
                                  1 if reuse_col else 0, self.ws, self.ws_bytes)
         return dw, (db if want_bias else None)
+
+    def backward(self, x, w, dy, reuse_col=False, want_bias=True, dx=None, dw=None, db=None):
+        """dx, dw, db of one layer through d4r_conv_backward."""
+        import torch
+        if not reuse_col:
+            _require(x, "x", self.dtype, self.x_shape)
+        _require(w, "w", self.dtype, self.w_shape)
+        _require(dy, "dy", self.dtype, self.y_shape)
+        if dx is None:
+            dx = torch.empty(self.x_shape, dtype=torch.float32, device=dy.device)
+        if dw is None:
+            dw = torch.empty(self.w_shape, dtype=torch.float32, device=dy.device)
+        if want_bias and db is None:
+            db = torch.empty((self.shape[8],), dtype=torch.float32, device=dy.device)
+        d4r_conv_backward(self.h, None if reuse_col else x, w, dy, dx, dw, db if want_bias else None,
+                          1 if reuse_col else 0, self.ws, self.ws_bytes)
+        return dx, dw, (db if want_bias else None)
 
     def col_view(self):
         """The col matrix the last forward / im2col left at the start of ws."""

@@ -353,7 +353,7 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
         if (!bs.db)
             return hipSuccess;
         ProfScope pb(s, std::string("bias_final:") + pass, 0.0, 4.0 * bs.O * (bs.parts + 1.0));
-        e = launch_bias_final(bs.partial, bs.db, bs.O, bs.parts, s);
+        e = launch_bias_sum(bs, s);
         pb.done();
         return e;
     }
@@ -399,6 +399,10 @@ struct d4r_conv {
     bool dgrad_nhwc;
     GemmPlan bwd_data_nhwc;
     size_t off_zero;
+    size_t off_gt;  // Gt (NHWC dy), a region of its own next to G
+    // d4r_conv_backward prepares dy for both gradient GEMMs in one pass
+    // (NHWC data gradient and a copied G for the filter gradient)
+    bool fused_bwd;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -623,10 +627,14 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     }
 
     choose_grad_paths(h);
+    h->fused_bwd = h->dgrad_nhwc && h->wgrad == GP_COPY && !h->pointwise;
     h->col_bytes = (size_t)col_el * h->es;
     size_t off = align_up(h->col_bytes);
     h->off_g = off;
-    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE || h->dgrad_nhwc)
+    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
+        off += align_up((size_t)y_el * h->es);
+    h->off_gt = off;
+    if (h->dgrad_nhwc)
         off += align_up((size_t)y_el * h->es);
     h->off_wt = off;
     if (h->dgrad_wt)
@@ -638,7 +646,8 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     if (h->dgrad_nhwc)
         off += align_up(256);
     h->off_bias = off;
-    off += align_up((size_t)outC * bias_part_cols * sizeof(float));
+    off += align_up((size_t)outC * std::max(bias_part_cols, h->fused_bwd ? dy_prep_bias_parts(g) : 0) *
+                    sizeof(float));
     h->off_big = off;
     size_t big = plan_partial_bytes(h->fwd, g.O, g.N);
     size_t dd = align_up((size_t)col_el * sizeof(float)) + plan_partial_bytes(h->bwd_data, g.Kc, g.N);
@@ -915,7 +924,7 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     if (h->dgrad_nhwc) {
         // dx = Wd(C x kH*kW*O) * im2col(dy as NHWC): dy transposed to
         // Gt[b][pix][o], the filter flipped with k ordered (u, v, o)
-        void *gt = wsb + h->off_g;
+        void *gt = wsb + h->off_gt;
         void *zero = wsb + h->off_zero;
         {
             // one launch: dy -> Gt per image, and the filter (O x C*kH*kW)
@@ -1000,6 +1009,63 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     if (db)
         D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s),
                    "bias gradient");
+    return ok();
+}
+
+d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const void *dy, float *dx, float *dw,
+                             float *db, int reuse_col, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    if (reuse_col != 0 && reuse_col != 1)
+        return fail(D4R_ERR_INVALID_ARG, "reuse_col must be 0 or 1");
+    if (reuse_col && x)
+        return fail(D4R_ERR_INVALID_ARG, "x must be NULL when reuse_col = 1");
+    if (!reuse_col)
+        D4R_TRY(check_tensor(x, "x"));
+    D4R_TRY(check_tensor(w, "w"));
+    D4R_TRY(check_tensor(dy, "dy"));
+    D4R_TRY(check_tensor(dx, "dx"));
+    D4R_TRY(check_tensor(dw, "dw"));
+    D4R_TRY(check_vec(db, "db"));
+    D4R_TRY(check_ws(h, ws, ws_bytes));
+    if (!h->fused_bwd) {
+        // the two calls in sequence (the data gradient leaves col intact)
+        d4r_status st = d4r_conv_backward_data_implicit(h, w, dy, dx, ws, ws_bytes, hip_stream);
+        if (st != D4R_OK)
+            return st;
+        return d4r_conv_backward_filter(h, x, dy, dw, db, reuse_col, ws, ws_bytes, hip_stream);
+    }
+    hipStream_t s = (hipStream_t)hip_stream;
+    const ConvGeom &g = h->g, &d = h->gd;
+    char *wsb = (char *)ws;
+    void *col = wsb;
+    void *G = wsb + h->off_g;
+    void *gt = wsb + h->off_gt;
+    void *wf = wsb + h->off_wflip;
+    void *zero = wsb + h->off_zero;
+    float *bias_part = db ? (float *)(wsb + h->off_bias) : nullptr;
+    float *partial = (float *)(wsb + h->off_big);
+    {
+        // one pass over dy: G, Gt and the bias partial sums; the flipped
+        // filter and the zero page in the same launch
+        ProfScope ps(s, std::string("dy_prep_") + dt_name(h->dt) + ":bwd", 0.0,
+                     3.0 * h->es * (double)g.B * g.O * g.P + 2.0 * h->es * (double)g.O * g.Kc);
+        const DyPrep a{dy, gt, G, bias_part, g.B, g.O, g.P, 0, 0};
+        const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0};
+        hipError_t e = launch_dy_prep(h->dt, a, jw, s);
+        ps.done();
+        D4R_LAUNCH(e, "dy preparation");
+    }
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_data_nhwc, OP_KC, OP_IMPL_T, wf, d.Kc, gt, 0, d.O, d.N, d.Kc, EPI_NCHW,
+                        dx, 0, nullptr, d.P, partial, s, "dgrad", &d, 0, 0, zero),
+               "implicit data-gradient GEMM");
+    if (!reuse_col)
+        D4R_LAUNCH(step_im2col(h, x, col, s, "wgrad"), "im2col");
+    const BiasSum bs{bias_part, db, g.O, dy_prep_bias_parts(g)};
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N, EPI_ROWMAJOR, dw,
+                        g.Kc, nullptr, 0, partial, s, "wgrad", nullptr, 0, 0, nullptr, 0, db ? &bs : nullptr),
+               "filter-gradient GEMM and bias gradient");
     return ok();
 }
 

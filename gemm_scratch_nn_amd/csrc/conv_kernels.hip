@@ -583,6 +583,74 @@ __global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob a, Transpos
 }
 
 // ---------------------------------------------------------------------------
+// dy prepared for both gradients in one pass (combined backward): a block
+// reads one 64 (channel) x 64 (pixel) tile of dy[b] once and writes it
+//   * as G[o][b*P + pix] (the filter gradient's k-contiguous operand),
+//   * transposed as Gt[b][pix][o] (the NHWC data gradient's operand),
+//   * and, when bias_part is set, the tile row sums (one wavefront per row,
+//     fixed butterfly order) as bias_part[o*parts + b*ceil(P/64) + tile].
+// Blocks past the tiles run the filter job w (transposed with its taps
+// reversed, zero page cleared), as transpose2_kernel does.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void dy_prep_kernel(DyPrep a, TransposeJob w)
+{
+    if ((int)blockIdx.x >= a.blocks) {
+        const int local = (int)blockIdx.x - a.blocks;
+        const int gx = (w.Cc + 63) / 64, gy = (w.R + 63) / 64;
+        if (w.zero && local == 0 && threadIdx.x < 64)
+            w.zero[threadIdx.x] = 0u;
+        transpose_tile<T>((const T *)w.in, (T *)w.out, w.R, w.Cc, w.flip, local % gx, (local / gx) % gy,
+                          local / (gx * gy));
+        return;
+    }
+    __shared__ T tile[64][65];
+    const int gx = (a.P + 63) / 64, gy = (a.O + 63) / 64;
+    const int bx = (int)blockIdx.x % gx, by = ((int)blockIdx.x / gx) % gy, b = (int)blockIdx.x / (gx * gy);
+    const int p0 = bx * 64, o0 = by * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    constexpr int ROWS = 64 / (NT / 64);
+    const T *dy = (const T *)a.dy + (long long)b * a.O * a.P;
+    const bool pin = p0 + tx < a.P;
+    T v[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int o = o0 + ty + i * (NT / 64);
+        v[i] = (pin && o < a.O) ? dy[(long long)o * a.P + p0 + tx] : (T)0;
+    }
+    const long long N = (long long)a.B * a.P;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int o = o0 + ty + i * (NT / 64);
+        if (pin && o < a.O)
+            ((T *)a.g)[(long long)o * N + (long long)b * a.P + p0 + tx] = v[i];
+        tile[ty + i * (NT / 64)][tx] = v[i];
+    }
+    __syncthreads();
+    if (a.bias_part) {
+        // row r of the tile: four threads add 16 columns each (zeros past
+        // P), then the quarters combine in a fixed order (lanes t^1, t^2)
+        const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            t += to_f32(tile[r][q * 16 + k], a.dt);
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        if (q == 0 && o0 + r < a.O)
+            a.bias_part[(long long)(o0 + r) * (a.B * gx) + b * gx + bx] = t;
+    }
+    T *gt = (T *)a.gt + (long long)b * a.O * a.P;
+    const bool oin = o0 + tx < a.O;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int pix = p0 + ty + i * (NT / 64);
+        if (oin && pix < a.P)
+            gt[(long long)pix * a.O + o0 + tx] = tile[tx][ty + i * (NT / 64)];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Bias gradient.  Pass 1: block (s, o) sums images [s*per, (s+1)*per) of
 // channel o: its threads stride through the flattened (image, pixel) range
 // of those planes, four elements in flight per thread, then the block
@@ -655,18 +723,24 @@ __global__ __launch_bounds__(NT) void bias_final_kernel(const float *__restrict_
     db[o] = tot;
 }
 
-// The same per-channel sum as bias_final_kernel, run by extra blocks of a
-// split-K reduction (block j of the job covers channels j*NT ..).
+// A BiasSum's per-channel sums: one wavefront per channel (block j covers
+// channels 4j .. 4j+3); lane l adds partials l, l+64, .. in order, then the
+// lanes combine through the fixed butterfly of wave_sum.  Run by extra
+// blocks of a split-K reduction, or alone (bias_sum_kernel).
 __device__ __forceinline__ void bias_sum_job(const BiasSum &bs, int j)
 {
-    const int o = j * NT + threadIdx.x;
+    const int o = j * (NT / 64) + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (o >= bs.O)
-        return;
-    float tot = 0.0f;
-    for (int s = 0; s < bs.parts; ++s)
-        tot += bs.partial[o * bs.parts + s];
-    bs.db[o] = tot;
+        return;  // whole wavefront
+    float t = 0.0f;
+    for (int s = lane; s < bs.parts; s += 64)
+        t += bs.partial[(long long)o * bs.parts + s];
+    t = wave_sum(t);
+    if (lane == 0)
+        bs.db[o] = t;
 }
+
+__global__ __launch_bounds__(NT) void bias_sum_kernel(BiasSum bs) { bias_sum_job(bs, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Split-K reduction: C = sum_{s} part[s], then the GEMM epilogue (row-major
@@ -1036,6 +1110,31 @@ hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf
 // wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v]: W (O x Kc) transposed through
 // LDS tiles, each output row's tap reversed (rows come in groups of kH*kW
 // taps); plus the zero page.
+int dy_prep_bias_parts(const ConvGeom &g) { return g.B * ((g.P + 63) / 64); }
+
+hipError_t launch_dy_prep(int dt, DyPrep a, TransposeJob w, hipStream_t s)
+{
+    const long long na = (long long)((a.P + 63) / 64) * ((a.O + 63) / 64) * a.B;
+    const long long nw = (long long)((w.Cc + 63) / 64) * ((w.R + 63) / 64) * w.batch;
+    if (na + nw > INT32_MAX)
+        return hipErrorInvalidValue;
+    a.blocks = (int)na;
+    a.dt = dt;
+    if (dt == DT_F32)
+        hipLaunchKernelGGL(dy_prep_kernel<uint32_t>, dim3((unsigned)(na + nw)), dim3(NT), 0, s, a, w);
+    else
+        hipLaunchKernelGGL(dy_prep_kernel<uint16_t>, dim3((unsigned)(na + nw)), dim3(NT), 0, s, a, w);
+    return hipGetLastError();
+}
+
+int bias_sum_blocks(const BiasSum &bs) { return (bs.O + NT / 64 - 1) / (NT / 64); }
+
+hipError_t launch_bias_sum(const BiasSum &bs, hipStream_t s)
+{
+    hipLaunchKernelGGL(bias_sum_kernel, dim3((unsigned)bias_sum_blocks(bs)), dim3(NT), 0, s, bs);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s)
 {
     auto blocks = [](const TransposeJob &j) {
@@ -1060,7 +1159,7 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, lon
     const long long total = (long long)M * N;
     const long long vthreads = (total + 3) / 4;
     const bool vec = (N % 4) == 0 && (split_stride % 4) == 0 && ((uintptr_t)part % 16) == 0;
-    const int bblocks = bs.db ? (bs.O + NT - 1) / NT : 0;
+    const int bblocks = bs.db ? bias_sum_blocks(bs) : 0;
     // the vector path needs enough threads to fill the chip
     if (vec && vthreads >= 64LL * 1024) {
         const int rb = (int)((vthreads + NT - 1) / NT);

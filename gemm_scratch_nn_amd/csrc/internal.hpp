@@ -199,6 +199,24 @@ struct TransposeJob {
 // overlap in memory)
 hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s);
 
+// dy (B x O x P) read once, written as G[o][b*P + pix] and Gt[b][pix][o],
+// with the bias gradient's partial sums (dy_prep_bias_parts(g) per channel)
+// when bias_part is set; the filter job w rides in the same launch.  dt and
+// blocks are filled in by launch_dy_prep.
+struct DyPrep {
+    const void *dy;
+    void *gt, *g;
+    float *bias_part;
+    int B, O, P, dt, blocks;
+};
+int dy_prep_bias_parts(const ConvGeom &g);
+hipError_t launch_dy_prep(int dt, DyPrep a, TransposeJob w, hipStream_t s);
+
+// the BiasSum on its own (wavefront per channel), and the block count it
+// takes as extra blocks of a reduction
+int bias_sum_blocks(const BiasSum &bs);
+hipError_t launch_bias_sum(const BiasSum &bs, hipStream_t s);
+
 // out = sum over s of part[s] (fixed order) with the GEMM epilogue, plus the
 // bias sum bs when bs.db is set
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,

@@ -247,6 +247,25 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
                                     void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
+ * The whole backward pass of one layer in one call (the page's backward,
+ * "Convolution: The im2col Approach": data, filter and bias gradients from
+ * one upstream gradient dy): dx as d4r_conv_backward_data_implicit, dw and
+ * db as d4r_conv_backward_filter with the same x / reuse_col rules, all
+ * arguments as in those two calls (db NULL skips the bias).  When the
+ * implicit data gradient reads dy as NHWC and the filter gradient copies dy
+ * (16-bit, or float32 with C*kH*kW >= 1024), one pass over dy writes both
+ * gradients' operands and the bias partial sums (the reshape the page runs
+ * as conv_grad_reshape, and the NHWC transpose) and the filter flip rides
+ * in the same launch; dx and dw then equal the two separate calls bit for
+ * bit, db agrees up to summation order.  Otherwise it is those two calls in
+ * sequence.  col in ws is left intact with reuse_col = 1 and rebuilt from x
+ * with reuse_col = 0.
+ */
+d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const void *dy,
+                             float *dx, float *dw, float *db, int reuse_col, void *ws,
+                             size_t ws_bytes, void *hip_stream);
+
+/*
  * Single steps of the path, for measurement and for checking the index
  * maps bit for bit.
  *

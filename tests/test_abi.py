@@ -22,7 +22,7 @@ def test_every_declared_symbol_is_exported():
                 "d4r_profile_reset", "d4r_profile_read", "d4r_relu_forward", "d4r_relu_backward",
                 "d4r_maxpool_forward", "d4r_maxpool_backward", "d4r_add_bias_rows",
                 "d4r_bias_grad_rows", "d4r_softmax", "d4r_softmax_ce_grad", "d4r_sgd_update",
-                "d4r_grad_accum"}
+                "d4r_grad_accum", "d4r_conv_forward_ex", "d4r_gemm_bias_act", "d4r_conv_backward"}
     assert expected <= set(names)
     for n in names:
         assert d4r.exported(n), n
@@ -183,6 +183,32 @@ def test_backward_argument_errors(handle):
     assert e.value.status == INVALID
     with pytest.raises(D4RError) as e:
         d4r.d4r_conv_col2im(handle, None, FAKE, stream=0)
+    assert e.value.status == INVALID
+
+
+def test_combined_backward_argument_errors(handle):
+    ws = _ws(handle)
+    call = d4r.d4r_conv_backward
+    # (x, w, dy, dx, dw, db, reuse_col, ws, nb) -> status
+    cases = [
+        ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, ws), INVALID),     # x given with reuse_col = 1
+        ((None, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, ws), INVALID),     # x missing with reuse_col = 0
+        ((None, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, ws), INVALID),     # reuse_col not 0/1
+        ((None, None, FAKE, FAKE, FAKE, None, 1, FAKE, ws), INVALID),     # w NULL
+        ((None, FAKE, None, FAKE, FAKE, None, 1, FAKE, ws), INVALID),     # dy NULL
+        ((None, FAKE, FAKE, None, FAKE, None, 1, FAKE, ws), INVALID),     # dx NULL
+        ((None, FAKE, FAKE, FAKE, None, None, 1, FAKE, ws), INVALID),     # dw NULL
+        ((None, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, FAKE, ws), INVALID), # db misaligned
+        ((None, FAKE, MISALIGNED, FAKE, FAKE, None, 1, FAKE, ws), INVALID),
+        ((None, FAKE, FAKE, FAKE, FAKE, None, 1, None, ws), WORKSPACE),
+        ((None, FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, ws - 1), WORKSPACE),
+    ]
+    for args, code in cases:
+        with pytest.raises(D4RError) as e:
+            call(handle, *args, stream=0)
+        assert e.value.status == code, args
+    with pytest.raises(D4RError) as e:
+        call(None, None, FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, ws, stream=0)
     assert e.value.status == INVALID
 
 

@@ -89,3 +89,33 @@ def test_gradients_on_two_streams_match_one_stream(key, li, dt, batch):
     torch.cuda.synchronize()
     for k in ref:
         assert torch.equal(ref[k], t[k]), k
+
+
+@pytest.mark.parametrize("key,li,dt,batch", [("c4", 1, "f32", 4), ("c4", 2, "bf16", 4)])
+def test_graph_replay_combined_backward(key, li, dt, batch):
+    # the combined backward (one dy preparation launch for both gradients)
+    # captured once and replayed after in-place input changes
+    pl, t = _setup(key, li, dt, batch)
+
+    def step():
+        st = torch.cuda.current_stream().cuda_stream  # the capture stream inside the graph block
+        d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, st)
+        d4r.d4r_conv_backward(pl.h, None, t["w"], t["g"], t["dx"], t["dw"], t["db"], 1, pl.ws, pl.ws_bytes, st)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        t["x"].mul_(-0.5 if r % 2 else 1.25)
+        t["g"].add_(0.125)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: t[k].clone() for k in ("y", "dx", "dw", "db")}
+        step()
+        torch.cuda.synchronize()
+        for k in got:
+            assert torch.equal(got[k], t[k]), (r, k)
