@@ -261,8 +261,11 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
 // per axis (ceil(k / s)) at compile time so every load of a thread is issued
 // before the adds; TU = TV = 0 is the general loop.
 // ---------------------------------------------------------------------------
+// Taps of dx element idx: the candidate (u, v) pairs, their dcol offsets
+// and whether each lies inside the tap range (TU x TV candidates).
 template <int TU, int TV>
-__device__ __forceinline__ float col2im_one(const float *__restrict__ dcol, const ConvGeom &g, int idx)
+__device__ __forceinline__ void col2im_taps(const ConvGeom &g, int idx, long long (&off)[TU][TV],
+                                            bool (&ok)[TU][TV])
 {
     const int w = idx % g.W;
     int t = idx / g.W;
@@ -283,64 +286,102 @@ __device__ __forceinline__ float col2im_one(const float *__restrict__ dcol, cons
         v_lo = 0;
     v_lo += ((wp - v_lo) % g.s);
     const int v_hi = min(g.kW - 1, wp);
+    const int nb = b * g.P;
+#pragma unroll
+    for (int a = 0; a < TU; ++a) {
+        const int u = u_lo + a * g.s;
+        const int i = (hp - u) / g.s;
+#pragma unroll
+        for (int q = 0; q < TV; ++q) {
+            const int v = v_lo + q * g.s;
+            const int j = (wp - v) / g.s;
+            ok[a][q] = (u <= u_hi) && (v <= v_hi);
+            off[a][q] = ok[a][q] ? (long long)((c * g.kH + u) * g.kW + v) * g.N + nb + i * g.OW + j : 0;
+        }
+    }
+}
 
+// General tap loop (tap counts not fixed at compile time).
+__device__ __forceinline__ float col2im_one_general(const float *__restrict__ dcol, const ConvGeom &g, int idx)
+{
+    const int w = idx % g.W;
+    int t = idx / g.W;
+    const int h = t % g.H;
+    t /= g.H;
+    const int c = t % g.C;
+    const int b = t / g.C;
+    const int hp = h + g.p, wp = w + g.p;
+    int u_lo = hp - g.s * (g.OH - 1);
+    if (u_lo < 0)
+        u_lo = 0;
+    u_lo += ((hp - u_lo) % g.s);
+    const int u_hi = min(g.kH - 1, hp);
+    int v_lo = wp - g.s * (g.OW - 1);
+    if (v_lo < 0)
+        v_lo = 0;
+    v_lo += ((wp - v_lo) % g.s);
+    const int v_hi = min(g.kW - 1, wp);
     const long long Nl = g.N;
     const int nb = b * g.P;
     float acc = 0.0f;
-    if constexpr (TU > 0) {
-        float vals[TU][TV];
-#pragma unroll
-        for (int a = 0; a < TU; ++a) {
-            const int u = u_lo + a * g.s;
-            const int i = (hp - u) / g.s;
-#pragma unroll
-            for (int q = 0; q < TV; ++q) {
-                const int v = v_lo + q * g.s;
-                const int j = (wp - v) / g.s;
-                const bool ok = (u <= u_hi) && (v <= v_hi);
-                vals[a][q] = ok ? dcol[(long long)((c * g.kH + u) * g.kW + v) * Nl + nb + i * g.OW + j]
-                                : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int a = 0; a < TU; ++a)
-#pragma unroll
-            for (int q = 0; q < TV; ++q)
-                acc += vals[a][q];
-    } else {
-        for (int u = u_lo; u <= u_hi; u += g.s) {
-            const int i = (hp - u) / g.s;
-            const int rbase = (c * g.kH + u) * g.kW;
-            for (int v = v_lo; v <= v_hi; v += g.s) {
-                const int j = (wp - v) / g.s;
-                acc += dcol[(long long)(rbase + v) * Nl + nb + i * g.OW + j];
-            }
+    for (int u = u_lo; u <= u_hi; u += g.s) {
+        const int i = (hp - u) / g.s;
+        const int rbase = (c * g.kH + u) * g.kW;
+        for (int v = v_lo; v <= v_hi; v += g.s) {
+            const int j = (wp - v) / g.s;
+            acc += dcol[(long long)(rbase + v) * Nl + nb + i * g.OW + j];
         }
     }
     return acc;
 }
 
-// A thread computes COLS_PER_THREAD dx elements NT apart (so the lanes of a
-// wavefront stay on consecutive elements for every tap); with the tap counts
-// fixed at compile time all their loads are in flight before the first add.
-constexpr int COLS_PER_THREAD = 4;
-
+// A thread computes four dx elements NT apart (so the lanes of a wavefront
+// stay on consecutive elements for every tap).  With the tap counts fixed
+// at compile time (TU, TV > 0) the loads of CPT elements are all issued
+// before the first add: loads are unconditional (offset 0 outside the tap
+// range, the value then dropped), and elements past the end repeat the
+// last one.  Each element adds its taps in the order u, then v ascending.
 template <int TU, int TV>
 __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dcol,
                                                     float *__restrict__ dx, ConvGeom g, int total)
 {
-    const int base = blockIdx.x * NT * COLS_PER_THREAD + threadIdx.x;
-    float r[COLS_PER_THREAD];
+    constexpr int CPT = (TU > 0 && TU * TV > 9) ? 2 : 4;
+    const int base = blockIdx.x * NT * 4 + threadIdx.x;
+    if constexpr (TU > 0) {
 #pragma unroll
-    for (int e = 0; e < COLS_PER_THREAD; ++e) {
-        const int idx = base + e * NT;
-        r[e] = (idx < total) ? col2im_one<TU, TV>(dcol, g, idx) : 0.0f;
-    }
+        for (int half = 0; half < 4 / CPT; ++half) {
+            float vals[CPT][TU][TV];
+            bool ok[CPT][TU][TV];
 #pragma unroll
-    for (int e = 0; e < COLS_PER_THREAD; ++e) {
-        const int idx = base + e * NT;
-        if (idx < total)
-            dx[idx] = r[e];
+            for (int e = 0; e < CPT; ++e) {
+                long long off[TU][TV];
+                col2im_taps<TU, TV>(g, min(base + (half * CPT + e) * NT, total - 1), off, ok[e]);
+#pragma unroll
+                for (int a = 0; a < TU; ++a)
+#pragma unroll
+                    for (int q = 0; q < TV; ++q)
+                        vals[e][a][q] = dcol[off[a][q]];
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int a = 0; a < TU; ++a)
+#pragma unroll
+                    for (int q = 0; q < TV; ++q)
+                        acc += ok[e][a][q] ? vals[e][a][q] : 0.0f;
+                const int idx = base + (half * CPT + e) * NT;
+                if (idx < total)
+                    dx[idx] = acc;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = base + e * NT;
+            if (idx < total)
+                dx[idx] = col2im_one_general(dcol, g, idx);
+        }
     }
 }
 
@@ -1006,7 +1047,7 @@ hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStr
         }
     }
     const int total = g.B * g.C * g.H * g.W;
-    const int threads = (total + COLS_PER_THREAD - 1) / COLS_PER_THREAD;
+    const int threads = (total + 3) / 4;  // four dx elements per thread
     const dim3 grid((threads + NT - 1) / NT), block(NT);
     const int tu = (g.kH + g.s - 1) / g.s, tv = (g.kW + g.s - 1) / g.s;
     if (tu == 1 && tv == 1)
