@@ -475,13 +475,31 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_kernel(GemmParams p)
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kDlBK = 64;  // k per stage
+constexpr int kDlBK = 64;  // k per stage, 16-bit operands (f32: 32)
+
+// Element type of the direct-to-LDS kernel's operands: 16-bit halves, or
+// f32 words (DT_F32).  A stage is one 128-byte LDS row per tile row, i.e.
+// 64 halves or 32 floats; a 16-byte chunk holds EPC elements.
+template <int DTID>
+struct DlElem {
+    using T = std::conditional_t<DTID == DT_F32, uint32_t, uint16_t>;
+    static constexpr int EPC = 16 / (int)sizeof(T);
+    static constexpr int BK = 8 * EPC;
+};
+
+// 16-byte chunk c of row `row` of a tile stage (swizzled position)
+__device__ __forceinline__ u32x4_t dl_chunk(const char *lds, int row, int c)
+{
+    return *(const u32x4_t *)(lds + row * 128 + ((c ^ swz(row)) << 4));
+}
 
 // Per-lane load offsets of one k-contiguous operand (BR rows of the tile,
 // NW wavefronts): a wavefront load covers 8 rows of 128 bytes.
-template <int BR, int NW>
+template <int BR, int NW, int DTID>
 struct DlOperand {
-    static constexpr int ROWB = kDlBK * 2;          // bytes per LDS row
+    using T = typename DlElem<DTID>::T;
+    static constexpr int EPC = DlElem<DTID>::EPC;
+    static constexpr int ROWB = 128;                // bytes per LDS row
     static constexpr int LPL = 8;                   // rows per wavefront load
     static constexpr int LD = BR / (LPL * NW);      // loads per wavefront per stage
     static constexpr int BYTES = BR * ROWB;
@@ -495,36 +513,33 @@ struct DlOperand {
         for (int j = 0; j < LD; ++j) {
             const int lr = (j * NW + wave) * LPL + lane / 8;  // tile row
             const int gr = min(r0 + lr, R - 1);
-            off[j] = (long long)gr * ld + ((lane % 8) ^ swz(lr)) * 8;
+            off[j] = (long long)gr * ld + ((lane % 8) ^ swz(lr)) * EPC;
         }
     }
 
     // stage starting at k0 into LDS stage base `lds`
-    __device__ __forceinline__ void issue(const uint16_t *X, int k0, char *lds, int wave) const
+    __device__ __forceinline__ void issue(const T *X, int k0, char *lds, int wave) const
     {
 #pragma unroll
         for (int j = 0; j < LD; ++j)
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(X + off[j] + k0),
                                              (lds_void_t *)(lds + (j * NW + wave) * LPL * ROWB), 16, 0, 0);
     }
-
-    // 16-byte fragment: row `row` of the tile, k = 16q + 8h .. +7
-    __device__ __forceinline__ static u32x4_t frag(const char *lds, int row, int q, int h)
-    {
-        return *(const u32x4_t *)(lds + row * ROWB + (((2 * q + h) ^ swz(row)) << 4));
-    }
 };
 
 // B operand of the implicit GEMM over an NHWC tensor t[b][h][w][c] (OP_IMPL_T,
 // geometry g, stride 1): tile row n = (b, i, j) is an output pixel and a
-// 64-deep stage covers channels c0 .. c0+63 of one tap (u, v), so each row's
-// stage is one contiguous 128-byte run of t at (b, i-p+u, j-p+v, c0), or the
-// zero page when that position is in the padding.  The same lane-to-LDS
-// mapping and swizzle as DlOperand; a lane decodes its rows' pixels once
-// and each stage's tap once.
-template <int BR, int NW>
+// stage covers channels c0 .. c0+BK-1 of one tap (u, v), so each row's stage
+// is one contiguous 128-byte run of t at (b, i-p+u, j-p+v, c0), or the zero
+// page when that position is in the padding.  The same lane-to-LDS mapping
+// and swizzle as DlOperand; a lane decodes its rows' pixels once and each
+// stage's tap once.
+template <int BR, int NW, int DTID>
 struct DlImplNhwc {
-    static constexpr int ROWB = kDlBK * 2;
+    using T = typename DlElem<DTID>::T;
+    static constexpr int EPC = DlElem<DTID>::EPC;
+    static constexpr int BK = DlElem<DTID>::BK;
+    static constexpr int ROWB = 128;
     static constexpr int LPL = 8;
     static constexpr int LD = BR / (LPL * NW);
     static constexpr int BYTES = BR * ROWB;
@@ -532,7 +547,7 @@ struct DlImplNhwc {
 
     // per load: window origin (h0 far negative for rows past N, so no tap
     // is ever in range) and the element offset of the origin's channel
-    // chunk, ((b*H + h0)*W + w0)*C + chunk*8; a stage adds its tap's
+    // chunk, ((b*H + h0)*W + w0)*C + chunk*EPC; a stage adds its tap's
     // uniform offset (u*W + v)*C + c0
     int h0[LD], w0[LD];
     long long base[LD];
@@ -548,43 +563,44 @@ struct DlImplNhwc {
             const int i = r / g.OW;
             h0[j] = n < g.N ? i - g.p : -(1 << 30);
             w0[j] = r - i * g.OW - g.p;
-            base[j] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[j]) * g.C + chk * 8;
+            base[j] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[j]) * g.C + chk * EPC;
         }
     }
 
-    __device__ __forceinline__ void issue(const uint16_t *X, const uint16_t *zero, int k0, char *lds, int wave,
+    __device__ __forceinline__ void issue(const T *X, const T *zero, int k0, char *lds, int wave,
                                           const ConvGeom &g) const
     {
-        // k0 is a whole stage (kDlBK channels of one tap); divisor
-        // C / kDlBK <= 1024 and stage index < 2^20 (checked by the host)
-        const int ks = k0 / kDlBK, cb = g.C / kDlBK;
-        const int tap = small_div(ks, cb), c0 = (ks - tap * cb) * kDlBK;
+        // k0 is a whole stage (BK channels of one tap); divisor C / BK <=
+        // 1024 and stage index < 2^20 (checked by the host).  The chunk's
+        // offset inside the zero page is base mod BK (C is a multiple of BK).
+        const int ks = k0 / BK, cb = g.C / BK;
+        const int tap = small_div(ks, cb), c0 = (ks - tap * cb) * BK;
         const int u = small_div(tap, g.kW), v = tap - u * g.kW;
         const long long toff = ((long long)u * g.W + v) * g.C + c0;
 #pragma unroll
         for (int j = 0; j < LD; ++j) {
             const bool ok = (unsigned)(h0[j] + u) < (unsigned)g.H && (unsigned)(w0[j] + v) < (unsigned)g.W;
-            const uint16_t *src = ok ? X + base[j] + toff : zero + (base[j] & 63);
+            const T *src = ok ? X + base[j] + toff : zero + (base[j] & (BK - 1));
             __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)(lds + (j * NW + wave) * LPL * ROWB),
                                              16, 0, 0);
         }
     }
-
-    // the LDS layout is DlOperand's
-    __device__ __forceinline__ static u32x4_t frag(const char *lds, int row, int q, int h)
-    {
-        return DlOperand<BR, NW>::frag(lds, row, q, h);
-    }
 };
 
 // BI: B is OP_IMPL_T (DlImplNhwc) instead of a k-contiguous matrix.
+// 16-bit: one 16-byte fragment per 16 k and one v_mfma_f32_32x32x16; f32
+// (DTID == DT_F32): floats k = 16q + 8h .. +7 from two chunks and eight
+// v_mfma_f32_32x32x2_f32 (lane half h supplies k = 8h + t of step t for
+// both operands, so every k is summed once).
 template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
-__global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
+__global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
 {
+    using E = DlElem<DTID>;
+    using T = typename E::T;
     constexpr int NW = NWM * NWN;
-    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = kDlBK;
-    using OA = DlOperand<BM, NW>;
-    using OB = std::conditional_t<BI, DlImplNhwc<BN, NW>, DlOperand<BN, NW>>;
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = E::BK;
+    using OA = DlOperand<BM, NW, DTID>;
+    using OB = std::conditional_t<BI, DlImplNhwc<BN, NW, DTID>, DlOperand<BN, NW, DTID>>;
     constexpr int STAGE = OA::BYTES + OB::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
@@ -601,8 +617,8 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
     const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg) / BK;
 
-    const uint16_t *A = (const uint16_t *)p.A;
-    const uint16_t *B = (const uint16_t *)p.B;
+    const T *A = (const T *)p.A;
+    const T *B = (const T *)p.B;
     OA oa;
     OB ob;
     oa.setup(m_blk, p.M, p.lda, wave, lane);
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
         char *base = smem + (s % NBUF) * STAGE;
         oa.issue(A, k0, base, wave);
         if constexpr (BI)
-            ob.issue(B, (const uint16_t *)p.zero, k0, base + OA::BYTES, wave, p.g);
+            ob.issue(B, (const T *)p.zero, k0, base + OA::BYTES, wave, p.g);
         else
             ob.issue(B, k0, base + OA::BYTES, wave);
     };
@@ -654,20 +670,46 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm16_dl_kernel(GemmParams p)
         issue(t + NBUF - 1);
         const char *la = smem + (t % NBUF) * STAGE;
         const char *lb = la + OA::BYTES;
+        if constexpr (DTID == DT_F32) {
 #pragma unroll
-        for (int q = 0; q < BK / 16; ++q) {
-            u32x4_t af[TM], bf[TN];
+            for (int q = 0; q < BK / 16; ++q) {
+                u32x4_t af[TM][2], bf[TN][2];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = OA::frag(la, (wm * TM + i) * 32 + l32, q, h);
+                for (int i = 0; i < TM; ++i) {
+                    af[i][0] = dl_chunk(la, (wm * TM + i) * 32 + l32, 4 * q + 2 * h);
+                    af[i][1] = dl_chunk(la, (wm * TM + i) * 32 + l32, 4 * q + 2 * h + 1);
+                }
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bf[j] = OB::frag(lb, (wn * TN + j) * 32 + l32, q, h);
+                for (int j = 0; j < TN; ++j) {
+                    bf[j][0] = dl_chunk(lb, (wn * TN + j) * 32 + l32, 4 * q + 2 * h);
+                    bf[j][1] = dl_chunk(lb, (wn * TN + j) * 32 + l32, 4 * q + 2 * h + 1);
+                }
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                __uint_as_float(af[i][tt >> 2][tt & 3]), __uint_as_float(bf[j][tt >> 2][tt & 3]),
+                                acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < BK / 16; ++q) {
+                u32x4_t af[TM], bf[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[i] = dl_chunk(la, (wm * TM + i) * 32 + l32, 2 * q + h);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = mfma16<DTID>(af[i], bf[j], acc[i][j]);
+                    bf[j] = dl_chunk(lb, (wn * TN + j) * 32 + l32, 2 * q + h);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = mfma16<DTID>(af[i], bf[j], acc[i][j]);
+            }
         }
     }
     // drain the loads of the stages past the end before the workgroup exits
@@ -697,10 +739,10 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
     const dim3 grid(tiles * p.splits), b8(512);
     switch (cfg) {
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm16_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -6,9 +6,13 @@
 namespace d4r {
 
 hipError_t launch_gemm_f32_nchw(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s);
+bool try_gemm_f32_dl(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s, hipError_t *err);
 
 hipError_t launch_gemm_f32(int cfg, int amode, int bmode, const GemmParams &p, hipStream_t s)
 {
+    hipError_t e;
+    if (try_gemm_f32_dl(cfg, amode, bmode, p, s, &e))
+        return e;
     if (amode == OP_KC && bmode == OP_ROWS)
         return launch_gemm32_modes<OP_KC, OP_ROWS>(cfg, p, s);
     if (amode == OP_KC && bmode == OP_KC)
