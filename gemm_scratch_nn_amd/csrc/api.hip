@@ -114,13 +114,17 @@ int tile_from_env(int dt)
 }
 
 // dl16: only the tiles of the 16-bit direct-to-LDS kernel (OP_IMPL_T).
-GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false)
+GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = false)
 {
     TileCand cands[6];
     int nc = 0;
     if (dl16) {
         cands[nc++] = {TILE_128x256, 1.0};
         cands[nc++] = {TILE_256x128, 1.0};
+        // a shade below the larger direct tiles: preferred only where it
+        // saves whole waves (the 129-tile data gradients of conv4/conv5)
+        if (dl128_enabled())
+            cands[nc++] = {TILE_128x128, 0.95};
     } else if (M <= 32) {
         cands[nc++] = {TILE_32x128, 1.0};
     } else if (M <= 64 || N <= 64) {
@@ -138,7 +142,9 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false)
                 cands[nc++] = {TILE_128x64, 0.92};
         }
     } else {
-        cands[nc++] = {TILE_128x128, 0.85};
+        // kk16: both operands k-contiguous, 16-byte rows, whole 64-deep
+        // stages, so 128x128 runs on the direct-to-LDS kernel too
+        cands[nc++] = {TILE_128x128, kk16 && dl128_enabled() ? 0.95 : 0.85};
         cands[nc++] = {TILE_128x256, 1.0};
         cands[nc++] = {TILE_256x128, 1.0};
         // small products (a 1x1 layer on the 46x80 map): when the large
@@ -581,7 +587,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->es = dt_size(dtype);
     h->fwd = plan_gemm(g.O, g.N, g.Kc, dtype);
     h->bwd_data = plan_gemm(g.Kc, g.N, g.O, dtype);
-    h->bwd_filter = plan_gemm(g.O, g.Kc, g.N, dtype);
+    // 16-bit filter gradient on the copied dy: two k-contiguous operands
+    h->bwd_filter = plan_gemm(g.O, g.Kc, g.N, dtype, false,
+                              dtype != D4R_F32 && g.N % 64 == 0 && g.Kc % 8 == 0);
     // For stride 1, dx[b,c,h,w] = sum_{o,u,v} W[o,c,u,v] dy[b,o,h+p-u,w+p-v]
     // is a stride-1 convolution of dy (O channels, OH x OW, padding kH-1-p)
     // with Wf[c,o,u,v] = W[o,c,kH-1-u,kW-1-v], whose output is exactly H x W.

@@ -24,6 +24,7 @@
 //    with its own L2): the M tiles that share a B panel then share one L2.
 #pragma once
 
+#include <stdlib.h>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -744,6 +745,10 @@ hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
     case TILE_256x128:
         hipLaunchKernelGGL((gemm_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
         break;
+    case TILE_128x128:
+        // four wavefronts, a ring of two stages (64 KB): two workgroups per CU
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 2, 2, 2, 2, BI>), grid, dim3(256), 0, s, p);
+        break;
     default:
         return hipErrorInvalidValue;
     }
@@ -828,7 +833,8 @@ hipError_t launch_gemm16(int cfg, int amode, int bmode, const GemmParams &p, hip
     if (!a_ok || !b_ok)
         return hipErrorInvalidValue;
     const bool a_kc = amode == OP_KC, b_kc = bmode == OP_KC;
-    if ((cfg == TILE_128x256 || cfg == TILE_256x128) && dl_applies(amode, bmode, p))
+    if ((cfg == TILE_128x256 || cfg == TILE_256x128 || (cfg == TILE_128x128 && dl128_enabled())) &&
+        dl_applies(amode, bmode, p))
         return launch_gemm16_dl<DTID>(cfg, p, s);
     if (a_kc && b_kc)
         return launch_gemm16_layout<DTID, true, true>(cfg, p, s);

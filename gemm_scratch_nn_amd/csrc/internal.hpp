@@ -2,6 +2,8 @@
 // libd4r_conv.  Nothing here is part of the public ABI.
 #pragma once
 
+#include <stdlib.h>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -63,6 +65,18 @@ __device__ __forceinline__ int xcd_tile(int pid, int n)
 __device__ __forceinline__ int small_div(int n, int d)
 {
     return (int)(((float)n + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
+// 128x128 tiles of two k-contiguous 16-bit operands run on the direct-to-LDS
+// kernel (the planner then rates them like the larger direct tiles);
+// D4R_DL128=0 keeps them on the register-staged kernel (experiments).
+inline bool dl128_enabled()
+{
+    static const bool on = [] {
+        const char *e = getenv("D4R_DL128");
+        return !(e && e[0] == '0');
+    }();
+    return on;
 }
 
 // Work item of workgroup `pid` in a GEMM's 1-D grid of tiles x splits.  The
