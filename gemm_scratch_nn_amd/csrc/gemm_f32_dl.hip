@@ -16,11 +16,8 @@ namespace {
 bool dl_f32_enabled()
 {
     // experiments, tests: D4R_F32_DL=0 runs the register-staged kernel
-    static const bool on = [] {
-        const char *e = getenv("D4R_F32_DL");
-        return !(e && e[0] == '0');
-    }();
-    return on;
+    const char *e = getenv("D4R_F32_DL");
+    return !(e && e[0] == '0');
 }
 
 template <bool BI>

@@ -72,11 +72,8 @@ __device__ __forceinline__ int small_div(int n, int d)
 // D4R_DL128=0 keeps them on the register-staged kernel (experiments).
 inline bool dl128_enabled()
 {
-    static const bool on = [] {
-        const char *e = getenv("D4R_DL128");
-        return !(e && e[0] == '0');
-    }();
-    return on;
+    const char *e = getenv("D4R_DL128");
+    return !(e && e[0] == '0');
 }
 
 // Work item of workgroup `pid` in a GEMM's 1-D grid of tiles x splits.  The

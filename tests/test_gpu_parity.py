@@ -367,6 +367,36 @@ def test_gemm_every_tile_config(dt, tile, flags, monkeypatch):
         assert err < TOL[dt], (tile, M, K, N, err)
 
 
+# The direct-to-LDS kernel takes two k-contiguous operands (flags 2) on the
+# f32 128x128 / 128x64 and 16-bit 128x128 tiles by default; the switches
+# below run the register-staged kernels those GEMMs would otherwise use.
+@pytest.mark.parametrize("dt,tile,switch", [("f32", "128x128", "D4R_F32_DL"), ("f32", "128x64", "D4R_F32_DL"),
+                                            ("f16", "128x128", "D4R_DL128"), ("bf16", "128x128", "D4R_DL128")])
+@pytest.mark.parametrize("direct", [True, False])
+def test_gemm_direct_and_register_staged(dt, tile, switch, direct, monkeypatch):
+    monkeypatch.setenv("D4R_GEMM_TILE", tile)
+    monkeypatch.setenv(switch, "1" if direct else "0")
+    for (M, K, N) in [(300, 256, 333), (129, 64, 520), (296, 256, 336), (200, 4096, 304), (70, 96, 36)]:
+        rng = np.random.default_rng(M + K + N + 7)
+        a = wl.quantize(rng.normal(size=(M, K)), dt)
+        b = wl.quantize(rng.normal(size=(N, K)), dt)
+        ref = oracle.gemm(a.exact, b.exact, M, K, N, 2)
+        C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
+        torch.cuda.synchronize()
+        err = rel_err(host(C), ref)
+        assert err < TOL[dt], (tile, direct, M, K, N, err)
+
+
+@pytest.mark.parametrize("dt,switch", [("f32", "D4R_F32_DL"), ("bf16", "D4R_DL128")])
+def test_conv_c4_register_staged_gradients(dt, switch, monkeypatch):
+    # conv5 at batch 3 with the direct-to-LDS kernel switched off: the
+    # register-staged filter-gradient GEMM and NHWC data gradient
+    monkeypatch.setenv(switch, "0")
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[2].shape.with_batch(3)
+    _check_whole(sh, dt, wl.conv_inputs(w, 2, dt, batch=3), f"c4/conv5/b3/{switch}=0")
+
+
 # f32 conv passes with every tile and both ways of taking dy in the gradient
 # GEMMs (read in place by the NCHW operand loaders, or copied first), over
 # odd pixel counts whose images straddle tiles, with and without 16-byte
