@@ -49,9 +49,9 @@
  * float32 dcol, split-K partial sums) lives in a caller buffer ws of at least
  * d4r_conv_workspace_size() bytes.  d4r_conv_forward leaves the col matrix
  * of x at the start of ws; d4r_conv_backward_data does not touch that
- * region, so a following d4r_conv_backward_filter with reuse_col = 1 and the
- * same ws reuses it (the page saves the im2col buffer in forward for the
- * filter gradient, "Memory Management").
+ * region, so a following d4r_conv_backward_filter (or d4r_conv_backward)
+ * with reuse_col = 1 and the same ws reuses it (the page saves the im2col
+ * buffer in forward for the filter gradient, "Memory Management").
  *
  * Streams.  hip_stream is a hipStream_t (NULL = the null stream).  Calls
  * only enqueue kernels on it: no host synchronisation, no allocation.
