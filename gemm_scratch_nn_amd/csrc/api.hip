@@ -477,6 +477,18 @@ hipError_t step_grad_reshape(const d4r_conv *h, const void *dy, void *G, float *
     return e;
 }
 
+// The bias gradient's partial sums only; their per-channel sums ride on the
+// filter-gradient GEMM (a BiasSum with h->bias_splits parts).
+hipError_t step_bias_partials(const d4r_conv *h, const void *dy, float *partial, hipStream_t s)
+{
+    const ConvGeom &g = h->g;
+    ProfScope ps(s, std::string("bias_partial_") + dt_name(h->dt) + ":wgrad", 0.0,
+                 (double)h->es * g.O * g.N + 4.0 * g.O * h->bias_splits);
+    hipError_t e = launch_bias_partials(h->dt, g, dy, partial, h->bias_splits, s);
+    ps.done();
+    return e;
+}
+
 hipError_t step_bias(const d4r_conv *h, const void *dy, float *db, float *partial, hipStream_t s)
 {
     const ConvGeom &g = h->g;
@@ -984,13 +996,18 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     char *wsb = (char *)ws;
     void *col = wsb;
     float *partial = (float *)(wsb + h->off_big);
+    // dy read in place by the GEMM: the bias partials first, their sums
+    // with the GEMM's split-K reduction (or right after it)
+    float *bias_part = (float *)(wsb + h->off_bias);
+    const BiasSum bsum{bias_part, db, g.O, h->bias_splits};
     if (h->pointwise && !reuse_col) {
         // 1x1: dW = sum_b dy[b] * x[b]^T with dy and x read in place
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_NCHW, OP_NCHW_K, dy, 0, x, 0, g.O, g.Kc, g.N,
-                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g, g.O, g.C),
-                   "pointwise filter-gradient GEMM");
         if (db)
-            D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s), "bias gradient");
+            D4R_LAUNCH(step_bias_partials(h, dy, bias_part, s), "bias gradient");
+        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_NCHW, OP_NCHW_K, dy, 0, x, 0, g.O, g.Kc, g.N,
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g, g.O, g.C, nullptr, 0,
+                            db ? &bsum : nullptr),
+                   "pointwise filter-gradient GEMM");
         return ok();
     }
     if (!reuse_col)
@@ -998,25 +1015,22 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     // dW = G * col^T: A = G (O x N), read from dy in place or reshaped;
     // B = col (Kc x N) read k-contiguous as op(B) = col^T
     if (h->wgrad == GP_INPLACE) {
+        if (db)
+            D4R_LAUNCH(step_bias_partials(h, dy, bias_part, s), "bias gradient");
         D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_NCHW, OP_KC, dy, 0, col, g.N, g.O, g.Kc, g.N,
-                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g),
+                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", &g, 0, 0, nullptr, 0,
+                            db ? &bsum : nullptr),
                    "filter-gradient GEMM");
-    } else {
-        // the reshape's pass over dy also yields the bias partial sums
-        void *G = wsb + h->off_g;
-        float *bias_part = db ? (float *)(wsb + h->off_bias) : nullptr;
-        D4R_LAUNCH(step_grad_reshape(h, dy, G, bias_part, s), "grad reshape");
-        // the bias sum rides on the GEMM's split-K reduction (or follows it)
-        const BiasSum bs{bias_part, db, g.O, grad_reshape_blocks(h->dt, g)};
-        D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N,
-                            EPI_ROWMAJOR, dw, g.Kc, nullptr, 0, partial, s, "wgrad", nullptr, 0, 0, nullptr, 0,
-                            db ? &bs : nullptr),
-                   "filter-gradient GEMM and bias gradient");
         return ok();
     }
-    if (db)
-        D4R_LAUNCH(step_bias(h, dy, db, (float *)(wsb + h->off_bias), s),
-                   "bias gradient");
+    // the reshape's pass over dy also yields the bias partial sums
+    void *G = wsb + h->off_g;
+    D4R_LAUNCH(step_grad_reshape(h, dy, G, db ? bias_part : nullptr, s), "grad reshape");
+    // the bias sum rides on the GEMM's split-K reduction (or follows it)
+    const BiasSum bs{bias_part, db, g.O, grad_reshape_blocks(h->dt, g)};
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N, EPI_ROWMAJOR, dw,
+                        g.Kc, nullptr, 0, partial, s, "wgrad", nullptr, 0, 0, nullptr, 0, db ? &bs : nullptr),
+               "filter-gradient GEMM and bias gradient");
     return ok();
 }
 

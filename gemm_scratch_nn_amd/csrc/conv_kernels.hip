@@ -1116,8 +1116,8 @@ int bias_grad_splits(const ConvGeom &g)
     return (g.B + per - 1) / per;
 }
 
-hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db, float *partial,
-                            int splits, hipStream_t s)
+hipError_t launch_bias_partials(int dt, const ConvGeom &g, const void *dy, float *partial, int splits,
+                                hipStream_t s)
 {
     const int per = (g.B + splits - 1) / splits;
     dim3 grid(splits, g.O);
@@ -1127,7 +1127,13 @@ hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db
     else
         hipLaunchKernelGGL(bias_partial_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)dy,
                            partial, g, splits, per, dt);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db, float *partial,
+                            int splits, hipStream_t s)
+{
+    hipError_t e = launch_bias_partials(dt, g, dy, partial, splits, s);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(bias_final_kernel, dim3((g.O + NT - 1) / NT), dim3(NT), 0, s, partial, db, g.O,

@@ -181,6 +181,10 @@ hipError_t launch_bias_final(const float *partial, float *db, int O, int splits,
 hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, void *out,
                             hipStream_t s);
 // db[o] = sum_{b,pix} dy[b][o][pix]; partial holds O*splits floats
+// pass 1 of launch_bias_grad alone: partial[o*splits + k] (the per-channel
+// sums then come from a BiasSum)
+hipError_t launch_bias_partials(int dt, const ConvGeom &g, const void *dy, float *partial, int splits,
+                                hipStream_t s);
 hipError_t launch_bias_grad(int dt, const ConvGeom &g, const void *dy, float *db,
                             float *partial, int splits, hipStream_t s);
 int bias_grad_splits(const ConvGeom &g);
