@@ -43,9 +43,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4",
-                    help="c1..c5, or lenet: one whole LeNet-5 training step (conv, ReLU, pooling, "
-                         "linear layers, softmax-CE, SGD) at --batch")
-    ap.add_argument("--batch", type=int, default=64, help="batch of the lenet workload")
+                    help="c1..c5, or lenet / alexnet: one whole LeNet-5 / AlexNet training step "
+                         "(conv, ReLU, pooling, linear layers, softmax-CE, SGD) at --batch")
+    ap.add_argument("--batch", type=int, default=64, help="batch of the lenet / alexnet workload")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -178,17 +178,23 @@ def roofline_of(by_kernel, dom, peak_tf):
 
 
 def bench_lenet(args) -> int:
-    """Whole LeNet-5 training steps (forward, backward, SGD) at --batch, fp32."""
+    """Whole LeNet-5 or AlexNet training steps (forward, backward, SGD) at --batch, fp32."""
     import torch
 
     import workloads as W
-    from gemm_scratch_nn_amd.lenet import LeNetStep
 
     B = args.batch
-    lr, clip = 0.01, 0.05
-    inp = W.lenet_step_inputs(B, 0)
-    net = LeNetStep(B)
-    net.load({n: torch.from_numpy(inp[n]).cuda() for n, _ in W.LENET_PARAMS})
+    alex = args.workload == "alexnet"
+    if alex:
+        from gemm_scratch_nn_amd.alexnet import AlexNetStep as Net
+        lr, clip = 0.01, 0.002
+        inp, params = W.alexnet_step_inputs(B, 0), W.ALEXNET_PARAMS
+    else:
+        from gemm_scratch_nn_amd.lenet import LeNetStep as Net
+        lr, clip = 0.01, 0.05
+        inp, params = W.lenet_step_inputs(B, 0), W.LENET_PARAMS
+    net = Net(B)
+    net.load({n: torch.from_numpy(inp[n]).cuda() for n, _ in params})
     x = torch.from_numpy(inp["x"]).cuda()
     lab = torch.from_numpy(inp["labels"]).cuda()
 
@@ -232,15 +238,26 @@ def bench_lenet(args) -> int:
         if not os.path.exists(oracle.LIB_PATH):
             oracle.build()
         n, t = 0, 0.0
+        if alex:
+            # a bounded sample: the first two images of the batch
+            sample = {k: (v[:2] if k in ("x", "labels") else v) for k, v in inp.items()}
+            nb = 2
+        else:
+            sample, nb = inp, B
+        step_fn = oracle.alexnet_step if alex else oracle.lenet_step
         while t < args.cpu_seconds and n < 1000:
             t1 = time.perf_counter()
-            oracle.lenet_step(inp, lr, clip)
+            step_fn(sample, lr, clip)
             t += time.perf_counter() - t1
             n += 1
-        cpu = {"value": n * B / t, "unit": "images/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{n} whole LeNet-5 steps at batch {B} (float64); {t:.2f} s"}
+        cpu = {"value": n * nb / t, "unit": "images/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{n} whole {'AlexNet' if alex else 'LeNet-5'} steps at batch {nb} (float64); {t:.2f} s"}
+    net_name = "AlexNet" if alex else "LeNet-5"
+    desc = ("AlexNet 3x224x224: conv 11x11/4 3->96, pool 3/2, conv 5x5 96->256, pool, conv 3x3 256->384->"
+            "384->256, pool, linear 9216->4096->4096->2" if alex else
+            "LeNet-5 1x28x28: conv 5x5 1->6, pool 2, conv 5x5 6->16, pool 2, linear 256->120->84->10")
     line = {
-        "metric": "LeNet-5 training throughput (images/s): forward, backward and SGD update",
+        "metric": f"{net_name} training throughput (images/s): forward, backward and SGD update",
         "value": B / (ms * 1e-3),
         "unit": "images/s",
         "n_gpus": 1,
@@ -251,9 +268,9 @@ def bench_lenet(args) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded dyadic images and conv weights, Kaiming linear weights, uniform labels)",
-        "config": {"workload": f"LeNet-5 1x28x28: conv 5x5 1->6, pool 2, conv 5x5 6->16, pool 2, "
-                               f"linear 256->120->84->10, softmax-CE, SGD lr {lr} clip {clip}",
+        "data": ("synthetic (seeded U[0,1) images, Kaiming weights, uniform labels)" if alex else
+                 "synthetic (seeded dyadic images and conv weights, Kaiming linear weights, uniform labels)"),
+        "config": {"workload": f"{desc}, softmax-CE, SGD lr {lr} clip {clip}",
                    "batch": B, "hip_graph": bool(args.graph)},
         "kernel_busy_ms_per_step": busy_ms,
         "launches_per_step": sum(v["launches"] for v in by_kernel.values()) / args.steps,
@@ -272,7 +289,7 @@ def main() -> int:
               "multi-GPU batch sharding is a design note only", file=sys.stderr)
         return 2
 
-    if args.workload == "lenet":
+    if args.workload in ("lenet", "alexnet"):
         return bench_lenet(args)
 
     import torch

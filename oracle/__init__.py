@@ -378,3 +378,74 @@ def lenet_step(inp: dict, lr: float, clip: float) -> dict:
                  "fc3_w", "fc3_b"):
         r["new_" + name] = sgd(f[name], r["d" + name], lr, clip)
     return r
+
+
+def alexnet_step(inp: dict, lr: float, clip: float) -> dict:
+    """Forward, backward and SGD update of AlexNet on one batch, in float64.
+
+    The directcompute-nn page trains AlexNet on two-class PetImages ("File
+    Structure": 5 conv layers, 3 FC layers), with the same autograd rules as
+    lenet_step.  Layers (sizes of the AlexNet configs): conv1 11x11 stride 4
+    pad 2, ReLU, max pool 3x3 stride 2; conv2 5x5 pad 2, ReLU, pool; conv3,
+    conv4, conv5 3x3 pad 1 with ReLU after each and a pool after conv5;
+    flatten (NCHW order) to 9216; linear 9216->4096, ReLU, 4096->4096, ReLU,
+    4096->classes; softmax-cross-entropy (gradient softmax - one_hot, no
+    1/batch factor); param -= lr * clamp(grad, -clip, clip).
+
+    ``inp`` holds x, labels and the parameters named in
+    workloads.ALEXNET_PARAMS.  Returns the loss, the activations ("a1".."a5"
+    ReLU outputs, "p1", "p2", "p5" pooled, "h1", "h2", "z"), every gradient
+    ("d" + name) and every updated parameter ("new_" + name).
+    """
+    f = {k: _f64(v) if k != "labels" else np.asarray(v) for k, v in inp.items()}
+    B = f["x"].shape[0]
+    r = {}
+    # forward: (input, stride, padding, pool after)
+    convs = (("conv1", "x", 4, 2, True), ("conv2", "p1", 1, 2, True), ("conv3", "p2", 1, 1, False),
+             ("conv4", "a3", 1, 1, False), ("conv5", "a4", 1, 1, True))
+    src = {"x": f["x"]}
+    for i, (name, inp_key, s, p, pool) in enumerate(convs, start=1):
+        a = relu(conv_forward(src[inp_key], f[name + "_w"], f[name + "_b"], s, p))
+        r["a%d" % i] = src["a%d" % i] = a
+        if pool:
+            r["p%d" % i], r["idx%d" % i] = maxpool_forward(a, 3, 2)
+            src["p%d" % i] = r["p%d" % i]
+    flat = r["p5"].reshape(B, -1)
+    n_in, n_h, n_out = flat.shape[1], f["fc1_w"].shape[0], f["fc3_w"].shape[0]
+    r["pre1"] = add_bias_rows(gemm(flat, f["fc1_w"], B, n_in, n_h, 2), f["fc1_b"])
+    r["h1"] = relu(r["pre1"])
+    r["pre2"] = add_bias_rows(gemm(r["h1"], f["fc2_w"], B, n_h, n_h, 2), f["fc2_b"])
+    r["h2"] = relu(r["pre2"])
+    r["z"] = add_bias_rows(gemm(r["h2"], f["fc3_w"], B, n_h, n_out, 2), f["fc3_b"])
+    r["loss"] = ce_loss(r["z"], f["labels"])
+    # backward
+    dz = softmax_ce_grad(r["z"], f["labels"])
+    r["dz"] = dz
+    r["dfc3_w"] = gemm(dz, r["h2"], n_out, B, n_h, 1)
+    r["dfc3_b"] = bias_grad_rows(dz)
+    dh2 = relu_grad(r["pre2"], gemm(dz, f["fc3_w"], B, n_out, n_h, 0))
+    r["dfc2_w"] = gemm(dh2, r["h1"], n_h, B, n_h, 1)
+    r["dfc2_b"] = bias_grad_rows(dh2)
+    dh1 = relu_grad(r["pre1"], gemm(dh2, f["fc2_w"], B, n_h, n_h, 0))
+    r["dfc1_w"] = gemm(dh1, flat, n_h, B, n_in, 1)
+    r["dfc1_b"] = bias_grad_rows(dh1)
+    dflat = gemm(dh1, f["fc1_w"], B, n_h, n_in, 0)
+    # the gradient reaching each conv layer's ReLU output, from the top
+    d = maxpool_backward(dflat.reshape(r["p5"].shape), r["idx5"], r["a5"].shape, 3, 2)
+    for i in (5, 4, 3, 2, 1):
+        name, inp_key, s, p, _ = convs[i - 1]
+        g = relu_grad(r["a%d" % i], d)
+        x_in = src[inp_key]
+        r["d%s_w" % name] = conv_backward_filter(x_in, g, f[name + "_w"].shape, s, p)
+        r["d%s_b" % name] = conv_backward_bias(g)
+        if i == 1:
+            break
+        d = conv_backward_data(g, f[name + "_w"], x_in.shape, s, p)
+        if inp_key.startswith("p"):  # through the pool that produced this input
+            k = int(inp_key[1:])
+            d = maxpool_backward(d, r["idx%d" % k], r["a%d" % k].shape, 3, 2)
+    # update
+    for name in [n for n in inp if n not in ("x", "labels")]:
+        r["new_" + name] = sgd(f[name], r["d" + name], lr, clip)
+    return r
+

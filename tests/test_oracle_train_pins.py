@@ -212,3 +212,46 @@ def test_lenet_step_matches_torch_autograd(orc, batch, seed):
     # the clip acted on some gradients and not on others
     d = np.concatenate([np.abs(g).ravel() for g in grads.values()])
     assert (d > clip).any() and (d < clip).any()
+
+
+# ---------------------------------------------------- a whole AlexNet step
+def _alexnet_torch_f64(inp, lr, clip):
+    """The same network in torch float64 autograd (independent operators)."""
+    p = {k: _t(v).requires_grad_() for k, v in inp.items() if k not in ("x", "labels")}
+    a = _t(inp["x"])
+    for name, s, pad, pool in (("conv1", 4, 2, True), ("conv2", 1, 2, True), ("conv3", 1, 1, False),
+                               ("conv4", 1, 1, False), ("conv5", 1, 1, True)):
+        a = F.relu(F.conv2d(a, p[name + "_w"], p[name + "_b"], stride=s, padding=pad))
+        if pool:
+            a = F.max_pool2d(a, 3, 2)
+    h = a.reshape(a.shape[0], -1)
+    h = F.relu(F.linear(h, p["fc1_w"], p["fc1_b"]))
+    h = F.relu(F.linear(h, p["fc2_w"], p["fc2_b"]))
+    z = F.linear(h, p["fc3_w"], p["fc3_b"])
+    lab = torch.tensor(inp["labels"], dtype=torch.long)
+    F.cross_entropy(z, lab, reduction="sum").backward()
+    loss = F.cross_entropy(z, lab).item()
+    new = {k: (v - lr * torch.clamp(v.grad, -clip, clip)).detach().numpy() for k, v in p.items()}
+    return loss, {k: v.grad.numpy() for k, v in p.items()}, new
+
+
+def test_alexnet_step_matches_torch_autograd(orc):
+    # batch 1 (the oracle's float64 loops take a few seconds at 224x224);
+    # continuous inputs: no ReLU zeros or max-pool ties
+    import workloads as wl
+    rng = np.random.default_rng((881, 0))
+    inp = {"x": rng.uniform(0.0, 1.0, size=(1, 3, 224, 224)),
+           "labels": np.array([1], dtype=np.int32)}
+    for name, shape in wl.ALEXNET_PARAMS:
+        fan_in = int(np.prod(shape[1:]))
+        inp[name] = rng.normal(0.0, np.sqrt(2.0 / fan_in) if name.endswith("_w") else 0.05, size=shape)
+    lr, clip = 0.05, 0.002
+    r = orc.alexnet_step(inp, lr, clip)
+    loss, grads, new = _alexnet_torch_f64(inp, lr, clip)
+    assert abs(r["loss"] - loss) <= 1e-10 * max(1.0, abs(loss))
+    for name, g in grads.items():
+        scale = np.max(np.abs(g))
+        assert np.allclose(r["d" + name], g, rtol=1e-8, atol=1e-10 * scale), name
+        assert np.allclose(r["new_" + name], new[name], rtol=1e-10, atol=1e-14), name
+    d = np.concatenate([np.abs(g).ravel() for g in grads.values()])
+    assert (d > clip).any() and (d < clip).any()

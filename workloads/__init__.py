@@ -325,3 +325,39 @@ def lenet_step_inputs(batch: int, seed: int) -> Dict[str, np.ndarray]:
     for t, (name, shape) in enumerate(LENET_PARAMS):
         out[name] = f32_array(dists.get(name, ("normal", 0.01)), shape, (900 + seed, 2 + t))
     return out
+
+
+# AlexNet as the directcompute-nn page trains it on PetImages ("File
+# Structure": 5 conv layers, 3 FC layers; two classes), with the layer sizes
+# of the AlexNet configs above: conv1 3->96 11x11 s4 p2 (224 -> 55), ReLU,
+# max pool 3x3 s2 (-> 27); conv2 96->256 5x5 p2, ReLU, pool (-> 13); conv3
+# 256->384, conv4 384->384, conv5 384->256 (3x3 p1), ReLU after each, pool
+# after conv5 (-> 6); flatten to 9216; linear 9216->4096, ReLU, 4096->4096,
+# ReLU, 4096->2.
+ALEXNET_CLASSES = 2
+ALEXNET_PARAMS = (("conv1_w", (96, 3, 11, 11)), ("conv1_b", (96,)),
+                  ("conv2_w", (256, 96, 5, 5)), ("conv2_b", (256,)),
+                  ("conv3_w", (384, 256, 3, 3)), ("conv3_b", (384,)),
+                  ("conv4_w", (384, 384, 3, 3)), ("conv4_b", (384,)),
+                  ("conv5_w", (256, 384, 3, 3)), ("conv5_b", (256,)),
+                  ("fc1_w", (4096, 9216)), ("fc1_b", (4096,)),
+                  ("fc2_w", (4096, 4096)), ("fc2_b", (4096,)),
+                  ("fc3_w", (ALEXNET_CLASSES, 4096)), ("fc3_b", (ALEXNET_CLASSES,)))
+
+
+def alexnet_step_inputs(batch: int, seed: int) -> Dict[str, np.ndarray]:
+    """Seeded float32 inputs of one AlexNet training step.
+
+    x is U[0, 1) on 3x224x224 (the AlexNet conv1 config's input); every
+    weight is Kaiming-normal for its fan-in, biases N(0, 0.01); labels are
+    uniform over the two classes.
+    """
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = f32_array(("uniform", 0.0, 1.0), (batch, 3, 224, 224), (950 + seed, 0))
+    out["labels"] = labels(batch, ALEXNET_CLASSES, (950 + seed, 1))
+    for t, (name, shape) in enumerate(ALEXNET_PARAMS):
+        fan_in = int(np.prod(shape[1:]))
+        dist = _kaiming(fan_in) if name.endswith("_w") else ("normal", 0.01)
+        out[name] = f32_array(dist, shape, (950 + seed, 2 + t))
+    return out
+
