@@ -236,13 +236,20 @@ def _alexnet_torch_f64(inp, lr, clip):
 
 
 def test_alexnet_step_matches_torch_autograd(orc):
-    # batch 1 (the oracle's float64 loops take a few seconds at 224x224);
-    # continuous inputs: no ReLU zeros or max-pool ties
+    # the oracle's AlexNet composition (layer order, strides, paddings,
+    # pools, flatten, linear flags) on a smaller input and hidden width, so
+    # its float64 loops stay fast: 3x99x99 -> conv1 24x24 -> pool 11 ->
+    # conv2 11 -> pool 5 -> conv3-5 5 -> pool 2 -> flatten 1024 -> 256 -> 256
+    # -> 2; the same code runs at 224x224 in the GPU parity test.
+    # Continuous inputs: no ReLU zeros or max-pool ties.
     import workloads as wl
     rng = np.random.default_rng((881, 0))
-    inp = {"x": rng.uniform(0.0, 1.0, size=(1, 3, 224, 224)),
-           "labels": np.array([1], dtype=np.int32)}
-    for name, shape in wl.ALEXNET_PARAMS:
+    inp = {"x": rng.uniform(0.0, 1.0, size=(2, 3, 99, 99)),
+           "labels": np.array([1, 0], dtype=np.int32)}
+    shapes = dict(wl.ALEXNET_PARAMS)
+    shapes.update({"fc1_w": (256, 1024), "fc1_b": (256,), "fc2_w": (256, 256), "fc2_b": (256,),
+                   "fc3_w": (2, 256)})
+    for name, shape in shapes.items():
         fan_in = int(np.prod(shape[1:]))
         inp[name] = rng.normal(0.0, np.sqrt(2.0 / fan_in) if name.endswith("_w") else 0.05, size=shape)
     lr, clip = 0.05, 0.002
