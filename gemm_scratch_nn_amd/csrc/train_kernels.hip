@@ -97,6 +97,42 @@ __global__ __launch_bounds__(NT) void maxpool_fwd_kernel(const float *__restrict
     }
 }
 
+// The same scan with the window size K fixed at compile time: blockIdx.y is
+// the plane, blockIdx.x * NT + thread the output position (the host checks
+// OH*OW < 2^20, OW <= 1024 for small_div, planes <= 65535).  The K*K loads
+// are issued before the scan, which keeps the first strict maximum in
+// row-major order as above.
+template <int K>
+__global__ __launch_bounds__(NT) void maxpool_fwd_fixed_kernel(const float *__restrict__ x, float *__restrict__ y,
+                                                               int32_t *__restrict__ idx, int H, int W, int OH,
+                                                               int OW, int s)
+{
+    const int r = blockIdx.x * NT + threadIdx.x;
+    if (r >= OH * OW)
+        return;
+    const int i = small_div(r, OW), j = r - i * OW;
+    const float *xp = x + (long long)blockIdx.y * H * W;
+    float v[K][K];
+#pragma unroll
+    for (int u = 0; u < K; ++u)
+#pragma unroll
+        for (int q = 0; q < K; ++q)
+            v[u][q] = xp[(i * s + u) * W + (j * s + q)];
+    int best = (i * s) * W + j * s;
+    float bv = v[0][0];
+#pragma unroll
+    for (int u = 0; u < K; ++u)
+#pragma unroll
+        for (int q = 0; q < K; ++q)
+            if (v[u][q] > bv) {
+                bv = v[u][q];
+                best = (i * s + u) * W + (j * s + q);
+            }
+    const long long o = (long long)blockIdx.y * OH * OW + r;
+    y[o] = bv;
+    idx[o] = best;
+}
+
 // One thread per input element: add dy of every window that covers it and
 // saved it as the maximum, windows i ascending then j ascending.  A gather,
 // so overlapping windows (stride < k) need no atomics and every dx element
@@ -125,6 +161,49 @@ __global__ __launch_bounds__(NT) void maxpool_bwd_kernel(const float *__restrict
             }
         dx[e] = acc;
     }
+}
+
+// The same gather with T = ceil(k/s) candidate windows per axis fixed at
+// compile time: blockIdx.y is the plane and blockIdx.x * NT + thread the
+// position in it (the host checks H*W < 2^20, W <= 1024 for small_div, and
+// planes <= 65535).  Every candidate's argmax and dy are loaded
+// unconditionally (a candidate outside the window range reads window 0 of
+// the plane and is dropped), so all loads of an element are in flight
+// together; they are added in the same order as above (i, then j
+// ascending), so the sums are identical.
+template <int T>
+__global__ __launch_bounds__(NT) void maxpool_bwd_fixed_kernel(const float *__restrict__ dy,
+                                                               const int32_t *__restrict__ idx,
+                                                               float *__restrict__ dx, int H, int W, int OH,
+                                                               int OW, int k, int s)
+{
+    const int at = blockIdx.x * NT + threadIdx.x;
+    if (at >= H * W)
+        return;
+    const int h = small_div(at, W), w = at - h * W;
+    const int i0 = h >= k ? (h - k) / s + 1 : 0, i1 = min(h / s, OH - 1);
+    const int j0 = w >= k ? (w - k) / s + 1 : 0, j1 = min(w / s, OW - 1);
+    const long long base = (long long)blockIdx.y * OH * OW;
+    int id[T][T];
+    float v[T][T];
+#pragma unroll
+    for (int a = 0; a < T; ++a)
+#pragma unroll
+        for (int b = 0; b < T; ++b) {
+            const bool ok = i0 + a <= i1 && j0 + b <= j1;
+            const long long o = base + (ok ? (i0 + a) * OW + j0 + b : 0);
+            const int32_t io = idx[o];
+            id[a][b] = ok ? io : -1;
+            v[a][b] = dy[o];
+        }
+    float acc = 0.0f;
+#pragma unroll
+    for (int a = 0; a < T; ++a)
+#pragma unroll
+        for (int b = 0; b < T; ++b)
+            if (id[a][b] == at)
+                acc += v[a][b];
+    dx[(long long)blockIdx.y * H * W + at] = acc;
 }
 
 // y[i][j] = x[i][j] + bias[j]; y may be x (one thread per element)
@@ -333,6 +412,14 @@ hipError_t launch_relu_backward(const float *x, const float *dy, float *dx, long
 hipError_t launch_maxpool_forward(const float *x, float *y, int32_t *idx, long long planes, int H, int W,
                                   int OH, int OW, int k, int st, hipStream_t s)
 {
+    if (planes <= 65535 && (long long)OH * OW < (1 << 20) && OW <= 1024 && (k == 2 || k == 3)) {
+        const dim3 grid((unsigned)((OH * OW + NT - 1) / NT), (unsigned)planes);
+        if (k == 2)
+            hipLaunchKernelGGL(maxpool_fwd_fixed_kernel<2>, grid, dim3(NT), 0, s, x, y, idx, H, W, OH, OW, st);
+        else
+            hipLaunchKernelGGL(maxpool_fwd_fixed_kernel<3>, grid, dim3(NT), 0, s, x, y, idx, H, W, OH, OW, st);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(maxpool_fwd_kernel, dim3(blocks_for(planes * OH * OW, 1)), dim3(NT), 0, s, x, y, idx,
                        planes, H, W, OH, OW, k, st);
     return hipGetLastError();
@@ -341,8 +428,20 @@ hipError_t launch_maxpool_forward(const float *x, float *y, int32_t *idx, long l
 hipError_t launch_maxpool_backward(const float *dy, const int32_t *idx, float *dx, long long planes, int H,
                                    int W, int OH, int OW, int k, int st, hipStream_t s)
 {
-    hipLaunchKernelGGL(maxpool_bwd_kernel, dim3(blocks_for(planes * H * W, 1)), dim3(NT), 0, s, dy, idx, dx,
-                       planes, H, W, OH, OW, k, st);
+    const long long total = planes * H * W;
+    const int t = (k + st - 1) / st;  // candidate windows per axis
+    if (planes <= 65535 && (long long)H * W < (1 << 20) && W <= 1024 && t <= 3) {
+        const dim3 grid((unsigned)((H * W + NT - 1) / NT), (unsigned)planes);
+        if (t == 1)
+            hipLaunchKernelGGL(maxpool_bwd_fixed_kernel<1>, grid, dim3(NT), 0, s, dy, idx, dx, H, W, OH, OW, k, st);
+        else if (t == 2)
+            hipLaunchKernelGGL(maxpool_bwd_fixed_kernel<2>, grid, dim3(NT), 0, s, dy, idx, dx, H, W, OH, OW, k, st);
+        else
+            hipLaunchKernelGGL(maxpool_bwd_fixed_kernel<3>, grid, dim3(NT), 0, s, dy, idx, dx, H, W, OH, OW, k, st);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(maxpool_bwd_kernel, dim3(blocks_for(total, 1)), dim3(NT), 0, s, dy, idx, dx, planes, H, W,
+                       OH, OW, k, st);
     return hipGetLastError();
 }
 
