@@ -253,6 +253,75 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
+// im2col for stride 1 when OW is a multiple of the vector width VW.  A block
+// owns channel c, images [b0, b0+BB) and output rows [i0, i0+RB) as above;
+// LDS holds, for every column tap v, the Rl window rows restricted to the
+// OW columns that tap reads: copy[v][bb][r][j] = x(b0+bb, c, i0-p+r, j+v-p)
+// (0 in the padding).  The VW outputs (b, i, j0..j0+VW-1) of tap (u, v) are
+// then copy[v][bb][i-i0+u][j0..j0+VW-1]: one aligned 16-byte LDS read per
+// 16-byte store (the general kernel reads VW single elements).  The fill
+// walks the copies in their LDS order, eight loads in flight per thread.
+// Host checks: OW <= 1024, BB*Rl <= 1024 and kW*BB*Rl*OW < 2^20 (small_div),
+// LDS within 48 KB.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void im2col_shift_kernel(const T *__restrict__ x, T *__restrict__ col,
+                                                          ConvGeom g, int RB, int BB, int Rl)
+{
+    constexpr int VW = Vec16<T>::N;
+    using V = typename Vec16<T>::type;
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    T *lds = (T *)lds_raw;
+    const int c = blockIdx.y;
+    const int b0 = blockIdx.z * BB;
+    const int nbb = min(BB, g.B - b0);
+    const int i0 = blockIdx.x * RB;
+    const int rows = min(g.OH, i0 + RB) - i0;
+    const int OW = g.OW;
+    const int rows_c = nbb * Rl;          // window rows of one tap copy
+    const int total = g.kW * rows_c * OW;  // LDS elements
+    {
+        constexpr int FB = 8;
+        for (int t0 = threadIdx.x; t0 < total; t0 += FB * NT) {
+            T val[FB];
+#pragma unroll
+            for (int k = 0; k < FB; ++k) {
+                const int t = t0 + k * NT;
+                const int rid = small_div(t, OW), j = t - rid * OW;
+                const int v = small_div(rid, rows_c), rr = rid - v * rows_c;
+                const int bb = small_div(rr, Rl), r = rr - bb * Rl;
+                const int hh = i0 - g.p + r, ww = j + v - g.p;
+                const bool ok = t < total && (unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W;
+                const long long a = (((long long)(b0 + bb) * g.C + c) * g.H + hh) * g.W + ww;
+                const T xv = x[ok ? a : 0];
+                val[k] = ok ? xv : (T)0;
+            }
+#pragma unroll
+            for (int k = 0; k < FB; ++k)
+                if (t0 + k * NT < total)
+                    lds[t0 + k * NT] = val[k];
+        }
+    }
+    __syncthreads();
+    const int khw = g.kH * g.kW;
+    const int n_start = (b0 * g.OH + i0) * OW;  // a multiple of OW, so of VW
+    const int per_img = rows * OW;
+    const int nvec = nbb * per_img / VW;
+    for (int q = threadIdx.x; q < nvec; q += NT) {
+        const int lo = q * VW;
+        const int bb = lo / per_img, rem = lo - bb * per_img;
+        const int il = rem / OW, j0 = rem - il * OW;
+        T *dst = col + (long long)c * khw * g.N + n_start + lo;
+        const T *src0 = lds + (bb * Rl + il) * OW + j0;
+        for (int u = 0; u < g.kH; ++u)
+            for (int v = 0; v < g.kW; ++v) {
+                *(V *)dst = *(const V *)(src0 + (v * rows_c + u) * OW);
+                dst += g.N;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // col2im as a gather: one thread per dx element (b, c, h, w) sums the dcol
 // entries that im2col copied from (b, c, h, w).  Tap u contributes when
 // h + p - u >= 0, divisible by s and (h + p - u)/s < OH, i.e. u runs over one
@@ -946,6 +1015,14 @@ inline dim3 grid2(long long x, long long y)
 
 }  // namespace
 
+// experiments, tests: D4R_IM2COL_SHIFT=0 keeps stride-1 layers on the
+// general LDS kernel
+static bool im2col_shift_enabled()
+{
+    const char *e = getenv("D4R_IM2COL_SHIFT");
+    return !(e && e[0] == '0');
+}
+
 hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s)
 {
     const int VW = dt == DT_F32 ? 4 : 8;
@@ -991,6 +1068,29 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
         const long long win_elems = (long long)BB * Rl * Wl;
         const size_t shm = (size_t)(es == 4 ? lds_padded_elems<uint32_t>(win_elems)
                                             : lds_padded_elems<uint16_t>(win_elems)) * es;
+        // stride 1 with whole vectors per output row: the shifted-copy kernel
+        // (its LDS holds kW copies of the window's OW-wide part)
+        if (g.s == 1 && g.OW % VW == 0 && g.OW <= 1024 && g.C <= 65535 && im2col_shift_enabled()) {
+            int rb = RB, bb = BB;
+            auto rl = [&](int r) { return r - 1 + g.kH; };
+            auto elems = [&](int r, int b) { return (long long)g.kW * b * rl(r) * g.OW; };
+            while (bb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
+                bb = (bb + 1) / 2;
+            while (rb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
+                rb = (rb + 1) / 2;
+            if (elems(rb, bb) * es <= 48 * 1024 && (long long)bb * rl(rb) <= 1024 && elems(rb, bb) < (1 << 20) &&
+                (g.B + bb - 1) / bb <= 65535) {
+                dim3 grid((g.OH + rb - 1) / rb, g.C, (g.B + bb - 1) / bb);
+                const size_t shm2 = (size_t)elems(rb, bb) * es;
+                if (dt == DT_F32)
+                    hipLaunchKernelGGL(im2col_shift_kernel<uint32_t>, grid, dim3(NT), shm2, s, (const uint32_t *)x,
+                                       (uint32_t *)col, g, rb, bb, rl(rb));
+                else
+                    hipLaunchKernelGGL(im2col_shift_kernel<uint16_t>, grid, dim3(NT), shm2, s, (const uint16_t *)x,
+                                       (uint16_t *)col, g, rb, bb, rl(rb));
+                return hipGetLastError();
+            }
+        }
         if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535 && Rl <= 1024) {
             dim3 grid((g.OH + RB - 1) / RB, g.C, (g.B + BB - 1) / BB);
             const int vec = (g.N % VW) == 0;
