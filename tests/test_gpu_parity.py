@@ -106,6 +106,21 @@ def test_im2col_bit_exact(sh, dt):
         assert np.array_equal(bits16(col).astype(np.int64), ref.astype(np.int64))
 
 
+# Stride-1 maps whose output width is a multiple of 8 take the shifted-copy
+# im2col (8x8 with 256 channels: several images per block); the general
+# LDS kernel must give the same bits with it switched off.
+SHIFT_SHAPES = [(64, 256, 8, 8, 16, 3, 3, 1, 1), (3, 5, 6, 16, 4, 5, 5, 1, 2), (2, 4, 9, 24, 3, 1, 1, 1, 0),
+                (4, 7, 10, 8, 2, 3, 3, 1, 1)]
+
+
+@pytest.mark.parametrize("t", SHIFT_SHAPES, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shift", ["1", "0"])
+def test_im2col_shifted_copies_bit_exact(t, dt, shift, monkeypatch):
+    monkeypatch.setenv("D4R_IM2COL_SHIFT", shift)
+    test_im2col_bit_exact(_shape(t), dt)
+
+
 @pytest.mark.parametrize("sh", [_shape(t) for t in TINY] +
                          [l.shape.with_batch(min(l.shape.batch, 2)) for w in wl.WORKLOADS.values()
                           for l in w.layers], ids=str)
