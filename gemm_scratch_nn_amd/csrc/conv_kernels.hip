@@ -927,20 +927,36 @@ __global__ __launch_bounds__(NT) void splitk_reduce_vec_kernel(const float *__re
     // one row m for all four; the NCHW position decoded once and stepped
     const int m = (int)(i0 / N);
     const int n0 = (int)(i0 - (long long)m * N);
+    // one 16-byte store when the four outputs are contiguous and aligned
+    // (row-major rows; NCHW when they stay in one image), else four
+    float out[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        out[e] = epi_value(acc[e], bias, relu, epi, m, n0 + e);
     if (epi == EPI_NCHW) {
         int b = n0 / P, pix = n0 - b * P;
+        float *dst = C + ((long long)b * M + m) * P + pix;
+        if (pix + 4 <= P && ((uintptr_t)dst & 15) == 0) {
+            *(float4 *)dst = make_float4(out[0], out[1], out[2], out[3]);
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            C[((long long)b * M + m) * P + pix] = epi_value(acc[e], bias, relu, epi, m, n0 + e);
+            C[((long long)b * M + m) * P + pix] = out[e];
             if (++pix == P) {
                 pix = 0;
                 ++b;
             }
         }
     } else {
+        float *dst = C + (long long)m * ldc + n0;
+        if (((uintptr_t)dst & 15) == 0) {
+            *(float4 *)dst = make_float4(out[0], out[1], out[2], out[3]);
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            C[(long long)m * ldc + n0 + e] = epi_value(acc[e], bias, relu, epi, m, n0 + e);
+            dst[e] = out[e];
     }
 }
 
