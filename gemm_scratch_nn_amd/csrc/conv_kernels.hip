@@ -1045,15 +1045,17 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
     const int es = dt == DT_F32 ? 4 : 2;
     // LDS-staged path: a block covers up to ~128K col elements (whole images
     // of one channel when an image is small, else a range of output rows),
-    // halved until the grid has 2048 blocks, and its input window must fit
-    // in 48 KB; otherwise the direct gather below.  (Measured against 16K
-    // and 1024 blocks: C4 bf16 im2col 25.3 -> 22.1 us, others level.)
+    // halved until the grid has 2048 blocks (16-bit) or 512 (f32), and its
+    // input window must fit in 48 KB; otherwise the direct gather below.
+    // (16-bit, against 16K and 1024 blocks: AlexNet conv3-5 bf16 im2col
+    // 25.3 -> 22.1 us.  f32 with 512 instead of 2048: LeNet conv2 11.2 ->
+    // 6.4 us, AlexNet conv1 46.7 -> 43.8 us, conv3-5 32.3 -> 30.0 us.)
     {
         const int khw = g.kH * g.kW;
         const int Wl = (g.OW - 1) * g.s + g.kW;
         const long long per_img = (long long)khw * g.OH * g.OW;
         long long target = 131072;
-        long long min_blocks = 2048;
+        long long min_blocks = dt == DT_F32 ? 512 : 2048;
         if (const char *e = getenv("D4R_IM2COL_TARGET"))  // experiments
             target = atoll(e);
         if (const char *e = getenv("D4R_IM2COL_MINBLK"))  // experiments
