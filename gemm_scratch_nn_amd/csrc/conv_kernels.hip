@@ -1060,6 +1060,11 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
             target = atoll(e);
         if (const char *e = getenv("D4R_IM2COL_MINBLK"))  // experiments
             min_blocks = atoll(e);
+        // f32 row-range blocks at half the size: their windows then fit four
+        // blocks per CU in LDS (AlexNet conv1: 10 -> 9 output rows of 11x11
+        // stride-4 taps, 42.7 -> 39 KB; im2col 44.0 -> 38.7 us)
+        if (dt == DT_F32 && per_img >= target)
+            target /= 2;
         int RB = g.OH, BB = 1;
         if (per_img >= target) {
             RB = (int)(target / ((long long)khw * g.OW));
