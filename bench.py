@@ -75,6 +75,9 @@ def parse_args():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (counter "
                          "calibration for rocprofv3 --pmc runs; untimed)")
+    ap.add_argument("--gemm", default=None, metavar="M,K,N,FLAGS",
+                    help="time one standalone d4r_gemm of this shape and transpose flags instead of "
+                         "a convolution workload (seeded N(0,1) operands in --dtype)")
     return ap.parse_args()
 
 
@@ -282,6 +285,70 @@ def bench_lenet(args) -> int:
     return 0
 
 
+def bench_gemm(args) -> int:
+    """One standalone d4r_gemm (C = op(A) op(B)) of the --gemm shape, timed like a step."""
+    import numpy as np
+    import torch
+
+    import gemm_scratch_nn_amd as d4r
+    import workloads as W
+
+    M, K, N, flags = (int(v) for v in args.gemm.split(","))
+    dtype = args.dtype or "bf16"
+    code = {"f32": d4r.D4R_F32, "f16": d4r.D4R_F16, "bf16": d4r.D4R_BF16}[dtype]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    dev = torch.device("cuda:0")
+
+    def operand(shape, tid):
+        op = W.quantize(W.draw(("normal", 1.0), shape, (77, 0, tid)), dtype)
+        if dtype == "f32":
+            return torch.from_numpy(op.stored).to(dev)
+        return torch.from_numpy(op.stored.view(np.int16)).to(dev).view(tdt)
+
+    A = operand((K, M) if flags & 1 else (M, K), W.TID_A)
+    B = operand((N, K) if flags & 2 else (K, N), W.TID_BM)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    wsb = d4r.d4r_gemm_workspace_size(M, K, N, flags, code)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        d4r.d4r_gemm(M, K, N, flags, code, A, B, C, ws, wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    d4r.d4r_profile_reset()
+    d4r.d4r_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    d4r.d4r_profile_enable(False)
+    by_kernel, kernels = kernel_table(d4r.d4r_profile_read(), MFMA_PEAK[dtype])
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
+    ms = elapsed * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "standalone GEMM TFLOP/s and % of MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded N(0,1) operands)",
+        "config": {"workload": f"GEMM M={M} K={K} N={N} flags={flags}", "M": M, "K": K, "N": N,
+                   "flags": flags},
+        "pct_mfma_peak": value / MFMA_PEAK[dtype],
+        "roofline": roofline_of(by_kernel, dom, MFMA_PEAK[dtype]),
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -289,6 +356,8 @@ def main() -> int:
               "multi-GPU batch sharding is a design note only", file=sys.stderr)
         return 2
 
+    if args.gemm:
+        return bench_gemm(args)
     if args.workload in ("lenet", "alexnet"):
         return bench_lenet(args)
 

@@ -39,18 +39,26 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 
-def _hip_runtimes() -> set:
-    try:
-        with open("/proc/self/maps") as f:
-            return {ln.split()[-1] for ln in f if "libamdhip64" in ln}
-    except OSError:
-        return set()
+def hip_runtimes(maps_text: str) -> set:
+    """Paths of the libamdhip64 files mapped, from /proc/<pid>/maps text."""
+    return {ln.split()[-1] for ln in maps_text.splitlines() if "libamdhip64" in ln}
 
 
-if len(_hip_runtimes()) > 1:
-    raise ImportError("two HIP runtimes are mapped into this process "
-                      f"({sorted(_hip_runtimes())}); import torch before anything "
-                      "that loads /opt/rocm's libamdhip64")
+def check_single_hip_runtime(maps_text: str) -> None:
+    """ImportError when the maps show two HIP runtimes (every launch would fail)."""
+    found = hip_runtimes(maps_text)
+    if len(found) > 1:
+        raise ImportError("two HIP runtimes are mapped into this process "
+                          f"({sorted(found)}); import torch before anything "
+                          "that loads /opt/rocm's libamdhip64")
+
+
+try:
+    with open("/proc/self/maps") as _maps:
+        _maps_text = _maps.read()
+except OSError:
+    _maps_text = ""
+check_single_hip_runtime(_maps_text)
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -72,6 +80,7 @@ _c = {
     "d4r_conv_destroy": _sig("d4r_conv_destroy", [_vp]),
     "d4r_conv_output_dims": _sig("d4r_conv_output_dims", [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "d4r_conv_workspace_size": _sig("d4r_conv_workspace_size", [_vp, ctypes.POINTER(_sz)]),
+    "d4r_conv_describe": _sig("d4r_conv_describe", [_vp, ctypes.c_char_p, _sz, ctypes.POINTER(_sz)]),
     "d4r_conv_forward": _sig("d4r_conv_forward", [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_conv_forward_implicit": _sig("d4r_conv_forward_implicit",
                                       [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -203,6 +212,15 @@ def d4r_conv_workspace_size(h) -> int:
     n = _sz()
     _check("d4r_conv_workspace_size", _c["d4r_conv_workspace_size"](h, ctypes.byref(n)))
     return n.value
+
+
+def d4r_conv_describe(h) -> dict:
+    """The handle's launch plan as a dict of the key=value pairs the C call returns."""
+    need = _sz()
+    _check("d4r_conv_describe", _c["d4r_conv_describe"](h, None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value)
+    _check("d4r_conv_describe", _c["d4r_conv_describe"](h, buf, need.value, ctypes.byref(need)))
+    return dict(kv.split("=", 1) for kv in buf.value.decode().split())
 
 
 def d4r_conv_forward(h, x, w, bias, y, ws, ws_bytes=None, stream=None) -> None:

@@ -716,6 +716,49 @@ d4r_status d4r_conv_workspace_size(d4r_conv_t h, size_t *bytes)
 
 namespace {
 
+std::string plan_text(const GemmPlan &pl)
+{
+    const TileShape ts = tile_shape(pl.cfg);
+    return std::to_string(ts.bm) + "x" + std::to_string(ts.bn) + "/s" + std::to_string(pl.splits);
+}
+
+}  // namespace
+
+d4r_status d4r_conv_describe(d4r_conv_t h, char *buf, size_t cap, size_t *needed)
+{
+    if (!h)
+        return fail(D4R_ERR_INVALID_ARG, "handle is NULL");
+    const ConvGeom &g = h->g;
+    static const char *const im2col_kinds[] = {"gather", "lds", "shift"};
+    static const char *const col2im_kinds[] = {"gather", "lds"};
+    const Im2colPlan ip = plan_im2col(h->dt, g);
+    const Col2imPlan cp = plan_col2im(g);
+    std::string s = std::string("dtype=") + dt_name(h->dt) + " im2col=" + im2col_kinds[ip.kind] +
+                    " im2col_rb=" + std::to_string(ip.RB) + " im2col_bb=" + std::to_string(ip.BB) +
+                    " col2im=" + col2im_kinds[cp.kind] + " col2im_bb=" + std::to_string(cp.BB) +
+                    " fwd=" + plan_text(h->fwd) + " dgrad_explicit=" + plan_text(h->bwd_data) +
+                    " wgrad=" + plan_text(h->bwd_filter) +
+                    " dgrad_implicit=" + (h->pointwise ? "pointwise" : h->dgrad_nhwc ? "nhwc" :
+                                          h->dgrad_impl ? "gathered" : "explicit");
+    if (h->dgrad_nhwc)
+        s += " dgrad_nhwc=" + plan_text(h->bwd_data_nhwc);
+    else if (h->dgrad_impl)
+        s += " dgrad_gathered=" + plan_text(h->bwd_data_impl);
+    s += std::string(" dy_dgrad=") + (h->dgrad == GP_INPLACE ? "inplace" : "copy") +
+         " dy_wgrad=" + (h->wgrad == GP_INPLACE ? "inplace" : "copy") + " dgrad_wt=" + (h->dgrad_wt ? "1" : "0") +
+         " fused_backward=" + (h->fused_bwd ? "1" : "0") + " workspace=" + std::to_string(h->ws_bytes);
+    if (needed)
+        *needed = s.size() + 1;
+    if (buf) {
+        if (cap < s.size() + 1)
+            return fail(D4R_ERR_INVALID_ARG, "buffer holds %zu bytes, the description needs %zu", cap, s.size() + 1);
+        memcpy(buf, s.c_str(), s.size() + 1);
+    }
+    return ok();
+}
+
+namespace {
+
 d4r_status check_tensor(const void *p, const char *name)
 {
     if (!p)

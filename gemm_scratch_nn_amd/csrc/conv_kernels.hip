@@ -1039,92 +1039,102 @@ static bool im2col_shift_enabled()
     return !(e && e[0] == '0');
 }
 
-hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s)
+// Which im2col kernel a launch runs and its block shape.  LDS-staged path:
+// a block covers up to ~128K col elements (whole images of one channel when
+// an image is small, else a range of output rows), halved until the grid
+// has 2048 blocks (16-bit) or 512 (f32), and its input window must fit in
+// 48 KB; otherwise the direct gather.  (16-bit, against 16K and 1024
+// blocks: AlexNet conv3-5 bf16 im2col 25.3 -> 22.1 us.  f32 with 512
+// instead of 2048: LeNet conv2 11.2 -> 6.4 us, AlexNet conv1 46.7 -> 43.8
+// us, conv3-5 32.3 -> 30.0 us.)
+Im2colPlan plan_im2col(int dt, const ConvGeom &g)
 {
     const int VW = dt == DT_F32 ? 4 : 8;
     const int es = dt == DT_F32 ? 4 : 2;
-    // LDS-staged path: a block covers up to ~128K col elements (whole images
-    // of one channel when an image is small, else a range of output rows),
-    // halved until the grid has 2048 blocks (16-bit) or 512 (f32), and its
-    // input window must fit in 48 KB; otherwise the direct gather below.
-    // (16-bit, against 16K and 1024 blocks: AlexNet conv3-5 bf16 im2col
-    // 25.3 -> 22.1 us.  f32 with 512 instead of 2048: LeNet conv2 11.2 ->
-    // 6.4 us, AlexNet conv1 46.7 -> 43.8 us, conv3-5 32.3 -> 30.0 us.)
-    {
-        const int khw = g.kH * g.kW;
-        const int Wl = (g.OW - 1) * g.s + g.kW;
-        const long long per_img = (long long)khw * g.OH * g.OW;
-        long long target = 131072;
-        long long min_blocks = dt == DT_F32 ? 512 : 2048;
-        if (const char *e = getenv("D4R_IM2COL_TARGET"))  // experiments
-            target = atoll(e);
-        if (const char *e = getenv("D4R_IM2COL_MINBLK"))  // experiments
-            min_blocks = atoll(e);
-        // f32 row-range blocks at half the size: their windows then fit four
-        // blocks per CU in LDS (AlexNet conv1: 10 -> 9 output rows of 11x11
-        // stride-4 taps, 42.7 -> 39 KB; im2col 44.0 -> 38.7 us)
-        if (dt == DT_F32 && per_img >= target)
-            target /= 2;
-        int RB = g.OH, BB = 1;
-        if (per_img >= target) {
-            RB = (int)(target / ((long long)khw * g.OW));
-            RB = RB < 1 ? 1 : (RB > g.OH ? g.OH : RB);
-        } else {
-            BB = (int)(target / per_img);
-            BB = BB < 1 ? 1 : (BB > g.B ? g.B : BB);
-        }
-        // enough blocks to fill the chip: split images, then output rows
-        auto blocks = [&](int rb, int bb) {
-            return (long long)((g.OH + rb - 1) / rb) * g.C * ((g.B + bb - 1) / bb);
-        };
-        while (BB > 1 && blocks(RB, BB) < min_blocks)
-            BB = (BB + 1) / 2;
-        while (RB > 1 && blocks(RB, BB) < min_blocks)
-            RB = (RB + 1) / 2;
-        int Rl = (RB - 1) * g.s + g.kH;
-        while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
-            BB = (BB + 1) / 2;
-        while (RB > 1 && (long long)Rl * Wl * es > 48 * 1024) {
-            RB = (RB + 1) / 2;
-            Rl = (RB - 1) * g.s + g.kH;
-        }
-        const long long win_elems = (long long)BB * Rl * Wl;
-        const size_t shm = (size_t)(es == 4 ? lds_padded_elems<uint32_t>(win_elems)
-                                            : lds_padded_elems<uint16_t>(win_elems)) * es;
-        // stride 1 with whole vectors per output row: the shifted-copy kernel
-        // (its LDS holds kW copies of the window's OW-wide part)
-        if (g.s == 1 && g.OW % VW == 0 && g.OW <= 1024 && g.C <= 65535 && im2col_shift_enabled()) {
-            int rb = RB, bb = BB;
-            auto rl = [&](int r) { return r - 1 + g.kH; };
-            auto elems = [&](int r, int b) { return (long long)g.kW * b * rl(r) * g.OW; };
-            while (bb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
-                bb = (bb + 1) / 2;
-            while (rb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
-                rb = (rb + 1) / 2;
-            if (elems(rb, bb) * es <= 48 * 1024 && (long long)bb * rl(rb) <= 1024 && elems(rb, bb) < (1 << 20) &&
-                (g.B + bb - 1) / bb <= 65535) {
-                dim3 grid((g.OH + rb - 1) / rb, g.C, (g.B + bb - 1) / bb);
-                const size_t shm2 = (size_t)elems(rb, bb) * es;
-                if (dt == DT_F32)
-                    hipLaunchKernelGGL(im2col_shift_kernel<uint32_t>, grid, dim3(NT), shm2, s, (const uint32_t *)x,
-                                       (uint32_t *)col, g, rb, bb, rl(rb));
-                else
-                    hipLaunchKernelGGL(im2col_shift_kernel<uint16_t>, grid, dim3(NT), shm2, s, (const uint16_t *)x,
-                                       (uint16_t *)col, g, rb, bb, rl(rb));
-                return hipGetLastError();
-            }
-        }
-        if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535 && Rl <= 1024) {
-            dim3 grid((g.OH + RB - 1) / RB, g.C, (g.B + BB - 1) / BB);
-            const int vec = (g.N % VW) == 0;
-            if (dt == DT_F32)
-                hipLaunchKernelGGL(im2col_lds_kernel<uint32_t>, grid, dim3(NT), shm, s, (const uint32_t *)x,
-                                   (uint32_t *)col, g, RB, BB, Rl, Wl, vec);
-            else
-                hipLaunchKernelGGL(im2col_lds_kernel<uint16_t>, grid, dim3(NT), shm, s, (const uint16_t *)x,
-                                   (uint16_t *)col, g, RB, BB, Rl, Wl, vec);
-            return hipGetLastError();
-        }
+    Im2colPlan pl{IM2COL_GATHER, g.OH, 1, 0, 0, 0};
+    const int khw = g.kH * g.kW;
+    const int Wl = (g.OW - 1) * g.s + g.kW;
+    const long long per_img = (long long)khw * g.OH * g.OW;
+    long long target = 131072;
+    long long min_blocks = dt == DT_F32 ? 512 : 2048;
+    if (const char *e = getenv("D4R_IM2COL_TARGET"))  // experiments
+        target = atoll(e);
+    if (const char *e = getenv("D4R_IM2COL_MINBLK"))  // experiments
+        min_blocks = atoll(e);
+    // f32 row-range blocks at half the size: their windows then fit four
+    // blocks per CU in LDS (AlexNet conv1: 10 -> 9 output rows of 11x11
+    // stride-4 taps, 42.7 -> 39 KB; im2col 44.0 -> 38.7 us)
+    if (dt == DT_F32 && per_img >= target)
+        target /= 2;
+    int RB = g.OH, BB = 1;
+    if (per_img >= target) {
+        RB = (int)(target / ((long long)khw * g.OW));
+        RB = RB < 1 ? 1 : (RB > g.OH ? g.OH : RB);
+    } else {
+        BB = (int)(target / per_img);
+        BB = BB < 1 ? 1 : (BB > g.B ? g.B : BB);
+    }
+    // enough blocks to fill the chip: split images, then output rows
+    auto blocks = [&](int rb, int bb) {
+        return (long long)((g.OH + rb - 1) / rb) * g.C * ((g.B + bb - 1) / bb);
+    };
+    while (BB > 1 && blocks(RB, BB) < min_blocks)
+        BB = (BB + 1) / 2;
+    while (RB > 1 && blocks(RB, BB) < min_blocks)
+        RB = (RB + 1) / 2;
+    int Rl = (RB - 1) * g.s + g.kH;
+    while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
+        BB = (BB + 1) / 2;
+    while (RB > 1 && (long long)Rl * Wl * es > 48 * 1024) {
+        RB = (RB + 1) / 2;
+        Rl = (RB - 1) * g.s + g.kH;
+    }
+    const long long win_elems = (long long)BB * Rl * Wl;
+    const size_t shm = (size_t)(es == 4 ? lds_padded_elems<uint32_t>(win_elems)
+                                        : lds_padded_elems<uint16_t>(win_elems)) * es;
+    // stride 1 with whole vectors per output row: the shifted-copy kernel
+    // (its LDS holds kW copies of the window's OW-wide part)
+    if (g.s == 1 && g.OW % VW == 0 && g.OW <= 1024 && g.C <= 65535 && im2col_shift_enabled()) {
+        int rb = RB, bb = BB;
+        auto rl = [&](int r) { return r - 1 + g.kH; };
+        auto elems = [&](int r, int b) { return (long long)g.kW * b * rl(r) * g.OW; };
+        while (bb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
+            bb = (bb + 1) / 2;
+        while (rb > 1 && (elems(rb, bb) * es > 48 * 1024 || (long long)bb * rl(rb) > 1024))
+            rb = (rb + 1) / 2;
+        if (elems(rb, bb) * es <= 48 * 1024 && (long long)bb * rl(rb) <= 1024 && elems(rb, bb) < (1 << 20) &&
+            (g.B + bb - 1) / bb <= 65535)
+            return Im2colPlan{IM2COL_SHIFT, rb, bb, rl(rb), g.OW, (size_t)elems(rb, bb) * es};
+    }
+    if (shm <= 50 * 1024 && g.C <= 65535 && (g.B + BB - 1) / BB <= 65535 && Rl <= 1024)
+        return Im2colPlan{IM2COL_LDS, RB, BB, Rl, Wl, shm};
+    return pl;
+}
+
+hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s)
+{
+    const int VW = dt == DT_F32 ? 4 : 8;
+    const Im2colPlan pl = plan_im2col(dt, g);
+    if (pl.kind == IM2COL_SHIFT) {
+        dim3 grid((g.OH + pl.RB - 1) / pl.RB, g.C, (g.B + pl.BB - 1) / pl.BB);
+        if (dt == DT_F32)
+            hipLaunchKernelGGL(im2col_shift_kernel<uint32_t>, grid, dim3(NT), pl.shm, s, (const uint32_t *)x,
+                               (uint32_t *)col, g, pl.RB, pl.BB, pl.Rl);
+        else
+            hipLaunchKernelGGL(im2col_shift_kernel<uint16_t>, grid, dim3(NT), pl.shm, s, (const uint16_t *)x,
+                               (uint16_t *)col, g, pl.RB, pl.BB, pl.Rl);
+        return hipGetLastError();
+    }
+    if (pl.kind == IM2COL_LDS) {
+        dim3 grid((g.OH + pl.RB - 1) / pl.RB, g.C, (g.B + pl.BB - 1) / pl.BB);
+        const int vec = (g.N % VW) == 0;
+        if (dt == DT_F32)
+            hipLaunchKernelGGL(im2col_lds_kernel<uint32_t>, grid, dim3(NT), pl.shm, s, (const uint32_t *)x,
+                               (uint32_t *)col, g, pl.RB, pl.BB, pl.Rl, pl.Wl, vec);
+        else
+            hipLaunchKernelGGL(im2col_lds_kernel<uint16_t>, grid, dim3(NT), pl.shm, s, (const uint16_t *)x,
+                               (uint16_t *)col, g, pl.RB, pl.BB, pl.Rl, pl.Wl, vec);
+        return hipGetLastError();
     }
     const long long threads = (g.N + VW - 1) / VW;
     dim3 grid = grid2((threads + NT - 1) / NT, (long long)g.C * g.kH);
@@ -1138,36 +1148,42 @@ hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hi
     return hipGetLastError();
 }
 
+// LDS path of col2im: whole padded image windows of one channel fit in 48
+// KB and a block's columns fit in QMAX vectors per thread; BB images per
+// block, halved until the grid has 1024 blocks, and at least 256 blocks;
+// otherwise the element-parallel gather.
+Col2imPlan plan_col2im(const ConvGeom &g)
+{
+    const int Rl = (g.OH - 1) * g.s + g.kH;
+    const int Wl = (g.OW - 1) * g.s + g.kW;
+    const long long win = (long long)Rl * Wl * 4;
+    const long long max_cols = (long long)C2I_QMAX * NT * 4 - 4;
+    if (win <= 48 * 1024 && g.P <= max_cols && g.C <= 65535) {
+        long long BB = (48 * 1024) / win;
+        const long long by_cols = max_cols / g.P;
+        if (BB > by_cols)
+            BB = by_cols;
+        if (BB > g.B)
+            BB = g.B;
+        if (BB < 1)
+            BB = 1;
+        while (BB > 1 && (long long)g.C * ((g.B + BB - 1) / BB) < 1024)
+            BB = (BB + 1) / 2;
+        if ((long long)g.C * ((g.B + BB - 1) / BB) >= 256 && (g.B + BB - 1) / BB <= 65535)
+            return Col2imPlan{COL2IM_LDS, (int)BB, Rl, Wl,
+                              (size_t)lds_padded_elems<float>(BB * (long long)Rl * Wl) * 4};
+    }
+    return Col2imPlan{COL2IM_GATHER, 1, 0, 0, 0};
+}
+
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s)
 {
-    // LDS path: whole padded image windows of one channel fit in 48 KB and a
-    // block's columns fit in QMAX vectors per thread.
-    {
-        const int Rl = (g.OH - 1) * g.s + g.kH;
-        const int Wl = (g.OW - 1) * g.s + g.kW;
-        const long long win = (long long)Rl * Wl * 4;
-        const long long max_cols = (long long)C2I_QMAX * NT * 4 - 4;
-        if (win <= 48 * 1024 && g.P <= max_cols && g.C <= 65535) {
-            long long BB = (48 * 1024) / win;
-            const long long by_cols = max_cols / g.P;
-            if (BB > by_cols)
-                BB = by_cols;
-            if (BB > g.B)
-                BB = g.B;
-            if (BB < 1)
-                BB = 1;
-            // enough blocks to fill the chip, else the element-parallel gather
-            while (BB > 1 && (long long)g.C * ((g.B + BB - 1) / BB) < 1024)
-                BB = (BB + 1) / 2;
-            if ((long long)g.C * ((g.B + BB - 1) / BB) >= 256 && (g.B + BB - 1) / BB <= 65535) {
-                dim3 grid(1, g.C, (unsigned)((g.B + BB - 1) / BB));
-                const int vec = (g.N % 4) == 0;
-                const size_t shm = (size_t)lds_padded_elems<float>(BB * (long long)Rl * Wl) * 4;
-                hipLaunchKernelGGL(col2im_lds_kernel, grid, dim3(NT), shm, s, dcol, dx, g, (int)BB, Rl, Wl,
-                                   vec);
-                return hipGetLastError();
-            }
-        }
+    const Col2imPlan pl = plan_col2im(g);
+    if (pl.kind == COL2IM_LDS) {
+        dim3 grid(1, g.C, (unsigned)((g.B + pl.BB - 1) / pl.BB));
+        const int vec = (g.N % 4) == 0;
+        hipLaunchKernelGGL(col2im_lds_kernel, grid, dim3(NT), pl.shm, s, dcol, dx, g, pl.BB, pl.Rl, pl.Wl, vec);
+        return hipGetLastError();
     }
     const int total = g.B * g.C * g.H * g.W;
     const int threads = (total + 3) / 4;  // four dx elements per thread

@@ -167,6 +167,22 @@ int gemm_bk(int dt);  // K depth of one LDS stage, in elements
 
 
 
+// The kernel an im2col / col2im launch runs and its block shape (host only;
+// launch_im2col / launch_col2im follow exactly this plan).  RB output rows
+// and BB images of one channel per block; Rl x Wl window; shm LDS bytes.
+enum Im2colKind : int { IM2COL_GATHER = 0, IM2COL_LDS = 1, IM2COL_SHIFT = 2 };
+struct Im2colPlan {
+    int kind, RB, BB, Rl, Wl;
+    size_t shm;
+};
+Im2colPlan plan_im2col(int dt, const ConvGeom &g);
+enum Col2imKind : int { COL2IM_GATHER = 0, COL2IM_LDS = 1 };
+struct Col2imPlan {
+    int kind, BB, Rl, Wl;
+    size_t shm;
+};
+Col2imPlan plan_col2im(const ConvGeom &g);
+
 hipError_t launch_im2col(int dt, const ConvGeom &g, const void *x, void *col, hipStream_t s);
 hipError_t launch_col2im(const ConvGeom &g, const float *dcol, float *dx, hipStream_t s);
 // G[o][n] = dy[b][o][pix], n = b*P + pix  (O x N row-major); with bias_part

@@ -122,6 +122,20 @@ d4r_status d4r_conv_output_dims(d4r_conv_t h, int *outH, int *outW);
 d4r_status d4r_conv_workspace_size(d4r_conv_t h, size_t *bytes);
 
 /*
+ * The launch plan of a handle, as text: space-separated key=value pairs
+ * naming the kernel each step runs and its shape (im2col / col2im kernel
+ * and images per block, GEMM tile and split-K count of every pass, how the
+ * gradient GEMMs take dy, the workspace size).  Host only, no HIP call;
+ * the plan reflects the D4R_* experiment switches set at the time of the
+ * call, as a launch made then would.  *needed (if not NULL) receives the
+ * length including the terminating NUL; buf may be NULL to query it.
+ * Errors: D4R_ERR_INVALID_ARG for a NULL handle or when buf is not NULL and
+ * cap is below *needed (nothing is written then).  (Not a step of the
+ * pages' method: it lets tests confirm which kernel configuration ran.)
+ */
+d4r_status d4r_conv_describe(d4r_conv_t h, char *buf, size_t cap, size_t *needed);
+
+/*
  * 1x1 convolutions.  When kH = kW = 1, stride = 1 and padding = 0, col is x
  * itself with the batch folded into its columns, so three calls read x and
  * dy in place instead of going through col (the mlvc.cpp design page runs

@@ -22,7 +22,8 @@ def test_every_declared_symbol_is_exported():
                 "d4r_profile_reset", "d4r_profile_read", "d4r_relu_forward", "d4r_relu_backward",
                 "d4r_maxpool_forward", "d4r_maxpool_backward", "d4r_add_bias_rows",
                 "d4r_bias_grad_rows", "d4r_softmax", "d4r_softmax_ce_grad", "d4r_sgd_update",
-                "d4r_grad_accum", "d4r_conv_forward_ex", "d4r_gemm_bias_act", "d4r_conv_backward"}
+                "d4r_grad_accum", "d4r_conv_forward_ex", "d4r_gemm_bias_act", "d4r_conv_backward",
+                "d4r_conv_describe"}
     assert expected <= set(names)
     for n in names:
         assert d4r.exported(n), n
@@ -358,3 +359,60 @@ def test_packed_filter_size_and_argument_errors(handle):
         with pytest.raises(D4RError) as e:
             d4r.d4r_conv_backward_data_packed(handle, *args, stream=0)
         assert e.value.status == code, args
+
+
+def test_describe_reports_the_plan(monkeypatch):
+    # AlexNet conv4 at batch 64: the multi-image im2col and col2im windows
+    h = d4r.d4r_conv_create(64, 384, 13, 13, 3, 3, 1, 1, 384, D4R_F32)
+    try:
+        d = d4r.d4r_conv_describe(h)
+        assert d["dtype"] == "f32" and d["im2col"] == "lds" and int(d["im2col_bb"]) > 1
+        assert d["col2im"] == "lds" and int(d["col2im_bb"]) > 1
+        assert d["dgrad_implicit"] == "nhwc" and d["fused_backward"] == "1"
+        assert int(d["workspace"]) == d4r.d4r_conv_workspace_size(h)
+        # the switches are read when the plan is made, as a launch would
+        monkeypatch.setenv("D4R_IM2COL_MINBLK", "100000000")
+        assert d4r.d4r_conv_describe(h)["im2col_bb"] == "1"
+    finally:
+        d4r.d4r_conv_destroy(h)
+    # the same layer at batch 2: one image per block
+    h = d4r.d4r_conv_create(2, 384, 13, 13, 3, 3, 1, 1, 384, D4R_BF16)
+    try:
+        d = d4r.d4r_conv_describe(h)
+        assert d["dtype"] == "bf16" and d["im2col_bb"] == "1" and d["col2im_bb"] == "1"
+    finally:
+        d4r.d4r_conv_destroy(h)
+    # AlexNet conv1: a 227x227 window is too large for the LDS col2im
+    h = d4r.d4r_conv_create(32, 3, 224, 224, 11, 11, 4, 2, 96, D4R_F32)
+    try:
+        d = d4r.d4r_conv_describe(h)
+        assert d["col2im"] == "gather" and d["dgrad_implicit"] == "explicit"
+    finally:
+        d4r.d4r_conv_destroy(h)
+
+
+def test_describe_argument_errors():
+    import ctypes
+    with pytest.raises(D4RError) as e:
+        d4r.d4r_conv_describe(None)
+    assert e.value.status == INVALID
+    h = d4r.d4r_conv_create(1, 1, 5, 5, 3, 3, 1, 0, 1, D4R_F32)
+    try:
+        need = ctypes.c_size_t()
+        buf = ctypes.create_string_buffer(4)
+        st = d4r._c["d4r_conv_describe"](h, buf, 4, ctypes.byref(need))
+        assert st == INVALID and need.value > 4 and buf.raw == b"\0" * 4
+    finally:
+        d4r.d4r_conv_destroy(h)
+
+
+def test_two_hip_runtimes_are_refused():
+    one = ("7f00-7f01 r-xp 0 08:01 1 /usr/lib/python3/site-packages/torch/lib/libamdhip64.so.7\n"
+           "7f02-7f03 r--p 0 08:01 1 /usr/lib/python3/site-packages/torch/lib/libamdhip64.so.7\n"
+           "7f04-7f05 r-xp 0 08:01 2 /usr/lib/libc.so.6\n")
+    d4r.check_single_hip_runtime(one)
+    d4r.check_single_hip_runtime("")
+    two = one + "7f06-7f07 r-xp 0 08:01 3 /opt/rocm/lib/libamdhip64.so.7\n"
+    assert len(d4r.hip_runtimes(two)) == 2
+    with pytest.raises(ImportError):
+        d4r.check_single_hip_runtime(two)

@@ -30,6 +30,9 @@ SHAPES = [
     ((2, 32, 8, 8, 3, 3, 1, 1, 40), set()),                      # O not a whole GEMM stage
     ((1, 128, 1, 1, 3, 3, 1, 1, 64), {"f32", "f16", "bf16"}),    # one output pixel (P = 1)
     ((3, 128, 2, 5, 3, 3, 1, 1, 128), {"f32", "f16", "bf16"}),   # P = 10: one partial pixel tile per image
+    # padding above kH - 1: the NHWC data gradient with a negative flipped padding
+    ((2, 32, 6, 6, 2, 2, 1, 3, 64), {"f16", "bf16"}),
+    ((1, 64, 5, 5, 3, 3, 1, 3, 128), {"f16", "bf16"}),
 ]
 
 

@@ -203,6 +203,30 @@ def _run_conv(sh, dt, ops):
     return pl, y, dx, dw, db
 
 
+def elementwise_bound(got, ref, aref, n_terms, what):
+    """Per-element forward-error bound of float32 summation: every output is
+    a sum of at most n_terms products (exact for 16-bit operands, one
+    rounding each for float32), so |got - exact| <= gamma * sum |terms| with
+    gamma = 2 (n_terms + 2) 2^-24 (a factor 2 over the textbook n u for
+    accumulators that do not round to nearest).  aref is the oracle on the
+    absolute values of the operands, i.e. sum |terms| per element.  A wrong
+    or dropped block of terms leaves errors of order |y| >> gamma sum |terms|."""
+    got = np.asarray(got, dtype=np.float64)
+    bound = 2.0 * (n_terms + 2) * 2.0 ** -24 * np.asarray(aref, dtype=np.float64) + 1e-30
+    viol = np.abs(got - ref) > bound
+    assert not viol.any(), (what, int(viol.sum()), float(np.max(np.abs(got - ref) / bound)))
+
+
+def _abs_refs(sh, X, Wt, G, bias):
+    """The oracle on |x|, |W|, |g|, |bias|: sum of |terms| of every output."""
+    s, p = sh.stride, sh.padding
+    ax, aw, ag = np.abs(X), np.abs(Wt), np.abs(G)
+    return (oracle.conv_forward(ax, aw, np.abs(bias), s, p),
+            oracle.conv_backward_data(ag, aw, X.shape, s, p),
+            oracle.conv_backward_filter(ax, ag, Wt.shape, s, p),
+            oracle.conv_backward_bias(ag))
+
+
 def _check_whole(sh, dt, ops, tag):
     _say("conv", tag, sh, dt)
     pl, y, dx, dw, db = _run_conv(sh, dt, ops)
@@ -216,6 +240,11 @@ def _check_whole(sh, dt, ops, tag):
     _say("  rel errors", errs)
     for k, e in errs.items():
         assert e < TOL[dt], (tag, k, e)
+    ay, adx, adw, adb = _abs_refs(sh, ops["x"].exact, ops["w"].exact, ops["g"].exact, ops["bias"].exact)
+    elementwise_bound(host(y), ry, ay, sh.Kc + 1, (tag, "y"))
+    elementwise_bound(host(dx), rdx, adx, sh.outC * sh.kH * sh.kW + 1, (tag, "dx"))
+    elementwise_bound(host(dw), rdw, adw, sh.N, (tag, "dw"))
+    elementwise_bound(host(db), rdb, adb, sh.N, (tag, "db"))
     return y, dx, dw, db
 
 
@@ -292,6 +321,13 @@ def test_conv_full_size_sampled(key, li, dt):
     _say("  sampled rel errors", errs)
     for k, e in errs.items():
         assert e < TOL[dt], (k, e)
+    ax, aw, ag = np.abs(X), np.abs(Wt), np.abs(G)
+    elementwise_bound(gy, ry, oracle.conv_forward(ax[bs], aw[os_], np.abs(bias[os_]), s, p), sh.Kc + 1, "y")
+    elementwise_bound(gdx, rdx, oracle.conv_backward_data(ag[bs], aw[:, cs], (len(bs), len(cs), sh.inH, sh.inW),
+                                                          s, p), sh.outC * sh.kH * sh.kW + 1, "dx")
+    elementwise_bound(gdw, rdw, oracle.conv_backward_filter(ax[:, cs], ag[:, os_], (len(os_), len(cs), sh.kH, sh.kW),
+                                                            s, p), sh.N, "dw")
+    elementwise_bound(host(db), rdb, oracle.conv_backward_bias(ag), sh.N, "db")
     # independent of the oracle: <y - bias, g> = <x, dx> = <W, dW>
     ysb = host(y) - bias[None, :, None, None]
     lhs = float(np.vdot(ysb, G))
@@ -550,6 +586,10 @@ DGRAD_TINY = TINY + [
     (1, 2, 6, 6, 3, 2, 2, 1, 3),
     (2, 4, 9, 11, 5, 5, 5, 1, 2),
     (3, 5, 7, 7, 6, 1, 1, 1, 0),
+    # dy channels a multiple of the GEMM stage and padding above kH - 1: the
+    # NHWC path with a negative flipped padding (kH - 1 - p < 0)
+    (2, 32, 6, 6, 64, 2, 2, 1, 3),
+    (1, 64, 5, 5, 128, 3, 3, 1, 3),
 ]
 
 
