@@ -100,6 +100,8 @@ _c = {
     "d4r_conv_bias_grad": _sig("d4r_conv_bias_grad", [_vp, _vp, _vp, _vp, _sz, _vp]),
     "d4r_gemm_workspace_size": _sig("d4r_gemm_workspace_size", [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "d4r_gemm": _sig("d4r_gemm", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "d4r_gemm_noalloc": _sig("d4r_gemm_noalloc", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "d4r_gemm_noalloc_scratch_bytes": _sig("d4r_gemm_noalloc_scratch_bytes", [], _sz),
     "d4r_gemm_bias_act": _sig("d4r_gemm_bias_act", [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "d4r_relu_forward": _sig("d4r_relu_forward", [_vp, _vp, _ll, _vp]),
     "d4r_relu_backward": _sig("d4r_relu_backward", [_vp, _vp, _vp, _ll, _vp]),
@@ -313,6 +315,15 @@ def d4r_gemm(M, K, N, flags, dtype, A, B, C, ws=None, ws_bytes=None, stream=None
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check("d4r_gemm", _c["d4r_gemm"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(C), _ptr(ws), nb,
                                       _stream(stream)))
+
+
+def d4r_gemm_noalloc(M, K, N, flags, dtype, A, B, C, stream=None) -> None:
+    _check("d4r_gemm_noalloc", _c["d4r_gemm_noalloc"](M, K, N, flags, dtype, _ptr(A), _ptr(B), _ptr(C),
+                                                      _stream(stream)))
+
+
+def d4r_gemm_noalloc_scratch_bytes() -> int:
+    return int(_c["d4r_gemm_noalloc_scratch_bytes"]())
 
 
 def d4r_gemm_bias_act(M, K, N, flags, dtype, A, B, bias, relu, C, ws=None, ws_bytes=None,

@@ -1236,6 +1236,84 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
     return gemm_call("gemm", M, K, N, flags, dtype, A, B, nullptr, 0, C, ws, ws_bytes, hip_stream);
 }
 
+// ---------------------------------------------------------------------------
+// d4r_gemm without a workspace argument: the split-K partial sums go to a
+// file-scope device array the library owns, so the call allocates nothing.
+// Each device holds its own copy of the array (from when the library's code
+// object is loaded on it until the process ends); host code only ever uses
+// the device address hipGetSymbolAddress returns for the current device,
+// never the array's name, which on the host is a stand-in symbol.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch array's address on the current device, looked up once per
+// device (with that device current) and cached.
+d4r_status scratch_on_current_device(void **out)
+{
+    int devc = -1;
+    hipError_t e = hipGetDevice(&devc);
+    if (e != hipSuccess)
+        return fail(D4R_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (devc < 0 || devc >= kMaxDevices)
+        return fail(D4R_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", devc,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[devc]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(D4R_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", devc,
+                        hipGetErrorString(e));
+        g_scratch_ptr[devc] = p;
+    }
+    *out = g_scratch_ptr[devc];
+    return D4R_OK;
+}
+
+}  // namespace
+
+size_t d4r_gemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+d4r_status d4r_gemm_noalloc(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
+                            float *C, void *hip_stream)
+{
+    D4R_TRY(check_gemm_args(M, K, N, flags, dtype));
+    D4R_TRY(check_tensor(A, "A"));
+    D4R_TRY(check_tensor(B, "B"));
+    D4R_TRY(check_tensor(C, "C"));
+    // the same plan as d4r_gemm, so the result is the same bit for bit
+    const GemmPlan pl = plan_gemm(M, N, K, dtype);
+    const size_t need = plan_partial_bytes(pl, M, N);
+    if (need > kScratchBytes)
+        return fail(D4R_ERR_UNSUPPORTED,
+                    "this GEMM needs %zu bytes of split-K scratch; d4r_gemm_noalloc holds %zu (use d4r_gemm "
+                    "with a workspace)",
+                    need, kScratchBytes);
+    void *ws = nullptr;
+    if (need)
+        D4R_TRY(scratch_on_current_device(&ws));
+    const int amode = (flags & 1) ? OP_ROWS : OP_KC;
+    const int bmode = (flags & 2) ? OP_KC : OP_ROWS;
+    const int lda = amode == OP_KC ? K : M;
+    const int ldb = bmode == OP_KC ? K : N;
+    D4R_LAUNCH(run_gemm(dtype, pl, amode, bmode, A, lda, B, ldb, M, N, K, EPI_ROWMAJOR, C, N, nullptr, 0,
+                        (float *)ws, (hipStream_t)hip_stream, "gemm_noalloc"),
+               "GEMM");
+    return ok();
+}
+
 d4r_status d4r_gemm_bias_act(int M, int K, int N, int flags, d4r_dtype dtype, const void *A, const void *B,
                              const float *bias, int relu, float *C, void *ws, size_t ws_bytes,
                              void *hip_stream)

@@ -320,6 +320,27 @@ d4r_status d4r_gemm(int M, int K, int N, int flags, d4r_dtype dtype, const void 
                     void *hip_stream);
 
 /*
+ * d4r_gemm for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same product,
+ * plan and kernels as d4r_gemm, so C equals d4r_gemm's bit for bit, but
+ * the split-K partial sums go to a device array the library owns
+ * (d4r_gemm_noalloc_scratch_bytes() = 64 MiB per GPU, held from when the
+ * library is loaded on that GPU until the process ends) instead of a
+ * workspace argument.  No hipMalloc, hipFree or allocating library call is
+ * made; the array's address on the current device is looked up on the
+ * first call there.  Every call on one GPU shares that GPU's array, so
+ * calls that may overlap on one GPU (different streams, or host threads)
+ * race and give wrong results: serialise them.  The array keeps the last
+ * call's partial sums; each call overwrites what it reads.
+ * Errors: those of d4r_gemm; D4R_ERR_UNSUPPORTED when the plan needs more
+ * split-K scratch than the array holds (d4r_gemm_workspace_size() bytes >
+ * d4r_gemm_noalloc_scratch_bytes(): call d4r_gemm with a workspace).
+ */
+d4r_status d4r_gemm_noalloc(int M, int K, int N, int flags, d4r_dtype dtype, const void *A,
+                            const void *B, float *C, void *hip_stream);
+size_t d4r_gemm_noalloc_scratch_bytes(void);
+
+/*
  * A linear layer's forward in one call: C = op(A) * op(B) + bias, then
  * ReLU when relu != 0 (the directcompute-nn page's fully connected layer is
  * matmul then add_bias, x * W^T being flags 2, "Matmul Shaders" and
