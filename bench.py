@@ -51,9 +51,11 @@ def parse_args():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", default=None, help="write per-kernel detail JSON here")
-    ap.add_argument("--forward", choices=("explicit", "implicit"), default="explicit",
+    ap.add_argument("--forward", choices=("auto", "explicit", "implicit"), default="auto",
                     help="explicit: im2col + GEMM (col saved for the filter gradient); "
-                         "implicit: implicit-GEMM forward, im2col redone in the filter gradient")
+                         "implicit: implicit-GEMM forward, im2col redone in the filter gradient; "
+                         "auto: implicit for the 16-bit layers whose forward reads x as NHWC on the "
+                         "direct-to-LDS kernel, explicit elsewhere")
     ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="implicit",
                     help="implicit: implicit-GEMM data gradient, no dcol (stride-1 square-kernel "
                          "layers; others run explicit); explicit: the page's GEMM to dcol + col2im")
@@ -395,6 +397,10 @@ def main() -> int:
             t["dx"] = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
             t["dw"] = torch.empty(sh.w_shape(), dtype=torch.float32, device=dev)
             t["db"] = torch.empty((sh.outC,), dtype=torch.float32, device=dev)
+            if args.forward == "auto":
+                t["implicit"] = dtype != "f32" and d4r.d4r_conv_describe(pl.h)["fwd_implicit"] == "nhwc"
+            else:
+                t["implicit"] = args.forward == "implicit"
             out.append((layer, pl, t))
         return out
 
@@ -413,17 +419,18 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    implicit = args.forward == "implicit"
     dgrad_fn = (d4r.d4r_conv_backward_data_implicit if args.dgrad == "implicit"
                 else d4r.d4r_conv_backward_data)
 
     def forward(layer, pl, t, stream):
-        if implicit:
+        if t["implicit"]:
             d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
         else:
             d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, stream)
 
     def wgrad(layer, pl, t, stream):
+        # the implicit forward leaves no col: the filter gradient redoes im2col
+        implicit = t["implicit"]
         d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
                                      0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
 
@@ -442,6 +449,7 @@ def main() -> int:
             for layer, pl, t in layers:
                 forward(layer, pl, t, stream)
                 if combined:
+                    implicit = t["implicit"]
                     d4r.d4r_conv_backward(pl.h, t["x"] if implicit else None, t["w"], t["g"], t["dx"],
                                           t["dw"], t["db"], 0 if implicit else 1, pl.ws, pl.ws_bytes,
                                           stream)
@@ -545,7 +553,9 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": f"{wl.title}: {desc}", "batch": wl.layers[0].shape.batch,
-                   "dtype": dtype, "forward": args.forward, "dgrad": args.dgrad,
+                   "dtype": dtype, "forward": args.forward,
+                   "implicit_forward_layers": [l.name for l, _, t in layers if t["implicit"]],
+                   "dgrad": args.dgrad,
                    "backward": "combined" if combined and args.streams == 1 else "separate",
                    "streams": args.streams,
                    "rotate": args.rotate, "hip_graph": bool(args.graph),

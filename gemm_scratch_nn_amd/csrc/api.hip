@@ -65,21 +65,36 @@ struct GemmPlan {
     int k_per_split;
 };
 
-// Tile and split-K choice.  The chip has 256 compute units; a tile config
-// keeps wg_per_cu workgroups resident per CU (from its LDS and register
-// use), so a launch runs in ceil(workgroups / slots) waves.  Splitting K
-// into s slices multiplies the workgroups by s and divides each one's work
-// by s, at the price of writing and re-reading s partial M x N slabs.  The
-// split count minimises a small cost model of those two terms.
-constexpr int kComputeUnits = 256;
+// Tile and split-K choice.  A tile config keeps wg_per_cu workgroups
+// resident per compute unit (from its LDS and register use), so a launch
+// runs in ceil(workgroups / slots) waves.  Splitting K into s slices
+// multiplies the workgroups by s and divides each one's work by s, at the
+// price of writing and re-reading s partial M x N slabs.  The split count
+// minimises a small cost model of those two terms.
+//
+// Compute units of the current device (256 on MI355X), read once per
+// process; 256 when no device answers (the host-only tests).
+int compute_units()
+{
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            return n;
+        (void)hipGetLastError();
+        return 256;
+    }();
+    return cus;
+}
 
 // Workgroups resident per CU for each tile config (LDS and register use of
-// the compiled kernels), f32 and 16-bit builds respectively.
-int wg_per_cu(int cfg, int dt)
+// the compiled kernels), f32 and 16-bit builds; dl: the 16-bit product runs
+// on the direct-to-LDS kernel (whose 128x128 form sets its own count).
+int wg_per_cu(int cfg, int dt, bool dl)
 {
     const bool h = dt != DT_F32;
     switch (cfg) {
-    case TILE_128x128: return 2;
+    case TILE_128x128: return h && dl && dl128_enabled() ? dl128_form().wg_per_cu : 2;
     case TILE_64x64: return h ? 3 : 4;
     case TILE_32x128: return 3;
     case TILE_96x128: return 2;
@@ -100,7 +115,7 @@ int tile_from_env(int dt)
     if (!e)
         return -1;
     for (int c = 0; c < TILE_COUNT; ++c) {
-        if (dt == DT_F32 && (c == TILE_128x256 || c == TILE_256x128))
+        if (dt == DT_F32 && (c == TILE_128x256 || c == TILE_256x128 || c == TILE_256x256))
             continue;
         if (dt != DT_F32 && c == TILE_128x64)
             continue;
@@ -116,11 +131,16 @@ int tile_from_env(int dt)
 // dl16: only the tiles of the 16-bit direct-to-LDS kernel (OP_IMPL_T).
 GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = false)
 {
-    TileCand cands[6];
+    TileCand cands[8];
     int nc = 0;
+    // 256x256 (direct-to-LDS only, one workgroup per CU): a third less
+    // operand traffic per flop than 128x256; measured 1.25x its rate on
+    // square products (4096^3 bf16 977 against 780 TFLOP/s)
+    const double e256 = 1.25;
     if (dl16) {
         cands[nc++] = {TILE_128x256, 1.0};
         cands[nc++] = {TILE_256x128, 1.0};
+        cands[nc++] = {TILE_256x256, e256};
         // a shade below the larger direct tiles: preferred only where it
         // saves whole waves (the 129-tile data gradients of conv4/conv5)
         if (dl128_enabled())
@@ -138,7 +158,7 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = f
             // slower per flop, more than the model's wave rounding shows
             cands[nc++] = {TILE_128x128, 1.0};
             const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
-            if (t128 < (long long)kComputeUnits * wg_per_cu(TILE_128x128, dt))
+            if (t128 < (long long)compute_units() * wg_per_cu(TILE_128x128, dt, false))
                 cands[nc++] = {TILE_128x64, 0.92};
         }
     } else {
@@ -147,11 +167,13 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = f
         cands[nc++] = {TILE_128x128, kk16 && dl128_enabled() ? 0.95 : 0.85};
         cands[nc++] = {TILE_128x256, 1.0};
         cands[nc++] = {TILE_256x128, 1.0};
+        if (kk16)
+            cands[nc++] = {TILE_256x256, e256};
         // small products (a 1x1 layer on the 46x80 map): when the large
         // tiles leave most CUs idle, 64x64 tiles at three per CU hide the
         // load latency better than split-K (measured 12 against 22 us)
         const long long tbig = (long long)((M + 127) / 128) * ((N + 255) / 256);
-        if (tbig < kComputeUnits)
+        if (tbig < compute_units())
             cands[nc++] = {TILE_64x64, 0.5};
         if (M % 128 != 0 && M % 96 == 0 && M <= 192)
             cands[nc++] = {TILE_96x128, 0.8};
@@ -171,7 +193,7 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = f
     for (int ci = 0; ci < nc; ++ci) {
         const TileShape ts = tile_shape(cands[ci].cfg);
         const long long tiles = (long long)((M + ts.bm - 1) / ts.bm) * ((N + ts.bn - 1) / ts.bn);
-        const long long slots = (long long)kComputeUnits * wg_per_cu(cands[ci].cfg, dt);
+        const long long slots = (long long)compute_units() * wg_per_cu(cands[ci].cfg, dt, dl16 || kk16);
         // seconds per K stage of one workgroup when every slot is busy
         const double t_stage = 2.0 * ts.bm * ts.bn * bk / (peak * cands[ci].eff / (double)slots);
         long long smax = ktiles < 256 ? ktiles : 256;
@@ -196,6 +218,10 @@ GemmPlan plan_gemm(int M, int N, int K, int dt, bool dl16 = false, bool kk16 = f
     }
     return pl;
 }
+
+// d4r_gemm with both operands k-contiguous (flags 2), 16-bit, whole 64-deep
+// stages and 16-byte aligned rows: the direct-to-LDS kernel applies
+bool gemm_kk16(int K, int flags, int dt) { return dt != DT_F32 && flags == 2 && K % 64 == 0; }
 
 size_t plan_partial_bytes(const GemmPlan &pl, int M, int N)
 {
@@ -409,6 +435,12 @@ struct d4r_conv {
     // d4r_conv_backward prepares dy for both gradient GEMMs in one pass
     // (NHWC data gradient and a copied G for the filter gradient)
     bool fused_bwd;
+    // implicit forward from x read as NHWC (stride 1, whole GEMM stages of
+    // input channels): x transposed to xt[b][h][w][c], the filter reordered
+    // to wr[o][u][v][c]; the direct-to-LDS loader of the NHWC data gradient
+    bool fwd_nhwc;
+    GemmPlan fwd_nhwc_plan;
+    size_t off_xt, off_wr;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -627,6 +659,13 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     h->pointwise = kH == 1 && kW == 1 && stride == 1 && padding == 0;
     if (const char *e = getenv("D4R_POINTWISE"))  // experiments, tests: 0 = im2col path
         h->pointwise = h->pointwise && e[0] != '0';
+    // the forward's NHWC form: the same loader conditions on x (inC channels)
+    h->fwd_nhwc = stride == 1 && !h->pointwise && inC % gemm_bk(dtype) == 0 &&
+                  (long long)g.Kc / gemm_bk(dtype) < (1 << 20) && inC / gemm_bk(dtype) <= 1024 && kW <= 1024;
+    if (const char *e = getenv("D4R_FWD_NHWC"))  // experiments, tests: 0 = gathered implicit forward
+        h->fwd_nhwc = h->fwd_nhwc && e[0] != '0';
+    if (h->fwd_nhwc)
+        h->fwd_nhwc_plan = plan_gemm(g.O, g.N, g.Kc, dtype, dtype != D4R_F32);
     h->bias_splits = bias_grad_splits(g);
     // bias partials: the bias kernel's splits, or the fused reshape's blocks
     const int bias_part_cols = std::max(h->bias_splits, grad_reshape_blocks(dtype, g));
@@ -663,8 +702,15 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     if (h->dgrad_impl)
         off += align_up((size_t)w_el * h->es);
     h->off_zero = off;
-    if (h->dgrad_nhwc)
+    if (h->dgrad_nhwc || h->fwd_nhwc)
         off += align_up(256);
+    h->off_xt = off;
+    h->off_wr = off;
+    if (h->fwd_nhwc) {
+        off += align_up((size_t)x_el * h->es);
+        h->off_wr = off;
+        off += align_up((size_t)w_el * h->es);
+    }
     h->off_bias = off;
     off += align_up((size_t)outC * std::max(bias_part_cols, h->fused_bwd ? dy_prep_bias_parts(g) : 0) *
                     sizeof(float));
@@ -685,6 +731,11 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         size_t dn = plan_partial_bytes(h->bwd_data_nhwc, h->gd.O, h->gd.N);
         if (dn > big)
             big = dn;
+    }
+    if (h->fwd_nhwc) {
+        size_t fn = plan_partial_bytes(h->fwd_nhwc_plan, g.O, g.N);
+        if (fn > big)
+            big = fn;
     }
     h->ws_bytes = off + align_up(big);
     *out = h;
@@ -738,8 +789,11 @@ d4r_status d4r_conv_describe(d4r_conv_t h, char *buf, size_t cap, size_t *needed
                     " col2im=" + col2im_kinds[cp.kind] + " col2im_bb=" + std::to_string(cp.BB) +
                     " fwd=" + plan_text(h->fwd) + " dgrad_explicit=" + plan_text(h->bwd_data) +
                     " wgrad=" + plan_text(h->bwd_filter) +
+                    " fwd_implicit=" + (h->pointwise ? "pointwise" : h->fwd_nhwc ? "nhwc" : "gathered") +
                     " dgrad_implicit=" + (h->pointwise ? "pointwise" : h->dgrad_nhwc ? "nhwc" :
                                           h->dgrad_impl ? "gathered" : "explicit");
+    if (h->fwd_nhwc)
+        s += " fwd_nhwc=" + plan_text(h->fwd_nhwc_plan);
     if (h->dgrad_nhwc)
         s += " dgrad_nhwc=" + plan_text(h->bwd_data_nhwc);
     else if (h->dgrad_impl)
@@ -833,6 +887,24 @@ d4r_status conv_forward(d4r_conv_t h, const void *x, const void *w, const float 
         D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_ROWS, w, g.Kc, col, g.N, g.O, g.N, g.Kc, EPI_NCHW, y,
                             0, bias, g.P, partial, s, "fwd", nullptr, 0, 0, nullptr, relu),
                    "forward GEMM");
+    } else if (h->fwd_nhwc) {
+        // y = Wr(O x kH*kW*C) * im2col(x as NHWC): one launch transposes x to
+        // xt[b][pix][c] and reorders the filter to wr[o][u][v][c] (clearing
+        // the zero page the loader reads for padding)
+        char *wsb = (char *)ws;
+        void *xt = wsb + h->off_xt, *wr = wsb + h->off_wr, *zero = wsb + h->off_zero;
+        {
+            ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":fwd_x_w", 0.0,
+                         2.0 * h->es * ((double)g.B * g.C * g.H * g.W + (double)g.O * g.Kc));
+            const TransposeJob jx{x, xt, g.C, g.H * g.W, g.B, 0, (uint32_t *)zero, 0};
+            const TransposeJob jw{w, wr, g.C, g.kH * g.kW, g.O, 0, nullptr, 0};
+            hipError_t e = launch_transpose_pair(h->dt, jx, jw, s);
+            ps.done();
+            D4R_LAUNCH(e, "input transpose and filter reorder");
+        }
+        D4R_LAUNCH(run_gemm(h->dt, h->fwd_nhwc_plan, OP_KC, OP_IMPL_T, wr, g.Kc, xt, 0, g.O, g.N, g.Kc, EPI_NCHW,
+                            y, 0, bias, g.P, partial, s, "fwd", &g, 0, 0, zero, relu),
+                   "implicit forward GEMM (NHWC)");
     } else if (h->pointwise) {
         // 1x1: y[b] = Wmat * x[b] with x read in place (C channels)
         D4R_LAUNCH(run_gemm(h->dt, h->fwd, OP_KC, OP_NCHW, w, g.Kc, x, 0, g.O, g.N, g.Kc, EPI_NCHW, y, 0,
@@ -1191,7 +1263,7 @@ d4r_status d4r_gemm_workspace_size(int M, int K, int N, int flags, d4r_dtype dty
     D4R_TRY(check_gemm_args(M, K, N, flags, dtype));
     if (!bytes)
         return fail(D4R_ERR_INVALID_ARG, "bytes is NULL");
-    GemmPlan pl = plan_gemm(M, N, K, dtype);
+    GemmPlan pl = plan_gemm(M, N, K, dtype, false, gemm_kk16(K, flags, dtype));
     *bytes = plan_partial_bytes(pl, M, N);
     return ok();
 }
@@ -1206,7 +1278,7 @@ d4r_status gemm_call(const char *what, int M, int K, int N, int flags, d4r_dtype
     D4R_TRY(check_tensor(A, "A"));
     D4R_TRY(check_tensor(B, "B"));
     D4R_TRY(check_tensor(C, "C"));
-    GemmPlan pl = plan_gemm(M, N, K, dtype);
+    GemmPlan pl = plan_gemm(M, N, K, dtype, false, gemm_kk16(K, flags, dtype));
     size_t need = plan_partial_bytes(pl, M, N);
     if (need) {
         if (!ws)
@@ -1294,7 +1366,7 @@ d4r_status d4r_gemm_noalloc(int M, int K, int N, int flags, d4r_dtype dtype, con
     D4R_TRY(check_tensor(B, "B"));
     D4R_TRY(check_tensor(C, "C"));
     // the same plan as d4r_gemm, so the result is the same bit for bit
-    const GemmPlan pl = plan_gemm(M, N, K, dtype);
+    const GemmPlan pl = plan_gemm(M, N, K, dtype, false, gemm_kk16(K, flags, dtype));
     const size_t need = plan_partial_bytes(pl, M, N);
     if (need > kScratchBytes)
         return fail(D4R_ERR_UNSUPPORTED,

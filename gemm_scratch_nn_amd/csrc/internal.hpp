@@ -3,6 +3,7 @@
 #pragma once
 
 #include <stdlib.h>
+#include <string.h>
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -24,7 +25,8 @@ enum TileCfg : int {
     TILE_128x256 = 4,  // 2x4 waves, 2x2 blocks (16-bit operands only)
     TILE_256x128 = 5,  // 4x2 waves, 2x2 blocks (16-bit operands only)
     TILE_128x64 = 6,   // 2x2 waves, 2x1 blocks (f32 operands only)
-    TILE_COUNT = 7
+    TILE_256x256 = 7,  // 2x4 waves, 4x2 blocks (16-bit, direct-to-LDS kernel only)
+    TILE_COUNT = 8
 };
 
 struct TileShape { int bm, bn; };
@@ -37,6 +39,7 @@ inline TileShape tile_shape(int cfg)
     case TILE_96x128: return {96, 128};
     case TILE_128x256: return {128, 256};
     case TILE_128x64: return {128, 64};
+    case TILE_256x256: return {256, 256};
     default: return {256, 128};
     }
 }
@@ -74,6 +77,27 @@ inline bool dl128_enabled()
 {
     const char *e = getenv("D4R_DL128");
     return !(e && e[0] == '0');
+}
+
+// The 16-bit direct-to-LDS 128x128 tile: eight wavefronts of 64x32 with a
+// ring of four 32 KB stages (one workgroup per CU), the default, or the
+// other forms measured against it (D4R_DL128_FORM = w4n2 | w8n2 | w8n3 |
+// w8n4; experiments): four wavefronts of 64x64, rings of two or three.
+// On the AlexNet conv3-5 bf16 step the default plans take 4 split-K
+// reductions instead of 9 (0.543 -> 0.516 ms against w4n2).
+struct Dl128Form {
+    int waves, nbuf, wg_per_cu;
+};
+inline Dl128Form dl128_form()
+{
+    const char *e = getenv("D4R_DL128_FORM");
+    if (e && !strcmp(e, "w4n2"))
+        return {4, 2, 2};
+    if (e && !strcmp(e, "w8n2"))
+        return {8, 2, 2};
+    if (e && !strcmp(e, "w8n3"))
+        return {8, 3, 1};
+    return {8, 4, 1};
 }
 
 // Work item of workgroup `pid` in a GEMM's 1-D grid of tiles x splits.  The

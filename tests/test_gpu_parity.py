@@ -396,8 +396,8 @@ def test_forward_without_bias():
 # ---------------------------------------------------------------------------
 
 TILES = {"f32": ["128x128", "64x64", "32x128", "96x128", "128x64"],
-         "f16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"],
-         "bf16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128"]}
+         "f16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128", "256x256"],
+         "bf16": ["128x128", "64x64", "32x128", "96x128", "128x256", "256x128", "256x256"]}
 
 
 @pytest.mark.parametrize("dt,tile", [(d, t) for d in TILES for t in TILES[d]])
@@ -436,6 +436,45 @@ def test_gemm_direct_and_register_staged(dt, tile, switch, direct, monkeypatch):
         torch.cuda.synchronize()
         err = rel_err(host(C), ref)
         assert err < TOL[dt], (tile, direct, M, K, N, err)
+
+
+# The 16-bit direct-to-LDS 128x128 tile in each of its forms (four
+# wavefronts of 64x64 or eight of 64x32; rings of two to four stages) on the
+# ragged direct-kernel GEMM shapes and on a conv3-5 layer.
+@pytest.mark.parametrize("form", ["w4n2", "w8n2", "w8n3", "w8n4"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_dl128_forms(form, dt, monkeypatch):
+    monkeypatch.setenv("D4R_DL128_FORM", form)
+    monkeypatch.setenv("D4R_GEMM_TILE", "128x128")
+    for (M, K, N) in [(300, 256, 333), (129, 64, 520), (200, 4096, 304), (70, 128, 36)]:
+        rng = np.random.default_rng(M + K + N + 13)
+        a = wl.quantize(rng.normal(size=(M, K)), dt)
+        b = wl.quantize(rng.normal(size=(N, K)), dt)
+        ref = oracle.gemm(a.exact, b.exact, M, K, N, 2)
+        C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
+        torch.cuda.synchronize()
+        err = rel_err(host(C), ref)
+        assert err < TOL[dt], (form, M, K, N, err)
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[1].shape.with_batch(3)
+    _check_whole(sh, dt, wl.conv_inputs(w, 1, dt, batch=3), f"c4/conv4/b3/{form}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_gemm_256x256_square_sampled(dt):
+    # the planner's tile for large square k-contiguous products
+    M = K = N = 2048
+    rng = np.random.default_rng(2048)
+    a = wl.quantize(rng.normal(size=(M, K)), dt)
+    b = wl.quantize(rng.normal(size=(N, K)), dt)
+    C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
+    torch.cuda.synchronize()
+    rows = _sample_idx(M, 24)
+    ref = oracle.gemm(a.exact[rows].copy(), b.exact, len(rows), K, N, 2)
+    got = host(C)[rows]
+    assert rel_err(got, ref) < TOL[dt]
+    elementwise_bound(got, ref, oracle.gemm(np.abs(a.exact[rows]), np.abs(b.exact), len(rows), K, N, 2), K,
+                      "C")
 
 
 @pytest.mark.parametrize("dt,switch", [("f32", "D4R_F32_DL"), ("bf16", "D4R_DL128")])
@@ -550,6 +589,35 @@ def test_implicit_forward_every_tile(dt, tile, monkeypatch):
     _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=11), f"tile {tile}")
     sh = _shape((2, 17, 12, 12, 130, 3, 3, 1, 1))
     _check_implicit(sh, dt, wl.random_conv(sh, dt, seed=12), f"tile {tile}")
+
+
+# implicit forward from x read as NHWC (input channels a multiple of the
+# GEMM stage: 32 f32, 64 16-bit; the 16-bit one on the direct-to-LDS
+# kernel): ragged pixel counts and output channels, padding above kH - 1,
+# non-square kernels, split K; the gathered implicit forward must agree
+FWD_NHWC = [
+    (2, 64, 8, 7, 5, 3, 3, 1, 1),
+    (3, 128, 9, 11, 40, 3, 3, 1, 0),
+    (2, 64, 7, 7, 130, 3, 3, 1, 2),
+    (1, 192, 6, 6, 16, 5, 5, 1, 2),
+    (2, 64, 5, 5, 8, 3, 3, 1, 3),
+    (2, 64, 6, 9, 33, 2, 3, 1, 1),
+    (4, 256, 5, 9, 24, 3, 3, 1, 1),
+    (2, 32, 5, 9, 24, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("t", FWD_NHWC, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_forward_implicit_nhwc(t, dt, monkeypatch):
+    sh = _shape(t)
+    pl = _plan(sh, dt)
+    applies = sh.inC % (32 if dt == "f32" else 64) == 0
+    assert d4r.d4r_conv_describe(pl.h)["fwd_implicit"] == ("nhwc" if applies else "gathered")
+    ops = wl.random_conv(sh, dt, seed=sum(t) + 29)
+    _check_implicit(sh, dt, ops, "nhwc")
+    monkeypatch.setenv("D4R_FWD_NHWC", "0")
+    _check_implicit(sh, dt, ops, "gathered")
 
 
 # ---------------------------------------------------------------------------
