@@ -41,7 +41,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-o", tmp] + objs
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
+           "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

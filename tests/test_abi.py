@@ -416,3 +416,14 @@ def test_two_hip_runtimes_are_refused():
     assert len(d4r.hip_runtimes(two)) == 2
     with pytest.raises(ImportError):
         d4r.check_single_hip_runtime(two)
+
+
+def test_exports_only_the_declared_c_abi():
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", d4r.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] in "TtWw"}
+    assert funcs == set(d4r.declared_functions()), funcs ^ set(d4r.declared_functions())
