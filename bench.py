@@ -77,6 +77,9 @@ def parse_args():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup (counter "
                          "calibration for rocprofv3 --pmc runs; untimed)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="headline only: skip the other GEMM-dominated configurations (AlexNet conv1 "
+                         "fp32, conv3-5 bf16, the 46x80 feature-map convs f16) the default run reports")
     ap.add_argument("--gemm", default=None, metavar="M,K,N,FLAGS",
                     help="time one standalone d4r_gemm of this shape and transpose flags instead of "
                          "a convolution workload (seeded N(0,1) operands in --dtype)")
@@ -162,6 +165,9 @@ def kernel_table(stats, peak_tf):
         if a["flops"] > 0:
             e["TFLOPs"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
             e["frac_mfma"] = e["TFLOPs"] / peak_tf
+            # roofline of the launch class: min(peak, intensity * HBM bandwidth)
+            e["attainable_TFLOPs"] = attainable_tf(a["flops"], a["bytes"], peak_tf)
+            e["frac_attainable"] = e["TFLOPs"] / e["attainable_TFLOPs"]
         else:
             e["GBps"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
             e["frac_hbm"] = e["GBps"] / HBM_PEAK_GBPS
@@ -351,38 +357,42 @@ def bench_gemm(args) -> int:
     return 0
 
 
-def main() -> int:
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
-              "multi-GPU batch sharding is a design note only", file=sys.stderr)
-        return 2
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    if args.gemm:
-        return bench_gemm(args)
-    if args.workload in ("lenet", "alexnet"):
-        return bench_lenet(args)
 
+# The GEMM-dominated configurations reported beside the headline (each
+# convolution layer also separately): AlexNet conv1 (fp32), AlexNet conv3-5
+# (bf16) and the 46x80 feature-map convolutions (f16).
+SECONDARY = (("c3", "f32"), ("c4", "bf16"), ("c5", "f16"))
+
+
+def bench_conv(args, key: str, dtype: str, steps: int, warmup: int, rotate: int, graph_mode: bool,
+               streams: int, with_cpu: bool, per_layer: bool):
+    """Times `steps` steps of one convolution workload; returns (line, stats)."""
+    import numpy as np
     import torch
 
     import gemm_scratch_nn_amd as d4r
     import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
-    dtype = args.dtype or wl.dtypes[0]
+    wl = W.WORKLOADS[key]
     code = {"f32": d4r.D4R_F32, "f16": d4r.D4R_F16, "bf16": d4r.D4R_BF16}[dtype]
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    peak = MFMA_PEAK[dtype]
 
     def to_dev(op):
-        import numpy as np
         if op.dtype == "f32":
             return torch.from_numpy(op.stored).to(dev)
         return torch.from_numpy(op.stored.view(np.int16)).to(dev).view(tdt)
-
-    if args.rotate < 1 or (args.rotate > 1 and args.graph):
-        print("bench.py: --rotate must be >= 1 and cannot be combined with --graph", file=sys.stderr)
-        return 2
 
     def build_layers():
         out = []
@@ -404,10 +414,9 @@ def main() -> int:
             out.append((layer, pl, t))
         return out
 
-    sets = [build_layers() for _ in range(args.rotate)]
+    sets = [build_layers() for _ in range(rotate)]
     layers = sets[0]
     n_step = [0]
-
     stream = torch.cuda.current_stream().cuda_stream
 
     if args.copy_mib > 0:
@@ -434,7 +443,7 @@ def main() -> int:
         d4r.d4r_conv_backward_filter(pl.h, t["x"] if implicit else None, t["g"], t["dw"], t["db"],
                                      0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
 
-    if args.streams == 2:
+    if streams == 2:
         aux = torch.cuda.Stream()  # default priority
         for st in sets:
             for _, pl, t in st:
@@ -442,20 +451,22 @@ def main() -> int:
 
     combined = args.backward == "combined" and args.dgrad == "implicit"
 
-    def step(stream=stream, streams=args.streams):
+    def layer_step(layer, pl, t, stream):
+        forward(layer, pl, t, stream)
+        if combined:
+            implicit = t["implicit"]
+            d4r.d4r_conv_backward(pl.h, t["x"] if implicit else None, t["w"], t["g"], t["dx"], t["dw"],
+                                  t["db"], 0 if implicit else 1, pl.ws, pl.ws_bytes, stream)
+        else:
+            dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
+            wgrad(layer, pl, t, stream)
+
+    def step(stream=stream, streams=streams):
         layers = sets[n_step[0] % len(sets)]
         n_step[0] += 1
         if streams == 1:
             for layer, pl, t in layers:
-                forward(layer, pl, t, stream)
-                if combined:
-                    implicit = t["implicit"]
-                    d4r.d4r_conv_backward(pl.h, t["x"] if implicit else None, t["w"], t["g"], t["dx"],
-                                          t["dw"], t["db"], 0 if implicit else 1, pl.ws, pl.ws_bytes,
-                                          stream)
-                else:
-                    dgrad_fn(pl.h, t["w"], t["g"], t["dx"], pl.ws, pl.ws_bytes, stream)
-                    wgrad(layer, pl, t, stream)
+                layer_step(layer, pl, t, stream)
             return
         # forwards, then per layer (last first, as a backward pass runs) the
         # filter gradient on this stream and the data gradient on the other
@@ -468,16 +479,16 @@ def main() -> int:
             wgrad(layer, pl, t, stream)
         cur.wait_stream(aux)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     graph = None
-    if args.graph:
+    if graph_mode:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step(torch.cuda.current_stream().cuda_stream)
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             graph.replay()
         torch.cuda.synchronize()
 
@@ -485,7 +496,7 @@ def main() -> int:
     # launch adds GPU-side gaps between kernels).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         if graph is None:
             step()
         else:
@@ -496,45 +507,90 @@ def main() -> int:
     # Kernel timing: the same K steps again, eager and on one stream (so no
     # kernel shares the GPU with another), with the library's HIP event pair
     # around every launch on its stream.
-    d4r.d4r_profile_reset()
-    d4r.d4r_profile_enable(True)
-    for _ in range(args.steps):
-        step(streams=1)
-    torch.cuda.synchronize()
-    d4r.d4r_profile_enable(False)
-    stats = d4r.d4r_profile_read()
+    def profiled(fn, reps):
+        d4r.d4r_profile_reset()
+        d4r.d4r_profile_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        d4r.d4r_profile_enable(False)
+        out = d4r.d4r_profile_read()
+        d4r.d4r_profile_reset()
+        return out
 
-    ms_per_step = elapsed * 1e3 / args.steps
+    stats = profiled(lambda: step(streams=1), steps)
+
+    ms_per_step = elapsed * 1e3 / steps
     step_flops = sum(layer_flops(l.shape) for l, _, _ in layers)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     # per kernel symbol (the part before ':' is one template instantiation)
-    by_kernel, kernels = kernel_table(stats, MFMA_PEAK[dtype])
+    by_kernel, kernels = kernel_table(stats, peak)
     dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
     d = by_kernel[dom]
-    roof = roofline_of(by_kernel, dom, MFMA_PEAK[dtype])
-
+    roof = roofline_of(by_kernel, dom, peak)
     tr = recorded_traffic(dom)
     if tr is not None:
         roof["traffic"] = tr[0]
         roof["traffic_source"] = tr[1]
         roof["algorithmic_bytes_per_launch"] = d["bytes"] / d["launches"]
 
-    def stage(prefix):
-        sel = [v for k, v in by_kernel.items() if k.startswith(prefix)]
-        if not sel:
-            return None
-        ms = sum(v["ms"] for v in sel)
-        gbps = sum(v["bytes"] for v in sel) / (ms * 1e-3) / 1e9
-        return {"GBps": gbps, "frac_hbm": gbps / HBM_PEAK_GBPS}
+    def col2im_alone(layer, pl):
+        """col2im timed through d4r_conv_col2im (the page's data gradient runs it;
+        the default implicit data gradient does not)."""
+        sh = layer.shape
+        dcol = torch.zeros((sh.Kc, sh.N), dtype=torch.float32, device=dev)
+        dx = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            d4r.d4r_conv_col2im(pl.h, dcol, dx)
+        st = profiled(lambda: d4r.d4r_conv_col2im(pl.h, dcol, dx), max(5, steps // 2))
+        del dcol, dx
+        return stage_of(kernel_table(st, peak)[0], "col2im")
 
-    gemm_ms = sum(v["ms"] for k, v in by_kernel.items() if k.startswith("gemm"))
-    gemm_tf = sum(v["flops"] for k, v in by_kernel.items() if k.startswith("gemm")) / (gemm_ms * 1e-3) / 1e12
+    col2im_standalone = {}
+    per = []
+    if per_layer:
+        for layer, pl, t in layers:
+            sh = layer.shape
+            for _ in range(2):
+                layer_step(layer, pl, t, stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(steps):
+                layer_step(layer, pl, t, stream)
+            torch.cuda.synchronize()
+            lms = (time.perf_counter() - t1) * 1e3 / steps
+            lst = profiled(lambda: layer_step(layer, pl, t, stream), steps)
+            lbk, _ = kernel_table(lst, peak)
+            ltf = layer_flops(sh) / (lms * 1e-3) / 1e12
+            entry = {"layer": layer.name,
+                     "shape": f"{sh.batch}x{sh.inC}x{sh.inH}x{sh.inW} -> {sh.outC} {sh.kH}x{sh.kW} "
+                              f"s{sh.stride} p{sh.padding}",
+                     "ms": lms, "TFLOPs": ltf, "frac_mfma": ltf / peak,
+                     "forward": "implicit (NHWC)" if t["implicit"] else "explicit (im2col + GEMM)"}
+            entry.update(gemm_summary(lbk, peak))
+            entry["im2col"] = stage_of(lbk, "im2col")
+            c2 = stage_of(lbk, "col2im")
+            if c2 is None:
+                c2 = col2im_alone(layer, pl)
+                if c2 is not None:
+                    c2["timed"] = "standalone d4r_conv_col2im (the step's data gradient has no col2im)"
+            entry["col2im"] = c2
+            per.append(entry)
+    else:
+        c2 = stage_of(by_kernel, "col2im")
+        if c2 is None:
+            parts = [col2im_alone(layer, pl) for layer, pl, _ in layers]
+            parts = [p for p in parts if p]
+            if parts:
+                col2im_standalone = {"GBps": sum(p["GBps"] for p in parts) / len(parts),
+                                     "timed": "standalone d4r_conv_col2im per layer (mean)"}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(wl, dtype, args.cpu_seconds)
         cpu.pop("seconds", None)
+        cpu["cpu_model"] = cpu_model()
 
     desc = "; ".join(f"{l.name} {l.shape.inC}x{l.shape.inH}x{l.shape.inW}->{l.shape.outC} "
                      f"{l.shape.kH}x{l.shape.kW} s{l.shape.stride} p{l.shape.padding}"
@@ -544,8 +600,8 @@ def main() -> int:
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -556,22 +612,89 @@ def main() -> int:
                    "dtype": dtype, "forward": args.forward,
                    "implicit_forward_layers": [l.name for l, _, t in layers if t["implicit"]],
                    "dgrad": args.dgrad,
-                   "backward": "combined" if combined and args.streams == 1 else "separate",
-                   "streams": args.streams,
-                   "rotate": args.rotate, "hip_graph": bool(args.graph),
+                   "backward": "combined" if combined and streams == 1 else "separate",
+                   "streams": streams,
+                   "rotate": rotate, "hip_graph": bool(graph_mode),
                    "step_gflop": step_flops / 1e9},
-        "pct_mfma_peak": value / MFMA_PEAK[dtype],
-        "gemm_TFLOPs": gemm_tf,
-        "gemm_frac_mfma": gemm_tf / MFMA_PEAK[dtype],
-        "im2col": stage("im2col"),
-        "col2im": stage("col2im"),
-        "roofline": roof,
-        "kernel_timing": "HIP event pair per launch, recorded by the library on its launch stream "
-                         "during a second, single-stream pass of the same steps (step time from an "
-                         "event-free pass)",
-        "cpu_baseline": cpu,
-        "kernels": kernels,
+        "pct_mfma_peak": value / peak,
     }
+    line.update(gemm_summary(by_kernel, peak))
+    line["im2col"] = stage_of(by_kernel, "im2col")
+    line["col2im"] = stage_of(by_kernel, "col2im") or (col2im_standalone or None)
+    line["roofline"] = roof
+    if per:
+        line["layers"] = per
+    line["kernel_timing"] = ("HIP event pair per launch, recorded by the library on its launch stream "
+                             "during a second, single-stream pass of the same steps (step time from an "
+                             "event-free pass)")
+    line["cpu_baseline"] = cpu
+    line["kernels"] = kernels
+    return line, stats
+
+
+def stage_of(by_kernel, prefix):
+    sel = [v for k, v in by_kernel.items() if k.startswith(prefix)]
+    if not sel:
+        return None
+    ms = sum(v["ms"] for v in sel)
+    gbps = sum(v["bytes"] for v in sel) / (ms * 1e-3) / 1e9
+    return {"GBps": gbps, "frac_hbm": gbps / HBM_PEAK_GBPS}
+
+
+def gemm_summary(by_kernel, peak):
+    """The GEMMs of a step together: TFLOP/s, fraction of the MFMA peak and of
+    the attainable rate min(peak, I * HBM bandwidth), I = algorithmic flops per
+    algorithmic byte of each launch class (time-weighted)."""
+    g = {k: v for k, v in by_kernel.items() if k.startswith("gemm") and v["flops"] > 0}
+    if not g:
+        return {}
+    ms = sum(v["ms"] for v in g.values())
+    tf = sum(v["flops"] for v in g.values()) / (ms * 1e-3) / 1e12
+    # time at the attainable rate of each class, summed
+    t_att = sum(v["flops"] / (attainable_tf(v["flops"], v["bytes"], peak) * 1e12) for v in g.values())
+    return {"gemm_TFLOPs": tf, "gemm_frac_mfma": tf / peak,
+            "gemm_frac_attainable": (t_att * 1e3) / ms}
+
+
+def attainable_tf(flops, bytes_, peak):
+    if bytes_ <= 0:
+        return peak
+    return min(peak, flops / bytes_ * HBM_PEAK_GBPS / 1e3)
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
+              "multi-GPU batch sharding is a design note only", file=sys.stderr)
+        return 2
+
+    if args.gemm:
+        return bench_gemm(args)
+    if args.workload in ("lenet", "alexnet"):
+        return bench_lenet(args)
+    if args.rotate < 1 or (args.rotate > 1 and args.graph):
+        print("bench.py: --rotate must be >= 1 and cannot be combined with --graph", file=sys.stderr)
+        return 2
+
+    import workloads as W
+    wl = W.WORKLOADS[args.workload]
+    dtype = args.dtype or wl.dtypes[0]
+    line, stats = bench_conv(args, args.workload, dtype, args.steps, args.warmup, args.rotate, args.graph,
+                             args.streams, not args.no_cpu_baseline, per_layer=True)
+    if not args.no_configs and args.workload == "c4" and dtype == "f32":
+        # the other GEMM-dominated configurations, each with its layers
+        sec_steps = max(5, min(args.steps, 20))
+        configs = []
+        for key, dt in SECONDARY:
+            sl, _ = bench_conv(args, key, dt, sec_steps, min(args.warmup, 3), 1, False, 1, False,
+                               per_layer=True)
+            keep = ("value", "unit", "ms_per_step", "dtype", "pct_mfma_peak", "gemm_TFLOPs",
+                    "gemm_frac_mfma", "gemm_frac_attainable", "im2col", "col2im", "layers", "roofline")
+            entry = {"workload": sl["config"]["workload"], "steps": sec_steps}
+            entry.update({k: sl[k] for k in keep if k in sl})
+            configs.append(entry)
+        line["configs"] = configs
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump({"line": line, "stats": stats}, f, indent=1)
