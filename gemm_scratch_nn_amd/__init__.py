@@ -434,6 +434,10 @@ class ConvPlan:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.device = device
 
+    def describe(self) -> dict:
+        """The launch plan of this handle (d4r_conv_describe)."""
+        return d4r_conv_describe(self.h)
+
     def __del__(self):
         h = getattr(self, "h", None)
         if h:

@@ -441,6 +441,10 @@ struct d4r_conv {
     bool fwd_nhwc;
     GemmPlan fwd_nhwc_plan;
     size_t off_xt, off_wr;
+    // data gradient of a strided layer as stride^2 stride-1 sub-convolutions
+    // of dy read as NHWC (one per output phase), in one launch
+    bool dgrad_phased;
+    PhaseArgs phases;
     size_t col_bytes;
     double in_image_col;  // col entries copied from inside the image
 };
@@ -459,6 +463,19 @@ hipError_t launch_gemm(int dt, int cfg, int amode, int bmode, const GemmParams &
     case DT_F32: return launch_gemm_f32(cfg, amode, bmode, p, s);
     case DT_F16: return launch_gemm_f16(cfg, amode, bmode, p, s);
     default: return launch_gemm_bf16(cfg, amode, bmode, p, s);
+    }
+}
+
+hipError_t launch_gemm_phased_f32(const GemmParams &, const PhaseArgs &, hipStream_t);
+hipError_t launch_gemm_phased_f16(const GemmParams &, const PhaseArgs &, hipStream_t);
+hipError_t launch_gemm_phased_bf16(const GemmParams &, const PhaseArgs &, hipStream_t);
+
+hipError_t launch_gemm_phased(int dt, const GemmParams &p, const PhaseArgs &pa, hipStream_t s)
+{
+    switch (dt) {
+    case DT_F32: return launch_gemm_phased_f32(p, pa, s);
+    case DT_F16: return launch_gemm_phased_f16(p, pa, s);
+    default: return launch_gemm_phased_bf16(p, pa, s);
     }
 }
 
@@ -593,6 +610,60 @@ void choose_grad_paths(d4r_conv *h)
 
 }  // namespace
 
+namespace {
+
+// The output phases of a strided layer's data gradient (see PhaseArgs).  The
+// phased form applies when every phase has taps and outputs (stride at most
+// the kernel and the input extents), dy's channels fill whole GEMM stages,
+// the NHWC loader's divisions stay in range, and the GEMM rows (the input
+// channels) fill at least half a 128-row tile: with fewer (AlexNet conv1's
+// 3) the explicit GEMM, whose rows are C*kH*kW, keeps the matrix cores busy.
+bool plan_phases(const ConvGeom &g, int dt, PhaseArgs *pa)
+{
+    memset(pa, 0, sizeof *pa);
+    const int s = g.s, bk = gemm_bk(dt);
+    if (s < 2 || s * s > kMaxPhases || s > g.kH || s > g.kW || g.H < s || g.W < s || g.O % bk != 0 ||
+        g.O / bk > 1024 || g.C < 64)
+        return false;
+    long long a_off = 0;
+    int tiles = 0;
+    for (int rh = 0; rh < s; ++rh)
+        for (int rw = 0; rw < s; ++rw) {
+            // per axis: taps t = ceil((k - r) / s), first output x0 with
+            // (x0 + p) mod s = r, outputs m, offset q0 = (x0 + p - r) / s of
+            // dy's window, padding t - 1 - q0 of the sub-convolution
+            auto axis = [&](int r, int n, int k, int *t, int *x0, int *m, int *pad) {
+                *t = (k - r + s - 1) / s;
+                *x0 = ((r - g.p) % s + s) % s;
+                *m = (n - *x0 + s - 1) / s;
+                *pad = *t - 1 - (*x0 + g.p - r) / s;
+            };
+            int tu, h0, hm, ph, tv, w0, wm, pw;
+            axis(rh, g.H, g.kH, &tu, &h0, &hm, &ph);
+            axis(rw, g.W, g.kW, &tv, &w0, &wm, &pw);
+            if (tu < 1 || tv < 1 || hm < 1 || wm < 1 || tv > 1024)
+                return false;
+            PhaseItem &it = pa->ph[pa->n++];
+            ConvGeom &q = it.g;
+            q.B = g.B; q.C = g.O; q.H = g.OH; q.W = g.OW; q.O = g.C; q.kH = tu; q.kW = tv;
+            q.s = 1; q.p = ph; q.pw = pw; q.OH = hm; q.OW = wm;
+            q.P = hm * wm; q.Kc = g.O * tu * tv; q.N = g.B * q.P;
+            if ((long long)q.Kc / bk >= (1 << 20) || (long long)q.N > 0x7fffffffLL)
+                return false;
+            it.a_off = a_off;
+            it.K = q.Kc;
+            it.tile0 = tiles;
+            it.h0 = h0;
+            it.w0 = w0;
+            a_off += (long long)g.C * q.Kc;
+            tiles += ((g.C + 127) / 128) * ((q.N + 127) / 128);
+        }
+    pa->tiles = tiles;
+    return a_off == (long long)g.O * g.C * g.kH * g.kW;
+}
+
+}  // namespace
+
 d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW, int kH, int kW,
                            int stride, int padding, int outC, d4r_dtype dtype)
 {
@@ -626,7 +697,7 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     ConvGeom &g = h->g;
     g.B = batch; g.C = inC; g.H = inH; g.W = inW; g.O = outC; g.kH = kH; g.kW = kW;
     g.s = stride; g.p = padding; g.OH = (int)OH; g.OW = (int)OW;
-    g.P = (int)P; g.Kc = (int)Kc; g.N = (int)N;
+    g.P = (int)P; g.Kc = (int)Kc; g.N = (int)N; g.pw = padding;
     h->dt = dtype;
     h->es = dt_size(dtype);
     h->fwd = plan_gemm(g.O, g.N, g.Kc, dtype);
@@ -643,7 +714,7 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         ConvGeom &d = h->gd;
         d.B = batch; d.C = outC; d.H = g.OH; d.W = g.OW; d.O = inC; d.kH = kH; d.kW = kW;
         d.s = 1; d.p = kH - 1 - padding; d.OH = inH; d.OW = inW;
-        d.P = inH * inW; d.Kc = outC * kH * kW; d.N = batch * d.P;
+        d.P = inH * inW; d.Kc = outC * kH * kW; d.N = batch * d.P; d.pw = d.p;
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
     // the NHWC form needs whole GEMM stages of dy (32 f32 / 64 16-bit
@@ -656,6 +727,9 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->dgrad_nhwc = h->dgrad_nhwc && e[0] != '0';
     if (h->dgrad_nhwc)
         h->bwd_data_nhwc = plan_gemm(h->gd.O, h->gd.N, h->gd.Kc, dtype, dtype != D4R_F32);
+    h->dgrad_phased = plan_phases(g, dtype, &h->phases);
+    if (const char *e = getenv("D4R_DGRAD_PHASED"))  // experiments, tests: 0 = explicit data gradient
+        h->dgrad_phased = h->dgrad_phased && e[0] != '0';
     h->pointwise = kH == 1 && kW == 1 && stride == 1 && padding == 0;
     if (const char *e = getenv("D4R_POINTWISE"))  // experiments, tests: 0 = im2col path
         h->pointwise = h->pointwise && e[0] != '0';
@@ -693,16 +767,16 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
     if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
         off += align_up((size_t)y_el * h->es);
     h->off_gt = off;
-    if (h->dgrad_nhwc)
+    if (h->dgrad_nhwc || h->dgrad_phased)
         off += align_up((size_t)y_el * h->es);
     h->off_wt = off;
     if (h->dgrad_wt)
         off += align_up((size_t)w_el * h->es);
     h->off_wflip = off;
-    if (h->dgrad_impl)
+    if (h->dgrad_impl || h->dgrad_phased)
         off += align_up((size_t)w_el * h->es);
     h->off_zero = off;
-    if (h->dgrad_nhwc || h->fwd_nhwc)
+    if (h->dgrad_nhwc || h->fwd_nhwc || h->dgrad_phased)
         off += align_up(256);
     h->off_xt = off;
     h->off_wr = off;
@@ -790,8 +864,10 @@ d4r_status d4r_conv_describe(d4r_conv_t h, char *buf, size_t cap, size_t *needed
                     " fwd=" + plan_text(h->fwd) + " dgrad_explicit=" + plan_text(h->bwd_data) +
                     " wgrad=" + plan_text(h->bwd_filter) +
                     " fwd_implicit=" + (h->pointwise ? "pointwise" : h->fwd_nhwc ? "nhwc" : "gathered") +
-                    " dgrad_implicit=" + (h->pointwise ? "pointwise" : h->dgrad_nhwc ? "nhwc" :
-                                          h->dgrad_impl ? "gathered" : "explicit");
+                    " dgrad_implicit=" + (h->dgrad_phased ? "phased" : h->pointwise ? "pointwise" :
+                                          h->dgrad_nhwc ? "nhwc" : h->dgrad_impl ? "gathered" : "explicit");
+    if (h->dgrad_phased)
+        s += " dgrad_phases=" + std::to_string(h->phases.n);
     if (h->fwd_nhwc)
         s += " fwd_nhwc=" + plan_text(h->fwd_nhwc_plan);
     if (h->dgrad_nhwc)
@@ -991,6 +1067,57 @@ d4r_status dgrad_explicit(d4r_conv_t h, const void *w, const void *wt_packed, co
     return ok();
 }
 
+// dx of a strided layer without dcol or col2im: dy transposed to NHWC
+// (zero page cleared in the same launch), the phase filters gathered from
+// W, then one GEMM launch over every output phase, each storing its rows and
+// columns of dx.
+d4r_status dgrad_phased(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws, hipStream_t s)
+{
+    const ConvGeom &g = h->g;
+    char *wsb = (char *)ws;
+    void *gt = wsb + h->off_gt, *wph = wsb + h->off_wflip, *zero = wsb + h->off_zero;
+    {
+        ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":dgrad_dy", 0.0,
+                     2.0 * h->es * (double)g.B * g.O * g.P);
+        const TransposeJob jdy{dy, gt, g.O, g.P, g.B, 0, (uint32_t *)zero, 0};
+        const TransposeJob none{nullptr, nullptr, 0, 0, 0, 0, nullptr, 0};
+        hipError_t e = launch_transpose_pair(h->dt, jdy, none, s);
+        ps.done();
+        D4R_LAUNCH(e, "grad transpose");
+    }
+    {
+        ProfScope ps(s, std::string("phase_filter_") + dt_name(h->dt) + ":dgrad", 0.0,
+                     2.0 * h->es * (double)g.O * g.Kc);
+        hipError_t e = launch_phase_filter(h->dt, g, h->phases, w, wph, s);
+        ps.done();
+        D4R_LAUNCH(e, "phase filters");
+    }
+    GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.A = wph;
+    p.B = gt;
+    p.C = dx;
+    p.M = g.C;
+    p.epi = EPI_PHASE;
+    p.splits = 1;
+    p.a_vec = 1;
+    p.b_vec = 1;
+    p.zero = zero;
+    p.ph_s = g.s;
+    p.ph_H = g.H;
+    p.ph_W = g.W;
+    double flops = 0.0;
+    for (int k = 0; k < h->phases.n; ++k)
+        flops += 2.0 * g.C * (double)h->phases.ph[k].g.N * h->phases.ph[k].K;
+    ProfScope ps(s, std::string("gemm_") + dt_name(h->dt) + "_128x128_kn_phased:dgrad", flops,
+                 (double)h->es * ((double)g.O * g.Kc + (double)g.B * g.O * g.P) +
+                     4.0 * (double)g.B * g.C * g.H * g.W);
+    hipError_t e = launch_gemm_phased(h->dt, p, h->phases, s);
+    ps.done();
+    D4R_LAUNCH(e, "phased data-gradient GEMM");
+    return ok();
+}
+
 }  // namespace
 
 d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy, float *dx, void *ws,
@@ -1050,6 +1177,8 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     D4R_TRY(check_tensor(dx, "dx"));
     D4R_TRY(check_ws(h, ws, ws_bytes));
     hipStream_t s = (hipStream_t)hip_stream;
+    if (h->dgrad_phased)
+        return dgrad_phased(h, w, dy, dx, ws, s);
     if (!h->dgrad_impl || h->pointwise)
         return dgrad_explicit(h, w, nullptr, dy, dx, ws, s);
     const ConvGeom &g = h->g, &d = h->gd;

@@ -1031,6 +1031,54 @@ inline dim3 grid2(long long x, long long y)
 
 }  // namespace
 
+namespace {
+
+// Phase filters of a strided data gradient: for phase k of pa, element
+// e = ((c*Tu + u')*Tv + v')*O + o of its block (at pa.ph[k].a_off) is
+// W[o][c][rh + s*(Tu-1-u')][rw + s*(Tv-1-v')], where the phase's first dx
+// row h0 fixes rh = (h0 + p) mod s (likewise rw).  Every tap of W lands in
+// exactly one phase, so the blocks together hold |W| elements.  One thread
+// per element, writes in order.
+template <typename T>
+__global__ __launch_bounds__(NT) void phase_filter_kernel(const T *__restrict__ w, T *__restrict__ wph,
+                                                          ConvGeom g, PhaseArgs pa, long long total)
+{
+    const long long e = (long long)blockIdx.x * NT + threadIdx.x;
+    if (e >= total)
+        return;
+    int k = 0;
+    while (k + 1 < pa.n && e >= pa.ph[k + 1].a_off)
+        ++k;
+    const PhaseItem &it = pa.ph[k];
+    const int Tu = it.g.kH, Tv = it.g.kW, O = g.O;
+    const int rh = (it.h0 + g.p) % g.s, rw = (it.w0 + g.p) % g.s;
+    long long r = e - it.a_off;
+    const int o = (int)(r % O);
+    r /= O;
+    const int vv = (int)(r % Tv);
+    r /= Tv;
+    const int uu = (int)(r % Tu);
+    const int c = (int)(r / Tu);
+    const int u = rh + g.s * (Tu - 1 - uu), v = rw + g.s * (Tv - 1 - vv);
+    wph[e] = w[(((long long)o * g.C + c) * g.kH + u) * g.kW + v];
+}
+
+}  // namespace
+
+hipError_t launch_phase_filter(int dt, const ConvGeom &g, const PhaseArgs &pa, const void *w, void *wph,
+                               hipStream_t s)
+{
+    const long long total = (long long)g.O * g.C * g.kH * g.kW;
+    const dim3 grid((unsigned)((total + NT - 1) / NT));
+    if (dt == DT_F32)
+        hipLaunchKernelGGL(phase_filter_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)w,
+                           (uint32_t *)wph, g, pa, total);
+    else
+        hipLaunchKernelGGL(phase_filter_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w,
+                           (uint16_t *)wph, g, pa, total);
+    return hipGetLastError();
+}
+
 // experiments, tests: D4R_IM2COL_SHIFT=0 keeps stride-1 layers on the
 // general LDS kernel
 static bool im2col_shift_enabled()

@@ -319,14 +319,21 @@ __device__ __forceinline__ void store_acc(const GemmParams &p, const f32x16_t (&
         const int n = n0 + j * 32 + l32;
         if (n >= p.N)
             continue;
-        long long col_off;
+        long long col_off, row_stride;
         if (p.epi == EPI_NCHW) {
             const int b = n / p.P;
             col_off = (long long)b * p.M * p.P + (n - b * p.P);
+            row_stride = p.P;
+        } else if (p.epi == EPI_PHASE) {
+            const int b = n / p.P, r = n - b * p.P;
+            const int i = r / p.g.OW, jj = r - i * p.g.OW;
+            row_stride = (long long)p.ph_H * p.ph_W;
+            col_off = (long long)b * p.M * row_stride + (long long)(p.ph_h0 + p.ph_s * i) * p.ph_W + p.ph_w0 +
+                      p.ph_s * jj;
         } else {
             col_off = n;
+            row_stride = p.ldc;
         }
-        const long long row_stride = (p.epi == EPI_NCHW) ? p.P : p.ldc;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -563,7 +570,7 @@ struct DlImplNhwc {
             const int bb = n / g.P, r = n - (n / g.P) * g.P;
             const int i = r / g.OW;
             h0[j] = n < g.N ? i - g.p : -(1 << 30);
-            w0[j] = r - i * g.OW - g.p;
+            w0[j] = r - i * g.OW - g.pw;
             base[j] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[j]) * g.C + chk * EPC;
         }
     }
@@ -593,8 +600,10 @@ struct DlImplNhwc {
 // (DTID == DT_F32): floats k = 16q + 8h .. +7 from two chunks and eight
 // v_mfma_f32_32x32x2_f32 (lane half h supplies k = 8h + t of step t for
 // both operands, so every k is summed once).
-template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
-__global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
+// One output tile (m_blk, n_blk) over k in [kbeg, kend) of split `split`.
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI>
+__device__ __forceinline__ void dl_gemm_tile(const GemmParams &p, int m_blk, int n_blk, int kbeg, int kend,
+                                             int split)
 {
     using E = DlElem<DTID>;
     using T = typename E::T;
@@ -609,13 +618,6 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % NWM, wn = wave / NWM;
     const int h = lane >> 5, l32 = lane & 31;
-
-    const int mt = (p.M + BM - 1) / BM;
-    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
-    const int m_blk = (wi.tile % mt) * BM;
-    const int n_blk = (wi.tile / mt) * BN;
-    const int kbeg = wi.split * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
     const int nk = (kend - kbeg) / BK;
 
     const T *A = (const T *)p.A;
@@ -723,7 +725,65 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
     // drain the loads of the stages past the end before the workgroup exits
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
-    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, wi.split);
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, split);
+}
+
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
+__global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
+{
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
+    const int mt = (p.M + BM - 1) / BM;
+    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
+    const int kbeg = wi.split * p.k_per_split;
+    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, (wi.tile % mt) * BM, (wi.tile / mt) * BN, kbeg,
+                                                   min(p.K, kbeg + p.k_per_split), wi.split);
+}
+
+// Every phase of a strided data gradient in one launch: work item w (after
+// the XCD renumbering) belongs to the last phase whose first item is <= w;
+// that phase's filter, K, sub-convolution geometry and dx placement replace
+// the launch-wide ones.  No split: the phases' K are short.
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF>
+__global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_phased_kernel(GemmParams p, PhaseArgs pa)
+{
+    using T = typename DlElem<DTID>::T;
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
+    const int w = xcd_tile(blockIdx.x, pa.tiles);
+    int k = 0;
+    while (k + 1 < pa.n && w >= pa.ph[k + 1].tile0)
+        ++k;
+    const PhaseItem &it = pa.ph[k];
+    GemmParams q = p;
+    q.A = (const T *)p.A + it.a_off;
+    q.K = it.K;
+    q.lda = it.K;
+    q.k_per_split = it.K;
+    q.splits = 1;
+    q.g = it.g;
+    q.N = it.g.N;
+    q.P = it.g.P;
+    q.ph_h0 = it.h0;
+    q.ph_w0 = it.w0;
+    const int mt = (p.M + BM - 1) / BM;
+    const int local = w - it.tile0;
+    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, true>(q, (local % mt) * BM, (local / mt) * BN, 0, it.K, 0);
+}
+
+// All phases of a strided data gradient in one launch on 128x128 tiles:
+// 16-bit as eight wavefronts of 64x32 with a ring of four stages, f32 as
+// four wavefronts of 64x64 with a ring of two (the forms the NHWC data
+// gradient uses).  The host checks that every phase's K is a whole number
+// of stages and that the NHWC loader's divisions are in range.
+template <int DTID>
+hipError_t launch_gemm_dl_phased(const GemmParams &p, const PhaseArgs &pa, hipStream_t s)
+{
+    if (pa.n < 1 || pa.n > kMaxPhases || pa.tiles < 1 || !p.zero)
+        return hipErrorInvalidValue;
+    if constexpr (DTID == DT_F32)
+        hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 2, 2, 2, 2>), dim3(pa.tiles), dim3(256), 0, s, p, pa);
+    else
+        hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 4, 2, 1, 4>), dim3(pa.tiles), dim3(512), 0, s, p, pa);
+    return hipGetLastError();
 }
 
 // 64-deep stages in a ring of three (two stages of loads in flight):

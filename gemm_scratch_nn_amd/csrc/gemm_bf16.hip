@@ -8,4 +8,9 @@ hipError_t launch_gemm_bf16(int cfg, int amode, int bmode, const GemmParams &p, 
     return launch_gemm16<DT_BF16>(cfg, amode, bmode, p, s);
 }
 
+hipError_t launch_gemm_phased_bf16(const GemmParams &p, const PhaseArgs &pa, hipStream_t s)
+{
+    return launch_gemm_dl_phased<DT_BF16>(p, pa, s);
+}
+
 }  // namespace d4r

@@ -62,4 +62,9 @@ bool try_gemm_f32_dl(int cfg, int amode, int bmode, const GemmParams &p, hipStre
     return false;
 }
 
+hipError_t launch_gemm_phased_f32(const GemmParams &p, const PhaseArgs &pa, hipStream_t s)
+{
+    return launch_gemm_dl_phased<DT_F32>(p, pa, s);
+}
+
 }  // namespace d4r

@@ -154,7 +154,7 @@ struct NhwcRows {
             const int bb = n / g.P, r = n - (n / g.P) * g.P;
             const int i = r / g.OW;
             h0[s] = (live && n < g.N) ? i - g.p : -(1 << 30);
-            w0[s] = r - i * g.OW - g.p;
+            w0[s] = r - i * g.OW - g.pw;
             base[s] = (((long long)bb * g.H + (i - g.p)) * g.W + w0[s]) * g.C + kk;
         }
     }

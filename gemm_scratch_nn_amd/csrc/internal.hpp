@@ -117,7 +117,10 @@ __device__ __forceinline__ WorkItem xcd_work(int pid, int tiles, int splits)
 // Store of a GEMM result v = acc (+ bias) (then max(v, 0) with p.relu):
 enum Epilogue : int {
     EPI_ROWMAJOR = 0,  // C[m*ldc + n] (+ blockIdx.z * c_split_stride); bias per column n
-    EPI_NCHW = 1       // y[((n/P)*M + m)*P + n%P]; bias per row m (the output channel)
+    EPI_NCHW = 1,      // y[((n/P)*M + m)*P + n%P]; bias per row m (the output channel)
+    EPI_PHASE = 2      // one phase of a strided data gradient: column n = (b, i, j) of a
+                       // g.OH x g.OW sub-grid lands at dx[b][m][ph_h0 + ph_s*i][ph_w0 + ph_s*j]
+                       // of a ph_H x ph_W map (no bias)
 };
 
 // The epilogue's value: bias (per row for EPI_NCHW, per column otherwise)
@@ -136,6 +139,8 @@ struct ConvGeom {
     int P;    // OH*OW
     int Kc;   // C*kH*kW
     int N;    // B*P
+    int pw;   // padding along the width for the NHWC loaders (OP_IMPL_T); equals
+              // p except in the sub-convolutions of a strided data gradient
 };
 
 // How a GEMM operand is laid out in memory.  Operand "rows" are m for A and
@@ -180,7 +185,37 @@ struct GemmParams {
     int a_ch, b_ch;     // channel counts of OP_NCHW / OP_NCHW_K operands
     const void *zero;   // OP_IMPL_T: 256 zero bytes, 16-byte aligned
     ConvGeom g;         // OP_IMPL and OP_NCHW operands
+    int ph_s, ph_h0, ph_w0, ph_H, ph_W;  // EPI_PHASE: stride, first row / column, full map
 };
+
+// The data gradient of a stride-s convolution as s*s stride-1 sub-
+// convolutions of dy, one per output phase (rh, rw): dx rows h with
+// (h + p) mod s = rh take the taps u = rh + s*t, and
+//   dx[b][c][h0 + s*i][w0 + s*j] = sum_{u', v', o} Wph[c][u'][v'][o] *
+//       dy[b][o][i - ph + u'][j - pw + v'],
+//   Wph[c][u'][v'][o] = W[o][c][rh + s*(Tu-1-u')][rw + s*(Tv-1-v')]
+// with Tu = ceil((kH - rh)/s) taps, ph = Tu - 1 - (h0 + p - rh)/s (likewise
+// for the width).  Each phase is one GEMM (M = C, K = Tu*Tv*O, N = B * its
+// pixels) over dy read as NHWC; all phases run in one launch.
+constexpr int kMaxPhases = 16;
+struct PhaseItem {
+    long long a_off;  // element offset of the phase filter Wph (C x K) in A
+    int K;            // Tu*Tv*O
+    int tile0;        // the phase's first work item
+    int h0, w0;       // its first dx row and column
+    ConvGeom g;       // the stride-1 sub-convolution over dy (C = O, O = dx channels)
+};
+struct PhaseArgs {
+    int n, tiles;     // phases, work items of all phases
+    PhaseItem ph[kMaxPhases];
+};
+// one launch over every phase of pa (tile 128x128, direct-to-LDS kernel,
+// K of each phase a whole number of stages); p carries M, A (the phase
+// filters, concatenated), B (dy as NHWC), C (dx) and the EPI_PHASE fields
+hipError_t launch_gemm_phased(int dt, const GemmParams &p, const PhaseArgs &pa, hipStream_t s);
+// Wph of every phase (offsets and tap counts in pa), from W (O x C x kH x kW)
+hipError_t launch_phase_filter(int dt, const ConvGeom &g, const PhaseArgs &pa, const void *w, void *wph,
+                               hipStream_t s);
 
 // Supported (A, B) modes: every pair of OP_ROWS / OP_KC, (OP_KC, OP_IMPL),
 // (OP_KC, OP_NCHW), (OP_ROWS, OP_NCHW), (OP_NCHW, OP_NCHW_K), and for f32

@@ -235,7 +235,8 @@ class Guarded:
 
 
 GUARD_SHAPES = [(3, 5, 9, 9, 37, 3, 3, 1, 1), (2, 3, 7, 6, 5, 3, 2, 1, 1), (3, 7, 23, 29, 65, 5, 3, 2, 2),
-                (2, 130, 7, 7, 64, 3, 3, 1, 2), (3, 4, 11, 10, 130, 1, 1, 1, 0), (2, 40, 9, 11, 128, 3, 3, 1, 0)]
+                (2, 130, 7, 7, 64, 3, 3, 1, 2), (3, 4, 11, 10, 130, 1, 1, 1, 0), (2, 40, 9, 11, 128, 3, 3, 1, 0),
+                (2, 130, 9, 11, 64, 3, 3, 2, 1), (2, 64, 7, 8, 64, 3, 3, 1, 1)]
 
 
 def _guarded_inputs(sh, dt, seed):

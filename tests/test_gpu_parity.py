@@ -728,8 +728,46 @@ def test_dgrad_implicit_nhwc(t, dt, monkeypatch):
     _check_dgrad_implicit(sh, dt, ops, "gathered")
 
 
+# strided layers: stride^2 stride-1 sub-convolutions of dy (one per output
+# phase) in one launch, no dcol, no col2im; stride 2 to 4, ragged input
+# channel counts, non-square kernels, per-axis and negative paddings
+DGRAD_PHASED = [
+    (2, 64, 9, 11, 64, 3, 3, 2, 1),
+    (1, 96, 10, 9, 128, 5, 5, 2, 2),
+    (2, 64, 13, 12, 64, 4, 4, 3, 1),
+    (1, 64, 12, 12, 64, 11, 11, 4, 2),
+    (2, 130, 7, 8, 64, 3, 2, 2, 0),
+    (1, 64, 8, 10, 64, 3, 3, 3, 3),
+    (3, 64, 6, 5, 192, 2, 2, 2, 1),
+]
+
+
+@pytest.mark.parametrize("t", DGRAD_PHASED, ids=str)
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_dgrad_phased(t, dt, monkeypatch):
+    sh = _shape(t)
+    pl = _plan(sh, dt)      # keeps the handle alive while it is described
+    assert d4r.d4r_conv_describe(pl.h)["dgrad_implicit"] == "phased"
+    ops = wl.random_conv(sh, dt, seed=sum(t) + 37)
+    _check_dgrad_implicit(sh, dt, ops, "phased")
+    monkeypatch.setenv("D4R_DGRAD_PHASED", "0")
+    pl = _plan(sh, dt)
+    assert d4r.d4r_conv_describe(pl.h)["dgrad_implicit"] == "explicit"
+    _check_dgrad_implicit(sh, dt, ops, "explicit")
+
+
+def test_dgrad_phased_applies_to_the_workloads():
+    # the 46x80 map's stride-2 layer takes it; AlexNet conv1 (3 input channels) does not
+    c5 = wl.WORKLOADS["c5"].layers[2].shape
+    c3 = wl.WORKLOADS["c3"].layers[0].shape
+    p5, p3 = _plan(c5, "f16"), _plan(c3, "f32")
+    d5 = d4r.d4r_conv_describe(p5.h)
+    assert d5["dgrad_implicit"] == "phased" and d5["dgrad_phases"] == "4"
+    assert d4r.d4r_conv_describe(p3.h)["dgrad_implicit"] == "explicit"
+
+
 @pytest.mark.parametrize("key,li,dt", [("c4", 0, "bf16"), ("c4", 1, "bf16"), ("c4", 2, "bf16"), ("c5", 0, "f16"),
-                                       ("c4", 1, "f32")])
+                                       ("c4", 1, "f32"), ("c5", 2, "f16")])
 def test_dgrad_implicit_nhwc_full_size(key, li, dt):
     w = wl.WORKLOADS[key]
     sh = w.layers[li].shape
