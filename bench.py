@@ -86,12 +86,28 @@ def parse_args():
     return ap.parse_args()
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summaries
-    (profiles/traffic_*.txt), or None when none matches or the kernel's source
-    changed since the counters were taken."""
+def library_digest() -> str:
+    """sha256 over every library source and the C header (file names and
+    contents, in sorted order): any change to a kernel, the planner or the
+    launch sequence changes it."""
     import glob
     import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "gemm_scratch_nn_amd", "csrc", "*")) +
+                   [os.path.join(ROOT, "include", "d4r_conv.h")])
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summaries
+    (profiles/traffic_*.txt), or None when none matches or the library
+    (kernels, planner, launch sequence) changed since the counters were
+    taken."""
+    import glob
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt"))):
         fields = {}
         with open(path) as f:
@@ -101,12 +117,8 @@ def recorded_traffic(kernel: str):
                     fields[k.strip()] = v.strip()
         if fields.get("traffic_kernel") != kernel:
             continue
-        src = os.path.join(ROOT, fields.get("traffic_source", ""))
-        if not os.path.isfile(src):
+        if fields.get("traffic_library_sha256") != library_digest():
             continue
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != fields.get("traffic_source_sha256"):
-                continue
         return float(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
     return None
 
