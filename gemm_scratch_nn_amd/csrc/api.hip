@@ -328,6 +328,7 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
     const bool implicit = bmode == OP_IMPL;
     const int vw = dt == DT_F32 ? 4 : 8;
     GemmParams p;
+    memset(&p, 0, sizeof p);
     p.A = A;
     p.B = B;
     p.bias = bias;
@@ -339,6 +340,14 @@ hipError_t run_gemm(int dt, const GemmPlan &pl, int amode, int bmode, const void
     p.P = P;
     p.k_per_split = pl.k_per_split;
     p.splits = pl.splits;
+    {
+        // large grids run in bands of 8 M tiles: each XCD's range of tiles is
+        // a near-square block (8192^3 bf16 953 -> 1027 TFLOP/s on 256x256
+        // tiles; conv shapes, with a few M tiles, are unaffected)
+        const TileShape ts = tile_shape(pl.cfg);
+        const int mt = (M + ts.bm - 1) / ts.bm, nt = (N + ts.bn - 1) / ts.bn;
+        p.group_m = (mt >= 16 && nt >= 16) ? 8 : 0;
+    }
     // vector loads need every 16-byte vector wholly inside or outside the
     // operand: leading dimension and the contiguous extent multiples of vw
     p.a_vec = (lda % vw) == 0 && ((amode == OP_KC ? K : M) % vw) == 0;

@@ -732,11 +732,13 @@ template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
 {
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
-    const int mt = (p.M + BM - 1) / BM;
-    const WorkItem wi = xcd_work(blockIdx.x, mt * ((p.N + BN - 1) / BN), p.splits);
+    const int mt = (p.M + BM - 1) / BM, nt = (p.N + BN - 1) / BN;
+    const WorkItem wi = xcd_work(blockIdx.x, mt * nt, p.splits);
     const int kbeg = wi.split * p.k_per_split;
-    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, (wi.tile % mt) * BM, (wi.tile / mt) * BN, kbeg,
-                                                   min(p.K, kbeg + p.k_per_split), wi.split);
+    int tm, tn;
+    tile_mn(wi.tile, mt, nt, p.group_m, tm, tn);
+    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, tm * BM, tn * BN, kbeg, min(p.K, kbeg + p.k_per_split),
+                                                   wi.split);
 }
 
 // Every phase of a strided data gradient in one launch: work item w (after

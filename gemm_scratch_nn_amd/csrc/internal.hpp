@@ -186,7 +186,28 @@ struct GemmParams {
     const void *zero;   // OP_IMPL_T: 256 zero bytes, 16-byte aligned
     ConvGeom g;         // OP_IMPL and OP_NCHW operands
     int ph_s, ph_h0, ph_w0, ph_H, ph_W;  // EPI_PHASE: stride, first row / column, full map
+    int group_m;        // direct-to-LDS kernel: tiles ordered in groups of group_m M tiles
+                        // (0 or 1: M tiles fastest)
 };
+
+// Tile (m, n) of tile index t in an mt x nt grid.  With group > 1 the tiles
+// run in bands of `group` M tiles, N fastest within a band, so the
+// contiguous range of tiles an XCD receives is a near-square block (fewer
+// distinct operand panels per L2) instead of whole columns of M tiles.
+__device__ __forceinline__ void tile_mn(int t, int mt, int nt, int group, int &tm, int &tn)
+{
+    if (group <= 1) {
+        tm = t % mt;
+        tn = t / mt;
+        return;
+    }
+    const int per = group * nt;
+    const int first = (t / per) * group;
+    const int size = min(mt - first, group);
+    const int r = t - (t / per) * per;
+    tm = first + r % size;
+    tn = r / size;
+}
 
 // The data gradient of a stride-s convolution as s*s stride-1 sub-
 // convolutions of dy, one per output phase (rh, rw): dx rows h with

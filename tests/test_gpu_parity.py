@@ -460,16 +460,18 @@ def test_dl128_forms(form, dt, monkeypatch):
     _check_whole(sh, dt, wl.conv_inputs(w, 1, dt, batch=3), f"c4/conv4/b3/{form}")
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_gemm_256x256_square_sampled(dt):
-    # the planner's tile for large square k-contiguous products
-    M = K = N = 2048
-    rng = np.random.default_rng(2048)
+# large k-contiguous products: the 256x256 tile, and grids of 16+ tiles each
+# way, which run in bands of 8 M tiles (ragged last band and tiles)
+@pytest.mark.parametrize("dt,M,K,N", [("f16", 2048, 2048, 2048), ("bf16", 2048, 2048, 2048),
+                                      ("bf16", 4000, 128, 4100), ("f16", 4200, 192, 3900),
+                                      ("f32", 2100, 96, 2050)])
+def test_gemm_large_sampled(dt, M, K, N):
+    rng = np.random.default_rng(M + K + N)
     a = wl.quantize(rng.normal(size=(M, K)), dt)
     b = wl.quantize(rng.normal(size=(N, K)), dt)
     C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
     torch.cuda.synchronize()
-    rows = _sample_idx(M, 24)
+    rows = _sample_idx(M, 40)
     ref = oracle.gemm(a.exact[rows].copy(), b.exact, len(rows), K, N, 2)
     got = host(C)[rows]
     assert rel_err(got, ref) < TOL[dt]
