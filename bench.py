@@ -674,6 +674,36 @@ def attainable_tf(flops, bytes_, peak):
     return min(peak, flops / bytes_ * HBM_PEAK_GBPS / 1e3)
 
 
+def hbm_reference(reps: int = 10) -> dict:
+    """The attainable HBM rates of the library's own streaming kernels on 1 GiB
+    buffers: d4r_stream_copy (read + write) and d4r_stream_fill (write)."""
+    import torch
+
+    import gemm_scratch_nn_amd as d4r
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    d4r.d4r_stream_fill(src, 0x3F800000, n)
+    out = {"bytes": n, "kernels": "d4r_stream_copy (read + write), d4r_stream_fill (write only)"}
+    for name, fn in (("copy", lambda: d4r.d4r_stream_copy(dst, src, n)),
+                     ("fill", lambda: d4r.d4r_stream_fill(dst, 0, n))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        d4r.d4r_profile_reset()
+        d4r.d4r_profile_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        d4r.d4r_profile_enable(False)
+        st = d4r.d4r_profile_read()
+        d4r.d4r_profile_reset()
+        ms = sum(r["ms"] for r in st)
+        out[f"{name}_GBps"] = sum(r["bytes"] for r in st) / (ms * 1e-3) / 1e9
+    del src, dst
+    return out
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -694,6 +724,25 @@ def main() -> int:
     dtype = args.dtype or wl.dtypes[0]
     line, stats = bench_conv(args, args.workload, dtype, args.steps, args.warmup, args.rotate, args.graph,
                              args.streams, not args.no_cpu_baseline, per_layer=True)
+    if not args.no_configs and args.workload == "c4" and dtype == "f32" and not args.graph and args.rotate == 1:
+        # cold caches: three independent copies of every buffer in rotation,
+        # so a step's operands come from HBM, not from the 256 MB MALL
+        cl, _ = bench_conv(args, "c4", "f32", max(5, min(args.steps, 20)), min(args.warmup, 3), 3, False, 1,
+                           False, per_layer=False)
+        line["cold"] = {"rotate": 3, "ms_per_step": cl["ms_per_step"], "value": cl["value"],
+                        "pct_mfma_peak": cl["pct_mfma_peak"], "im2col": cl["im2col"]}
+        ref = hbm_reference()
+        line["hbm_reference"] = ref
+
+        def rel(stage):
+            if stage and "GBps" in stage:
+                stage["frac_of_stream_copy"] = stage["GBps"] / ref["copy_GBps"]
+                stage["frac_of_stream_fill"] = stage["GBps"] / ref["fill_GBps"]
+        rel(line["im2col"])
+        rel(line["col2im"])
+        for l in line.get("layers", []):
+            rel(l["im2col"])
+            rel(l["col2im"])
     if not args.no_configs and args.workload == "c4" and dtype == "f32":
         # the other GEMM-dominated configurations, each with its layers
         sec_steps = max(5, min(args.steps, 20))
@@ -705,6 +754,13 @@ def main() -> int:
                     "gemm_frac_mfma", "gemm_frac_attainable", "im2col", "col2im", "layers", "roofline")
             entry = {"workload": sl["config"]["workload"], "steps": sec_steps}
             entry.update({k: sl[k] for k in keep if k in sl})
+            ref = line.get("hbm_reference")
+            if ref:
+                for st in [entry.get("im2col"), entry.get("col2im")] + \
+                          [x for l in entry.get("layers", []) for x in (l["im2col"], l["col2im"])]:
+                    if st and "GBps" in st:
+                        st["frac_of_stream_copy"] = st["GBps"] / ref["copy_GBps"]
+                        st["frac_of_stream_fill"] = st["GBps"] / ref["fill_GBps"]
             configs.append(entry)
         line["configs"] = configs
     if args.detail:

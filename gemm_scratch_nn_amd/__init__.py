@@ -113,6 +113,8 @@ _c = {
     "d4r_softmax_ce_grad": _sig("d4r_softmax_ce_grad", [_vp, _vp, _vp, _vp, _i, _i, _vp]),
     "d4r_sgd_update": _sig("d4r_sgd_update", [_vp, _vp, _ll, _f, _f, _vp]),
     "d4r_grad_accum": _sig("d4r_grad_accum", [_vp, _vp, _ll, _vp]),
+    "d4r_stream_copy": _sig("d4r_stream_copy", [_vp, _vp, _sz, _vp]),
+    "d4r_stream_fill": _sig("d4r_stream_fill", [_vp, ctypes.c_uint, _sz, _vp]),
     "d4r_profile_enable": _sig("d4r_profile_enable", [_i]),
     "d4r_profile_reset": _sig("d4r_profile_reset", []),
     "d4r_status_string": _sig("d4r_status_string", [_i], ctypes.c_char_p),
@@ -376,6 +378,15 @@ def d4r_sgd_update(param, grad, n, lr, clip, stream=None) -> None:
 
 def d4r_grad_accum(acc, grad, n, stream=None) -> None:
     _check("d4r_grad_accum", _c["d4r_grad_accum"](_ptr(acc), _ptr(grad), n, _stream(stream)))
+
+
+def d4r_stream_copy(dst, src, nbytes, stream=None) -> None:
+    _check("d4r_stream_copy", _c["d4r_stream_copy"](_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+def d4r_stream_fill(dst, value, nbytes, stream=None) -> None:
+    _check("d4r_stream_fill", _c["d4r_stream_fill"](_ptr(dst), int(value) & 0xFFFFFFFF, nbytes,
+                                                    _stream(stream)))
 
 
 def d4r_profile_enable(on: bool) -> None:

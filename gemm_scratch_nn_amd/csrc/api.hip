@@ -1757,6 +1757,33 @@ d4r_status d4r_grad_accum(float *acc, const float *grad, long long n, void *hip_
                     [&] { return launch_grad_accum(acc, grad, n, s); });
 }
 
+d4r_status d4r_stream_copy(void *dst, const void *src, size_t bytes, void *hip_stream)
+{
+    if (bytes % 16 != 0)
+        return fail(D4R_ERR_INVALID_ARG, "bytes = %zu is not a multiple of 16", bytes);
+    if (bytes == 0)
+        return ok();
+    D4R_TRY(check_tensor(dst, "dst"));
+    D4R_TRY(check_tensor(src, "src"));
+    if (overlaps(dst, bytes, src, bytes))
+        return fail(D4R_ERR_INVALID_ARG, "dst overlaps src");
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "stream_copy", 2.0 * bytes, "stream copy",
+                    [&] { return launch_stream_copy(dst, src, bytes, s); });
+}
+
+d4r_status d4r_stream_fill(void *dst, unsigned int value, size_t bytes, void *hip_stream)
+{
+    if (bytes % 16 != 0)
+        return fail(D4R_ERR_INVALID_ARG, "bytes = %zu is not a multiple of 16", bytes);
+    if (bytes == 0)
+        return ok();
+    D4R_TRY(check_tensor(dst, "dst"));
+    hipStream_t s = (hipStream_t)hip_stream;
+    return run_step(s, "stream_fill", 1.0 * bytes, "stream fill",
+                    [&] { return launch_stream_fill(dst, value, bytes, s); });
+}
+
 d4r_status d4r_profile_enable(int on)
 {
     Profiler &P = prof();

@@ -334,6 +334,11 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
                                 long long split_stride, int epi, float *C, int ldc,
                                 const float *bias, int P, int relu, const BiasSum &bs, hipStream_t s);
 
+// Streaming reference kernels (stream_kernels.hip): bytes a multiple of 16,
+// 16-byte aligned pointers.
+hipError_t launch_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_stream_fill(void *dst, uint32_t value, size_t bytes, hipStream_t s);
+
 // The rest of a training step (f32; train_kernels.hip).  Elementwise
 // kernels take 16-byte aligned pointers; n may be 0.
 hipError_t launch_relu_forward(const float *x, float *y, long long n, hipStream_t s);

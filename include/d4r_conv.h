@@ -42,8 +42,11 @@
  *
  * Memory ownership.  Every pointer argument is a caller-owned device
  * pointer (e.g. a torch tensor's data_ptr()).  The library never allocates,
- * frees or keeps device memory.  Pointers to tensors must be 16-byte
- * aligned, bias and db 4-byte aligned, ws 256-byte aligned.
+ * frees or keeps device memory of the caller's; its only device memory is
+ * the static 64 MiB split-K array of d4r_gemm_noalloc, which each GPU holds
+ * from when the library's code is loaded on it until the process ends.
+ * Pointers to tensors must be 16-byte aligned, bias and db 4-byte aligned,
+ * ws 256-byte aligned.
  *
  * Workspace.  Scratch memory (the col matrix, the reshaped gradient, the
  * float32 dcol, split-K partial sums) lives in a caller buffer ws of at least
@@ -452,7 +455,18 @@ typedef struct {
     int launches;
     double ms;     /* summed event-to-event time of all launches */
     double flops;  /* summed algorithmic flops (0 for data movement) */
-    double bytes;  /* summed algorithmic bytes */
+    double bytes;  /*
+ * Measurement aids (not steps of the method): plain streaming kernels whose
+ * rates are the attainable HBM reference the bench reports beside the
+ * HBM-bound steps.  d4r_stream_copy: dst[i] = src[i] over `bytes` (read +
+ * write stream); d4r_stream_fill: every 32-bit word of dst = value (write
+ * stream).  16-byte aligned device pointers, bytes a multiple of 16 (0 does
+ * nothing), dst and src must not overlap.  Errors: D4R_ERR_INVALID_ARG.
+ */
+d4r_status d4r_stream_copy(void *dst, const void *src, size_t bytes, void *hip_stream);
+d4r_status d4r_stream_fill(void *dst, unsigned int value, size_t bytes, void *hip_stream);
+
+/* summed algorithmic bytes */
 } d4r_kernel_stat;
 
 d4r_status d4r_profile_enable(int on);

@@ -427,3 +427,16 @@ def test_exports_only_the_declared_c_abi():
                          check=True).stdout
     funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] in "TtWw"}
     assert funcs == set(d4r.declared_functions()), funcs ^ set(d4r.declared_functions())
+
+
+def test_stream_reference_argument_errors():
+    for call in (lambda: d4r.d4r_stream_copy(FAKE, FAKE + (1 << 20), 100, 0),      # not a multiple of 16
+                 lambda: d4r.d4r_stream_copy(MISALIGNED, FAKE, 64, 0),
+                 lambda: d4r.d4r_stream_copy(FAKE, FAKE + 32, 64, 0),            # overlap
+                 lambda: d4r.d4r_stream_fill(MISALIGNED, 0, 64, 0),
+                 lambda: d4r.d4r_stream_fill(FAKE, 0, 8, 0)):
+        with pytest.raises(D4RError) as e:
+            call()
+        assert e.value.status == INVALID
+    d4r.d4r_stream_copy(FAKE, FAKE, 0, 0)    # nothing to do: no launch
+    d4r.d4r_stream_fill(FAKE, 0, 0, 0)

@@ -243,3 +243,16 @@ def test_grad_accum_matches_oracle(n):
     ref = oracle.grad_accum(_f64(a), _f64(g))
     # one rounding of an exact sum
     assert np.array_equal(ad.cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("n", [16, 4096, 1 << 20, (1 << 22) + 48])
+def test_stream_reference_kernels(n):
+    # the streaming reference kernels: exact copies and fills, tails included
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    d4r.d4r_stream_copy(dst, src, n)
+    fill = torch.zeros_like(src)
+    d4r.d4r_stream_fill(fill, 0xDEADBEEF, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert bool(torch.all(fill == torch.tensor(0xDEADBEEF, dtype=torch.int64).to(torch.int32).item()))
