@@ -26,6 +26,7 @@ SHAPES = [
     ((3, 64, 13, 13, 3, 3, 1, 1, 128), {"f16", "bf16"}),         # P = 169: three pixel tiles
     ((1, 32, 20, 20, 5, 5, 1, 2, 64), {"f16", "bf16"}),
     ((2, 16, 9, 9, 3, 3, 2, 1, 64), set()),                      # stride 2: explicit data gradient
+    ((3, 3, 23, 23, 5, 5, 4, 2, 40), set()),                     # stride 4, 3 channels (AlexNet conv1-like)
     ((2, 64, 9, 9, 3, 3, 2, 1, 64), set()),                      # stride 2: phased data gradient
     ((2, 16, 5, 7, 1, 1, 1, 0, 64), set()),                      # 1x1: direct path
     ((2, 32, 8, 8, 3, 3, 1, 1, 40), set()),                      # O not a whole GEMM stage
