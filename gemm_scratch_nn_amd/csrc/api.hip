@@ -436,7 +436,8 @@ struct d4r_conv {
     // dcol, no col2im)
     bool pointwise;
     // implicit data gradient from dy read as NHWC (its transpose Gt): filter
-    // wd[c][u][v][o], a zero page (16-bit direct-to-LDS loads of padding)
+    // wd[c][ob][u][v][oi] (o = ob*BK + oi, the loader's k order), a zero
+    // page (direct-to-LDS loads of padding)
     bool dgrad_nhwc;
     GemmPlan bwd_data_nhwc;
     size_t off_zero;
@@ -446,7 +447,8 @@ struct d4r_conv {
     bool fused_bwd;
     // implicit forward from x read as NHWC (stride 1, whole GEMM stages of
     // input channels): x transposed to xt[b][h][w][c], the filter reordered
-    // to wr[o][u][v][c]; the direct-to-LDS loader of the NHWC data gradient
+    // to wr[o][cb][u][v][ci] (c = cb*BK + ci); the loader of the NHWC data
+    // gradient
     bool fwd_nhwc;
     GemmPlan fwd_nhwc_plan;
     size_t off_xt, off_wr;
@@ -632,7 +634,7 @@ bool plan_phases(const ConvGeom &g, int dt, PhaseArgs *pa)
     memset(pa, 0, sizeof *pa);
     const int s = g.s, bk = gemm_bk(dt);
     if (s < 2 || s * s > kMaxPhases || s > g.kH || s > g.kW || g.H < s || g.W < s || g.O % bk != 0 ||
-        g.O / bk > 1024 || g.C < 64)
+        g.C < 64)
         return false;
     long long a_off = 0;
     int tiles = 0;
@@ -650,7 +652,7 @@ bool plan_phases(const ConvGeom &g, int dt, PhaseArgs *pa)
             int tu, h0, hm, ph, tv, w0, wm, pw;
             axis(rh, g.H, g.kH, &tu, &h0, &hm, &ph);
             axis(rw, g.W, g.kW, &tv, &w0, &wm, &pw);
-            if (tu < 1 || tv < 1 || hm < 1 || wm < 1 || tv > 1024)
+            if (tu < 1 || tv < 1 || hm < 1 || wm < 1 || tu * tv > 1024)
                 return false;
             PhaseItem &it = pa->ph[pa->n++];
             ConvGeom &q = it.g;
@@ -727,11 +729,11 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->bwd_data_impl = plan_gemm(d.O, d.N, d.Kc, dtype);
     }
     // the NHWC form needs whole GEMM stages of dy (32 f32 / 64 16-bit
-    // channels) within one tap; the 16-bit loader decodes a stage's tap
-    // with small_div, exact for stage indices below 2^20 and divisors <= 1024
+    // channels) within one tap; the direct-to-LDS loader decodes a stage's
+    // channel block and tap with small_div, exact for stage indices below
+    // 2^20 and divisors (kH*kW, kW) <= 1024
     h->dgrad_nhwc = h->dgrad_impl && outC % gemm_bk(dtype) == 0 &&
-                    (long long)h->gd.Kc / gemm_bk(dtype) < (1 << 20) && outC / gemm_bk(dtype) <= 1024 &&
-                    kW <= 1024;
+                    (long long)h->gd.Kc / gemm_bk(dtype) < (1 << 20) && (long long)kH * kW <= 1024;
     if (const char *e = getenv("D4R_DGRAD_NHWC"))  // experiments, tests: 0 = gathered path
         h->dgrad_nhwc = h->dgrad_nhwc && e[0] != '0';
     if (h->dgrad_nhwc)
@@ -744,7 +746,7 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->pointwise = h->pointwise && e[0] != '0';
     // the forward's NHWC form: the same loader conditions on x (inC channels)
     h->fwd_nhwc = stride == 1 && !h->pointwise && inC % gemm_bk(dtype) == 0 &&
-                  (long long)g.Kc / gemm_bk(dtype) < (1 << 20) && inC / gemm_bk(dtype) <= 1024 && kW <= 1024;
+                  (long long)g.Kc / gemm_bk(dtype) < (1 << 20) && (long long)kH * kW <= 1024;
     if (const char *e = getenv("D4R_FWD_NHWC"))  // experiments, tests: 0 = gathered implicit forward
         h->fwd_nhwc = h->fwd_nhwc && e[0] != '0';
     if (h->fwd_nhwc)
@@ -974,15 +976,15 @@ d4r_status conv_forward(d4r_conv_t h, const void *x, const void *w, const float 
                    "forward GEMM");
     } else if (h->fwd_nhwc) {
         // y = Wr(O x kH*kW*C) * im2col(x as NHWC): one launch transposes x to
-        // xt[b][pix][c] and reorders the filter to wr[o][u][v][c] (clearing
-        // the zero page the loader reads for padding)
+        // xt[b][pix][c] and reorders the filter to wr[o][cb][u][v][ci], the
+        // loader's k order (clearing the zero page it reads for padding)
         char *wsb = (char *)ws;
         void *xt = wsb + h->off_xt, *wr = wsb + h->off_wr, *zero = wsb + h->off_zero;
         {
             ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":fwd_x_w", 0.0,
                          2.0 * h->es * ((double)g.B * g.C * g.H * g.W + (double)g.O * g.Kc));
             const TransposeJob jx{x, xt, g.C, g.H * g.W, g.B, 0, (uint32_t *)zero, 0};
-            const TransposeJob jw{w, wr, g.C, g.kH * g.kW, g.O, 0, nullptr, 0};
+            const TransposeJob jw{w, wr, g.C, g.kH * g.kW, g.O, 0, nullptr, 0, gemm_bk(h->dt)};
             hipError_t e = launch_transpose_pair(h->dt, jx, jw, s);
             ps.done();
             D4R_LAUNCH(e, "input transpose and filter reorder");
@@ -1196,7 +1198,8 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
     float *partial = (float *)(wsb + h->off_big);
     if (h->dgrad_nhwc) {
         // dx = Wd(C x kH*kW*O) * im2col(dy as NHWC): dy transposed to
-        // Gt[b][pix][o], the filter flipped with k ordered (u, v, o)
+        // Gt[b][pix][o], the filter flipped with k ordered (channel block,
+        // u, v, channel)
         void *gt = wsb + h->off_gt;
         void *zero = wsb + h->off_zero;
         {
@@ -1205,7 +1208,7 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
             ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":dgrad_dy_w", 0.0,
                          2.0 * h->es * ((double)g.B * g.O * g.P + (double)g.O * g.Kc));
             const TransposeJob jdy{dy, gt, g.O, g.P, g.B, 0, nullptr, 0};
-            const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0};
+            const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0, gemm_bk(h->dt)};
             hipError_t e = launch_transpose_pair(h->dt, jdy, jw, s);
             ps.done();
             D4R_LAUNCH(e, "grad transpose and filter flip");
@@ -1327,7 +1330,7 @@ d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const v
         ProfScope ps(s, std::string("dy_prep_") + dt_name(h->dt) + ":bwd", 0.0,
                      3.0 * h->es * (double)g.B * g.O * g.P + 2.0 * h->es * (double)g.O * g.Kc);
         const DyPrep a{dy, gt, G, bias_part, g.B, g.O, g.P, 0, 0};
-        const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0};
+        const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0, gemm_bk(h->dt)};
         hipError_t e = launch_dy_prep(h->dt, a, jw, s);
         ps.done();
         D4R_LAUNCH(e, "dy preparation");

@@ -638,9 +638,14 @@ __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ 
 // flip > 0 (the data gradient's filter for an NHWC dy): the columns come in
 // groups of flip taps and output row c takes input column c with its tap
 // reversed inside the group; block 0 also clears 256 bytes at `zero`.
+// kb > 0 (filters for the NHWC loaders, whose k runs over channel blocks of
+// kb, then taps, then the channel inside the block): with groups of gs =
+// flip (or Cc) output rows, element (row c, column r) goes to
+// ((c / gs)*R + (r / kb)*kb)*gs + (c % gs)*kb + r % kb instead of c*R + r.
+// Needs R % kb == 0.
 template <typename T>
 __device__ __forceinline__ void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int R, int Cc,
-                                               int flip, int bx, int by, int bz)
+                                               int flip, int kb, int bx, int by, int bz)
 {
     __shared__ T tile[64][65];
     const long long base = (long long)bz * R * Cc;
@@ -659,12 +664,29 @@ __device__ __forceinline__ void transpose_tile(const T *__restrict__ in, T *__re
         tile[ty + i * (NT / 64)][tx] = v[i];
     __syncthreads();
     const bool rin = r0 + tx < R;
+    const int r = r0 + tx;
+    if (kb > 0) {
+        // gs = flip (or Cc, one group); the group of c and its flipped tap
+        // come from one division
+        const int gs = flip > 0 ? flip : Cc;
+        const int rb = r / kb;
+        const long long rpart = (long long)rb * kb * gs + (r - rb * kb);
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            const int c = c0 + ty + i * (NT / 64);
+            const int q = flip > 0 ? c / flip : 0;
+            const int t = flip > 0 ? flip - 1 - (c - q * flip) : c;
+            if (rin && c < Cc)
+                out[base + (long long)q * gs * R + (long long)t * kb + rpart] = tile[tx][ty + i * (NT / 64)];
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int c = c0 + ty + i * (NT / 64);
         const int oc = flip > 0 ? c - c % flip + (flip - 1 - c % flip) : c;
         if (rin && c < Cc)
-            out[base + (long long)oc * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
+            out[base + (long long)oc * R + r] = tile[tx][ty + i * (NT / 64)];
     }
 }
 
@@ -674,7 +696,7 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in,
 {
     if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
         zero[threadIdx.x] = 0u;
-    transpose_tile<T>(in, out, R, Cc, flip, blockIdx.x, blockIdx.y, blockIdx.z);
+    transpose_tile<T>(in, out, R, Cc, flip, 0, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Two independent batched transposes in one launch: blocks [0, a.blocks)
@@ -688,7 +710,7 @@ __global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob a, Transpos
     const int gx = (j.Cc + 63) / 64, gy = (j.R + 63) / 64;
     if (j.zero && local == 0 && threadIdx.x < 64)
         j.zero[threadIdx.x] = 0u;
-    transpose_tile<T>((const T *)j.in, (T *)j.out, j.R, j.Cc, j.flip, local % gx, (local / gx) % gy,
+    transpose_tile<T>((const T *)j.in, (T *)j.out, j.R, j.Cc, j.flip, j.kb, local % gx, (local / gx) % gy,
                       local / (gx * gy));
 }
 
@@ -710,7 +732,7 @@ __global__ __launch_bounds__(NT) void dy_prep_kernel(DyPrep a, TransposeJob w)
         const int gx = (w.Cc + 63) / 64, gy = (w.R + 63) / 64;
         if (w.zero && local == 0 && threadIdx.x < 64)
             w.zero[threadIdx.x] = 0u;
-        transpose_tile<T>((const T *)w.in, (T *)w.out, w.R, w.Cc, w.flip, local % gx, (local / gx) % gy,
+        transpose_tile<T>((const T *)w.in, (T *)w.out, w.R, w.Cc, w.flip, w.kb, local % gx, (local / gx) % gy,
                           local / (gx * gy));
         return;
     }
@@ -1034,14 +1056,15 @@ inline dim3 grid2(long long x, long long y)
 namespace {
 
 // Phase filters of a strided data gradient: for phase k of pa, element
-// e = ((c*Tu + u')*Tv + v')*O + o of its block (at pa.ph[k].a_off) is
-// W[o][c][rh + s*(Tu-1-u')][rw + s*(Tv-1-v')], where the phase's first dx
-// row h0 fixes rh = (h0 + p) mod s (likewise rw).  Every tap of W lands in
-// exactly one phase, so the blocks together hold |W| elements.  One thread
-// per element, writes in order.
+// e = c*K + ((ob*Tu + u')*Tv + v')*bk + oi of its block (at pa.ph[k].a_off;
+// K = Tu*Tv*O, o = ob*bk + oi: the NHWC loader's order of channel block,
+// tap, channel) is W[o][c][rh + s*(Tu-1-u')][rw + s*(Tv-1-v')], where the
+// phase's first dx row h0 fixes rh = (h0 + p) mod s (likewise rw).  Every
+// tap of W lands in exactly one phase, so the blocks together hold |W|
+// elements.  One thread per element, writes in order.
 template <typename T>
 __global__ __launch_bounds__(NT) void phase_filter_kernel(const T *__restrict__ w, T *__restrict__ wph,
-                                                          ConvGeom g, PhaseArgs pa, long long total)
+                                                          ConvGeom g, PhaseArgs pa, long long total, int bk)
 {
     const long long e = (long long)blockIdx.x * NT + threadIdx.x;
     if (e >= total)
@@ -1052,13 +1075,16 @@ __global__ __launch_bounds__(NT) void phase_filter_kernel(const T *__restrict__ 
     const PhaseItem &it = pa.ph[k];
     const int Tu = it.g.kH, Tv = it.g.kW, O = g.O;
     const int rh = (it.h0 + g.p) % g.s, rw = (it.w0 + g.p) % g.s;
-    long long r = e - it.a_off;
-    const int o = (int)(r % O);
-    r /= O;
-    const int vv = (int)(r % Tv);
-    r /= Tv;
-    const int uu = (int)(r % Tu);
-    const int c = (int)(r / Tu);
+    const long long K = (long long)Tu * Tv * O;
+    const long long r = e - it.a_off;
+    const int c = (int)(r / K);
+    int q = (int)(r - c * K);
+    const int oi = q % bk;
+    q /= bk;
+    const int vv = q % Tv;
+    q /= Tv;
+    const int uu = q % Tu;
+    const int o = (q / Tu) * bk + oi;
     const int u = rh + g.s * (Tu - 1 - uu), v = rw + g.s * (Tv - 1 - vv);
     wph[e] = w[(((long long)o * g.C + c) * g.kH + u) * g.kW + v];
 }
@@ -1072,10 +1098,10 @@ hipError_t launch_phase_filter(int dt, const ConvGeom &g, const PhaseArgs &pa, c
     const dim3 grid((unsigned)((total + NT - 1) / NT));
     if (dt == DT_F32)
         hipLaunchKernelGGL(phase_filter_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)w,
-                           (uint32_t *)wph, g, pa, total);
+                           (uint32_t *)wph, g, pa, total, gemm_bk(dt));
     else
         hipLaunchKernelGGL(phase_filter_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)w,
-                           (uint16_t *)wph, g, pa, total);
+                           (uint16_t *)wph, g, pa, total, gemm_bk(dt));
     return hipGetLastError();
 }
 

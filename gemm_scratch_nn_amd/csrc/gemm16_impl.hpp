@@ -578,11 +578,14 @@ struct DlImplNhwc {
     __device__ __forceinline__ void issue(const T *X, const T *zero, int k0, char *lds, int wave,
                                           const ConvGeom &g) const
     {
-        // k0 is a whole stage (BK channels of one tap); divisor C / BK <=
-        // 1024 and stage index < 2^20 (checked by the host).  The chunk's
-        // offset inside the zero page is base mod BK (C is a multiple of BK).
-        const int ks = k0 / BK, cb = g.C / BK;
-        const int tap = small_div(ks, cb), c0 = (ks - tap * cb) * BK;
+        // k0 is a whole stage: BK channels of one tap, stages ordered by
+        // channel block, then tap (so the taps of one block reread its
+        // channels at shifted pixels while they are in cache); divisors
+        // kH*kW, kW <= 1024 and stage index < 2^20 (checked by the host).
+        // The chunk's offset inside the zero page is base mod BK (C is a
+        // multiple of BK).
+        const int ks = k0 / BK, taps = g.kH * g.kW;
+        const int cblk = small_div(ks, taps), tap = ks - cblk * taps, c0 = cblk * BK;
         const int u = small_div(tap, g.kW), v = tap - u * g.kW;
         const long long toff = ((long long)u * g.W + v) * g.C + c0;
 #pragma unroll

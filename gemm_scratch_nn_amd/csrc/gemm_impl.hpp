@@ -127,8 +127,9 @@ struct OperandTile {
 };
 
 // B operand: the im2col of an NHWC tensor t[b][h][w][c] (OP_IMPL_T, stride
-// 1, C % 32 == 0) with k ordered (u, v, c): op(B)[k][n] = t[b][i-p+u][j-p+v][c]
-// for n = (b, i, j).  A 32-deep stage lies inside one tap, so every 16-byte
+// 1, C % 32 == 0) with 32-deep stages ordered by channel block, then tap:
+// op(B)[k][n] = t[b][i-p+u][j-p+v][c] for n = (b, i, j), k = (cb*kH*kW +
+// u*kW + v)*32 + ci, c = cb*32 + ci.  A stage lies inside one tap, so every 16-byte
 // slot is 4 consecutive channels of one pixel; loads are unconditional (offset
 // 0 in the padding or past N) and zeroed at the LDS store, the layout [n][k]
 // of a k-contiguous operand.  The slots' pixels are the same in every stage:
@@ -167,7 +168,9 @@ struct ImplNhwcTileF32 : OperandTile<BR, true, NT> {
     __device__ __forceinline__ void load(const uint32_t *__restrict__ X, const ConvGeom &g,
                                          const NhwcRows<BR, NT> &rows, int K, int k0, int tid)
     {
-        const int tap = k0 / g.C, c0 = k0 - tap * g.C;
+        // stages ordered by channel block, then tap (OP_IMPL_T)
+        const int ks = k0 / kBK32, taps = g.kH * g.kW;
+        const int cblk = ks / taps, tap = ks - cblk * taps, c0 = cblk * kBK32;
         const int u = tap / g.kW, v = tap - (tap / g.kW) * g.kW;
         const long long toff = ((long long)u * g.W + v) * g.C + c0;
 #pragma unroll

@@ -159,11 +159,15 @@ enum OperandMode : int {
                   // B and whose (image, pixel) pair is the k index:
                   // op(B)[k][c] = t[k / P][c][k % P] (x in the filter
                   // gradient of a 1x1 stride-1 unpadded convolution)
-    OP_IMPL_T = 5 // B only, 16-bit direct-to-LDS GEMM: the im2col of an
-                  // NHWC tensor t[b][h][w][c] (geometry p.g, stride 1) with k
-                  // ordered (u, v, c), c fastest: op(B)[k][n] =
+    OP_IMPL_T = 5 // B only: the im2col of an NHWC tensor t[b][h][w][c]
+                  // (geometry p.g, stride 1) with k ordered by channel block,
+                  // then tap, then channel inside the block: k = (cb*kH*kW +
+                  // u*kW + v)*BK + ci for c = cb*BK + ci, BK the GEMM stage
+                  // depth (32 f32, 64 16-bit); op(B)[k][n] =
                   // t[b][i-p+u][j-p+v][c] for n = (b, i, j), or 0 in the
-                  // padding (read from p.zero).  Needs p.g.C % 64 == 0.
+                  // padding (read from p.zero).  Needs p.g.C % BK == 0.  The
+                  // kH*kW stages of one channel block read overlapping
+                  // windows of the same BK channels back to back.
 };
 
 // C = op(A) * op(B) over k in [z*k_per_split, min(K, (z+1)*k_per_split)).
@@ -304,6 +308,7 @@ struct TransposeJob {
     int R, Cc, batch, flip;
     uint32_t *zero;
     int blocks;
+    int kb;  // > 0: output rows interleaved in blocks of kb (see transpose_tile)
 };
 
 // jobs a and b in one launch (each 64x64 tile a block; the jobs must not
