@@ -217,8 +217,10 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy,
  * Wf[c][o][u][v] = w[o][c][kH-1-u][kW-1-v]; it runs as an implicit GEMM on
  * that geometry: no dcol, no col2im.  When outC is a multiple of 32 (f32)
  * or 64 (f16, bf16), dy is first transposed to NHWC and the filter flipped
- * with k ordered (u, v, o), so that every GEMM stage reads contiguous
- * channel runs of dy (16-byte loads; straight into LDS for 16-bit);
+ * with k ordered by blocks of 32 / 64 output channels, then tap (u, v),
+ * then channel, so that every GEMM stage reads contiguous channel runs of
+ * dy (16-byte loads straight into LDS) and the taps of one block reread
+ * the same channels while they are cached;
  * otherwise the GEMM gathers im2col(dy) element by element.  1x1 stride-1
  * unpadded convolutions take their direct path, other shapes the explicit
  * path of d4r_conv_backward_data.  Same arguments, result equal up to
