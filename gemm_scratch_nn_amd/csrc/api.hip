@@ -626,15 +626,16 @@ namespace {
 // The output phases of a strided layer's data gradient (see PhaseArgs).  The
 // phased form applies when every phase has taps and outputs (stride at most
 // the kernel and the input extents), dy's channels fill whole GEMM stages,
-// the NHWC loader's divisions stay in range, and the GEMM rows (the input
-// channels) fill at least half a 128-row tile: with fewer (AlexNet conv1's
-// 3) the explicit GEMM, whose rows are C*kH*kW, keeps the matrix cores busy.
-bool plan_phases(const ConvGeom &g, int dt, PhaseArgs *pa)
+// the NHWC loader's divisions stay in range, and (unless any_rows) the GEMM
+// rows (the input channels) fill at least half a 128-row tile: with fewer
+// (AlexNet conv1's 3) the explicit GEMM, whose rows are C*kH*kW, keeps the
+// matrix cores busy, so the phased form runs there only when forced.
+bool plan_phases(const ConvGeom &g, int dt, PhaseArgs *pa, bool any_rows)
 {
     memset(pa, 0, sizeof *pa);
     const int s = g.s, bk = gemm_bk(dt);
     if (s < 2 || s * s > kMaxPhases || s > g.kH || s > g.kW || g.H < s || g.W < s || g.O % bk != 0 ||
-        g.C < 64)
+        (g.C < 64 && !any_rows))
         return false;
     long long a_off = 0;
     int tiles = 0;
@@ -738,9 +739,16 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
         h->dgrad_nhwc = h->dgrad_nhwc && e[0] != '0';
     if (h->dgrad_nhwc)
         h->bwd_data_nhwc = plan_gemm(h->gd.O, h->gd.N, h->gd.Kc, dtype, dtype != D4R_F32);
-    h->dgrad_phased = plan_phases(g, dtype, &h->phases);
-    if (const char *e = getenv("D4R_DGRAD_PHASED"))  // experiments, tests: 0 = explicit data gradient
-        h->dgrad_phased = h->dgrad_phased && e[0] != '0';
+    {
+        // experiments, tests: D4R_DGRAD_PHASED=0 keeps the explicit data
+        // gradient; =force takes the phased one wherever it is correct,
+        // whatever the input channel count
+        const char *e = getenv("D4R_DGRAD_PHASED");
+        const bool force = e && !strcmp(e, "force");
+        h->dgrad_phased = plan_phases(g, dtype, &h->phases, force);
+        if (e && e[0] == '0')
+            h->dgrad_phased = false;
+    }
     h->pointwise = kH == 1 && kW == 1 && stride == 1 && padding == 0;
     if (const char *e = getenv("D4R_POINTWISE"))  // experiments, tests: 0 = im2col path
         h->pointwise = h->pointwise && e[0] != '0';

@@ -221,11 +221,20 @@ d4r_status d4r_conv_backward_data(d4r_conv_t h, const void *w, const void *dy,
  * then channel, so that every GEMM stage reads contiguous channel runs of
  * dy (16-byte loads straight into LDS) and the taps of one block reread
  * the same channels while they are cached;
- * otherwise the GEMM gathers im2col(dy) element by element.  1x1 stride-1
- * unpadded convolutions take their direct path, other shapes the explicit
- * path of d4r_conv_backward_data.  Same arguments, result equal up to
- * summation order; ws holds dy^T, the flipped filter and split-K partials,
- * and the col region is left untouched (reuse_col stays valid).
+ * otherwise the GEMM gathers im2col(dy) element by element.  For stride
+ * s >= 2 (s <= kH, kW, inH, inW; s*s <= 16; outC a multiple of 32 f32 / 64
+ * 16-bit; inC >= 64) dx splits into s*s output phases, the rows and columns
+ * with (h + p) mod s and (w + p) mod s fixed; each phase is a stride-1
+ * convolution of dy (read as NHWC) with a sub-filter of ceil(kH/s) x
+ * ceil(kW/s) taps of w, and all phases run in one GEMM launch.  With fewer
+ * input channels (AlexNet conv1's 3) the explicit path runs instead: its
+ * GEMM rows are inC*kH*kW, where the phases' would be inC (the environment
+ * switch D4R_DGRAD_PHASED=force takes the phased form there too; =0 never).
+ * 1x1 stride-1 unpadded convolutions take their direct path, other shapes
+ * the explicit path of d4r_conv_backward_data.  Same arguments, result
+ * equal up to summation order; ws holds dy^T, the flipped (or phase)
+ * filters and split-K partials, and the col region is left untouched
+ * (reuse_col stays valid).
  */
 d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w,
                                            const void *dy, float *dx, void *ws,

@@ -758,6 +758,30 @@ def test_dgrad_phased(t, dt, monkeypatch):
     _check_dgrad_implicit(sh, dt, ops, "explicit")
 
 
+# Layers with few input channels, where the planner keeps the explicit data
+# gradient (its GEMM rows are C*kH*kW) and D4R_DGRAD_PHASED=force takes the
+# phased one: AlexNet conv1's geometry (3 channels, 11x11, stride 4) at
+# batch 2, and small ragged cases (f32: dy channels a multiple of 32)
+DGRAD_PHASED_FORCED = [
+    (2, 3, 224, 224, 96, 11, 11, 4, 2),
+    (2, 3, 23, 21, 32, 5, 5, 2, 1),
+    (1, 5, 17, 19, 64, 7, 5, 3, 2),
+]
+
+
+@pytest.mark.parametrize("t", DGRAD_PHASED_FORCED, ids=str)
+def test_dgrad_phased_forced_few_channels(t, monkeypatch):
+    sh = _shape(t)
+    pl = _plan(sh, "f32")
+    assert d4r.d4r_conv_describe(pl.h)["dgrad_implicit"] == "explicit"
+    monkeypatch.setenv("D4R_DGRAD_PHASED", "force")
+    pl = _plan(sh, "f32")
+    d = d4r.d4r_conv_describe(pl.h)
+    assert d["dgrad_implicit"] == "phased" and int(d["dgrad_phases"]) == sh.stride ** 2, d
+    ops = wl.random_conv(sh, "f32", seed=sum(t) + 41)
+    _check_dgrad_implicit(sh, "f32", ops, "phased (forced)")
+
+
 def test_dgrad_phased_applies_to_the_workloads():
     # the 46x80 map's stride-2 layer takes it; AlexNet conv1 (3 input channels) does not
     c5 = wl.WORKLOADS["c5"].layers[2].shape
