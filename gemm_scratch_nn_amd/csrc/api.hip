@@ -991,9 +991,9 @@ d4r_status conv_forward(d4r_conv_t h, const void *x, const void *w, const float 
         {
             ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":fwd_x_w", 0.0,
                          2.0 * h->es * ((double)g.B * g.C * g.H * g.W + (double)g.O * g.Kc));
-            const TransposeJob jx{x, xt, g.C, g.H * g.W, g.B, 0, (uint32_t *)zero, 0};
-            const TransposeJob jw{w, wr, g.C, g.kH * g.kW, g.O, 0, nullptr, 0, gemm_bk(h->dt)};
-            hipError_t e = launch_transpose_pair(h->dt, jx, jw, s);
+            const TransposeJob jx{x, xt, g.C, g.H * g.W, g.B, (uint32_t *)zero, 0};
+            const FilterJob jw{w, wr, g.O, g.C, g.kH * g.kW, gemm_bk(h->dt), 0, nullptr, 0};
+            hipError_t e = launch_transpose_filter(h->dt, jx, jw, s);
             ps.done();
             D4R_LAUNCH(e, "input transpose and filter reorder");
         }
@@ -1098,9 +1098,9 @@ d4r_status dgrad_phased(d4r_conv_t h, const void *w, const void *dy, float *dx, 
     {
         ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":dgrad_dy", 0.0,
                      2.0 * h->es * (double)g.B * g.O * g.P);
-        const TransposeJob jdy{dy, gt, g.O, g.P, g.B, 0, (uint32_t *)zero, 0};
-        const TransposeJob none{nullptr, nullptr, 0, 0, 0, 0, nullptr, 0};
-        hipError_t e = launch_transpose_pair(h->dt, jdy, none, s);
+        const TransposeJob jdy{dy, gt, g.O, g.P, g.B, (uint32_t *)zero, 0};
+        const FilterJob none{nullptr, nullptr, 0, 0, 0, 1, 0, nullptr, 0};
+        hipError_t e = launch_transpose_filter(h->dt, jdy, none, s);
         ps.done();
         D4R_LAUNCH(e, "grad transpose");
     }
@@ -1215,9 +1215,9 @@ d4r_status d4r_conv_backward_data_implicit(d4r_conv_t h, const void *w, const vo
             // transposed with its taps reversed, clearing the zero page
             ProfScope ps(s, std::string("transpose_") + dt_name(h->dt) + ":dgrad_dy_w", 0.0,
                          2.0 * h->es * ((double)g.B * g.O * g.P + (double)g.O * g.Kc));
-            const TransposeJob jdy{dy, gt, g.O, g.P, g.B, 0, nullptr, 0};
-            const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0, gemm_bk(h->dt)};
-            hipError_t e = launch_transpose_pair(h->dt, jdy, jw, s);
+            const TransposeJob jdy{dy, gt, g.O, g.P, g.B, nullptr, 0};
+            const FilterJob jw{w, wf, g.O, g.C, g.kH * g.kW, gemm_bk(h->dt), 1, (uint32_t *)zero, 0};
+            hipError_t e = launch_transpose_filter(h->dt, jdy, jw, s);
             ps.done();
             D4R_LAUNCH(e, "grad transpose and filter flip");
         }
@@ -1338,7 +1338,7 @@ d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const v
         ProfScope ps(s, std::string("dy_prep_") + dt_name(h->dt) + ":bwd", 0.0,
                      3.0 * h->es * (double)g.B * g.O * g.P + 2.0 * h->es * (double)g.O * g.Kc);
         const DyPrep a{dy, gt, G, bias_part, g.B, g.O, g.P, 0, 0};
-        const TransposeJob jw{w, wf, g.O, g.Kc, 1, g.kH * g.kW, (uint32_t *)zero, 0, gemm_bk(h->dt)};
+        const FilterJob jw{w, wf, g.O, g.C, g.kH * g.kW, gemm_bk(h->dt), 1, (uint32_t *)zero, 0};
         hipError_t e = launch_dy_prep(h->dt, a, jw, s);
         ps.done();
         D4R_LAUNCH(e, "dy preparation");

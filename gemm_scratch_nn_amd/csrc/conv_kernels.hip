@@ -635,19 +635,10 @@ __global__ __launch_bounds__(NT) void grad_reshape_kernel(const T *__restrict__ 
 // consecutive elements of an output row; a thread's 16 loads are all issued
 // before the first is used.
 // ---------------------------------------------------------------------------
-// flip > 0 (the data gradient's filter for an NHWC dy): the columns come in
-// groups of flip taps and output row c takes input column c with its tap
-// reversed inside the group; block 0 also clears 256 bytes at `zero`.
-// kb > 0 (filters for the NHWC loaders, whose k runs over channel blocks of
-// kb, then taps, then the channel inside the block): with groups of gs =
-// flip (or Cc) output rows, element (row c, column r) goes to
-// ((c / gs)*R + (r / kb)*kb)*gs + (c % gs)*kb + r % kb instead of c*R + r.
-// Needs R % kb == 0.
 template <typename T>
 __device__ __forceinline__ void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int R, int Cc,
-                                               int flip, int kb, int bx, int by, int bz)
+                                               int bx, int by, int bz, T (*tile)[65])
 {
-    __shared__ T tile[64][65];
     const long long base = (long long)bz * R * Cc;
     const int r0 = by * 64, c0 = bx * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -664,54 +655,103 @@ __device__ __forceinline__ void transpose_tile(const T *__restrict__ in, T *__re
         tile[ty + i * (NT / 64)][tx] = v[i];
     __syncthreads();
     const bool rin = r0 + tx < R;
-    const int r = r0 + tx;
-    if (kb > 0) {
-        // gs = flip (or Cc, one group); the group of c and its flipped tap
-        // come from one division
-        const int gs = flip > 0 ? flip : Cc;
-        const int rb = r / kb;
-        const long long rpart = (long long)rb * kb * gs + (r - rb * kb);
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const int c = c0 + ty + i * (NT / 64);
-            const int q = flip > 0 ? c / flip : 0;
-            const int t = flip > 0 ? flip - 1 - (c - q * flip) : c;
-            if (rin && c < Cc)
-                out[base + (long long)q * gs * R + (long long)t * kb + rpart] = tile[tx][ty + i * (NT / 64)];
-        }
-        return;
-    }
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int c = c0 + ty + i * (NT / 64);
-        const int oc = flip > 0 ? c - c % flip + (flip - 1 - c % flip) : c;
         if (rin && c < Cc)
-            out[base + (long long)oc * R + r] = tile[tx][ty + i * (NT / 64)];
+            out[base + (long long)c * R + r0 + tx] = tile[tx][ty + i * (NT / 64)];
     }
 }
 
 template <typename T>
 __global__ __launch_bounds__(NT) void transpose_kernel(const T *__restrict__ in, T *__restrict__ out,
-                                                       int R, int Cc, int flip, uint32_t *__restrict__ zero)
+                                                       int R, int Cc)
 {
-    if (zero && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
-        zero[threadIdx.x] = 0u;
-    transpose_tile<T>(in, out, R, Cc, flip, 0, blockIdx.x, blockIdx.y, blockIdx.z);
+    __shared__ T tile[64][65];
+    transpose_tile<T>(in, out, R, Cc, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
-// Two independent batched transposes in one launch: blocks [0, a.blocks)
-// run job a, the rest job b (the choice is uniform per block).
+// A filter job (FilterJob).  Forward order (flip 0): one 16-byte output
+// vector per thread, in output order; its elements are w[o][c..c+VW-1][tap],
+// taps apart, so a wavefront reads one contiguous stretch of w.  Data
+// gradient order (flip 1): w viewed as O x C*taps is transposed through a
+// 64x64 LDS tile (rows o, 64 consecutive (c, tap) columns: 128-byte row
+// reads), and element (o, c, tap) is stored at out[c][ob][taps-1-tap][oi]
+// (o = ob*kb + oi): 64 consecutive o of a tile are one contiguous run when
+// kb = 64, two when kb = 32.  Block 0 clears the zero page.
 template <typename T>
-__global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob a, TransposeJob b)
+__device__ __forceinline__ void filter_job(const FilterJob &f, int block, T (*tile)[65])
 {
-    const bool first = (int)blockIdx.x < a.blocks;
-    const TransposeJob &j = first ? a : b;
-    const int local = first ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
-    const int gx = (j.Cc + 63) / 64, gy = (j.R + 63) / 64;
-    if (j.zero && local == 0 && threadIdx.x < 64)
-        j.zero[threadIdx.x] = 0u;
-    transpose_tile<T>((const T *)j.in, (T *)j.out, j.R, j.Cc, j.flip, j.kb, local % gx, (local / gx) % gy,
-                      local / (gx * gy));
+    using V = typename Vec16<T>::type;
+    constexpr int VW = Vec16<T>::N;
+    if (f.zero && block == 0 && threadIdx.x < 64)
+        f.zero[threadIdx.x] = 0u;
+    const T *w = (const T *)f.in;
+    if (!f.flip) {
+        const long long q = (long long)block * NT + threadIdx.x;
+        const long long total = (long long)f.O * f.C * f.taps / VW;
+        if (q >= total)
+            return;
+        const long long e0 = q * VW;
+        const int i0 = (int)(e0 % f.kb);  // channel inside the block (first of VW)
+        long long r = e0 / f.kb;
+        const int t = (int)(r % f.taps);
+        r /= f.taps;
+        const int cbn = f.C / f.kb;
+        const int cb = (int)(r % cbn);
+        const long long o = r / cbn;
+        const T *src = w + (o * f.C + (long long)cb * f.kb + i0) * f.taps + t;
+        V v;
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+            v[e] = src[(long long)e * f.taps];
+        *(V *)((T *)f.out + e0) = v;
+        return;
+    }
+    const int R = f.O, Cc = f.C * f.taps;
+    const int gx = (Cc + 63) / 64;
+    const int r0 = (block / gx) * 64, c0 = (block % gx) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    constexpr int ROWS = 64 / (NT / 64);
+    T v[ROWS];
+    const bool cin = c0 + tx < Cc;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = r0 + ty + i * (NT / 64);
+        v[i] = (cin && r < R) ? w[(long long)r * Cc + c0 + tx] : (T)0;
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+        tile[ty + i * (NT / 64)][tx] = v[i];
+    __syncthreads();
+    const int o = r0 + tx;  // the output's inner index runs over o
+    const int ob = o / f.kb, oi = o - ob * f.kb;
+    const long long opart = (long long)ob * f.kb * f.taps + oi;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int k = c0 + ty + i * (NT / 64);  // (c, tap) column of w
+        const int c = k / f.taps, t = f.taps - 1 - (k - c * f.taps);
+        if (o < R && k < Cc)
+            ((T *)f.out)[(long long)c * R * f.taps + (long long)t * f.kb + opart] = tile[tx][ty + i * (NT / 64)];
+    }
+}
+
+// A data transpose and a filter job in one launch: blocks [0, a.blocks) run
+// the transpose, the rest the filter job (the choice is uniform per block).
+template <typename T>
+__global__ __launch_bounds__(NT) void transpose_filter_kernel(TransposeJob a, FilterJob f)
+{
+    __shared__ T tile[64][65];  // one tile for either job
+    if ((int)blockIdx.x >= a.blocks) {
+        filter_job<T>(f, (int)blockIdx.x - a.blocks, tile);
+        return;
+    }
+    const int local = (int)blockIdx.x;
+    const int gx = (a.Cc + 63) / 64, gy = (a.R + 63) / 64;
+    if (a.zero && local == 0 && threadIdx.x < 64)
+        a.zero[threadIdx.x] = 0u;
+    transpose_tile<T>((const T *)a.in, (T *)a.out, a.R, a.Cc, local % gx, (local / gx) % gy, local / (gx * gy),
+                      tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -721,22 +761,17 @@ __global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob a, Transpos
 //   * transposed as Gt[b][pix][o] (the NHWC data gradient's operand),
 //   * and, when bias_part is set, the tile row sums (one wavefront per row,
 //     fixed butterfly order) as bias_part[o*parts + b*ceil(P/64) + tile].
-// Blocks past the tiles run the filter job w (transposed with its taps
-// reversed, zero page cleared), as transpose2_kernel does.
+// Blocks past the tiles run the filter job w, as transpose_filter_kernel
+// does.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(NT) void dy_prep_kernel(DyPrep a, TransposeJob w)
+__global__ __launch_bounds__(NT) void dy_prep_kernel(DyPrep a, FilterJob w)
 {
+    __shared__ T tile[64][65];  // one tile for either job
     if ((int)blockIdx.x >= a.blocks) {
-        const int local = (int)blockIdx.x - a.blocks;
-        const int gx = (w.Cc + 63) / 64, gy = (w.R + 63) / 64;
-        if (w.zero && local == 0 && threadIdx.x < 64)
-            w.zero[threadIdx.x] = 0u;
-        transpose_tile<T>((const T *)w.in, (T *)w.out, w.R, w.Cc, w.flip, w.kb, local % gx, (local / gx) % gy,
-                          local / (gx * gy));
+        filter_job<T>(w, (int)blockIdx.x - a.blocks, tile);
         return;
     }
-    __shared__ T tile[64][65];
     const int gx = (a.P + 63) / 64, gy = (a.O + 63) / 64;
     const int bx = (int)blockIdx.x % gx, by = ((int)blockIdx.x / gx) % gy, b = (int)blockIdx.x / (gx * gy);
     const int p0 = bx * 64, o0 = by * 64;
@@ -1309,10 +1344,10 @@ hipError_t launch_transpose(int dt, int batch, int R, int Cc, const void *in, vo
     dim3 grid((Cc + 63) / 64, (R + 63) / 64, batch);
     if (dt == DT_F32)
         hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(NT), 0, s, (const uint32_t *)in,
-                           (uint32_t *)out, R, Cc, 0, nullptr);
+                           (uint32_t *)out, R, Cc);
     else
         hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(NT), 0, s, (const uint16_t *)in,
-                           (uint16_t *)out, R, Cc, 0, nullptr);
+                           (uint16_t *)out, R, Cc);
     return hipGetLastError();
 }
 
@@ -1367,15 +1402,26 @@ hipError_t launch_flip_filter(int dt, const ConvGeom &g, const void *w, void *wf
     return hipGetLastError();
 }
 
-// wd[c][u][v][o] = w[o][c][kH-1-u][kW-1-v]: W (O x Kc) transposed through
-// LDS tiles, each output row's tap reversed (rows come in groups of kH*kW
-// taps); plus the zero page.
+// partial bias sums per channel of the one-pass dy preparation: one per
+// image and 64-pixel tile
 int dy_prep_bias_parts(const ConvGeom &g) { return g.B * ((g.P + 63) / 64); }
 
-hipError_t launch_dy_prep(int dt, DyPrep a, TransposeJob w, hipStream_t s)
+namespace {
+
+long long filter_blocks(int dt, const FilterJob &f)
+{
+    if (f.flip)  // 64x64 tiles of w viewed as O x C*taps
+        return (long long)((f.C * f.taps + 63) / 64) * ((f.O + 63) / 64);
+    const long long vw = dt == DT_F32 ? 4 : 8;
+    return ((long long)f.O * f.C * f.taps / vw + NT - 1) / NT;
+}
+
+}  // namespace
+
+hipError_t launch_dy_prep(int dt, DyPrep a, FilterJob w, hipStream_t s)
 {
     const long long na = (long long)((a.P + 63) / 64) * ((a.O + 63) / 64) * a.B;
-    const long long nw = (long long)((w.Cc + 63) / 64) * ((w.R + 63) / 64) * w.batch;
+    const long long nw = filter_blocks(dt, w);
     if (na + nw > INT32_MAX)
         return hipErrorInvalidValue;
     a.blocks = (int)na;
@@ -1395,20 +1441,17 @@ hipError_t launch_bias_sum(const BiasSum &bs, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s)
+hipError_t launch_transpose_filter(int dt, TransposeJob a, FilterJob f, hipStream_t s)
 {
-    auto blocks = [](const TransposeJob &j) {
-        return (long long)((j.Cc + 63) / 64) * ((j.R + 63) / 64) * j.batch;
-    };
-    const long long na = blocks(a), nb = blocks(b);
-    if (na + nb > INT32_MAX)
+    const long long na = (long long)((a.Cc + 63) / 64) * ((a.R + 63) / 64) * a.batch;
+    const long long nf = filter_blocks(dt, f);
+    if (na + nf > INT32_MAX)
         return hipErrorInvalidValue;
     a.blocks = (int)na;
-    b.blocks = (int)nb;
     if (dt == DT_F32)
-        hipLaunchKernelGGL(transpose2_kernel<uint32_t>, dim3((unsigned)(na + nb)), dim3(NT), 0, s, a, b);
+        hipLaunchKernelGGL(transpose_filter_kernel<uint32_t>, dim3((unsigned)(na + nf)), dim3(NT), 0, s, a, f);
     else
-        hipLaunchKernelGGL(transpose2_kernel<uint16_t>, dim3((unsigned)(na + nb)), dim3(NT), 0, s, a, b);
+        hipLaunchKernelGGL(transpose_filter_kernel<uint16_t>, dim3((unsigned)(na + nf)), dim3(NT), 0, s, a, f);
     return hipGetLastError();
 }
 

@@ -298,22 +298,34 @@ struct BiasSum {
     int O, parts;
 };
 
-// One batched transpose out[z][c'][r] = in[z][r][c] (batch z, R x Cc): with
-// flip > 0 the columns come in groups of flip taps and c' reverses the tap
-// inside its group; zero, when set, gets 256 bytes cleared.  `blocks` is
-// filled in by launch_transpose_pair.
+// One batched transpose out[z][c][r] = in[z][r][c] (batch z, R x Cc); zero,
+// when set, gets 256 bytes cleared.  `blocks` is filled in by the launcher.
 struct TransposeJob {
     const void *in;
     void *out;
-    int R, Cc, batch, flip;
+    int R, Cc, batch;
     uint32_t *zero;
     int blocks;
-    int kb;  // > 0: output rows interleaved in blocks of kb (see transpose_tile)
 };
 
-// jobs a and b in one launch (each 64x64 tile a block; the jobs must not
-// overlap in memory)
-hipError_t launch_transpose_pair(int dt, TransposeJob a, TransposeJob b, hipStream_t s);
+// The filter w (O x C x taps, taps = kH*kW) written in the NHWC loader's k
+// order, blocks of kb channels outermost, then tap, then the channel inside
+// the block: flip = 0 (forward) out[o][cb][tap][ci] = w[o][cb*kb+ci][tap];
+// flip = 1 (data gradient, taps reversed) out[c][ob][t][oi] =
+// w[ob*kb+oi][c][taps-1-t].  Needs C (flip 0) or O (flip 1) a multiple of
+// kb, kb a multiple of the 16-byte vector.  zero, when set, gets 256 bytes
+// cleared.  `blocks` is filled in by the launcher.
+struct FilterJob {
+    const void *in;
+    void *out;
+    int O, C, taps, kb, flip;
+    uint32_t *zero;
+    int blocks;
+};
+
+// a data transpose and a filter job in one launch (either may be empty: no
+// rows; they must not overlap in memory)
+hipError_t launch_transpose_filter(int dt, TransposeJob a, FilterJob f, hipStream_t s);
 
 // dy (B x O x P) read once, written as G[o][b*P + pix] and Gt[b][pix][o],
 // with the bias gradient's partial sums (dy_prep_bias_parts(g) per channel)
@@ -326,7 +338,7 @@ struct DyPrep {
     int B, O, P, dt, blocks;
 };
 int dy_prep_bias_parts(const ConvGeom &g);
-hipError_t launch_dy_prep(int dt, DyPrep a, TransposeJob w, hipStream_t s);
+hipError_t launch_dy_prep(int dt, DyPrep a, FilterJob w, hipStream_t s);
 
 // the BiasSum on its own (wavefront per channel), and the block count it
 // takes as extra blocks of a reduction
