@@ -242,8 +242,10 @@ def bench_lenet(args) -> int:
             step()
         else:
             graph.replay()
+    t_enqueued = time.perf_counter()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    host_ms = (t_enqueued - t0) * 1e3 / args.steps
     import gemm_scratch_nn_amd as d4r
     d4r.d4r_profile_reset()
     d4r.d4r_profile_enable(True)
@@ -296,6 +298,7 @@ def bench_lenet(args) -> int:
         "config": {"workload": f"{desc}, softmax-CE, SGD lr {lr} clip {clip}",
                    "batch": B, "hip_graph": bool(args.graph)},
         "kernel_busy_ms_per_step": busy_ms,
+        "host_enqueue_ms_per_step": host_ms,
         "launches_per_step": sum(v["launches"] for v in by_kernel.values()) / args.steps,
         "roofline": roofline_of(by_kernel, dom, MFMA_PEAK["f32"]),
         "cpu_baseline": cpu,
@@ -513,8 +516,12 @@ def bench_conv(args, key: str, dtype: str, steps: int, warmup: int, rotate: int,
             step()
         else:
             graph.replay()
+    t_enqueued = time.perf_counter()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # host time to enqueue the K steps (launches or graph replays): when it
+    # is close to the step time, the host, not the GPU, sets the pace
+    host_ms = (t_enqueued - t0) * 1e3 / steps
 
     # Kernel timing: the same K steps again, eager and on one stream (so no
     # kernel shares the GPU with another), with the library's HIP event pair
@@ -629,6 +636,7 @@ def bench_conv(args, key: str, dtype: str, steps: int, warmup: int, rotate: int,
                    "rotate": rotate, "hip_graph": bool(graph_mode),
                    "step_gflop": step_flops / 1e9},
         "pct_mfma_peak": value / peak,
+        "host_enqueue_ms_per_step": host_ms,
     }
     line.update(gemm_summary(by_kernel, peak))
     line["im2col"] = stage_of(by_kernel, "im2col")
