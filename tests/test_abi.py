@@ -382,11 +382,26 @@ def test_describe_reports_the_plan(monkeypatch):
         assert d["dtype"] == "bf16" and d["im2col_bb"] == "1" and d["col2im_bb"] == "1"
     finally:
         d4r.d4r_conv_destroy(h)
-    # AlexNet conv1: a 227x227 window is too large for the LDS col2im
+    # AlexNet conv1: a 227x227 window is too large for the LDS col2im; the
+    # data gradient stays explicit (3 input channels) unless the phased form
+    # is forced, which then runs all 16 phases
     h = d4r.d4r_conv_create(32, 3, 224, 224, 11, 11, 4, 2, 96, D4R_F32)
     try:
         d = d4r.d4r_conv_describe(h)
         assert d["col2im"] == "gather" and d["dgrad_implicit"] == "explicit"
+    finally:
+        d4r.d4r_conv_destroy(h)
+    monkeypatch.setenv("D4R_DGRAD_PHASED", "force")
+    h = d4r.d4r_conv_create(32, 3, 224, 224, 11, 11, 4, 2, 96, D4R_F32)
+    try:
+        d = d4r.d4r_conv_describe(h)
+        assert d["dgrad_implicit"] == "phased" and d["dgrad_phases"] == "16"
+    finally:
+        d4r.d4r_conv_destroy(h)
+    monkeypatch.setenv("D4R_DGRAD_PHASED", "0")
+    h = d4r.d4r_conv_create(4, 256, 46, 80, 3, 3, 2, 1, 128, D4R_F32)
+    try:
+        assert d4r.d4r_conv_describe(h)["dgrad_implicit"] == "explicit"
     finally:
         d4r.d4r_conv_destroy(h)
 
