@@ -712,6 +712,41 @@ def hbm_reference(reps: int = 10) -> dict:
     return out
 
 
+def mfma_reference(reps: int = 5) -> dict:
+    """The MFMA rate of the library's ceiling kernel (d4r_mfma_ceiling: MFMAs
+    on register-resident random operands, no loads) for each dtype, in
+    TFLOP/s: what the GPU sustains at the clock it holds under a full MFMA
+    load, the reference beside the GEMM rates (the roofline keeps the
+    published peak)."""
+    import torch
+
+    import gemm_scratch_nn_amd as d4r
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = {"kernel": "d4r_mfma_ceiling: 1024 workgroups x 8 wavefronts, 4 x 2 accumulators of 32 x 32 each, "
+                     "random operands (N(0,1)) read once"}
+    blocks = 1024
+    for dt, code, tdt, per_lane, iters in (("f32", d4r.D4R_F32, torch.float32, 1, 800),
+                                           ("bf16", d4r.D4R_BF16, torch.bfloat16, 8, 1500),
+                                           ("f16", d4r.D4R_F16, torch.float16, 8, 1500)):
+        src = torch.randn(6 * 64 * per_lane, generator=g).to(tdt).cuda()
+        res = torch.empty(blocks * 8, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            d4r.d4r_mfma_ceiling(code, src, res, blocks, iters)
+        torch.cuda.synchronize()
+        d4r.d4r_profile_reset()
+        d4r.d4r_profile_enable(True)
+        for _ in range(reps):
+            d4r.d4r_mfma_ceiling(code, src, res, blocks, iters)
+        torch.cuda.synchronize()
+        d4r.d4r_profile_enable(False)
+        st = d4r.d4r_profile_read()
+        d4r.d4r_profile_reset()
+        ms = sum(r["ms"] for r in st)
+        out[f"{dt}_TFLOPs"] = sum(r["flops"] for r in st) / (ms * 1e-3) / 1e12
+        out[f"{dt}_frac_of_peak"] = out[f"{dt}_TFLOPs"] / MFMA_PEAK[dt]
+    return out
+
+
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
@@ -741,6 +776,9 @@ def main() -> int:
                         "pct_mfma_peak": cl["pct_mfma_peak"], "im2col": cl["im2col"]}
         ref = hbm_reference()
         line["hbm_reference"] = ref
+        mref = mfma_reference()
+        line["mfma_reference"] = mref
+        line["gemm_frac_of_mfma_ceiling"] = line["gemm_TFLOPs"] / mref[f"{dtype}_TFLOPs"]
 
         def rel(stage):
             if stage and "GBps" in stage:
@@ -762,6 +800,9 @@ def main() -> int:
                     "gemm_frac_mfma", "gemm_frac_attainable", "im2col", "col2im", "layers", "roofline")
             entry = {"workload": sl["config"]["workload"], "steps": sec_steps}
             entry.update({k: sl[k] for k in keep if k in sl})
+            mref = line.get("mfma_reference")
+            if mref and entry.get("gemm_TFLOPs"):
+                entry["gemm_frac_of_mfma_ceiling"] = entry["gemm_TFLOPs"] / mref[f"{dt}_TFLOPs"]
             ref = line.get("hbm_reference")
             if ref:
                 for st in [entry.get("im2col"), entry.get("col2im")] + \

@@ -115,6 +115,7 @@ _c = {
     "d4r_grad_accum": _sig("d4r_grad_accum", [_vp, _vp, _ll, _vp]),
     "d4r_stream_copy": _sig("d4r_stream_copy", [_vp, _vp, _sz, _vp]),
     "d4r_stream_fill": _sig("d4r_stream_fill", [_vp, ctypes.c_uint, _sz, _vp]),
+    "d4r_mfma_ceiling": _sig("d4r_mfma_ceiling", [ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp]),
     "d4r_profile_enable": _sig("d4r_profile_enable", [_i]),
     "d4r_profile_reset": _sig("d4r_profile_reset", []),
     "d4r_status_string": _sig("d4r_status_string", [_i], ctypes.c_char_p),
@@ -387,6 +388,10 @@ def d4r_stream_copy(dst, src, nbytes, stream=None) -> None:
 def d4r_stream_fill(dst, value, nbytes, stream=None) -> None:
     _check("d4r_stream_fill", _c["d4r_stream_fill"](_ptr(dst), int(value) & 0xFFFFFFFF, nbytes,
                                                     _stream(stream)))
+
+
+def d4r_mfma_ceiling(dtype: int, src, out, blocks: int, iters: int, stream=None) -> None:
+    _check("d4r_mfma_ceiling", _c["d4r_mfma_ceiling"](dtype, _ptr(src), _ptr(out), blocks, iters, _stream(stream)))
 
 
 def d4r_profile_enable(on: bool) -> None:

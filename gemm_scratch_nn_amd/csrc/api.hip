@@ -1795,6 +1795,29 @@ d4r_status d4r_stream_fill(void *dst, unsigned int value, size_t bytes, void *hi
                     [&] { return launch_stream_fill(dst, value, bytes, s); });
 }
 
+d4r_status d4r_mfma_ceiling(d4r_dtype dtype, const void *src, float *out, int blocks, int iters,
+                            void *hip_stream)
+{
+    if (!valid_dtype(dtype))
+        return fail(D4R_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (blocks < 1 || blocks > (1 << 20) || iters < 1)
+        return fail(D4R_ERR_INVALID_ARG, "blocks must be in [1, 2^20] and iters >= 1");
+    D4R_TRY(check_tensor(src, "src"));
+    D4R_TRY(check_tensor(out, "out"));
+    if (overlaps(src, dtype == D4R_F32 ? 6 * 64 * 4 : 6 * 64 * 16, out, (size_t)blocks * 8 * sizeof(float)))
+        return fail(D4R_ERR_INVALID_ARG, "out overlaps src");
+    // 2*32*32*k flops per MFMA (k = 2 for f32, 16 for 16-bit), 8 per
+    // iteration and wavefront, 8 wavefronts per workgroup
+    const double k = dtype == D4R_F32 ? 2.0 : 16.0;
+    const double flops = 2.0 * 32 * 32 * k * 8.0 * 8.0 * (double)iters * blocks;
+    hipStream_t s = (hipStream_t)hip_stream;
+    ProfScope ps(s, std::string("mfma_ceiling_") + dt_name(dtype), flops, 0.0);
+    hipError_t e = launch_mfma_ceiling(dtype, src, out, blocks, iters, s);
+    ps.done();
+    D4R_LAUNCH(e, "MFMA ceiling");
+    return ok();
+}
+
 d4r_status d4r_profile_enable(int on)
 {
     Profiler &P = prof();

@@ -355,6 +355,10 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N,
 // 16-byte aligned pointers.
 hipError_t launch_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_stream_fill(void *dst, uint32_t value, size_t bytes, hipStream_t s);
+// MFMA ceiling (stream_kernels.hip): blocks x 8 wavefronts, iters x 8 MFMAs
+// each; src holds 6 x 64 16-byte fragments (16-bit) or 6 x 64 floats (f32);
+// out gets blocks * 8 floats
+hipError_t launch_mfma_ceiling(int dt, const void *src, float *out, int blocks, int iters, hipStream_t s);
 
 // The rest of a training step (f32; train_kernels.hip).  Elementwise
 // kernels take 16-byte aligned pointers; n may be 0.

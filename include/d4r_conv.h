@@ -477,6 +477,24 @@ typedef struct {
 d4r_status d4r_stream_copy(void *dst, const void *src, size_t bytes, void *hip_stream);
 d4r_status d4r_stream_fill(void *dst, unsigned int value, size_t bytes, void *hip_stream);
 
+/*
+ * Measurement aid (not a step of the method): the MFMA rate this GPU
+ * sustains with no data movement, the reference the bench reports beside
+ * the GEMMs (the published dense peak assumes a clock the chip does not
+ * hold under a full MFMA load).  blocks workgroups of eight wavefronts each
+ * run iters iterations of eight MFMAs -- the dtype's GEMM instruction,
+ * v_mfma_f32_32x32x16_{f16,bf16} or v_mfma_f32_32x32x2_f32 -- on operand
+ * fragments read once from src (6 x 64 x 16 bytes for f16/bf16, 6 x 64
+ * floats for f32, lane-major), for 2*32*32*k*64*iters*blocks flops (k = 16,
+ * or 2 for f32).  Lane 0 of each wavefront writes the sum of its 8 x 16
+ * accumulator elements to out (blocks * 8 floats): with every operand 1.0
+ * that is 128 * k * iters.  16-byte aligned device pointers that do not
+ * overlap.  Errors: D4R_ERR_INVALID_ARG (dtype, blocks outside [1, 2^20],
+ * iters < 1, pointers).
+ */
+d4r_status d4r_mfma_ceiling(d4r_dtype dtype, const void *src, float *out, int blocks, int iters,
+                            void *hip_stream);
+
 /* summed algorithmic bytes */
 } d4r_kernel_stat;
 

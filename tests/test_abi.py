@@ -455,3 +455,17 @@ def test_stream_reference_argument_errors():
         assert e.value.status == INVALID
     d4r.d4r_stream_copy(FAKE, FAKE, 0, 0)    # nothing to do: no launch
     d4r.d4r_stream_fill(FAKE, 0, 0, 0)
+
+
+def test_mfma_ceiling_argument_errors():
+    far = FAKE + (1 << 20)
+    for call in (lambda: d4r.d4r_mfma_ceiling(7, FAKE, far, 1, 1, 0),             # dtype
+                 lambda: d4r.d4r_mfma_ceiling(D4R_F32, FAKE, far, 0, 1, 0),       # blocks
+                 lambda: d4r.d4r_mfma_ceiling(D4R_F32, FAKE, far, (1 << 20) + 1, 1, 0),
+                 lambda: d4r.d4r_mfma_ceiling(D4R_BF16, FAKE, far, 1, 0, 0),      # iters
+                 lambda: d4r.d4r_mfma_ceiling(D4R_BF16, None, far, 1, 1, 0),
+                 lambda: d4r.d4r_mfma_ceiling(D4R_BF16, FAKE, MISALIGNED, 1, 1, 0),
+                 lambda: d4r.d4r_mfma_ceiling(D4R_BF16, FAKE, FAKE + 64, 1, 1, 0)):  # out overlaps src
+        with pytest.raises(D4RError) as e:
+            call()
+        assert e.value.status == INVALID

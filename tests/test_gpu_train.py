@@ -256,3 +256,20 @@ def test_stream_reference_kernels(n):
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     assert bool(torch.all(fill == torch.tensor(0xDEADBEEF, dtype=torch.int64).to(torch.int32).item()))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_mfma_ceiling_closed_form(dt):
+    # every operand 1.0: each MFMA adds k (2 for f32, 16 for f16/bf16) to every
+    # accumulator element, so each wavefront's sum of its 8 x 16 elements is
+    # 128 * k * iters, exactly
+    code = {"f32": d4r.D4R_F32, "f16": d4r.D4R_F16, "bf16": d4r.D4R_BF16}[dt]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    per_lane = 1 if dt == "f32" else 8
+    src = torch.ones(6 * 64 * per_lane, dtype=tdt, device="cuda")
+    blocks, iters = 37, 100
+    out = torch.full((blocks * 8,), float("nan"), dtype=torch.float32, device="cuda")
+    d4r.d4r_mfma_ceiling(code, src, out, blocks, iters)
+    torch.cuda.synchronize()
+    k = 2 if dt == "f32" else 16
+    assert bool(torch.all(out == 128.0 * k * iters)), out[:8]
