@@ -83,7 +83,12 @@ extern "C" {
 typedef enum {
     D4R_F32 = 0,  /* IEEE binary32 */
     D4R_F16 = 1,  /* IEEE binary16, float32 accumulation */
-    D4R_BF16 = 2  /* bfloat16, float32 accumulation */
+    D4R_BF16 = 2, /* bfloat16, float32 accumulation */
+    /* Not a dtype.  It widens the type's range of values to every int, so
+     * that an unknown value passed in is a defined value the argument
+     * checks report (D4R_ERR_INVALID_ARG) rather than undefined behaviour
+     * in the library's C++. */
+    D4R_DTYPE_INT_RANGE = -2147483647 - 1
 } d4r_dtype;
 
 typedef enum {
@@ -466,7 +471,14 @@ typedef struct {
     int launches;
     double ms;     /* summed event-to-event time of all launches */
     double flops;  /* summed algorithmic flops (0 for data movement) */
-    double bytes;  /*
+    double bytes;  /* summed algorithmic bytes */
+} d4r_kernel_stat;
+
+d4r_status d4r_profile_enable(int on);
+d4r_status d4r_profile_reset(void);
+d4r_status d4r_profile_read(d4r_kernel_stat *out, int max, int *count);
+
+/*
  * Measurement aids (not steps of the method): plain streaming kernels whose
  * rates are the attainable HBM reference the bench reports beside the
  * HBM-bound steps.  d4r_stream_copy: dst[i] = src[i] over `bytes` (read +
@@ -494,13 +506,6 @@ d4r_status d4r_stream_fill(void *dst, unsigned int value, size_t bytes, void *hi
  */
 d4r_status d4r_mfma_ceiling(d4r_dtype dtype, const void *src, float *out, int blocks, int iters,
                             void *hip_stream);
-
-/* summed algorithmic bytes */
-} d4r_kernel_stat;
-
-d4r_status d4r_profile_enable(int on);
-d4r_status d4r_profile_reset(void);
-d4r_status d4r_profile_read(d4r_kernel_stat *out, int max, int *count);
 
 /* Static string naming a status code. */
 const char *d4r_status_string(d4r_status s);
