@@ -445,6 +445,12 @@ struct d4r_conv {
     // d4r_conv_backward prepares dy for both gradient GEMMs in one pass
     // (NHWC data gradient and a copied G for the filter gradient)
     bool fused_bwd;
+    // f32 layers whose data gradient is explicit (dcol + col2im): the
+    // combined backward reshapes dy once into G (with the bias partials),
+    // which the data-gradient GEMM reads row-contiguous and the filter
+    // gradient k-contiguous; fx_wt: the data gradient reads a transposed
+    // copy of W (k-contiguous) instead of W row-contiguous
+    bool fused_explicit, fx_wt;
     // implicit forward from x read as NHWC (stride 1, whole GEMM stages of
     // input channels): x transposed to xt[b][h][w][c], the filter reordered
     // to wr[o][cb][u][v][ci] (c = cb*BK + ci); the loader of the NHWC data
@@ -780,16 +786,37 @@ d4r_status d4r_conv_create(d4r_conv_t *out, int batch, int inC, int inH, int inW
 
     choose_grad_paths(h);
     h->fused_bwd = h->dgrad_nhwc && h->wgrad == GP_COPY && !h->pointwise;
+    // One reshape pass over dy in place of the in-place loaders' single-
+    // element gathers (or of two copies, transposed for the data gradient
+    // and reshaped for the filter gradient).  Measured on AlexNet conv1 f32
+    // (O = 96, batch 32): data-gradient GEMM 111 -> 88 us (W read through a
+    // 5 us transposed copy; 97 us reading W row-contiguous), filter gradient
+    // 80 -> 72 us, no separate 11 us bias pass, for one 19 us reshape: step
+    // 0.416 -> 0.399 ms.  Layers with few output
+    // channels (LeNet's 6 and 16) keep the in-place loaders: their GEMMs are
+    // short and the step is launch-bound.  The 16-bit data gradient keeps its
+    // transposed copy: with both operands k-contiguous it runs on the
+    // direct-to-LDS kernel.  D4R_FUSED_EXPLICIT=0|1 overrides (experiments,
+    // tests; 1 still needs an explicit f32 data gradient).
+    {
+        const bool fits = dtype == D4R_F32 && !h->dgrad_phased && !h->dgrad_impl && !h->pointwise;
+        h->fused_explicit = fits && outC >= 32;
+        if (const char *e = getenv("D4R_FUSED_EXPLICIT"))
+            h->fused_explicit = fits && e[0] == '1';
+        h->fx_wt = true;
+        if (const char *e = getenv("D4R_FX_WT"))  // experiments, tests: 0 = W row-contiguous
+            h->fx_wt = e[0] != '0';
+    }
     h->col_bytes = (size_t)col_el * h->es;
     size_t off = align_up(h->col_bytes);
     h->off_g = off;
-    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE)
+    if (h->dgrad != GP_INPLACE || h->wgrad != GP_INPLACE || h->fused_explicit)
         off += align_up((size_t)y_el * h->es);
     h->off_gt = off;
     if (h->dgrad_nhwc || h->dgrad_phased)
         off += align_up((size_t)y_el * h->es);
     h->off_wt = off;
-    if (h->dgrad_wt)
+    if (h->dgrad_wt || (h->fused_explicit && h->fx_wt))
         off += align_up((size_t)w_el * h->es);
     h->off_wflip = off;
     if (h->dgrad_impl || h->dgrad_phased)
@@ -895,7 +922,9 @@ d4r_status d4r_conv_describe(d4r_conv_t h, char *buf, size_t cap, size_t *needed
         s += " dgrad_gathered=" + plan_text(h->bwd_data_impl);
     s += std::string(" dy_dgrad=") + (h->dgrad == GP_INPLACE ? "inplace" : "copy") +
          " dy_wgrad=" + (h->wgrad == GP_INPLACE ? "inplace" : "copy") + " dgrad_wt=" + (h->dgrad_wt ? "1" : "0") +
-         " fused_backward=" + (h->fused_bwd ? "1" : "0") + " workspace=" + std::to_string(h->ws_bytes);
+         " fused_backward=" + (h->fused_bwd ? "1" : h->fused_explicit ? "explicit" : "0") +
+         (h->fused_explicit ? std::string(" fx_wt=") + (h->fx_wt ? "1" : "0") : std::string()) +
+         " workspace=" + std::to_string(h->ws_bytes);
     if (needed)
         *needed = s.size() + 1;
     if (buf) {
@@ -1298,6 +1327,51 @@ d4r_status d4r_conv_backward_filter(d4r_conv_t h, const void *x, const void *dy,
     return ok();
 }
 
+namespace {
+
+// The page's data gradient (dcol = Wmat^T * G, then col2im) and filter
+// gradient (dW = G * col^T) of one layer from one pass over dy: the reshape
+// writes G (O x N, the batch folded into the columns) and the bias partial
+// sums; the data-gradient GEMM reads G row-contiguous, the filter-gradient
+// GEMM k-contiguous.  Results equal the separate calls' up to the order of
+// the f32 sums.
+d4r_status backward_explicit_fused(d4r_conv_t h, const void *x, const void *w, const void *dy, float *dx,
+                                   float *dw, float *db, int reuse_col, void *ws, hipStream_t s)
+{
+    const ConvGeom &g = h->g;
+    char *wsb = (char *)ws;
+    void *col = wsb;
+    void *G = wsb + h->off_g;
+    float *bias_part = db ? (float *)(wsb + h->off_bias) : nullptr;
+    float *dcol = (float *)(wsb + h->off_big);
+    float *partial = (float *)(wsb + h->off_big + align_up((size_t)g.Kc * g.N * sizeof(float)));
+    D4R_LAUNCH(step_grad_reshape(h, dy, G, bias_part, s), "grad reshape");
+    const void *a = w;
+    int am = OP_ROWS, lda = g.Kc;
+    if (h->fx_wt) {
+        // Wt[kc][o] = W[o][kc]
+        void *wt = wsb + h->off_wt;
+        D4R_LAUNCH(step_transpose(h, 1, g.O, g.Kc, w, wt, s, "dgrad_w"), "filter transpose");
+        a = wt;
+        am = OP_KC;
+        lda = g.O;
+    }
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_data, am, OP_ROWS, a, lda, G, g.N, g.Kc, g.N, g.O, EPI_ROWMAJOR, dcol,
+                        g.N, nullptr, 0, partial, s, "dgrad"),
+               "data-gradient GEMM");
+    D4R_LAUNCH(step_col2im(h, dcol, dx, s, "dgrad"), "col2im");
+    if (!reuse_col)
+        D4R_LAUNCH(step_im2col(h, x, col, s, "wgrad"), "im2col");
+    partial = (float *)(wsb + h->off_big);
+    const BiasSum bs{bias_part, db, g.O, grad_reshape_blocks(h->dt, g)};
+    D4R_LAUNCH(run_gemm(h->dt, h->bwd_filter, OP_KC, OP_KC, G, g.N, col, g.N, g.O, g.Kc, g.N, EPI_ROWMAJOR, dw,
+                        g.Kc, nullptr, 0, partial, s, "wgrad", nullptr, 0, 0, nullptr, 0, db ? &bs : nullptr),
+               "filter-gradient GEMM and bias gradient");
+    return ok();
+}
+
+}  // namespace
+
 d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const void *dy, float *dx, float *dw,
                              float *db, int reuse_col, void *ws, size_t ws_bytes, void *hip_stream)
 {
@@ -1315,6 +1389,8 @@ d4r_status d4r_conv_backward(d4r_conv_t h, const void *x, const void *w, const v
     D4R_TRY(check_tensor(dw, "dw"));
     D4R_TRY(check_vec(db, "db"));
     D4R_TRY(check_ws(h, ws, ws_bytes));
+    if (h->fused_explicit)
+        return backward_explicit_fused(h, x, w, dy, dx, dw, db, reuse_col, ws, (hipStream_t)hip_stream);
     if (!h->fused_bwd) {
         // the two calls in sequence (the data gradient leaves col intact)
         d4r_status st = d4r_conv_backward_data_implicit(h, w, dy, dx, ws, ws_bytes, hip_stream);

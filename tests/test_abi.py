@@ -361,6 +361,37 @@ def test_packed_filter_size_and_argument_errors(handle):
         assert e.value.status == code, args
 
 
+def test_describe_reports_the_explicit_one_pass_backward(monkeypatch):
+    # AlexNet conv1 f32 (explicit data gradient, 96 output channels): the
+    # combined backward reshapes dy once for both GEMMs, with G in the workspace
+    def plan():
+        h = d4r.d4r_conv_create(32, 3, 224, 224, 11, 11, 4, 2, 96, D4R_F32)
+        try:
+            return d4r.d4r_conv_describe(h), d4r.d4r_conv_workspace_size(h)
+        finally:
+            d4r.d4r_conv_destroy(h)
+    d, ws = plan()
+    assert d["dgrad_implicit"] == "explicit" and d["fused_backward"] == "explicit" and d["fx_wt"] == "1"
+    monkeypatch.setenv("D4R_FUSED_EXPLICIT", "0")
+    d0, ws0 = plan()
+    assert d0["fused_backward"] == "0" and "fx_wt" not in d0
+    # G (dy as a 96 x (32*55*55) f32 matrix) and the transposed filter
+    assert ws - ws0 >= 32 * 96 * 55 * 55 * 4 + 96 * 363 * 4
+    monkeypatch.setenv("D4R_FUSED_EXPLICIT", "1")
+    monkeypatch.setenv("D4R_FX_WT", "0")
+    d1, ws1 = plan()
+    assert d1["fused_backward"] == "explicit" and d1["fx_wt"] == "0" and ws1 <= ws - 96 * 363 * 4
+    # LeNet conv2 (16 output channels) and 16-bit layers keep the separate calls
+    monkeypatch.delenv("D4R_FUSED_EXPLICIT")
+    monkeypatch.delenv("D4R_FX_WT")
+    for args in [(64, 6, 12, 12, 5, 5, 1, 0, 16, D4R_F32), (32, 3, 224, 224, 11, 11, 4, 2, 96, D4R_BF16)]:
+        h = d4r.d4r_conv_create(*args)
+        try:
+            assert d4r.d4r_conv_describe(h)["fused_backward"] == "0", args
+        finally:
+            d4r.d4r_conv_destroy(h)
+
+
 def test_describe_reports_the_plan(monkeypatch):
     # AlexNet conv4 at batch 64: the multi-image im2col and col2im windows
     h = d4r.d4r_conv_create(64, 384, 13, 13, 3, 3, 1, 1, 384, D4R_F32)

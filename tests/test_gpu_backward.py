@@ -7,7 +7,14 @@ launch.  dx and dw must then equal the two separate calls bit for bit (same
 operands, same GEMMs); db differs from the separate path only in summation
 order, so it is checked against the oracle and for run-to-run equality.
 Shapes where the fused preparation does not apply must give exactly the
-separate calls.  Which path ran is read from the profile recorder.
+separate calls, except f32 layers with an explicit data gradient (dcol +
+col2im) and at least 32 output channels: there the combined call reshapes
+dy once into G for both GEMMs.  Its dx must still equal the separate call's
+bit for bit (same plan and kernel; the operands reach the MFMAs as the same
+fragments in the same k order); dw and db
+come from other kernels or another summation order, so they are checked
+against the oracle and for run-to-run equality.  Which path ran is read from
+the profile recorder and the plan description.
 """
 import numpy as np
 import pytest
@@ -72,6 +79,11 @@ def test_combined_backward(t, fused_dts, dt, reuse_col):
 
     names = _names(run)
     assert any(n.startswith("dy_prep_") for n in names) == (dt in fused_dts), names
+    explicit = pl.describe()["fused_backward"] == "explicit"
+    if explicit:
+        # one pass over dy: no transposed copy of it, no in-place bias pass
+        assert sum(n.startswith("grad_reshape") for n in names) == 1, names
+        assert not any("dgrad_dy" in n or n.startswith("bias_partial") for n in names), names
     dx, dw, db = out["c"]
     # the separate calls on the same inputs
     ref_dx = pl.backward_data_implicit(w, g)
@@ -80,8 +92,9 @@ def test_combined_backward(t, fused_dts, dt, reuse_col):
     ref_dw, ref_db = pl.backward_filter(x, g, reuse_col=reuse_col)
     torch.cuda.synchronize()
     assert torch.equal(dx, ref_dx)
-    assert torch.equal(dw, ref_dw)
-    if dt not in fused_dts:
+    if not explicit:
+        assert torch.equal(dw, ref_dw)
+    if dt not in fused_dts and not explicit:
         assert torch.equal(db, ref_db)
     # again: run-to-run identical
     if reuse_col:
@@ -135,3 +148,51 @@ def test_combined_backward_alexnet_conv4_full_size(dt):
     assert torch.equal(dw, ref_dw)
     err = rel_err(host(db), oracle.conv_backward_bias(ops["g"].exact))
     assert err < TOL[dt], err
+
+
+# f32 layers with an explicit data gradient: the combined call's one-pass
+# form (on by default from 32 output channels) against the separate calls,
+# with the switch forced either way and with the transposed-W variant
+EXPLICIT_SHAPES = [
+    (3, 3, 23, 23, 5, 5, 4, 2, 40),     # stride 4, 3 channels (AlexNet conv1-like)
+    (2, 16, 9, 9, 3, 3, 2, 1, 64),      # stride 2, too few channels for the phased form
+    (2, 5, 11, 9, 3, 2, 2, 1, 33),      # ragged: O, Kc and N off every tile
+    (1, 3, 12, 12, 4, 4, 3, 0, 8),      # few output channels: separate calls by default
+]
+
+
+@pytest.mark.parametrize("t", EXPLICIT_SHAPES, ids=[str(s) for s in EXPLICIT_SHAPES])
+@pytest.mark.parametrize("mode", ["default", "off", "on", "on_rows"])
+def test_combined_backward_explicit_one_pass(t, mode, monkeypatch):
+    env = {"off": {"D4R_FUSED_EXPLICIT": "0"}, "on": {"D4R_FUSED_EXPLICIT": "1"},
+           "on_rows": {"D4R_FUSED_EXPLICIT": "1", "D4R_FX_WT": "0"}}.get(mode, {})
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    sh = wl.ConvShape(*t)
+    ops = wl.random_conv(sh, "f32", seed=sum(t) + 17)
+    x, w, g = dev(ops["x"]), dev(ops["w"]), dev(ops["g"])
+    pl = _plan(sh, "f32")
+    d = pl.describe()
+    want = {"default": sh.outC >= 32, "off": False}.get(mode, True)
+    assert (d["fused_backward"] == "explicit") == want, d
+    assert d.get("fx_wt") == (None if not want else "0" if mode == "on_rows" else "1")
+    out = {}
+    names = _names(lambda: out.setdefault("c", pl.backward(x, w, g, reuse_col=False)))
+    assert any(n.startswith("grad_reshape") for n in names) == want, names
+    dx, dw, db = out["c"]
+    ref_dx = pl.backward_data_implicit(w, g)
+    torch.cuda.synchronize()
+    # W, row-contiguous or transposed, and dy, in place or reshaped, reach
+    # the MFMAs as the same fragments in the same k order
+    assert torch.equal(dx, ref_dx)
+    dx2, dw2, db2 = pl.backward(x, w, g, reuse_col=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dx2, dx) and torch.equal(dw2, dw) and torch.equal(db2, db)
+    X, Wt, G = ops["x"].exact, ops["w"].exact, ops["g"].exact
+    s, p = sh.stride, sh.padding
+    for k, got, ref in [("dx", dx, oracle.conv_backward_data(G, Wt, sh.x_shape(), s, p)),
+                        ("dw", dw, oracle.conv_backward_filter(X, G, sh.w_shape(), s, p)),
+                        ("db", db, oracle.conv_backward_bias(G))]:
+        err = rel_err(host(got), ref)
+        print(f"explicit one-pass backward {t} {mode} {k}: {err:.2e}", flush=True)
+        assert err < TOL["f32"], (k, err)
