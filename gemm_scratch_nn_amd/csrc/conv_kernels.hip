@@ -192,9 +192,12 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
     __syncthreads();
 
     // Output phase: a thread owns one 16-byte vector of columns, resolves its
-    // VW LDS offsets once, then walks every tap (u, v): one LDS read per
+    // VW LDS offsets once, then walks the taps (u, v): one LDS read per
     // element and one store per tap (the window in LDS already holds the
-    // padding zeros).
+    // padding zeros).  When the block has fewer vectors than threads, the
+    // threads form `groups` sets that share out the kernel rows u (set t
+    // takes u = t, t + groups, ...), so no thread sits idle through the taps
+    // (AlexNet conv1: 124 vectors per block of 256 threads).
     const int khw = g.kH * g.kW;
     const int n_start = (b0 * g.OH + i0) * g.OW;
     const int per_img = rows * g.OW;
@@ -202,7 +205,12 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
     const int n_al = n_start - (n_start % VW);
     const int nvec = (n_start + L - n_al + VW - 1) / VW;
     const long long row_stride = g.N;
-    for (int q = threadIdx.x; q < nvec; q += NT) {
+    const int span = nvec < NT ? nvec : NT;  // threads per set
+    const int groups = min(NT / span, g.kH);
+    const int grp = threadIdx.x / span;
+    if (grp >= groups)
+        return;  // no barrier follows
+    for (int q = threadIdx.x - grp * span; q < nvec; q += span) {
         const int n0 = n_al + q * VW;
         const int lo = n0 - n_start;
         int off[VW];
@@ -230,8 +238,8 @@ __global__ __launch_bounds__(NT) void im2col_lds_kernel(const T *__restrict__ x,
             }
         }
         const bool full = vec_store && lo >= 0 && lo + VW <= L;
-        T *dst = col + (long long)c * khw * row_stride + n0;
-        for (int u = 0; u < g.kH; ++u) {
+        for (int u = grp; u < g.kH; u += groups) {
+            T *dst = col + ((long long)c * khw + u * g.kW) * row_stride + n0;
             for (int v = 0; v < g.kW; ++v) {
                 const int tap = u * Wl + v;
                 typename Vec16<T>::type out;
@@ -404,18 +412,28 @@ __device__ __forceinline__ float col2im_one_general(const float *__restrict__ dc
     return acc;
 }
 
-// A thread computes four dx elements NT apart (so the lanes of a wavefront
-// stay on consecutive elements for every tap).  With the tap counts fixed
-// at compile time (TU, TV > 0) the loads of CPT elements are all issued
-// before the first add: loads are unconditional (offset 0 outside the tap
-// range, the value then dropped), and elements past the end repeat the
-// last one.  Each element adds its taps in the order u, then v ascending.
+// A thread computes four consecutive dx elements.  With the row width a
+// multiple of 4 and the stride 4 (AlexNet conv1), the lanes of a wavefront
+// then share one residue class of w for each of the four, so every tap's
+// load reads 64 consecutive floats of one dcol row (whole cache lines: the
+// form with elements NT apart read each line in 64-byte halves, 1.5x the
+// dcol bytes from HBM), and the four sums leave as one 16-byte store.
+// Blocks are renumbered so each XCD walks one contiguous range of dx: a
+// row segment of dcol that one block reads shares its cache lines with the
+// next output row, read by the block a few rows on, which round-robin
+// dispatch would put on another XCD (another L2).
+// With the tap counts fixed at compile time (TU, TV > 0) the loads of CPT
+// elements are all issued before the first add: loads are unconditional
+// (offset 0 outside the tap range, the value then dropped), and elements
+// past the end repeat the last one.  Each element adds its taps in the
+// order u, then v ascending.
 template <int TU, int TV>
 __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dcol,
                                                     float *__restrict__ dx, ConvGeom g, int total)
 {
     constexpr int CPT = (TU > 0 && TU * TV > 9) ? 2 : 4;
-    const int base = blockIdx.x * NT * 4 + threadIdx.x;
+    const int base = (xcd_tile(blockIdx.x, gridDim.x) * NT + threadIdx.x) * 4;
+    float res[4];
     if constexpr (TU > 0) {
 #pragma unroll
         for (int half = 0; half < 4 / CPT; ++half) {
@@ -424,7 +442,7 @@ __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dc
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
                 long long off[TU][TV];
-                col2im_taps<TU, TV>(g, min(base + (half * CPT + e) * NT, total - 1), off, ok[e]);
+                col2im_taps<TU, TV>(g, min(base + half * CPT + e, total - 1), off, ok[e]);
 #pragma unroll
                 for (int a = 0; a < TU; ++a)
 #pragma unroll
@@ -439,18 +457,22 @@ __global__ __launch_bounds__(NT) void col2im_kernel(const float *__restrict__ dc
 #pragma unroll
                     for (int q = 0; q < TV; ++q)
                         acc += ok[e][a][q] ? vals[e][a][q] : 0.0f;
-                const int idx = base + (half * CPT + e) * NT;
-                if (idx < total)
-                    dx[idx] = acc;
+                res[half * CPT + e] = acc;
             }
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = base + e * NT;
-            if (idx < total)
-                dx[idx] = col2im_one_general(dcol, g, idx);
-        }
+        for (int e = 0; e < 4; ++e)
+            res[e] = base + e < total ? col2im_one_general(dcol, g, base + e) : 0.0f;
+    }
+    // dx is 16-byte aligned, so a whole group of four is one aligned vector
+    if (base + 4 <= total) {
+        *(float4 *)(dx + base) = make_float4(res[0], res[1], res[2], res[3]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (base + e < total)
+                dx[base + e] = res[e];
     }
 }
 
@@ -1191,6 +1213,10 @@ Im2colPlan plan_im2col(int dt, const ConvGeom &g)
         BB = (BB + 1) / 2;
     while (RB > 1 && blocks(RB, BB) < min_blocks)
         RB = (RB + 1) / 2;
+    if (const char *e = getenv("D4R_IM2COL_RB")) {  // experiments: output rows per block
+        RB = std::max(1, std::min(atoi(e), g.OH));
+        BB = 1;
+    }
     int Rl = (RB - 1) * g.s + g.kH;
     while (BB > 1 && (long long)BB * Rl * Wl * es > 48 * 1024)
         BB = (BB + 1) / 2;
