@@ -731,7 +731,149 @@ __device__ __forceinline__ void dl_gemm_tile(const GemmParams &p, int m_blk, int
     store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, split);
 }
 
-template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false>
+// 16-bit tile with the fragment reads pipelined one 16-deep k step ahead.
+// In the plain loop every wavefront leaves the stage barrier with its
+// SIMD partner, and both read a step's fragments and wait for them before
+// that step's MFMAs, so the LDS latency is paid with the MFMA units idle
+// once per step.  Here step q reads the fragments of step q+1 (into the
+// other register set) before its own MFMAs, which use fragments read a step
+// earlier; the stage barrier moves into the last step, after which that
+// step reads step 0 of the next stage.  Scheduling hints keep that order
+// (the compiler otherwise moves each read next to its use).  The loads of
+// stage t+NBUF-1 go out in step 0 of stage t, interleaved with its MFMAs,
+// into the slot of stage t-1, whose last reads came before the barrier in
+// stage t-1's last step (which also waits for this wavefront's reads).
+// Stages past the end load stage 0 again into slots never used.
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI>
+__device__ __forceinline__ void dl_gemm_tile16p(const GemmParams &p, int m_blk, int n_blk, int kbeg, int kend,
+                                                int split)
+{
+    using E = DlElem<DTID>;
+    using T = typename E::T;
+    static_assert(DTID != DT_F32, "16-bit operands");
+    constexpr int NW = NWM * NWN;
+    constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32, BK = E::BK;
+    constexpr int NQ = BK / 16;
+    using OA = DlOperand<BM, NW, DTID>;
+    using OB = std::conditional_t<BI, DlImplNhwc<BN, NW, DTID>, DlOperand<BN, NW, DTID>>;
+    constexpr int STAGE = OA::BYTES + OB::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % NWM, wn = wave / NWM;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int nk = (kend - kbeg) / BK;
+
+    const T *A = (const T *)p.A;
+    const T *B = (const T *)p.B;
+    OA oa;
+    OB ob;
+    oa.setup(m_blk, p.M, p.lda, wave, lane);
+    if constexpr (BI)
+        ob.setup(n_blk, p.g, wave, lane);
+    else
+        ob.setup(n_blk, p.N, p.ldb, wave, lane);
+    auto issue = [&](int st) {
+        const int k0 = kbeg + (st < nk ? st : 0) * BK;
+        char *base = smem + (st % NBUF) * STAGE;
+        oa.issue(A, k0, base, wave);
+        if constexpr (BI)
+            ob.issue(B, (const T *)p.zero, k0, base + OA::BYTES, wave, p.g);
+        else
+            ob.issue(B, k0, base + OA::BYTES, wave);
+    };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    constexpr int LPS = OA::LD + OB::LD;
+    constexpr int VM = (NBUF - 2) * LPS;
+    static_assert(VM < 64, "vmcnt range");
+    constexpr int VMF = (VM & 15) | ((VM >> 4) << 14);
+    constexpr int WAIT_LANDED = VMF | (7 << 4) | (15 << 8);  // vmcnt(VM)
+    constexpr int WAIT_STAGE = VMF | (7 << 4);               // vmcnt(VM), lgkmcnt(0)
+    u32x4_t fa[2][TM], fb[2][TN];
+    auto read = [&](u32x4_t(&ra)[TM], u32x4_t(&rb)[TN], const char *slot, int q) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            ra[i] = dl_chunk(slot, (wm * TM + i) * 32 + l32, 2 * q + h);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            rb[j] = dl_chunk(slot + OA::BYTES, (wn * TN + j) * 32 + l32, 2 * q + h);
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < NBUF - 1; ++s0)
+        issue(s0);
+    __builtin_amdgcn_s_waitcnt(WAIT_LANDED);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read(fa[0], fb[0], smem, 0);
+    for (int t = 0; t < nk; ++t) {
+        const char *cur = smem + (t % NBUF) * STAGE;
+        const char *nxt = smem + ((t + 1) % NBUF) * STAGE;
+        auto step = [&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int RD = TM + TN, MF = TM * TN, H1 = MF / 2;
+            constexpr int LD_ = q == 0 ? LPS : 0;
+            constexpr int PER = (LD_ + H1 - 1) / H1;  // stage loads per MFMA of the first half
+            constexpr int C = q & 1, Nn = (q + 1) & 1;
+            // step 0 first issues the stage loads: an LDS-writing load waits
+            // for every LDS read in flight, which here are only this step's
+            // own fragments
+            if constexpr (q == 0)
+                issue(t + NBUF - 1);
+#pragma unroll
+            for (int x = 0; x < H1; ++x)
+                acc[x / TN][x % TN] = mfma16<DTID>(fa[C][x / TN], fb[C][x % TN], acc[x / TN][x % TN]);
+            if constexpr (q + 1 < NQ) {
+                read(fa[Nn], fb[Nn], cur, q + 1);
+            } else {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(WAIT_STAGE);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                read(fa[Nn], fb[Nn], nxt, 0);
+            }
+#pragma unroll
+            for (int x = H1; x < MF; ++x)
+                acc[x / TN][x % TN] = mfma16<DTID>(fa[C][x / TN], fb[C][x % TN], acc[x / TN][x % TN]);
+            // order (masks: 0x008 MFMA, 0x100 LDS read, 0x020 global load):
+            // first half of the MFMAs (with the stage loads between them in
+            // step 0), the next fragments, the second half
+            if constexpr (q + 1 < NQ) {
+#pragma unroll
+                for (int r = 0; r < H1; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (PER > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MF - (q + 1 < NQ ? H1 : 0), 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        static_assert(NQ == 4, "four k steps per stage");
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    }
+    // drain the loads of the stages past the end before the workgroup exits
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    store_acc<TM, TN>(p, acc, m_blk + wm * TM * 32, n_blk + wn * TN * 32, h, l32, split);
+}
+
+// PIPE (16-bit): dl_gemm_tile16p instead of dl_gemm_tile.
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool BI = false, bool PIPE = (DTID != DT_F32)>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
 {
     constexpr int BM = NWM * TM * 32, BN = NWN * TN * 32;
@@ -740,8 +882,12 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
     const int kbeg = wi.split * p.k_per_split;
     int tm, tn;
     tile_mn(wi.tile, mt, nt, p.group_m, tm, tn);
-    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, tm * BM, tn * BN, kbeg, min(p.K, kbeg + p.k_per_split),
-                                                   wi.split);
+    if constexpr (PIPE)
+        dl_gemm_tile16p<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, tm * BM, tn * BN, kbeg,
+                                                          min(p.K, kbeg + p.k_per_split), wi.split);
+    else
+        dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, BI>(p, tm * BM, tn * BN, kbeg, min(p.K, kbeg + p.k_per_split),
+                                                       wi.split);
 }
 
 // Every phase of a strided data gradient in one launch: work item w (after
@@ -804,42 +950,59 @@ inline bool dl_applies(int amode, int bmode, const GemmParams &p)
            p.k_per_split % kDlBK == 0;
 }
 
-template <int DTID, bool BI = false>
-hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
+template <int DTID, bool BI, bool PIPE>
+hipError_t launch_gemm16_dl_form(int cfg, const GemmParams &p, hipStream_t s)
 {
     TileShape ts = tile_shape(cfg);
     const int tiles = ((p.M + ts.bm - 1) / ts.bm) * ((p.N + ts.bn - 1) / ts.bn);
     const dim3 grid(tiles * p.splits), b8(512);
     switch (cfg) {
     case TILE_128x256:
-        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 2, kDlBuf, BI, PIPE>), grid, b8, 0, s, p);
         break;
     case TILE_256x128:
-        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 4, 2, 2, 2, kDlBuf, BI, PIPE>), grid, b8, 0, s, p);
         break;
     case TILE_256x256:
         // eight wavefronts of 128x64, a ring of two 64 KB stages (one
         // workgroup per CU): a third less operand traffic per flop than
         // 128x256 (4096^3 bf16 780 -> 977 TFLOP/s)
-        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 4, 2, 2, BI>), grid, b8, 0, s, p);
+        hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 4, 2, 2, BI, PIPE>), grid, b8, 0, s, p);
         break;
     case TILE_128x128: {
         const Dl128Form f = dl128_form();
         if (f.waves == 4)
             // four wavefronts, a ring of two stages (64 KB): two workgroups per CU
-            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 2, 2, 2, 2, BI>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 2, 2, 2, 2, BI, PIPE>), grid, dim3(256), 0, s, p);
         else if (f.nbuf == 2)
-            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 2, BI>), grid, b8, 0, s, p);
+            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 2, BI, PIPE>), grid, b8, 0, s, p);
         else if (f.nbuf == 3)
-            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 3, BI>), grid, b8, 0, s, p);
+            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 3, BI, PIPE>), grid, b8, 0, s, p);
         else
-            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 4, BI>), grid, b8, 0, s, p);
+            hipLaunchKernelGGL((gemm_dl_kernel<DTID, 2, 4, 2, 1, 4, BI, PIPE>), grid, b8, 0, s, p);
         break;
     }
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Loop of the 16-bit direct-to-LDS kernels: pipelined fragment reads
+// (dl_gemm_tile16p) unless D4R_DL16_PIPE=0 (the plain loop, kept for
+// comparison and tests).
+inline bool dl16_pipe()
+{
+    const char *e = getenv("D4R_DL16_PIPE");
+    return !(e && e[0] == '0');
+}
+
+template <int DTID, bool BI = false>
+hipError_t launch_gemm16_dl(int cfg, const GemmParams &p, hipStream_t s)
+{
+    if (dl16_pipe())
+        return launch_gemm16_dl_form<DTID, BI, true>(cfg, p, s);
+    return launch_gemm16_dl_form<DTID, BI, false>(cfg, p, s);
 }
 
 template <int DTID, bool A_KC, bool B_KC, bool VEC, bool IMPL = false, bool A_NC = false, bool B_NC = false>
