@@ -894,7 +894,8 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_kernel(GemmParams p)
 // the XCD renumbering) belongs to the last phase whose first item is <= w;
 // that phase's filter, K, sub-convolution geometry and dx placement replace
 // the launch-wide ones.  No split: the phases' K are short.
-template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF>
+// PIPE (16-bit): the pipelined tile loop (dl_gemm_tile16p).
+template <int DTID, int NWM, int NWN, int TM, int TN, int NBUF, bool PIPE = false>
 __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_phased_kernel(GemmParams p, PhaseArgs pa)
 {
     using T = typename DlElem<DTID>::T;
@@ -917,7 +918,19 @@ __global__ __launch_bounds__(NWM *NWN * 64) void gemm_dl_phased_kernel(GemmParam
     q.ph_w0 = it.w0;
     const int mt = (p.M + BM - 1) / BM;
     const int local = w - it.tile0;
-    dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, true>(q, (local % mt) * BM, (local / mt) * BN, 0, it.K, 0);
+    if constexpr (PIPE)
+        dl_gemm_tile16p<DTID, NWM, NWN, TM, TN, NBUF, true>(q, (local % mt) * BM, (local / mt) * BN, 0, it.K, 0);
+    else
+        dl_gemm_tile<DTID, NWM, NWN, TM, TN, NBUF, true>(q, (local % mt) * BM, (local / mt) * BN, 0, it.K, 0);
+}
+
+// Loop of the 16-bit direct-to-LDS kernels: pipelined fragment reads
+// (dl_gemm_tile16p) unless D4R_DL16_PIPE=0 (the plain loop, kept for
+// comparison and tests).
+inline bool dl16_pipe()
+{
+    const char *e = getenv("D4R_DL16_PIPE");
+    return !(e && e[0] == '0');
 }
 
 // All phases of a strided data gradient in one launch on 128x128 tiles:
@@ -930,10 +943,16 @@ hipError_t launch_gemm_dl_phased(const GemmParams &p, const PhaseArgs &pa, hipSt
 {
     if (pa.n < 1 || pa.n > kMaxPhases || pa.tiles < 1 || !p.zero)
         return hipErrorInvalidValue;
-    if constexpr (DTID == DT_F32)
+    if constexpr (DTID == DT_F32) {
         hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 2, 2, 2, 2>), dim3(pa.tiles), dim3(256), 0, s, p, pa);
-    else
-        hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 4, 2, 1, 4>), dim3(pa.tiles), dim3(512), 0, s, p, pa);
+    } else {
+        if (dl16_pipe())
+            hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 4, 2, 1, 4, true>), dim3(pa.tiles), dim3(512), 0, s,
+                               p, pa);
+        else
+            hipLaunchKernelGGL((gemm_dl_phased_kernel<DTID, 2, 4, 2, 1, 4, false>), dim3(pa.tiles), dim3(512), 0, s,
+                               p, pa);
+    }
     return hipGetLastError();
 }
 
@@ -986,15 +1005,6 @@ hipError_t launch_gemm16_dl_form(int cfg, const GemmParams &p, hipStream_t s)
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
-}
-
-// Loop of the 16-bit direct-to-LDS kernels: pipelined fragment reads
-// (dl_gemm_tile16p) unless D4R_DL16_PIPE=0 (the plain loop, kept for
-// comparison and tests).
-inline bool dl16_pipe()
-{
-    const char *e = getenv("D4R_DL16_PIPE");
-    return !(e && e[0] == '0');
 }
 
 template <int DTID, bool BI = false>

@@ -460,6 +460,37 @@ def test_dl128_forms(form, dt, monkeypatch):
     _check_whole(sh, dt, wl.conv_inputs(w, 1, dt, batch=3), f"c4/conv4/b3/{form}")
 
 
+# The 16-bit direct-to-LDS kernels' two loops (fragment reads pipelined one
+# k step ahead, the default; the plain loop with D4R_DL16_PIPE=0) on every
+# direct tile over ragged shapes (one stage, split K, rows and columns past
+# the matrix), on a conv3-5 layer (NHWC forward and data gradient, filter
+# gradient) and on the phased data gradient of strided layers.
+@pytest.mark.parametrize("pipe", ["1", "0"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_dl16_loop_forms(pipe, dt, monkeypatch):
+    monkeypatch.setenv("D4R_DL16_PIPE", pipe)
+    for tile in ["128x128", "128x256", "256x128", "256x256"]:
+        monkeypatch.setenv("D4R_GEMM_TILE", tile)
+        for (M, K, N) in [(300, 256, 333), (129, 64, 520), (200, 4096, 304), (513, 640, 257)]:
+            rng = np.random.default_rng(M + K + N + 41)
+            a = wl.quantize(rng.normal(size=(M, K)), dt)
+            b = wl.quantize(rng.normal(size=(N, K)), dt)
+            ref = oracle.gemm(a.exact, b.exact, M, K, N, 2)
+            C = d4r.gemm(dev(a), dev(b), M, K, N, 2)
+            torch.cuda.synchronize()
+            got = host(C)
+            assert rel_err(got, ref) < TOL[dt], (pipe, tile, M, K, N)
+            elementwise_bound(got, ref, oracle.gemm(np.abs(a.exact), np.abs(b.exact), M, K, N, 2), K,
+                              f"C pipe={pipe} {tile} {M}x{K}x{N}")
+    monkeypatch.delenv("D4R_GEMM_TILE")
+    w = wl.WORKLOADS["c4"]
+    sh = w.layers[2].shape.with_batch(3)
+    _check_whole(sh, dt, wl.conv_inputs(w, 2, dt, batch=3), f"c4/conv5/b3/pipe{pipe}")
+    for t in [(2, 64, 9, 11, 64, 3, 3, 2, 1), (1, 64, 12, 12, 64, 11, 11, 4, 2)]:
+        shp = _shape(t)
+        _check_dgrad_implicit(shp, dt, wl.random_conv(shp, dt, seed=sum(t) + 43), f"phased pipe={pipe}")
+
+
 # large k-contiguous products: the 256x256 tile, and grids of 16+ tiles each
 # way, which run in bands of 8 M tiles (ragged last band and tiles)
 @pytest.mark.parametrize("dt,M,K,N", [("f16", 2048, 2048, 2048), ("bf16", 2048, 2048, 2048),
