@@ -54,8 +54,9 @@ def parse_args():
     ap.add_argument("--forward", choices=("auto", "explicit", "implicit"), default="auto",
                     help="explicit: im2col + GEMM (col saved for the filter gradient); "
                          "implicit: implicit-GEMM forward, im2col redone in the filter gradient; "
-                         "auto: implicit for the 16-bit layers whose forward reads x as NHWC on the "
-                         "direct-to-LDS kernel, explicit elsewhere")
+                         "auto: implicit for the 1x1 layers (x read in place, no im2col) and for the "
+                         "16-bit layers whose forward reads x as NHWC on the direct-to-LDS kernel, "
+                         "explicit elsewhere")
     ap.add_argument("--dgrad", choices=("explicit", "implicit"), default="implicit",
                     help="implicit: implicit-GEMM data gradient, no dcol (stride-1 square-kernel "
                          "layers; others run explicit); explicit: the page's GEMM to dcol + col2im")
@@ -125,6 +126,14 @@ def recorded_traffic(kernel: str):
 
 def layer_flops(sh) -> float:
     return 3.0 * sh.gemm_flops()
+
+
+def forward_label(t: dict) -> str:
+    """How the step ran a layer's forward (the library's form for the implicit call)."""
+    if not t["implicit"]:
+        return "explicit (im2col + GEMM)"
+    return {"nhwc": "implicit (NHWC)", "pointwise": "pointwise (1x1: x read in place)",
+            "gathered": "implicit (gathered)"}.get(t["fwd_form"], "implicit")
 
 
 def cpu_baseline(wl, dtype: str, target_s: float) -> dict:
@@ -422,8 +431,10 @@ def bench_conv(args, key: str, dtype: str, steps: int, warmup: int, rotate: int,
             t["dx"] = torch.empty(sh.x_shape(), dtype=torch.float32, device=dev)
             t["dw"] = torch.empty(sh.w_shape(), dtype=torch.float32, device=dev)
             t["db"] = torch.empty((sh.outC,), dtype=torch.float32, device=dev)
+            t["fwd_form"] = d4r.d4r_conv_describe(pl.h)["fwd_implicit"]
             if args.forward == "auto":
-                t["implicit"] = dtype != "f32" and d4r.d4r_conv_describe(pl.h)["fwd_implicit"] == "nhwc"
+                # 1x1 layers read x in place (no im2col anywhere in the step)
+                t["implicit"] = t["fwd_form"] == "pointwise" or (dtype != "f32" and t["fwd_form"] == "nhwc")
             else:
                 t["implicit"] = args.forward == "implicit"
             out.append((layer, pl, t))
@@ -586,7 +597,7 @@ def bench_conv(args, key: str, dtype: str, steps: int, warmup: int, rotate: int,
                      "shape": f"{sh.batch}x{sh.inC}x{sh.inH}x{sh.inW} -> {sh.outC} {sh.kH}x{sh.kW} "
                               f"s{sh.stride} p{sh.padding}",
                      "ms": lms, "TFLOPs": ltf, "frac_mfma": ltf / peak,
-                     "forward": "implicit (NHWC)" if t["implicit"] else "explicit (im2col + GEMM)"}
+                     "forward": forward_label(t)}
             entry.update(gemm_summary(lbk, peak))
             entry["im2col"] = stage_of(lbk, "im2col")
             c2 = stage_of(lbk, "col2im")
