@@ -728,7 +728,9 @@ def mfma_reference(reps: int = 5) -> dict:
     on register-resident random operands, no loads) for each dtype, in
     TFLOP/s: what the GPU sustains at the clock it holds under a full MFMA
     load, the reference beside the GEMM rates (the roofline keeps the
-    published peak)."""
+    published peak).  Each launch runs several milliseconds, after two
+    warm-up launches: shorter ones (1-2 ms) read 10-15% low for fp32, the
+    clock still ramping."""
     import torch
 
     import gemm_scratch_nn_amd as d4r
@@ -736,9 +738,9 @@ def mfma_reference(reps: int = 5) -> dict:
     out = {"kernel": "d4r_mfma_ceiling: 1024 workgroups x 8 wavefronts, 4 x 2 accumulators of 32 x 32 each, "
                      "random operands (N(0,1)) read once"}
     blocks = 1024
-    for dt, code, tdt, per_lane, iters in (("f32", d4r.D4R_F32, torch.float32, 1, 800),
-                                           ("bf16", d4r.D4R_BF16, torch.bfloat16, 8, 1500),
-                                           ("f16", d4r.D4R_F16, torch.float16, 8, 1500)):
+    for dt, code, tdt, per_lane, iters in (("f32", d4r.D4R_F32, torch.float32, 1, 4000),
+                                           ("bf16", d4r.D4R_BF16, torch.bfloat16, 8, 6000),
+                                           ("f16", d4r.D4R_F16, torch.float16, 8, 6000)):
         src = torch.randn(6 * 64 * per_lane, generator=g).to(tdt).cuda()
         res = torch.empty(blocks * 8, dtype=torch.float32, device="cuda")
         for _ in range(2):
