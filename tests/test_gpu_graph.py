@@ -119,3 +119,43 @@ def test_graph_replay_combined_backward(key, li, dt, batch):
         torch.cuda.synchronize()
         for k in got:
             assert torch.equal(got[k], t[k]), (r, k)
+
+
+@pytest.mark.parametrize("key,li,dt,batch,implicit", [("c5", 1, "f16", 1, True), ("c4", 0, "bf16", 4, True),
+                                                      ("c5", 2, "f16", 1, False), ("c3", 0, "f32", 2, False)])
+def test_graph_replay_bench_step_forms(key, li, dt, batch, implicit):
+    # the step forms the bench times: the 1x1 in-place forward and the NHWC
+    # forward with the combined backward redoing im2col (implicit), and the
+    # explicit forward whose col the combined backward reuses (the phased
+    # data gradient on the stride-2 layer, the one-pass explicit backward on
+    # AlexNet conv1)
+    pl, t = _setup(key, li, dt, batch)
+
+    def step():
+        st = torch.cuda.current_stream().cuda_stream
+        if implicit:
+            d4r.d4r_conv_forward_implicit(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, st)
+            d4r.d4r_conv_backward(pl.h, t["x"], t["w"], t["g"], t["dx"], t["dw"], t["db"], 0, pl.ws, pl.ws_bytes,
+                                  st)
+        else:
+            d4r.d4r_conv_forward(pl.h, t["x"], t["w"], t["bias"], t["y"], pl.ws, pl.ws_bytes, st)
+            d4r.d4r_conv_backward(pl.h, None, t["w"], t["g"], t["dx"], t["dw"], t["db"], 1, pl.ws, pl.ws_bytes,
+                                  st)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        t["x"].mul_(-0.5 if r % 2 else 1.25)
+        t["g"].add_(0.125)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: t[k].clone() for k in ("y", "dx", "dw", "db")}
+        step()
+        torch.cuda.synchronize()
+        for k in got:
+            assert torch.equal(got[k], t[k]), (r, k)
